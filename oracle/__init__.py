@@ -1,0 +1,259 @@
+"""CPU oracle of the routed SwiGLU MoE forward (ctypes binding of moe_oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  The tests, the smoke check and the benchmark's
+cpu_baseline leg may import this package; the product package
+``swiglu_expert_mlp_amd`` never does, and shares no code with it.
+
+Every entry point takes and returns numpy arrays:
+  * bf16 data travels as uint16 bit patterns,
+  * MXFP8 data as uint8 E4M3 codes plus uint8 E8M0 scale bytes.
+
+Functions follow the method step by step (see the C source header for the
+pages and sections each one follows).  Error bits returned by the router,
+prepare and forward entry points use these values:
+  1 expert id outside [0, E) in a live token (the route is dropped),
+  2 duplicate expert id within a live token,
+  4 live count above capacity (clamped),
+  8 live count below zero (treated as zero).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+
+ERR_BAD_ID = 1
+ERR_DUP_ID = 2
+ERR_LIVE_HIGH = 4
+ERR_LIVE_NEG = 8
+
+
+def build(force: bool = False) -> str:
+    """Compile moe_oracle.c with gcc (plain -O2, no fast-math, no fp contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+             "-fno-fast-math", "-std=c11", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i64, i32, u32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
+        sig = {
+            "orc_bf16_bits": (ctypes.c_uint16, [ctypes.c_float]),
+            "orc_bf16_round_array": (None, [P, i64, P]),
+            "orc_e4m3_decode": (ctypes.c_double, [ctypes.c_uint8]),
+            "orc_e4m3_encode": (ctypes.c_uint8, [ctypes.c_double]),
+            "orc_e8m0_exponent": (ctypes.c_int, [ctypes.c_float]),
+            "orc_mx_quantize": (None, [P, i64, i64, P, P]),
+            "orc_mx_dequantize": (None, [P, P, i64, i64, P]),
+            "orc_route": (u32, [P, i64, i32, ctypes.c_int, ctypes.c_int, P, P]),
+            "orc_prepare": (u32, [P, P, i64, i32, ctypes.c_int, ctypes.c_int,
+                                  P, P, P, P, P, P, P]),
+            "orc_finalize": (None, [P, P, P, i32, ctypes.c_int, ctypes.c_int, P]),
+            "orc_weights_create": (P, [ctypes.c_int] * 5 + [P, P]),
+            "orc_weights_destroy": (None, [P]),
+            "orc_forward": (u32, [P, P, P, P, i64, i32, P, P, P]),
+            "orc_forward_tokens": (None, [P, P, P, P, P, i64, P]),
+            "orc_pack_bf16": (None, [ctypes.c_int] * 3 + [P, P, P]),
+            "orc_pack_mxfp8": (None, [ctypes.c_int] * 3 + [P, P, P]),
+            "orc_pack_bytes": (i64, [ctypes.c_int] * 4),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ---------------------------------------------------------------- formats
+
+def bf16_bits(v: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest even."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint16)
+    lib().orc_bf16_round_array(_p(v), v.size, _p(out))
+    return out
+
+
+def bf16_value(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> fp32 values (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def e4m3_decode(code: int) -> float:
+    return lib().orc_e4m3_decode(int(code))
+
+
+def e4m3_encode(v: float) -> int:
+    return lib().orc_e4m3_encode(float(v))
+
+
+def e8m0_exponent(amax: float) -> int:
+    return lib().orc_e8m0_exponent(float(amax))
+
+
+def mx_quantize(v: np.ndarray):
+    """[rows, cols] fp32 -> (codes uint8 [rows, cols], scales uint8 [rows, cols/32])."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    rows, cols = v.shape
+    assert cols % 32 == 0
+    codes = np.empty((rows, cols), dtype=np.uint8)
+    scales = np.empty((rows, cols // 32), dtype=np.uint8)
+    lib().orc_mx_quantize(_p(v), rows, cols, _p(codes), _p(scales))
+    return codes, scales
+
+
+def mx_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows, cols = codes.shape
+    out = np.empty((rows, cols), dtype=np.float64)
+    lib().orc_mx_dequantize(_p(codes), _p(scales), rows, cols, _p(out))
+    return out
+
+
+# ---------------------------------------------------------------- router / prepare
+
+def route(logits: np.ndarray, live: int, k: int):
+    """Softmax, top-k by logit (ties to lower id), renormalize, ids ascending.
+
+    Returns (ids int32 [T_cap, k], probs fp32 [T_cap, k], err).  Rows >= live
+    keep the fill value (-1 ids, NaN probs) to show they were not written.
+    """
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T_cap, E = logits.shape
+    ids = np.full((T_cap, k), -1, dtype=np.int32)
+    probs = np.full((T_cap, k), np.nan, dtype=np.float32)
+    err = lib().orc_route(_p(logits), T_cap, int(live), E, k, _p(ids), _p(probs))
+    return ids, probs, err
+
+
+def prepare(ids: np.ndarray, probs: np.ndarray, live: int, E: int):
+    """Canonical sort and stable expert permutation.  Returns a dict."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    probs = np.ascontiguousarray(probs, dtype=np.float32)
+    T_cap, k = ids.shape
+    n = T_cap * k + 1
+    sorted_ids = np.full(n, -7, dtype=np.int32)
+    sorted_probs = np.full(n, np.nan, dtype=np.float32)
+    counts = np.zeros(E, dtype=np.int32)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    perm_src = np.full(n, -7, dtype=np.int32)
+    dst = np.full(n, -7, dtype=np.int32)
+    T = np.zeros(1, dtype=np.int32)
+    err = lib().orc_prepare(_p(ids), _p(probs), T_cap, int(live), E, k, _p(sorted_ids),
+                            _p(sorted_probs), _p(counts), _p(offsets), _p(perm_src),
+                            _p(dst), _p(T))
+    T = int(T[0])
+    R = T * k
+    nrows = int(offsets[E])
+    return dict(T=T, err=err, sorted_ids=sorted_ids[:R].reshape(T, k),
+                sorted_probs=sorted_probs[:R].reshape(T, k), counts=counts,
+                offsets=offsets, perm_src=perm_src[:nrows], dst=dst[:R].reshape(T, k))
+
+
+def finalize(O: np.ndarray, dst: np.ndarray, sorted_probs: np.ndarray, H: int) -> np.ndarray:
+    O = np.ascontiguousarray(O, dtype=np.float32)
+    dst = np.ascontiguousarray(dst, dtype=np.int32)
+    sorted_probs = np.ascontiguousarray(sorted_probs, dtype=np.float32)
+    T, k = dst.shape
+    out = np.zeros((T, H), dtype=np.float32)
+    lib().orc_finalize(_p(O), _p(dst), _p(sorted_probs), T, k, H, _p(out))
+    return out
+
+
+# ---------------------------------------------------------------- forward
+
+class Model:
+    """Oracle weights: bf16 W1 [E, 2F, H] (gate rows first) and W2 [E, H, F].
+
+    precision: "bf16" or "mxfp8" (weights quantized per 32-block along K).
+    """
+
+    def __init__(self, E, H, F, k, w1_bits: np.ndarray, w2_bits: np.ndarray,
+                 precision: str = "bf16"):
+        assert precision in ("bf16", "mxfp8")
+        self.E, self.H, self.F, self.k = E, H, F, k
+        self.precision = precision
+        self._w1 = np.ascontiguousarray(w1_bits, dtype=np.uint16)
+        self._w2 = np.ascontiguousarray(w2_bits, dtype=np.uint16)
+        assert self._w1.size == E * 2 * F * H and self._w2.size == E * H * F
+        self._h = lib().orc_weights_create(E, H, F, k, int(precision == "mxfp8"),
+                                           _p(self._w1), _p(self._w2))
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            lib().orc_weights_destroy(h)
+            self._h = None
+
+    def forward(self, x_bits, ids, probs, live, want_rows: bool = False):
+        """Whole forward.  Returns (out [T_cap, H] fp32 with rows >= T left NaN, err,
+        extras) where extras holds O rows and FC2 operand rows when asked."""
+        x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        probs = np.ascontiguousarray(probs, dtype=np.float32)
+        T_cap = x_bits.shape[0]
+        out = np.full((T_cap, self.H), np.nan, dtype=np.float32)
+        extras = {}
+        O = Hr = None
+        if want_rows:
+            n = max(1, T_cap * self.k)
+            O = np.zeros((n, self.H), dtype=np.float32)
+            Hr = np.zeros((n, self.F), dtype=np.float32)
+        err = lib().orc_forward(self._h, _p(x_bits), _p(ids), _p(probs), T_cap, int(live),
+                                _p(out), _p(O), _p(Hr))
+        if want_rows:
+            extras = dict(O=O, H=Hr)
+        return out, err, extras
+
+    def forward_tokens(self, x_bits, ids, probs, tokens) -> np.ndarray:
+        """Naive per-token loop for the listed token indices: [len(tokens), H]."""
+        x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        probs = np.ascontiguousarray(probs, dtype=np.float32)
+        tokens = np.ascontiguousarray(tokens, dtype=np.int64)
+        out = np.empty((len(tokens), self.H), dtype=np.float32)
+        lib().orc_forward_tokens(self._h, _p(x_bits), _p(ids), _p(probs), _p(tokens),
+                                 len(tokens), _p(out))
+        return out
+
+
+def pack_bytes(E, H, F, precision="bf16") -> int:
+    return int(lib().orc_pack_bytes(E, H, F, int(precision == "mxfp8")))
+
+
+def pack(E, H, F, w1_bits, w2_bits, precision="bf16") -> np.ndarray:
+    """Kernel-weight buffer bytes in the documented layout (independent packer)."""
+    w1 = np.ascontiguousarray(w1_bits, dtype=np.uint16)
+    w2 = np.ascontiguousarray(w2_bits, dtype=np.uint16)
+    buf = np.zeros(pack_bytes(E, H, F, precision), dtype=np.uint8)
+    fn = lib().orc_pack_mxfp8 if precision == "mxfp8" else lib().orc_pack_bf16
+    fn(E, H, F, _p(w1), _p(w2), _p(buf))
+    return buf

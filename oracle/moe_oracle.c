@@ -1,0 +1,594 @@
+/*
+ * CPU oracle for the routed SwiGLU MoE forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the tests, the smoke check and the benchmark's
+ * cpu_baseline leg use it.  It shares no code, header or table with the HIP
+ * library; it is written from the method's description, one step at a time,
+ * in the order the sources give them.
+ *
+ * Sources (web pages):
+ *   [MEGA]  Megatron-LM PR #7830, "flashinfer_mega" backend, section
+ *           "1. Mega backend for generation" (canonical expert-id sort before
+ *           the combine; gate/up interleaved in blocks of 32, K-major).
+ *   [VALUE] Megatron-LM PR #7798, moe_training_matches_inference, sections
+ *           "Background" (activation and FC2-input quantization fused into
+ *           the FC1 epilogue, probabilities applied after FC2) and
+ *           "What is changed" (finalize = fp32 fused multiply-adds of
+ *           probability and row, from zero, in the listed order).
+ *   [BOUND] Megatron-LM PR #8367, "bound the FlashInfer MoE expert kernels by
+ *           token count", section "Problem" (device-side live token count;
+ *           fp32 finalize output without a bf16 downcast).
+ *   [API]   Megatron-Core API docs, core.transformer.moe.
+ *           training_matches_inference, `_route` ([tokens, topk] probs and
+ *           ids; the finalize sums routes in the order listed).
+ *   [CUDNN] cudnn-frontend PR #448, MoeEp class docstring (rows grouped by
+ *           expert ascending, token-major route order inside an expert) and
+ *           the MXFP8 32-element scale block.
+ *
+ * Precision.  Where the sources fix a precision (the fp32 finalize) the
+ * oracle uses it exactly (fmaf).  Where they fix only "fp32 accumulate"
+ * without an order (the expert GEMMs) the oracle computes the exact dot
+ * product in fp64 and rounds once to fp32: the plain definition that any
+ * fp32 accumulation order approximates.  Values that decide an integer
+ * (a bf16 rounding, an E4M3 code, an E8M0 exponent) are decided from an
+ * fp32 value, the kernel's precision.  The router softmax (precision not
+ * fixed) is fp64, rounded to fp32 at the end.
+ *
+ * Every function here is pinned by tests under tests/ against something
+ * other than itself (library casts, brute force, closed forms, dense fp64
+ * matmuls, hand-derived cases); see the test files for which pin covers which
+ * function.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_ERR_BAD_ID 1u      /* an expert id outside [0, E) in a live token */
+#define ORC_ERR_DUP_ID 2u      /* the same expert id twice in one live token  */
+#define ORC_ERR_LIVE_HIGH 4u   /* live count above capacity: clamped           */
+#define ORC_ERR_LIVE_NEG 8u    /* live count below zero: treated as zero       */
+
+/* ------------------------------------------------------------------------ */
+/* Number formats                                                            */
+/* ------------------------------------------------------------------------ */
+
+static uint32_t f32_bits(float v) { uint32_t u; memcpy(&u, &v, 4); return u; }
+static float bits_f32(uint32_t u) { float v; memcpy(&v, &u, 4); return v; }
+
+/* bfloat16 = the top 16 bits of an fp32.  Round to nearest, ties to even
+ * (RNE), written as: the kept part is rounded up when the dropped 16 bits
+ * exceed half, or equal half and the kept part is odd.  NaN stays NaN. */
+uint16_t orc_bf16_bits(float v)
+{
+    uint32_t u = f32_bits(v);
+    if ((u & 0x7fffffffu) > 0x7f800000u)           /* NaN: keep sign, quiet */
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t keep = u >> 16;
+    uint32_t drop = u & 0xffffu;
+    if (drop > 0x8000u || (drop == 0x8000u && (keep & 1u)))
+        keep += 1u;                                  /* may carry into inf */
+    return (uint16_t)keep;
+}
+
+float orc_bf16_value(uint16_t b) { return bits_f32((uint32_t)b << 16); }
+
+float orc_bf16_round(float v) { return orc_bf16_value(orc_bf16_bits(v)); }
+
+void orc_bf16_round_array(const float* in, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_bits(in[i]);
+}
+
+/* E4M3FN (OCP 8-bit float, "fn" variant): 1 sign bit, 4 exponent bits with
+ * bias 7, 3 mantissa bits; no infinities; S.1111.111 is NaN; largest finite
+ * value 1.75 * 2^8 = 448; subnormals 0.mmm * 2^-6, the smallest 2^-9.
+ * Decoding follows that definition. */
+double orc_e4m3_decode(uint8_t c)
+{
+    int sign = (c >> 7) & 1;
+    int ef = (c >> 3) & 15;
+    int m = c & 7;
+    double mag;
+    if (ef == 15 && m == 7) return NAN;
+    if (ef == 0) mag = ldexp((double)m, -9);           /* 0.mmm * 2^-6 */
+    else mag = ldexp(8.0 + m, ef - 7 - 3);              /* 1.mmm * 2^(e-7) */
+    return sign ? -mag : mag;
+}
+
+/* Encode a value whose magnitude is at most 448 (the caller's scale choice
+ * guarantees it) to the nearest E4M3FN value, ties to the even code.  The
+ * binade of |v| is found with frexp (exact); |v| is then expressed in units
+ * of the binade's code spacing (an exact power-of-two scaling) and rounded
+ * to an integer with nearbyint in the default round-to-nearest-even mode. */
+uint8_t orc_e4m3_encode(double v)
+{
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs(v);
+    if (isnan(v)) return (uint8_t)(sign | 0x7f);
+    if (a == 0.0) return sign;
+    int ex;
+    frexp(a, &ex);                 /* a = f * 2^ex, f in [0.5, 1) => 2^(ex-1) <= a */
+    int e = ex - 1;                /* unbiased exponent of the leading bit */
+    if (e < -6) {                  /* subnormal range: spacing 2^-9 */
+        double q = nearbyint(ldexp(a, 9));          /* 0..8 */
+        return (uint8_t)(sign | (uint8_t)q);        /* q == 8 is the smallest normal */
+    }
+    double q = nearbyint(ldexp(a, 3 - e));          /* in [8, 16] */
+    if (q == 16.0) { q = 8.0; e += 1; }
+    /* |v| <= 448 keeps e <= 8 and the code below 0x7f. */
+    return (uint8_t)(sign | (uint8_t)(((e + 7) << 3) | ((int)q - 8)));
+}
+
+/* E8M0 block exponent for one 32-element block: the smallest integer e in
+ * [-127, 127] with amax <= 448 * 2^e (the power-of-two ceiling of
+ * amax / 448).  amax == 0 gives -127.  Found by an exact search: the
+ * comparisons are exact in fp64 because amax is an fp32 value and 448 * 2^e
+ * is a power-of-two multiple of 448. */
+int orc_e8m0_exponent(float amax)
+{
+    if (!(amax > 0.0f)) return -127;
+    int ex;
+    frexp((double)amax, &ex);
+    int e = ex - 10;                                /* below the answer */
+    while (!((double)amax <= ldexp(448.0, e))) e += 1;
+    while (e > -127 && (double)amax <= ldexp(448.0, e - 1)) e -= 1;
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e;
+}
+
+/* MXFP8 quantization of a [rows][cols] fp32 matrix along cols, one E8M0
+ * scale per 32 consecutive elements: scale byte = e + 127, code =
+ * E4M3(v / 2^e).  cols must be a multiple of 32. */
+void orc_mx_quantize(const float* v, int64_t rows, int64_t cols, uint8_t* codes,
+                     uint8_t* scales)
+{
+    int64_t nb = cols / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const float* blk = v + r * cols + b * 32;
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i) {
+                float a = fabsf(blk[i]);
+                if (a > amax) amax = a;
+            }
+            int e = orc_e8m0_exponent(amax);
+            scales[r * nb + b] = (uint8_t)(e + 127);
+            for (int i = 0; i < 32; ++i)
+                codes[r * cols + b * 32 + i] = orc_e4m3_encode(ldexp((double)blk[i], -e));
+        }
+    }
+}
+
+/* Value of an MXFP8 element: E4M3 value times 2^(scale - 127). */
+void orc_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                       int64_t cols, double* out)
+{
+    int64_t nb = cols / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            out[r * cols + c] = ldexp(orc_e4m3_decode(codes[r * cols + c]),
+                                      (int)scales[r * nb + c / 32] - 127);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Router ([API] `_route`; softmax, top-k, renormalize)                      */
+/* ------------------------------------------------------------------------ */
+
+static int32_t clamp_live(int32_t live, int64_t T_cap, uint32_t* err)
+{
+    if (live < 0) { *err |= ORC_ERR_LIVE_NEG; return 0; }
+    if ((int64_t)live > T_cap) { *err |= ORC_ERR_LIVE_HIGH; return (int32_t)T_cap; }
+    return live;
+}
+
+/* For each live token: softmax over the E logits, select the k experts with
+ * the largest logits (ties to the lower id; selecting on the logits is the
+ * same as selecting on the probabilities, which softmax orders the same way,
+ * without ties that rounding could create), renormalize the selected
+ * probabilities to sum to one, and emit them with ids ascending.  Softmax
+ * and renormalization are fp64; the probabilities are rounded to fp32.
+ * Rows at or beyond the live count are not written.  Returns error bits. */
+uint32_t orc_route(const float* logits, int64_t T_cap, int32_t live, int E, int k,
+                   int32_t* ids, float* probs)
+{
+    uint32_t err = 0;
+    int32_t T = clamp_live(live, T_cap, &err);
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const float* l = logits + t * E;
+        double m = -INFINITY;
+        for (int e = 0; e < E; ++e) if ((double)l[e] > m) m = l[e];
+        double* p = (double*)malloc(sizeof(double) * E);
+        char* taken = (char*)calloc(E, 1);
+        double S = 0.0;
+        for (int e = 0; e < E; ++e) { p[e] = exp((double)l[e] - m); S += p[e]; }
+        for (int e = 0; e < E; ++e) p[e] /= S;
+        int sel[64];
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                if (best < 0 || l[e] > l[best]) best = e;   /* strict: ties keep the lower id */
+            }
+            taken[best] = 1;
+            sel[j] = best;
+        }
+        /* ascending id order */
+        for (int a = 1; a < k; ++a)
+            for (int b = a; b > 0 && sel[b - 1] > sel[b]; --b) {
+                int tmp = sel[b]; sel[b] = sel[b - 1]; sel[b - 1] = tmp;
+            }
+        double Sk = 0.0;
+        for (int j = 0; j < k; ++j) Sk += p[sel[j]];
+        for (int j = 0; j < k; ++j) {
+            ids[t * k + j] = sel[j];
+            probs[t * k + j] = (float)(p[sel[j]] / Sk);
+        }
+        free(p);
+        free(taken);
+    }
+    return err;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Permutation ([MEGA] canonical order; [CUDNN] row grouping)                */
+/* ------------------------------------------------------------------------ */
+
+/* Per live token, sort its k (id, prob) pairs by id ascending; equal ids
+ * (a contract violation) keep their listed order.  Then a stable counting
+ * sort of the routes r = t*k + j by expert: counts, exclusive offsets,
+ * position of route r = offsets[e_r] + number of earlier routes (in r order)
+ * to the same expert.  perm_src[pos] = r, dst[r] = pos.  A route whose id is
+ * outside [0, E) is dropped: dst = -1, not counted.  Outputs beyond the
+ * live routes are not written.  Returns error bits. */
+uint32_t orc_prepare(const int32_t* ids, const float* probs, int64_t T_cap, int32_t live,
+                     int E, int k, int32_t* sorted_ids, float* sorted_probs,
+                     int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* dst,
+                     int32_t* T_out)
+{
+    uint32_t err = 0;
+    int32_t T = clamp_live(live, T_cap, &err);
+    *T_out = T;
+    for (int64_t t = 0; t < T; ++t) {
+        int32_t id[64];
+        float p[64];
+        for (int j = 0; j < k; ++j) { id[j] = ids[t * k + j]; p[j] = probs[t * k + j]; }
+        /* insertion sort: stable */
+        for (int a = 1; a < k; ++a)
+            for (int b = a; b > 0 && id[b - 1] > id[b]; --b) {
+                int32_t ti = id[b]; id[b] = id[b - 1]; id[b - 1] = ti;
+                float tp = p[b]; p[b] = p[b - 1]; p[b - 1] = tp;
+            }
+        for (int j = 0; j < k; ++j) {
+            if (id[j] < 0 || id[j] >= E) err |= ORC_ERR_BAD_ID;
+            if (j > 0 && id[j] == id[j - 1]) err |= ORC_ERR_DUP_ID;
+            sorted_ids[t * k + j] = id[j];
+            sorted_probs[t * k + j] = p[j];
+        }
+    }
+    for (int e = 0; e < E; ++e) counts[e] = 0;
+    int64_t R = (int64_t)T * k;
+    for (int64_t r = 0; r < R; ++r) {
+        int32_t e = sorted_ids[r];
+        if (e >= 0 && e < E) counts[e] += 1;
+    }
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    int32_t* fill = (int32_t*)calloc((size_t)(E > 0 ? E : 1), sizeof(int32_t));
+    for (int64_t r = 0; r < R; ++r) {
+        int32_t e = sorted_ids[r];
+        if (e < 0 || e >= E) { dst[r] = -1; continue; }
+        int32_t pos = offsets[e] + fill[e]++;
+        perm_src[pos] = (int32_t)r;
+        dst[r] = pos;
+    }
+    free(fill);
+    return err;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Expert MLP and finalize                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* Exact dot product of two length-n rows, accumulated in fp64 and rounded
+ * once to fp32.  bf16 x bf16 and MXFP8 x MXFP8 products are exact in fp64. */
+static float dot_f32(const double* a, const double* b, int64_t n)
+{
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i) s += a[i] * b[i];
+    return (float)s;
+}
+
+/* SwiGLU of one (gate, up) pair, in fp64 from the fp32 accumulators, rounded
+ * to fp32: silu(g) * u = g / (1 + exp(-g)) * u.  No clamp ([MEGA]: SwiGLU
+ * only, no tanh clamp). */
+static float swiglu_f32(float g, float u)
+{
+    double gd = g;
+    return (float)(gd / (1.0 + exp(-gd)) * (double)u);
+}
+
+/* Operand storage of the oracle: every operand as exact fp64 values. */
+typedef struct {
+    int E, H, F, k;
+    int mx;                 /* 0: bf16 path, 1: MXFP8 path */
+    const double* w1;       /* [E][2F][H] operand values (gate rows 0..F-1, up rows F..2F-1) */
+    const double* w2;       /* [E][H][F] */
+} orc_model;
+
+/* The expert MLP of one routed row: FC1 gate/up from the operand row xr
+ * (length H), SwiGLU, the FC2-input rounding (bf16, or MXFP8 per 32-block),
+ * then FC2 into o (length H, fp32).  Scratch a (F doubles) and hbuf (F). */
+static void expert_row(const orc_model* m, int e, const double* xr, float* o,
+                       float* a32, double* hrow)
+{
+    const int64_t H = m->H, F = m->F;
+    const double* W1 = m->w1 + (int64_t)e * 2 * F * H;
+    const double* W2 = m->w2 + (int64_t)e * H * F;
+    for (int64_t n = 0; n < F; ++n) {
+        float g = dot_f32(xr, W1 + n * H, H);
+        float u = dot_f32(xr, W1 + (F + n) * H, H);
+        a32[n] = swiglu_f32(g, u);
+    }
+    if (!m->mx) {
+        for (int64_t n = 0; n < F; ++n) hrow[n] = orc_bf16_round(a32[n]);
+    } else {
+        for (int64_t b = 0; b < F / 32; ++b) {
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i) {
+                float a = fabsf(a32[b * 32 + i]);
+                if (a > amax) amax = a;
+            }
+            int ex = orc_e8m0_exponent(amax);
+            for (int i = 0; i < 32; ++i) {
+                uint8_t c = orc_e4m3_encode(ldexp((double)a32[b * 32 + i], -ex));
+                hrow[b * 32 + i] = ldexp(orc_e4m3_decode(c), ex);
+            }
+        }
+    }
+    for (int64_t mo = 0; mo < H; ++mo) o[mo] = dot_f32(hrow, W2 + mo * F, F);
+}
+
+/* Finalize ([VALUE] "What is changed"; [BOUND] "Problem"): for each live
+ * token, acc = +0.0f, then for its routes in canonical order
+ * acc = fmaf(p_j, O[dst[t*k+j]][m], acc); out[t][m] = acc in fp32.  A
+ * dropped route (dst < 0) adds nothing.  Rows >= T are not written. */
+void orc_finalize(const float* O, const int32_t* dst, const float* sorted_probs,
+                  int32_t T, int k, int H, float* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t mo = 0; mo < H; ++mo) {
+            float acc = 0.0f;
+            for (int j = 0; j < k; ++j) {
+                int32_t d = dst[t * k + j];
+                if (d < 0) continue;
+                acc = fmaf(sorted_probs[t * k + j], O[(int64_t)d * H + mo], acc);
+            }
+            out[t * H + mo] = acc;
+        }
+    }
+}
+
+/* Operand values of x for the live tokens: bf16 values, or the MXFP8
+ * quantization of those bf16 values (per token, per 32-block of H). */
+static double* x_operands(const uint16_t* x, int64_t T, int H, int mx)
+{
+    double* xo = (double*)malloc(sizeof(double) * T * H);
+    if (!mx) {
+        for (int64_t i = 0; i < T * H; ++i) xo[i] = orc_bf16_value(x[i]);
+    } else {
+        float* xf = (float*)malloc(sizeof(float) * T * H);
+        uint8_t* c = (uint8_t*)malloc(T * H);
+        uint8_t* s = (uint8_t*)malloc(T * (H / 32));
+        for (int64_t i = 0; i < T * H; ++i) xf[i] = orc_bf16_value(x[i]);
+        orc_mx_quantize(xf, T, H, c, s);
+        orc_mx_dequantize(c, s, T, H, xo);
+        free(xf); free(c); free(s);
+    }
+    return xo;
+}
+
+/* Weight operand values: bf16 values, or the MXFP8 quantization of the bf16
+ * values along K (H for W1 rows, F for W2 rows). */
+static double* w_operands(const uint16_t* w, int64_t rows, int64_t cols, int mx)
+{
+    double* wo = (double*)malloc(sizeof(double) * rows * cols);
+    if (!mx) {
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < rows * cols; ++i) wo[i] = orc_bf16_value(w[i]);
+    } else {
+        float* wf = (float*)malloc(sizeof(float) * rows * cols);
+        uint8_t* c = (uint8_t*)malloc(rows * cols);
+        uint8_t* s = (uint8_t*)malloc(rows * (cols / 32));
+        for (int64_t i = 0; i < rows * cols; ++i) wf[i] = orc_bf16_value(w[i]);
+        orc_mx_quantize(wf, rows, cols, c, s);
+        orc_mx_dequantize(c, s, rows, cols, wo);
+        free(wf); free(c); free(s);
+    }
+    return wo;
+}
+
+/* Opaque prepared weights, so that repeated oracle calls on the same model
+ * (sampled tokens, timing) do not rebuild the operand values. */
+typedef struct {
+    orc_model m;
+    double* w1;
+    double* w2;
+} orc_weights;
+
+void* orc_weights_create(int E, int H, int F, int k, int mx, const uint16_t* w1,
+                         const uint16_t* w2)
+{
+    orc_weights* w = (orc_weights*)calloc(1, sizeof(orc_weights));
+    w->w1 = w_operands(w1, (int64_t)E * 2 * F, H, mx);
+    w->w2 = w_operands(w2, (int64_t)E * H, F, mx);
+    w->m.E = E; w->m.H = H; w->m.F = F; w->m.k = k; w->m.mx = mx;
+    w->m.w1 = w->w1; w->m.w2 = w->w2;
+    return w;
+}
+
+void orc_weights_destroy(void* p)
+{
+    orc_weights* w = (orc_weights*)p;
+    if (!w) return;
+    free(w->w1); free(w->w2); free(w);
+}
+
+/* The whole forward, step by step: canonical sort and permutation
+ * (orc_prepare), the expert MLP of every permuted row, in permuted order,
+ * into O rows, then the finalize.  Optional outputs: O_out [T*k][H] fp32
+ * (permuted order) and H_out [T*k][F] fp32 (the FC2 operand values).
+ * Returns error bits. */
+uint32_t orc_forward(void* wp, const uint16_t* x, const int32_t* ids, const float* probs,
+                     int64_t T_cap, int32_t live, float* out, float* O_out, float* H_out)
+{
+    orc_weights* w = (orc_weights*)wp;
+    const orc_model* m = &w->m;
+    const int E = m->E, H = m->H, F = m->F, k = m->k;
+    int32_t T;
+    int32_t* sorted_ids = (int32_t*)malloc(sizeof(int32_t) * (T_cap * k + 1));
+    float* sorted_probs = (float*)malloc(sizeof(float) * (T_cap * k + 1));
+    int32_t* counts = (int32_t*)malloc(sizeof(int32_t) * E);
+    int32_t* offsets = (int32_t*)malloc(sizeof(int32_t) * (E + 1));
+    int32_t* perm_src = (int32_t*)malloc(sizeof(int32_t) * (T_cap * k + 1));
+    int32_t* dst = (int32_t*)malloc(sizeof(int32_t) * (T_cap * k + 1));
+    uint32_t err = orc_prepare(ids, probs, T_cap, live, E, k, sorted_ids, sorted_probs,
+                               counts, offsets, perm_src, dst, &T);
+    int64_t nrows = offsets[E];
+    double* xo = x_operands(x, T, H, m->mx);
+    float* O = (float*)malloc(sizeof(float) * (nrows * H + 1));
+#pragma omp parallel
+    {
+        float* a32 = (float*)malloc(sizeof(float) * F);
+        double* hrow = (double*)malloc(sizeof(double) * F);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < nrows; ++i) {
+            int32_t r = perm_src[i];
+            int32_t t = r / k;
+            int32_t e = sorted_ids[r];
+            expert_row(m, e, xo + (int64_t)t * H, O + i * H, a32, hrow);
+            if (H_out)
+                for (int64_t n = 0; n < F; ++n) H_out[i * F + n] = (float)hrow[n];
+        }
+        free(a32); free(hrow);
+    }
+    orc_finalize(O, dst, sorted_probs, T, k, H, out);
+    if (O_out) memcpy(O_out, O, sizeof(float) * nrows * H);
+    free(O); free(xo);
+    free(sorted_ids); free(sorted_probs); free(counts); free(offsets); free(perm_src); free(dst);
+    return err;
+}
+
+/* The naive per-token loop (no permutation): for each listed token, sort its
+ * routes by id, run each route's expert MLP on the token's own row, and sum
+ * the rows with the same fp32 fma chain.  out_rows is [n_tok][H].  Used to
+ * pin the permutation bookkeeping of orc_forward, and to check sampled
+ * tokens of large launches one by one. */
+void orc_forward_tokens(void* wp, const uint16_t* x, const int32_t* ids, const float* probs,
+                        const int64_t* tokens, int64_t n_tok, float* out_rows)
+{
+    orc_weights* w = (orc_weights*)wp;
+    const orc_model* m = &w->m;
+    const int E = m->E, H = m->H, F = m->F, k = m->k;
+#pragma omp parallel
+    {
+        float* a32 = (float*)malloc(sizeof(float) * F);
+        double* hrow = (double*)malloc(sizeof(double) * F);
+        float* o = (float*)malloc(sizeof(float) * (int64_t)k * H);
+        double* xr = (double*)malloc(sizeof(double) * H);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t q = 0; q < n_tok; ++q) {
+            int64_t t = tokens[q];
+            double* xo = x_operands(x + t * H, 1, H, m->mx);
+            memcpy(xr, xo, sizeof(double) * H);
+            free(xo);
+            int32_t id[64];
+            float p[64];
+            for (int j = 0; j < k; ++j) { id[j] = ids[t * k + j]; p[j] = probs[t * k + j]; }
+            for (int a = 1; a < k; ++a)
+                for (int b = a; b > 0 && id[b - 1] > id[b]; --b) {
+                    int32_t ti = id[b]; id[b] = id[b - 1]; id[b - 1] = ti;
+                    float tp = p[b]; p[b] = p[b - 1]; p[b - 1] = tp;
+                }
+            for (int j = 0; j < k; ++j)
+                if (id[j] >= 0 && id[j] < E) expert_row(m, id[j], xr, o + (int64_t)j * H, a32, hrow);
+            for (int64_t mo = 0; mo < H; ++mo) {
+                float acc = 0.0f;
+                for (int j = 0; j < k; ++j)
+                    if (id[j] >= 0 && id[j] < E) acc = fmaf(p[j], o[(int64_t)j * H + mo], acc);
+                out_rows[q * H + mo] = acc;
+            }
+        }
+        free(a32); free(hrow); free(o); free(xr);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Kernel-weight buffer layout ([MEGA]: gate/up interleaved in blocks of 32, */
+/* K-major)                                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* Row order of the packed FC1 weight of one expert: packed row 64*b + i is
+ * gate row 32*b + i for i < 32 and up row F + 32*b + (i - 32) for i >= 32.
+ * Rows stay K(H)-contiguous.  FC2 rows ([H][F], already K(F)-contiguous)
+ * keep their order. */
+static int64_t fc1_logical_row(int64_t packed, int64_t F)
+{
+    int64_t b = packed / 64, i = packed % 64;
+    return i < 32 ? 32 * b + i : F + 32 * b + (i - 32);
+}
+
+/* bf16 buffer: [E][2F][H] packed FC1 rows, then [E][H][F] FC2 rows, both
+ * bf16 bit patterns. */
+void orc_pack_bf16(int E, int H, int F, const uint16_t* w1, const uint16_t* w2, uint8_t* kbuf)
+{
+    uint16_t* p1 = (uint16_t*)kbuf;
+    uint16_t* p2 = p1 + (int64_t)E * 2 * F * H;
+    for (int64_t e = 0; e < E; ++e)
+        for (int64_t pr = 0; pr < 2 * (int64_t)F; ++pr)
+            memcpy(p1 + (e * 2 * F + pr) * H, w1 + (e * 2 * F + fc1_logical_row(pr, F)) * H,
+                   sizeof(uint16_t) * H);
+    memcpy(p2, w2, sizeof(uint16_t) * (size_t)E * H * F);
+}
+
+/* MXFP8 buffer: FC1 codes [E][2F][H] (packed row order), FC2 codes
+ * [E][H][F], FC1 scales [E][2F][H/32] (packed row order), FC2 scales
+ * [E][H][F/32].  Each section starts at a multiple of 256 bytes. */
+static int64_t up256(int64_t v) { return (v + 255) / 256 * 256; }
+
+void orc_pack_mxfp8(int E, int H, int F, const uint16_t* w1, const uint16_t* w2, uint8_t* kbuf)
+{
+    int64_t n1 = (int64_t)E * 2 * F * H, n2 = (int64_t)E * H * F;
+    uint8_t* c1 = kbuf;
+    uint8_t* c2 = c1 + up256(n1);
+    uint8_t* s1 = c2 + up256(n2);
+    uint8_t* s2 = s1 + up256(n1 / 32);
+    float* f1 = (float*)malloc(sizeof(float) * n1);
+    float* f2 = (float*)malloc(sizeof(float) * n2);
+    uint8_t* qc1 = (uint8_t*)malloc(n1);
+    uint8_t* qs1 = (uint8_t*)malloc(n1 / 32);
+    for (int64_t i = 0; i < n1; ++i) f1[i] = orc_bf16_value(w1[i]);
+    for (int64_t i = 0; i < n2; ++i) f2[i] = orc_bf16_value(w2[i]);
+    orc_mx_quantize(f1, (int64_t)E * 2 * F, H, qc1, qs1);
+    orc_mx_quantize(f2, (int64_t)E * H, F, c2, s2);
+    for (int64_t e = 0; e < E; ++e)
+        for (int64_t pr = 0; pr < 2 * (int64_t)F; ++pr) {
+            int64_t lr = e * 2 * F + fc1_logical_row(pr, F);
+            memcpy(c1 + (e * 2 * F + pr) * H, qc1 + lr * H, H);
+            memcpy(s1 + (e * 2 * F + pr) * (H / 32), qs1 + lr * (H / 32), H / 32);
+        }
+    free(f1); free(f2); free(qc1); free(qs1);
+}
+
+int64_t orc_pack_bytes(int E, int H, int F, int mx)
+{
+    int64_t n1 = (int64_t)E * 2 * F * H, n2 = (int64_t)E * H * F;
+    if (!mx) return 2 * (n1 + n2);
+    return up256(n1) + up256(n2) + up256(n1 / 32) + up256(n2 / 32);
+}

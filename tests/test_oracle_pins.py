@@ -1,0 +1,476 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test names the oracle function it pins and the independent source of
+truth: a library routine (torch casts, numpy/torch fp64 matmuls, Python's
+stable sort), a brute-force search, exact rational arithmetic, or the hand
+cases under tests/golden/ (exact by construction).
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import WORKLOADS, make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ------------------------------------------------------------------ bf16 RNE
+
+def test_bf16_rne_exhaustive_vs_torch_cast():
+    """orc_bf16_bits over all 2^32 fp32 bit patterns vs torch's CPU cast."""
+    step = 1 << 26
+    for start in range(0, 1 << 32, step):
+        bits = np.arange(start, start + step, dtype=np.uint64).astype(np.uint32)
+        v = bits.view(np.float32)
+        ours = oracle.bf16_bits(v)
+        ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        nan = np.isnan(v)
+        assert np.array_equal(ours[~nan], ref[~nan]), f"mismatch in chunk at {start:#x}"
+        # NaN stays NaN (payload is not part of the contract)
+        assert np.all((ours[nan] & 0x7F80) == 0x7F80) and np.all((ours[nan] & 0x7F) != 0)
+
+
+# ------------------------------------------------------------------ E4M3 / E8M0
+
+def _e4m3_table():
+    """All finite E4M3FN values from torch's float8 dtype (a library decode)."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    vals = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return vals
+
+
+def test_e4m3_decode_vs_torch():
+    vals = _e4m3_table()
+    for c in range(256):
+        ours = oracle.e4m3_decode(c)
+        if np.isnan(vals[c]):
+            assert np.isnan(ours)
+        else:
+            assert ours == vals[c], c
+
+
+def test_e4m3_encode_vs_brute_force_nearest():
+    """Nearest finite E4M3FN value, ties to the even code, by exhaustive search."""
+    vals = _e4m3_table()
+    finite = [c for c in range(256) if not np.isnan(vals[c])]
+    rng = np.random.default_rng(5)
+    # every midpoint between neighbours, every exact value, and random values
+    pos = sorted(set(vals[c] for c in finite if vals[c] >= 0))
+    mids = [(a + b) / 2 for a, b in zip(pos[:-1], pos[1:])]
+    samples = list(pos) + mids + list(rng.uniform(0, 448, 3000)) + \
+        list(2.0 ** rng.uniform(-12, 8.8, 3000))
+    samples = [s for s in samples if s <= 448]
+    for s in samples:
+        for v in (s, -s):
+            ours = oracle.e4m3_encode(v)
+            d = [abs(vals[c] - v) for c in finite]
+            best = min(d)
+            cands = [c for c, dd in zip(finite, d) if dd == best]
+            if len(cands) > 1:
+                cands = [c for c in cands if (c & 1) == 0] or cands
+                # +0/-0 both sit at distance |v|: keep the sign of v
+                if best == abs(v):
+                    cands = [c for c in cands if (c & 0x80) == (0x80 if v < 0 or
+                                                                 (v == 0 and np.signbit(v)) else 0)]
+            assert ours in cands, (v, ours, cands)
+
+
+def test_e4m3_encode_vs_torch_cast():
+    rng = np.random.default_rng(6)
+    v = np.concatenate([rng.uniform(-448, 448, 20000), 2.0 ** rng.uniform(-12, 8.8, 20000)])
+    v = v.astype(np.float32).astype(np.float64)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    ours = np.array([oracle.e4m3_encode(x) for x in v], dtype=np.uint8)
+    assert np.array_equal(ours, ref)
+
+
+def _e8m0_linear(amax):
+    if amax == 0:
+        return -127
+    for e in range(-127, 128):
+        if Fraction(amax) <= 448 * Fraction(2) ** e:
+            return e
+    return 127
+
+
+def test_e8m0_vs_linear_search():
+    rng = np.random.default_rng(7)
+    vals = [0.0, 448.0, 449.0, 2.0, 1.75, 1.7500001, 3.5, 3.4999998, 1e-45, 1e-38, 3.4e38]
+    vals += [float(np.float32(448.0 * 2.0 ** e)) for e in range(-126, 119)]
+    vals += [float(np.nextafter(np.float32(448.0 * 2.0 ** e), np.float32(np.inf)))
+             for e in range(-120, 119)]
+    vals += list((2.0 ** rng.uniform(-140, 127, 2000)).astype(np.float32).astype(float))
+    for a in vals:
+        a32 = float(np.float32(a))
+        assert oracle.e8m0_exponent(a32) == _e8m0_linear(a32), a32
+
+
+def test_mx_blocks_golden():
+    """Hand cases of the block quantizer (tests/golden/mx_blocks.json)."""
+    with open(os.path.join(GOLDEN, "mx_blocks.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        blk = np.array(c["block"], dtype=np.float32)[None, :]
+        codes, scales = oracle.mx_quantize(blk)
+        assert int(scales[0, 0]) == c["scale_exp"] + 127, c["name"]
+        deq = oracle.mx_dequantize(codes, scales)[0]
+        assert np.array_equal(deq, np.array(c["values"])), c["name"]
+
+
+def test_mx_quantize_vs_torch():
+    """Codes = torch E4M3 cast of v / 2^e with e from the linear search."""
+    rng = np.random.default_rng(8)
+    v = (rng.standard_normal((64, 256)) * 2.0 ** rng.integers(-20, 20, (64, 1))).astype(np.float32)
+    v[3, :32] = 0
+    codes, scales = oracle.mx_quantize(v)
+    for r in range(v.shape[0]):
+        for b in range(v.shape[1] // 32):
+            blk = v[r, b * 32:(b + 1) * 32]
+            e = _e8m0_linear(float(np.max(np.abs(blk))))
+            assert scales[r, b] == e + 127
+            ref = torch.from_numpy(blk.astype(np.float64) * 2.0 ** -e).to(
+                torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(codes[r, b * 32:(b + 1) * 32], ref)
+
+
+# ------------------------------------------------------------------ router
+
+def test_route_vs_sort_and_numpy_softmax():
+    rng = np.random.default_rng(9)
+    T, E, k = 300, 40, 6
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    lg[5, 3] = lg[5, 17] = lg[5].max() + 1       # tie at the top: lower id first
+    lg[7, :] = 0.0                                # all tied: ids 0..k-1
+    ids, probs, err = oracle.route(lg, T, k)
+    assert err == 0
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-float(lg[t, e]), e))[:k]
+        assert list(ids[t]) == sorted(order), t
+        z = np.exp(lg[t].astype(np.float64) - lg[t].max())
+        p = z / z.sum()
+        q = p[sorted(order)] / p[sorted(order)].sum()
+        np.testing.assert_allclose(probs[t], q, rtol=2e-7, atol=0)
+    assert list(ids[7]) == list(range(k))
+
+
+def test_route_live_bounds():
+    lg = np.random.default_rng(1).standard_normal((8, 8)).astype(np.float32)
+    ids, probs, err = oracle.route(lg, 3, 2)
+    assert err == 0 and np.all(ids[3:] == -1) and np.all(np.isnan(probs[3:]))
+    ids, probs, err = oracle.route(lg, 9, 2)
+    assert err == oracle.ERR_LIVE_HIGH and np.all(ids >= 0)
+    ids, probs, err = oracle.route(lg, -1, 2)
+    assert err == oracle.ERR_LIVE_NEG and np.all(ids == -1)
+
+
+# ------------------------------------------------------------------ permutation
+
+def _prepare_reference(ids, probs, live, E):
+    """Python's stable sorted() over the token-major route list."""
+    T, k = ids.shape
+    T = max(0, min(live, T))
+    routes = []
+    sorted_ids = np.zeros((T, k), np.int64)
+    for t in range(T):
+        pairs = sorted(((int(ids[t, j]), j) for j in range(k)), key=lambda q: q[0])
+        for j, (e, _) in enumerate(pairs):
+            sorted_ids[t, j] = e
+            routes.append((e, t * k + j))
+    valid = [(e, r) for e, r in routes if 0 <= e < E]
+    perm = [r for e, r in sorted(valid, key=lambda q: q[0])]
+    counts = np.bincount([e for e, _ in valid], minlength=E)
+    dst = -np.ones(T * k, np.int64)
+    for pos, r in enumerate(perm):
+        dst[r] = pos
+    return sorted_ids, counts, np.array(perm, np.int64), dst.reshape(T, k)
+
+
+@pytest.mark.parametrize("T,E,k,live", [(64, 8, 2, 64), (200, 16, 5, 137), (33, 128, 8, 33),
+                                        (16, 4, 4, 16), (10, 8, 1, 0)])
+def test_prepare_vs_python_sorted(T, E, k, live):
+    rng = np.random.default_rng(T + E + k)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    probs = rng.random((T, k)).astype(np.float32)
+    got = oracle.prepare(ids, probs, live, E)
+    s_ids, counts, perm, dst = _prepare_reference(ids, probs, live, E)
+    assert got["err"] == 0
+    assert np.array_equal(got["sorted_ids"], s_ids)
+    assert np.array_equal(got["counts"], counts)
+    assert np.array_equal(got["offsets"], np.concatenate([[0], np.cumsum(counts)]))
+    assert np.array_equal(got["perm_src"], perm)
+    assert np.array_equal(got["dst"], dst)
+    # probabilities travel with their ids
+    for t in range(got["T"]):
+        pairs = {int(ids[t, j]): probs[t, j] for j in range(k)}
+        assert all(got["sorted_probs"][t, j] == pairs[int(s_ids[t, j])] for j in range(k))
+
+
+def test_prepare_contract_violations():
+    ids = np.array([[0, 9], [1, 1], [2, 0]], np.int32)
+    probs = np.ones((3, 2), np.float32)
+    got = oracle.prepare(ids, probs, 3, 4)
+    assert got["err"] == oracle.ERR_BAD_ID | oracle.ERR_DUP_ID
+    s_ids, counts, perm, dst = _prepare_reference(ids, probs, 3, 4)
+    assert np.array_equal(got["dst"], dst) and np.array_equal(got["perm_src"], perm)
+
+
+# ------------------------------------------------------------------ finalize
+
+def _fma_f32_exact(a, b, c):
+    """Correctly rounded fp32 fma from exact rationals (ties to even)."""
+    exact = Fraction(float(a)) * Fraction(float(b)) + Fraction(float(c))
+    if exact == 0:
+        return np.float32(0.0)
+    guess = np.float32(float(exact))
+    cands = {guess, np.nextafter(guess, np.float32(np.inf)), np.nextafter(guess, np.float32(-np.inf))}
+    best = min(cands, key=lambda v: (abs(Fraction(float(v)) - exact),
+                                     int(np.array(v).view(np.uint32)) & 1))
+    return np.float32(best)
+
+
+def test_finalize_vs_exact_fma_chain():
+    rng = np.random.default_rng(10)
+    T, k, H = 40, 4, 8
+    R = T * k
+    O = (rng.standard_normal((R, H)) * 2.0 ** rng.integers(-30, 30, (R, 1))).astype(np.float32)
+    p = rng.random((T, k)).astype(np.float32)
+    dst = rng.permutation(R).astype(np.int32).reshape(T, k)
+    dst[3, 1] = -1                                       # a dropped route adds nothing
+    out = oracle.finalize(O, dst, p, H)
+    for t in range(T):
+        for m in range(H):
+            acc = np.float32(0.0)
+            for j in range(k):
+                if dst[t, j] >= 0:
+                    acc = _fma_f32_exact(p[t, j], O[dst[t, j], m], acc)
+            assert out[t, m].view(np.uint32) == np.float32(acc).view(np.uint32), (t, m)
+
+
+# ------------------------------------------------------------------ hand cases
+
+def _load_hand_cases():
+    with open(os.path.join(GOLDEN, "hand_cases.json")) as f:
+        return json.load(f)["cases"]
+
+
+def _bits(vals):
+    a = np.array(vals, dtype=np.float32)
+    b = a.view(np.uint32)
+    finite = ~np.isnan(a)
+    assert np.all((b[finite] & 0xFFFF) == 0), "hand-case values must be exact bf16"
+    out = (b >> 16).astype(np.uint16)
+    out[~finite] = 0x7FC0
+    return out
+
+
+def hand_case_arrays(c):
+    """Numpy inputs of a hand case; NaN patterns past the live count."""
+    x = _bits(c["x"])
+    ids = np.array([[0x7FC00000 if v is None else v for v in r] for r in c["ids"]],
+                   dtype=np.int64).astype(np.int32)
+    pr = np.array([[np.nan if v is None else v for v in r] for r in c["probs"]], np.float32)
+    w1 = _bits(c["w1"])
+    w2 = _bits(c["w2"])
+    return x, ids, pr, w1, w2
+
+
+@pytest.mark.parametrize("c", _load_hand_cases(), ids=lambda c: c["name"])
+def test_oracle_hand_cases(c):
+    x, ids, pr, w1, w2 = hand_case_arrays(c)
+    m = oracle.Model(c["E"], c["H"], c["F"], c["k"], w1, w2, c["precision"])
+    out, err, _ = m.forward(x, ids, pr, c["live"])
+    assert err == 0
+    for t, row in enumerate(c["expected"]):
+        if row is None:
+            assert np.all(np.isnan(out[t])), f"row {t} past live was written"
+        else:
+            assert np.array_equal(out[t], np.array(row, np.float32)), t
+    if c["name"].startswith("HC4"):
+        # a different order breaks the pin: +1 last gives 1, not 0
+        O = np.array([[2.0 ** 24], [-(2.0 ** 24)], [1.0]], np.float32)
+        assert oracle.finalize(O, np.array([[0, 1, 2]], np.int32),
+                               np.ones((1, 3), np.float32), 1)[0, 0] == 1.0
+
+
+def test_hand_case_hc3_bitwise_hc2():
+    cases = {c["name"]: c for c in _load_hand_cases()}
+    outs = []
+    for name in ("HC2_top2_quarters", "HC3_listed_order_irrelevant"):
+        x, ids, pr, w1, w2 = hand_case_arrays(cases[name])
+        c = cases[name]
+        outs.append(oracle.Model(c["E"], c["H"], c["F"], c["k"], w1, w2).forward(x, ids, pr, 2)[0])
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
+# ------------------------------------------------------------------ expert MLP
+
+def _dense_mlp_fp64(x_vals, w1_vals, w2_vals, F, mx_h=False):
+    """torch fp64 reference of one expert: g, u rounded to fp32, SwiGLU in fp64
+    rounded to fp32, FC2 operand rounded to bf16 (torch cast) or MXFP8, FC2 in
+    fp64 rounded to fp32."""
+    x = torch.from_numpy(x_vals)
+    w1 = torch.from_numpy(w1_vals)
+    w2 = torch.from_numpy(w2_vals)
+    g = (x @ w1[:F].T).float().double()
+    u = (x @ w1[F:].T).float().double()
+    a = (g / (1.0 + torch.exp(-g)) * u).float()
+    if not mx_h:
+        h = a.to(torch.bfloat16).double()
+    else:
+        codes, scales = oracle.mx_quantize(a.numpy())
+        h = torch.from_numpy(oracle.mx_dequantize(codes, scales))
+    return (h @ w2.T).float()
+
+
+@pytest.mark.parametrize("precision", ["bf16", "mxfp8"])
+def test_expert_mlp_top1_vs_dense_torch(precision):
+    """Top-1 routing with p = 1 reduces the layer to dense per-expert MLPs."""
+    w = WORKLOADS["tiny"]
+    inp = make_inputs(w, seed=12)
+    rng = np.random.default_rng(3)
+    ids = rng.integers(0, w.E, (w.T, 1)).astype(np.int32)
+    probs = np.ones((w.T, 1), np.float32)
+    m = oracle.Model(w.E, w.H, w.F, 1, inp["w1_bits"], inp["w2_bits"], precision)
+    out, err, _ = m.forward(inp["x_bits"], ids, probs, w.T)
+    assert err == 0
+    xv = oracle.bf16_value(inp["x_bits"]).astype(np.float64)
+    w1v = oracle.bf16_value(inp["w1_bits"]).astype(np.float64)
+    w2v = oracle.bf16_value(inp["w2_bits"]).astype(np.float64)
+    if precision == "mxfp8":
+        xv = oracle.mx_dequantize(*oracle.mx_quantize(xv.astype(np.float32)))
+        w1v = oracle.mx_dequantize(*oracle.mx_quantize(
+            w1v.reshape(-1, w.H).astype(np.float32))).reshape(w1v.shape)
+        w2v = oracle.mx_dequantize(*oracle.mx_quantize(
+            w2v.reshape(-1, w.F).astype(np.float32))).reshape(w2v.shape)
+    for e in range(w.E):
+        rows = np.nonzero(ids[:, 0] == e)[0]
+        if len(rows) == 0:
+            continue
+        ref = _dense_mlp_fp64(xv[rows], w1v[e], w2v[e], w.F, precision == "mxfp8").numpy()
+        got = out[rows]
+        # independent fp64 summation orders: agree to fp32 rounding, except where a
+        # rounding decision on the FC2 operand flips (rare, one operand step)
+        err_rel = np.abs(got - ref) / (np.abs(ref).max() + 1e-30)
+        assert np.quantile(err_rel, 0.99) < 1e-6 and err_rel.max() < 5e-3, (e, err_rel.max())
+
+
+def test_gate_up_roles_and_expert_index_matter():
+    """Swapping gate/up, or routing to a neighbouring expert, changes the output
+    well beyond tolerance (guards against transposed or shifted operands)."""
+    w = WORKLOADS["tiny"]
+    inp = make_inputs(w, seed=13)
+    ids, probs, _ = oracle.route(inp["logits"], w.T, w.k)
+    m = oracle.Model(w.E, w.H, w.F, w.k, inp["w1_bits"], inp["w2_bits"])
+    out, _, _ = m.forward(inp["x_bits"], ids, probs, w.T)
+    w1s = inp["w1_bits"].copy()
+    w1s[:, : w.F], w1s[:, w.F:] = inp["w1_bits"][:, w.F:], inp["w1_bits"][:, : w.F]
+    out_sw, _, _ = oracle.Model(w.E, w.H, w.F, w.k, w1s, inp["w2_bits"]).forward(
+        inp["x_bits"], ids, probs, w.T)
+    out_sh, _, _ = m.forward(inp["x_bits"], (ids + 1) % w.E, probs, w.T)
+    scale = np.linalg.norm(out)
+    assert np.linalg.norm(out_sw - out) > 0.1 * scale
+    assert np.linalg.norm(out_sh - out) > 0.1 * scale
+
+
+@pytest.mark.parametrize("precision", ["bf16", "mxfp8"])
+def test_forward_vs_numpy_fp64_formulation(precision):
+    """Whole layer vs an independent dense fp64 formulation (k = 2, real probs)."""
+    w = WORKLOADS["tiny"]
+    inp = make_inputs(w, seed=11)
+    ids, probs, err = oracle.route(inp["logits"], w.T, w.k)
+    assert err == 0
+    m = oracle.Model(w.E, w.H, w.F, w.k, inp["w1_bits"], inp["w2_bits"], precision)
+    out, err, _ = m.forward(inp["x_bits"], ids, probs, w.T)
+    xv = oracle.bf16_value(inp["x_bits"]).astype(np.float64)
+    w1v = oracle.bf16_value(inp["w1_bits"]).astype(np.float64)
+    w2v = oracle.bf16_value(inp["w2_bits"]).astype(np.float64)
+    if precision == "mxfp8":
+        xv = oracle.mx_dequantize(*oracle.mx_quantize(xv.astype(np.float32)))
+        w1v = oracle.mx_dequantize(*oracle.mx_quantize(
+            w1v.reshape(-1, w.H).astype(np.float32))).reshape(w1v.shape)
+        w2v = oracle.mx_dequantize(*oracle.mx_quantize(
+            w2v.reshape(-1, w.F).astype(np.float32))).reshape(w2v.shape)
+    ref = np.zeros((w.T, w.H))
+    for t in range(w.T):
+        for j in range(w.k):
+            e = ids[t, j]
+            o = _dense_mlp_fp64(xv[t:t + 1], w1v[e], w2v[e], w.F, precision == "mxfp8")
+            ref[t] += float(probs[t, j]) * o.numpy()[0].astype(np.float64)
+    rel = np.linalg.norm(out - ref) / np.linalg.norm(ref)
+    assert rel < 1e-5, rel
+
+
+@pytest.mark.parametrize("name,precision", [("tiny", "bf16"), ("tiny", "mxfp8")])
+def test_forward_bitwise_equals_naive_per_token_loop(name, precision):
+    """Permutation bookkeeping: permuted forward == per-token loop, bitwise."""
+    w = WORKLOADS[name]
+    inp = make_inputs(w, seed=12, outliers=(precision == "mxfp8"))
+    ids, probs, _ = oracle.route(inp["logits"], w.T, w.k)
+    ids = ids[:, ::-1].copy()          # listed in descending order: canonical sort must undo
+    probs = probs[:, ::-1].copy()
+    m = oracle.Model(w.E, w.H, w.F, w.k, inp["w1_bits"], inp["w2_bits"], precision)
+    out, _, _ = m.forward(inp["x_bits"], ids, probs, w.T)
+    naive = m.forward_tokens(inp["x_bits"], ids, probs, np.arange(w.T))
+    assert np.array_equal(out.view(np.uint32), naive.view(np.uint32))
+
+
+def test_forward_live_prefix_and_capacity():
+    """Rows past live are neither read (NaN there changes nothing) nor written."""
+    w = WORKLOADS["tiny"].with_tokens(40, 64)
+    inp = make_inputs(w, seed=11)
+    ids, probs, _ = oracle.route(inp["logits"], w.T, w.k)
+    m = oracle.Model(w.E, w.H, w.F, w.k, inp["w1_bits"], inp["w2_bits"])
+    out, err, _ = m.forward(inp["x_bits"], ids, probs, w.T)
+    assert err == 0 and np.all(np.isnan(out[w.T:])) and not np.any(np.isnan(out[: w.T]))
+    # the first 40 tokens alone give the same bits (batch invariance of the definition)
+    out2, _, _ = m.forward(inp["x_bits"][:20].copy(), ids[:20].copy(), probs[:20].copy(), 20)
+    assert np.array_equal(out2.view(np.uint32), out[:20].view(np.uint32))
+
+
+# ------------------------------------------------------------------ packer
+
+def test_pack_layout_definition():
+    """Packed FC1 row 64b+i = gate row 32b+i (i<32) or up row F+32b+i-32; FC2 verbatim."""
+    E, H, F = 2, 64, 96
+    rng = np.random.default_rng(4)
+    w1 = rng.integers(0, 65535, (E, 2 * F, H)).astype(np.uint16)
+    w2 = rng.integers(0, 65535, (E, H, F)).astype(np.uint16)
+    buf = oracle.pack(E, H, F, w1, w2, "bf16").view(np.uint16)
+    p1 = buf[: E * 2 * F * H].reshape(E, 2 * F, H)
+    p2 = buf[E * 2 * F * H:].reshape(E, H, F)
+    for b in range(F // 32):
+        for i in range(64):
+            src = 32 * b + i if i < 32 else F + 32 * b + i - 32
+            assert np.array_equal(p1[:, 64 * b + i], w1[:, src])
+    assert np.array_equal(p2, w2)
+
+
+def test_pack_mxfp8_sections():
+    E, H, F = 2, 64, 96
+    w = make_inputs(WORKLOADS["tiny"], seed=4)
+    rng = np.random.default_rng(4)
+    w1 = oracle.bf16_bits(rng.standard_normal((E, 2 * F, H)).astype(np.float32))
+    w2 = oracle.bf16_bits(rng.standard_normal((E, H, F)).astype(np.float32))
+    buf = oracle.pack(E, H, F, w1, w2, "mxfp8")
+    up = lambda v: (v + 255) // 256 * 256
+    n1, n2 = E * 2 * F * H, E * H * F
+    c1 = buf[:n1].reshape(E, 2 * F, H)
+    c2 = buf[up(n1):up(n1) + n2].reshape(E, H, F)
+    s1 = buf[up(n1) + up(n2):up(n1) + up(n2) + n1 // 32].reshape(E, 2 * F, H // 32)
+    o2 = up(n1) + up(n2) + up(n1 // 32)
+    s2 = buf[o2:o2 + n2 // 32].reshape(E, H, F // 32)
+    qc1, qs1 = oracle.mx_quantize(oracle.bf16_value(w1).reshape(-1, H))
+    qc2, qs2 = oracle.mx_quantize(oracle.bf16_value(w2).reshape(-1, F))
+    qc1, qs1 = qc1.reshape(E, 2 * F, H), qs1.reshape(E, 2 * F, H // 32)
+    for b in range(F // 32):
+        for i in range(64):
+            src = 32 * b + i if i < 32 else F + 32 * b + i - 32
+            assert np.array_equal(c1[:, 64 * b + i], qc1[:, src])
+            assert np.array_equal(s1[:, 64 * b + i], qs1[:, src])
+    assert np.array_equal(c2.reshape(-1, F), qc2) and np.array_equal(s2.reshape(-1, F // 32), qs2)
+    assert len(buf) == oracle.pack_bytes(E, H, F, "mxfp8")
