@@ -1,0 +1,162 @@
+/*
+ * moe.h: C ABI of the MI355X (gfx950) routed SwiGLU mixture-of-experts forward.
+ *
+ * What it computes (one GPU, every expert local):
+ *   for each live token t, with its top-k expert ids e_j and probabilities p_j,
+ *     out[t] = sum over j in ascending e_j order, as an fp32 fused
+ *              multiply-add chain from +0:  p_j * FC2_e( swiglu( FC1_e(x[t]) ) )
+ *   where FC1_e yields gate g and up u, swiglu = silu(g) * u = g/(1+exp(-g)) * u,
+ *   and the FC2 input is rounded to bf16 (bf16 precision) or re-quantized to
+ *   MXFP8 per 32-element block (mxfp8 precision).
+ *
+ * Sources (web pages):
+ *   Megatron-LM PR #7830 ("flashinfer_mega" backend), section "1. Mega backend
+ *     for generation": canonical (ascending) expert-id order before the combine;
+ *     kernel weight layout with gate/up interleaved in blocks of 32, K-major;
+ *     a caller-owned kernel-weight buffer that a refit rewrites in place;
+ *     construction-time rejection of configurations the kernels cannot run.
+ *   Megatron-LM PR #7798 (moe_training_matches_inference), "Background" and
+ *     "What is changed": activation and FC2-input quantization fused into the
+ *     FC1 epilogue; probabilities applied after FC2; finalize = fp32 fused
+ *     multiply-adds of probability and row, from zero, in the listed order.
+ *   Megatron-LM PR #8367 (bound the MoE expert kernels by token count),
+ *     "Problem": the live token count is a device-side value; the result is
+ *     returned in fp32 without a bf16 downcast.
+ *   Megatron-Core API docs, core.transformer.moe.training_matches_inference,
+ *     `_route`: [tokens, topk] probabilities and expert ids.
+ *   cudnn-frontend PR #448 (MoeEp), constructor/forward contract and the MoeEp
+ *     class docstring: rows grouped by expert ascending, token-major inside an
+ *     expert; MXFP8 = E4M3 data with one E8M0 scale per 32 elements.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers of the caller, 16-byte aligned,
+ *     row-major, dense.  bf16 data is passed as its 16-bit patterns.
+ *   - The library never allocates device memory and never synchronizes the
+ *     stream, except moe_check (which reads the error word) and
+ *     moe_get_indices (which copies to host).  moe_route and moe_forward only
+ *     enqueue kernels on `stream`, so they can be captured in a HIP graph.
+ *   - The live token count is read from device memory (live_rows_dev, int32,
+ *     in TOKENS).  It is clamped to [0, T_cap]; a value outside sets an error
+ *     bit (see moe_check).  Token rows >= live are never read and rows >= live
+ *     of every output are never written.
+ *   - Host-detectable errors return a negative moe_status and set a
+ *     thread-local message (moe_last_error); nothing is enqueued then.
+ *   - Calls that share a workspace must be ordered (same stream or events).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moe_ctx* moe_handle;
+
+typedef enum { MOE_BF16 = 0, MOE_MXFP8 = 1 } moe_precision;
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,      /* bad size, null or misaligned pointer     */
+    MOE_ERR_UNSUPPORTED = -2,      /* configuration the kernels cannot run     */
+    MOE_ERR_NOT_LOADED = -3,       /* forward before any moe_load_weights      */
+    MOE_ERR_HIP = -4,              /* a HIP runtime call failed                */
+} moe_status;
+
+/* Device-side contract-violation bits reported by moe_check. */
+#define MOE_DEVERR_BAD_EXPERT_ID 1u   /* id outside [0, E) in a live token: route dropped */
+#define MOE_DEVERR_DUP_EXPERT_ID 2u   /* same id twice in a live token: both rows summed  */
+#define MOE_DEVERR_LIVE_ABOVE_CAP 4u  /* live > T_cap: clamped to T_cap                  */
+#define MOE_DEVERR_LIVE_NEGATIVE 8u   /* live < 0: treated as 0                          */
+
+/* Create a handle for E experts, hidden size H, expert FFN size F, top-k.
+ * Checks (Megatron-LM PR #7830, construction-time validation; cudnn-frontend
+ * PR #448, MXFP8 block of 32): 1 <= E <= 1024; 1 <= topk <= min(E, 16);
+ * H and F positive multiples of 32 (the interleave block and the MXFP8
+ * block); precision MOE_BF16 or MOE_MXFP8, else MOE_ERR_UNSUPPORTED.  Host
+ * only: no device work; the device is the one current at the first launch. */
+moe_status moe_create(int E, int H, int F, int topk, int precision, moe_handle* out);
+
+/* Free the handle (host state only).  NULL is ignored. */
+void moe_destroy(moe_handle h);
+
+/* Size in bytes of the caller-owned kernel-weight buffer (kbuf). */
+size_t moe_weight_bytes(moe_handle h);
+
+/* Pack the weights into the caller-owned buffer kbuf, in place (Megatron-LM
+ * PR #7830: caller-owned kernel-weight buffer, refit rewrites it in place).
+ *   w1: bf16 [E][2F][H]; rows 0..F-1 of each expert are gate, F..2F-1 up.
+ *   w2: bf16 [E][H][F].
+ *   kbuf layout (bf16): FC1 [E][2F][H] with packed row 64b+i = gate row 32b+i
+ *     (i < 32) or up row F+32b+i-32 (i >= 32), then FC2 [E][H][F] unchanged.
+ *   kbuf layout (mxfp8), each section 256-byte aligned: FC1 E4M3 codes
+ *     [E][2F][H] (packed row order), FC2 codes [E][H][F], FC1 E8M0 scales
+ *     [E][2F][H/32], FC2 scales [E][H][F/32]; scale = power-of-two ceiling of
+ *     the block's max magnitude / 448.
+ * The handle remembers kbuf: every later forward reads it.  Calling again
+ * (same or another buffer) is the refit; forwards enqueued before it on the
+ * same stream read the old contents.  w1/w2 may be freed once the work on
+ * `stream` is complete.  kbuf_bytes must be >= moe_weight_bytes(h). */
+moe_status moe_load_weights(moe_handle h, const void* w1, const void* w2, void* kbuf,
+                            size_t kbuf_bytes, hipStream_t stream);
+
+/* Workspace bytes for a token capacity T_cap.  The first 256 bytes are a
+ * header that must be zero before the first use of a new workspace. */
+size_t moe_workspace_bytes(moe_handle h, int64_t T_cap);
+
+/* Router (Megatron-Core `_route`): for each live token, softmax over the E
+ * logits, the top-k experts by logit (ties to the lower id), probabilities
+ * renormalized over the selected experts, written with ids ascending.
+ *   logits: fp32 [T_cap][E]; ids: int32 [T_cap][topk]; probs: fp32 [T_cap][topk].
+ * ws: a workspace of this handle (its header receives the live-count bits). */
+moe_status moe_route(moe_handle h, const float* logits, int64_t T_cap,
+                     const int32_t* live_rows_dev, int32_t* ids, float* probs, void* ws,
+                     size_t ws_bytes, hipStream_t stream);
+
+/* The routed SwiGLU MoE forward.
+ *   x: bf16 [T_cap][H]; expert_ids: int32 [T_cap][topk], any order per token
+ *   (sorted ascending here); probs: fp32 [T_cap][topk]; out: fp32 [T_cap][H].
+ *   ws: ws_bytes >= moe_workspace_bytes(h, T_cap).
+ * Every token's output bits are independent of the other tokens, of T_cap
+ * and of the live count. */
+moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
+                       const float* probs, int64_t T_cap, const int32_t* live_rows_dev,
+                       float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Copy the permutation of the last forward to host arrays (synchronizes the
+ * stream).  counts: int32 [E]; offsets: int32 [E+1]; perm_src: int32 [n_rows]
+ * (= t*topk + j of the route at each grouped row, experts ascending, tokens
+ * ascending within an expert); dst: int32 [T*topk] (grouped row of each
+ * route, -1 if dropped); n_rows_out / T_out: the row and live-token counts.
+ * perm_src and dst must hold T_cap*topk entries.  Any output may be NULL. */
+moe_status moe_get_indices(moe_handle h, const void* ws, int64_t T_cap, int32_t* counts,
+                           int32_t* offsets, int32_t* perm_src, int32_t* dst,
+                           int32_t* n_rows_out, int32_t* T_out, hipStream_t stream);
+
+/* Copy intermediate rows of the last forward to host arrays (synchronizes
+ * the stream), in grouped-row order.  fc2_rows: fp32 [n_rows][H], the
+ * unweighted FC2 output rows.  fc1_out_rows: the FC2 operand rows, bf16
+ * [n_rows][F] (bf16 precision) or E4M3 codes [n_rows][F] followed by E8M0
+ * scales [n_rows][F/32] (mxfp8).  sorted_ids / sorted_probs: int32 / fp32
+ * [T][topk], each token's routes in canonical order.  Any output may be
+ * NULL.  For tests and debugging. */
+moe_status moe_get_rows(moe_handle h, const void* ws, int64_t T_cap, float* fc2_rows,
+                        void* fc1_out_rows, int32_t* sorted_ids, float* sorted_probs,
+                        hipStream_t stream);
+
+/* Synchronize the stream, return the OR of the contract-violation bits of the
+ * last moe_route and the last moe_forward on this workspace (MOE_DEVERR_*)
+ * in *err_bits, and clear them. */
+moe_status moe_check(moe_handle h, void* ws, hipStream_t stream, uint32_t* err_bits);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

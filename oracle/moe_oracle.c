@@ -295,12 +295,22 @@ uint32_t orc_prepare(const int32_t* ids, const float* probs, int64_t T_cap, int3
 /* Expert MLP and finalize                                                   */
 /* ------------------------------------------------------------------------ */
 
-/* Exact dot product of two length-n rows, accumulated in fp64 and rounded
- * once to fp32.  bf16 x bf16 and MXFP8 x MXFP8 products are exact in fp64. */
-static float dot_f32(const double* a, const double* b, int64_t n)
+/* Exact dot products of an operand row (fp64 values) with a weight row,
+ * accumulated in fp64 and rounded once to fp32.  bf16 x bf16 and
+ * MXFP8 x MXFP8 products are exact in fp64.  Weight rows are read either as
+ * bf16 bit patterns or as fp32 values (the MXFP8 operand values, which fp32
+ * holds exactly). */
+static float dot_bf16(const double* a, const uint16_t* b, int64_t n)
 {
     double s = 0.0;
-    for (int64_t i = 0; i < n; ++i) s += a[i] * b[i];
+    for (int64_t i = 0; i < n; ++i) s += a[i] * (double)orc_bf16_value(b[i]);
+    return (float)s;
+}
+
+static float dot_f32w(const double* a, const float* b, int64_t n)
+{
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i) s += a[i] * (double)b[i];
     return (float)s;
 }
 
@@ -313,13 +323,26 @@ static float swiglu_f32(float g, float u)
     return (float)(gd / (1.0 + exp(-gd)) * (double)u);
 }
 
-/* Operand storage of the oracle: every operand as exact fp64 values. */
+/* Weights of the oracle: the caller's bf16 bit patterns (bf16 path, not
+ * copied) or fp32 operand values (MXFP8 path: the dequantized quantization). */
 typedef struct {
     int E, H, F, k;
     int mx;                 /* 0: bf16 path, 1: MXFP8 path */
-    const double* w1;       /* [E][2F][H] operand values (gate rows 0..F-1, up rows F..2F-1) */
-    const double* w2;       /* [E][H][F] */
+    const uint16_t* w1b;    /* bf16 [E][2F][H] (gate rows 0..F-1, up rows F..2F-1) */
+    const uint16_t* w2b;    /* bf16 [E][H][F] */
+    const float* w1f;       /* MXFP8 operand values, same shapes */
+    const float* w2f;
 } orc_model;
+
+static float dot_w1(const orc_model* m, const double* xr, int64_t row)
+{
+    return m->mx ? dot_f32w(xr, m->w1f + row * m->H, m->H) : dot_bf16(xr, m->w1b + row * m->H, m->H);
+}
+
+static float dot_w2(const orc_model* m, const double* hr, int64_t row)
+{
+    return m->mx ? dot_f32w(hr, m->w2f + row * m->F, m->F) : dot_bf16(hr, m->w2b + row * m->F, m->F);
+}
 
 /* The expert MLP of one routed row: FC1 gate/up from the operand row xr
  * (length H), SwiGLU, the FC2-input rounding (bf16, or MXFP8 per 32-block),
@@ -328,11 +351,10 @@ static void expert_row(const orc_model* m, int e, const double* xr, float* o,
                        float* a32, double* hrow)
 {
     const int64_t H = m->H, F = m->F;
-    const double* W1 = m->w1 + (int64_t)e * 2 * F * H;
-    const double* W2 = m->w2 + (int64_t)e * H * F;
+    const int64_t r1 = (int64_t)e * 2 * F, r2 = (int64_t)e * H;
     for (int64_t n = 0; n < F; ++n) {
-        float g = dot_f32(xr, W1 + n * H, H);
-        float u = dot_f32(xr, W1 + (F + n) * H, H);
+        float g = dot_w1(m, xr, r1 + n);
+        float u = dot_w1(m, xr, r1 + F + n);
         a32[n] = swiglu_f32(g, u);
     }
     if (!m->mx) {
@@ -351,7 +373,7 @@ static void expert_row(const orc_model* m, int e, const double* xr, float* o,
             }
         }
     }
-    for (int64_t mo = 0; mo < H; ++mo) o[mo] = dot_f32(hrow, W2 + mo * F, F);
+    for (int64_t mo = 0; mo < H; ++mo) o[mo] = dot_w2(m, hrow, r2 + mo);
 }
 
 /* Finalize ([VALUE] "What is changed"; [BOUND] "Problem"): for each live
@@ -394,42 +416,46 @@ static double* x_operands(const uint16_t* x, int64_t T, int H, int mx)
     return xo;
 }
 
-/* Weight operand values: bf16 values, or the MXFP8 quantization of the bf16
- * values along K (H for W1 rows, F for W2 rows). */
-static double* w_operands(const uint16_t* w, int64_t rows, int64_t cols, int mx)
+/* MXFP8 weight operand values: the quantization of the bf16 values along K
+ * (H for W1 rows, F for W2 rows), dequantized to fp32 (exact). */
+static float* w_mx_operands(const uint16_t* w, int64_t rows, int64_t cols)
 {
-    double* wo = (double*)malloc(sizeof(double) * rows * cols);
-    if (!mx) {
+    float* wf = (float*)malloc(sizeof(float) * rows * cols);
+    uint8_t* c = (uint8_t*)malloc(rows * cols);
+    uint8_t* s = (uint8_t*)malloc(rows * (cols / 32));
 #pragma omp parallel for schedule(static)
-        for (int64_t i = 0; i < rows * cols; ++i) wo[i] = orc_bf16_value(w[i]);
-    } else {
-        float* wf = (float*)malloc(sizeof(float) * rows * cols);
-        uint8_t* c = (uint8_t*)malloc(rows * cols);
-        uint8_t* s = (uint8_t*)malloc(rows * (cols / 32));
-        for (int64_t i = 0; i < rows * cols; ++i) wf[i] = orc_bf16_value(w[i]);
-        orc_mx_quantize(wf, rows, cols, c, s);
-        orc_mx_dequantize(c, s, rows, cols, wo);
-        free(wf); free(c); free(s);
-    }
-    return wo;
+    for (int64_t i = 0; i < rows * cols; ++i) wf[i] = orc_bf16_value(w[i]);
+    orc_mx_quantize(wf, rows, cols, c, s);
+    int64_t nb = cols / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t q = 0; q < cols; ++q)
+            wf[r * cols + q] = (float)ldexp(orc_e4m3_decode(c[r * cols + q]),
+                                            (int)s[r * nb + q / 32] - 127);
+    free(c); free(s);
+    return wf;
 }
 
 /* Opaque prepared weights, so that repeated oracle calls on the same model
- * (sampled tokens, timing) do not rebuild the operand values. */
+ * (sampled tokens, timing) do not rebuild the operand values.  In the bf16
+ * path the caller's arrays are read in place and must outlive the handle. */
 typedef struct {
     orc_model m;
-    double* w1;
-    double* w2;
+    float* w1f;
+    float* w2f;
 } orc_weights;
 
 void* orc_weights_create(int E, int H, int F, int k, int mx, const uint16_t* w1,
                          const uint16_t* w2)
 {
     orc_weights* w = (orc_weights*)calloc(1, sizeof(orc_weights));
-    w->w1 = w_operands(w1, (int64_t)E * 2 * F, H, mx);
-    w->w2 = w_operands(w2, (int64_t)E * H, F, mx);
     w->m.E = E; w->m.H = H; w->m.F = F; w->m.k = k; w->m.mx = mx;
-    w->m.w1 = w->w1; w->m.w2 = w->w2;
+    if (mx) {
+        w->w1f = w_mx_operands(w1, (int64_t)E * 2 * F, H);
+        w->w2f = w_mx_operands(w2, (int64_t)E * H, F);
+    }
+    w->m.w1b = w1; w->m.w2b = w2;
+    w->m.w1f = w->w1f; w->m.w2f = w->w2f;
     return w;
 }
 
@@ -437,7 +463,7 @@ void orc_weights_destroy(void* p)
 {
     orc_weights* w = (orc_weights*)p;
     if (!w) return;
-    free(w->w1); free(w->w2); free(w);
+    free(w->w1f); free(w->w2f); free(w);
 }
 
 /* The whole forward, step by step: canonical sort and permutation

@@ -1,0 +1,244 @@
+"""MI355X-native routed SwiGLU MoE forward: Python binding of libmoe.so.
+
+Argument marshalling only.  Every step of the path (routing, permutation, the
+expert GEMMs, SwiGLU, quantization, the fp32 finalize) runs in the HIP kernels
+of ``libmoe.so`` (C ABI in ``include/moe.h``); torch supplies device memory
+and the current stream.  There is no CPU fallback: if the library is missing
+or no GPU is present, the calls raise.
+
+    moe = MoE(E=64, H=2048, F=1024, topk=6, precision="bf16")
+    kbuf = moe.load_weights(w1, w2)          # w1 [E, 2F, H], w2 [E, H, F], bf16, on GPU
+    ws = moe.new_workspace(T_cap)
+    ids, probs = moe.route(logits, live, ws=ws)
+    out = moe.forward(x, ids, probs, live, ws=ws)   # fp32 [T_cap, H]
+
+``live`` is an int32 device tensor holding the number of live tokens.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["MoE", "lib", "LIB_PATH", "MoEError", "DEVERR_BAD_EXPERT_ID", "DEVERR_DUP_EXPERT_ID",
+           "DEVERR_LIVE_ABOVE_CAP", "DEVERR_LIVE_NEGATIVE"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_BF16, MOE_MXFP8 = 0, 1
+_PRECISION = {"bf16": MOE_BF16, "mxfp8": MOE_MXFP8}
+DEVERR_BAD_EXPERT_ID = 1
+DEVERR_DUP_EXPERT_ID = 2
+DEVERR_LIVE_ABOVE_CAP = 4
+DEVERR_LIVE_NEGATIVE = 8
+WS_HEADER_BYTES = 256
+
+# every symbol include/moe.h declares, with its ctypes signature
+_P = ctypes.c_void_p
+_SIGNATURES = {
+    "moe_create": (ctypes.c_int, [ctypes.c_int] * 5 + [ctypes.POINTER(_P)]),
+    "moe_destroy": (None, [_P]),
+    "moe_weight_bytes": (ctypes.c_size_t, [_P]),
+    "moe_load_weights": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int64]),
+    "moe_route": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_forward": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_get_indices": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_get_rows": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P, _P, _P, _P, _P]),
+    "moe_check": (ctypes.c_int, [_P, _P, _P, ctypes.POINTER(ctypes.c_uint32)]),
+    "moe_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+class MoEError(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so (built by ``python -m swiglu_expert_mlp_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m swiglu_expert_mlp_amd.build` (there is no fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status == 0:
+        return
+    msg = lib().moe_last_error().decode(errors="replace")
+    if status == -1:
+        raise ValueError(f"{what}: {msg}")
+    if status == -2:
+        raise NotImplementedError(f"{what}: {msg}")
+    raise MoEError(f"{what} failed ({status}): {msg}")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dev(t, name, dtypes, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+class MoE:
+    """Handle of one routed SwiGLU MoE layer (E experts, hidden H, FFN F, top-k)."""
+
+    def __init__(self, E: int, H: int, F: int, topk: int, precision: str = "bf16"):
+        if precision not in _PRECISION:
+            raise NotImplementedError(f"precision {precision!r} is not supported (bf16, mxfp8)")
+        h = _P()
+        _check(lib().moe_create(E, H, F, topk, _PRECISION[precision], ctypes.byref(h)),
+               "moe_create")
+        self._h = h
+        self.E, self.H, self.F, self.topk, self.precision = E, H, F, topk, precision
+        self.kbuf = None
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            lib().moe_destroy(h)
+            self._h = None
+
+    # ------------------------------------------------------------- sizes
+
+    @property
+    def weight_bytes(self) -> int:
+        return int(lib().moe_weight_bytes(self._h))
+
+    def workspace_bytes(self, T_cap: int) -> int:
+        return int(lib().moe_workspace_bytes(self._h, int(T_cap)))
+
+    def new_workspace(self, T_cap: int, device=None):
+        """A workspace for capacity T_cap with its header zeroed."""
+        torch = _torch()
+        ws = torch.empty(self.workspace_bytes(T_cap), dtype=torch.uint8,
+                         device=device or "cuda")
+        ws[:WS_HEADER_BYTES].zero_()
+        return ws
+
+    # ------------------------------------------------------------- calls
+
+    def load_weights(self, w1, w2, kbuf=None, stream=None):
+        """Pack bf16 w1 [E, 2F, H] (gate rows first) and w2 [E, H, F] into kbuf
+        (allocated if None).  Calling again with the same kbuf is the refit."""
+        torch = _torch()
+        bf = (torch.bfloat16, torch.int16, torch.uint16)
+        p1 = _dev(w1, "w1", bf, (self.E, 2 * self.F, self.H))
+        p2 = _dev(w2, "w2", bf, (self.E, self.H, self.F))
+        if kbuf is None:
+            kbuf = torch.empty(self.weight_bytes, dtype=torch.uint8, device=w1.device)
+        pk = _dev(kbuf, "kbuf", (torch.uint8,))
+        _check(lib().moe_load_weights(self._h, p1, p2, pk, kbuf.numel(), _stream(stream)),
+               "moe_load_weights")
+        self.kbuf = kbuf          # keep the buffer alive as long as the handle reads it
+        return kbuf
+
+    def route(self, logits, live, ids=None, probs=None, ws=None, stream=None):
+        torch = _torch()
+        T_cap = logits.shape[0]
+        pl = _dev(logits, "logits", (torch.float32,), (T_cap, self.E))
+        plive = _dev(live, "live", (torch.int32,))
+        if ids is None:
+            ids = torch.empty((T_cap, self.topk), dtype=torch.int32, device=logits.device)
+        if probs is None:
+            probs = torch.empty((T_cap, self.topk), dtype=torch.float32, device=logits.device)
+        if ws is None:
+            ws = self.new_workspace(T_cap, logits.device)
+        pi = _dev(ids, "ids", (torch.int32,), (T_cap, self.topk))
+        pp = _dev(probs, "probs", (torch.float32,), (T_cap, self.topk))
+        pw = _dev(ws, "ws", (torch.uint8,))
+        _check(lib().moe_route(self._h, pl, T_cap, plive, pi, pp, pw, ws.numel(), _stream(stream)),
+               "moe_route")
+        return ids, probs
+
+    def forward(self, x, ids, probs, live, out=None, ws=None, stream=None):
+        torch = _torch()
+        T_cap = x.shape[0]
+        px = _dev(x, "x", (torch.bfloat16, torch.int16, torch.uint16), (T_cap, self.H))
+        pi = _dev(ids, "expert_ids", (torch.int32,), (T_cap, self.topk))
+        pp = _dev(probs, "probs", (torch.float32,), (T_cap, self.topk))
+        plive = _dev(live, "live", (torch.int32,))
+        if out is None:
+            out = torch.empty((T_cap, self.H), dtype=torch.float32, device=x.device)
+        po = _dev(out, "out", (torch.float32,), (T_cap, self.H))
+        if ws is None:
+            ws = self.new_workspace(T_cap, x.device)
+        pw = _dev(ws, "ws", (torch.uint8,))
+        _check(lib().moe_forward(self._h, px, pi, pp, T_cap, plive, po, pw, ws.numel(),
+                                 _stream(stream)), "moe_forward")
+        return out
+
+    # ------------------------------------------------------------- inspection
+
+    def get_indices(self, ws, T_cap: int, stream=None) -> dict:
+        import numpy as np
+        counts = np.zeros(self.E, np.int32)
+        offsets = np.zeros(self.E + 1, np.int32)
+        n = max(1, T_cap * self.topk)
+        perm = np.full(n, -7, np.int32)
+        dst = np.full(n, -7, np.int32)
+        n_rows = ctypes.c_int32(0)
+        T = ctypes.c_int32(0)
+        c = lambda a: a.ctypes.data_as(_P)
+        _check(lib().moe_get_indices(self._h, _dev(ws, "ws", (_torch().uint8,)), T_cap, c(counts),
+                                     c(offsets), c(perm), c(dst), ctypes.byref(n_rows),
+                                     ctypes.byref(T), _stream(stream)), "moe_get_indices")
+        T = T.value
+        return dict(counts=counts, offsets=offsets, perm_src=perm[: n_rows.value],
+                    dst=dst[: T * self.topk].reshape(T, self.topk), T=T, n_rows=n_rows.value)
+
+    def get_rows(self, ws, T_cap: int, n_rows: int, T: int, stream=None) -> dict:
+        import numpy as np
+        O = np.zeros((max(1, n_rows), self.H), np.float32)
+        if self.precision == "bf16":
+            hr = np.zeros((max(1, n_rows), self.F), np.uint16)
+        else:
+            hr = np.zeros(max(1, n_rows) * (self.F + self.F // 32), np.uint8)
+        sid = np.zeros((max(1, T), self.topk), np.int32)
+        sp = np.zeros((max(1, T), self.topk), np.float32)
+        c = lambda a: a.ctypes.data_as(_P)
+        _check(lib().moe_get_rows(self._h, _dev(ws, "ws", (_torch().uint8,)), T_cap, c(O), c(hr),
+                                  c(sid), c(sp), _stream(stream)), "moe_get_rows")
+        res = dict(fc2_rows=O[:n_rows], sorted_ids=sid[:T], sorted_probs=sp[:T])
+        if self.precision == "bf16":
+            res["fc1_out"] = hr[:n_rows]
+        else:
+            res["fc1_codes"] = hr[: n_rows * self.F].reshape(n_rows, self.F)
+            res["fc1_scales"] = hr[n_rows * self.F: n_rows * (self.F + self.F // 32)].reshape(
+                n_rows, self.F // 32)
+        return res
+
+    def check(self, ws, stream=None) -> int:
+        bits = ctypes.c_uint32(0)
+        _check(lib().moe_check(self._h, _dev(ws, "ws", (_torch().uint8,)), _stream(stream),
+                               ctypes.byref(bits)), "moe_check")
+        return int(bits.value)

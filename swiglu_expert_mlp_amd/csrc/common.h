@@ -1,0 +1,125 @@
+// Shared device-side definitions of the MI355X (gfx950) routed-MoE library.
+//
+// Vector types for the CDNA4 MFMA operands, number-format conversions done
+// in registers, and the workspace layout that every kernel and the host code
+// agree on.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;            // CDNA wavefront width
+constexpr int kMaxTopk = 16;
+constexpr int kMaxExperts = 1024;
+constexpr int kChunkTok = 256;       // tokens per prep workgroup
+constexpr int kBM = 64;              // rows per M tile of the grouped GEMMs
+
+// Error bits reported by moe_check (same values as the header's MOE_DEVERR_*).
+constexpr uint32_t kErrBadId = 1u;
+constexpr uint32_t kErrDupId = 2u;
+constexpr uint32_t kErrLiveHigh = 4u;
+constexpr uint32_t kErrLiveNeg = 8u;
+
+// ---------------------------------------------------------------- formats
+
+// fp32 -> bf16 bits, round to nearest even (gfx950 converts in hardware).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float v)
+{
+    __bf16 b = static_cast<__bf16>(v);
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b)
+{
+    return __uint_as_float(b << 16);
+}
+
+// Exponent e of the E8M0 block scale: the smallest e in [-127, 127] with
+// amax <= 448 * 2^e.  With amax = 1.m * 2^E (normal), 448 = 1.75 * 2^8, so
+// e = E - 8 when 1.m <= 1.75 (mantissa field <= 0x600000), else E - 7.
+// Zero and subnormal amax fall below 448 * 2^-127 and give -127.
+__device__ __forceinline__ int e8m0_exponent(float amax)
+{
+    uint32_t u = __float_as_uint(amax) & 0x7fffffffu;
+    int ef = (int)(u >> 23);
+    if (ef == 0) return -127;
+    int e = ef - 127 - 8 + ((u & 0x7fffffu) > 0x600000u ? 1 : 0);
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// fp32 -> E4M3FN code, round to nearest even, for |v| <= 448 (guaranteed by
+// the block scale).  Works on the fp32 bit pattern: the value is re-expressed
+// at 3 mantissa bits (normals) or in units of 2^-9 (subnormals) with an
+// integer round-half-even on the dropped bits.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v)
+{
+    uint32_t u = __float_as_uint(v);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return sign | 0x7fu;            // NaN
+    int ef = (int)(a >> 23);                               // biased fp32 exponent
+    int e = ef - 127;
+    if (e < -6) {
+        // subnormal E4M3: q = round(|v| * 2^9), |v| < 2^-6 => q in [0, 8]
+        if (ef == 0) return sign;                          // fp32 subnormal -> 0
+        uint32_t m = (a & 0x7fffffu) | 0x800000u;          // |v| = m * 2^(e-23)
+        int sh = 23 - 9 - e;                                // q = m >> sh, rounded
+        if (sh > 24) return sign;
+        uint32_t q = m >> sh;
+        uint32_t rem = m & ((1u << sh) - 1u);
+        uint32_t half = 1u << (sh - 1);
+        if (rem > half || (rem == half && (q & 1u))) q += 1u;
+        return sign | q;                                    // q == 8 is the smallest normal
+    }
+    uint32_t m = a & 0x7fffffu;
+    uint32_t q = m >> 20;                                   // 3 kept mantissa bits
+    uint32_t rem = m & 0xfffffu;
+    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) q += 1u;
+    uint32_t code = ((uint32_t)(e + 7) << 3) + q;           // carry moves into the exponent
+    return sign | code;
+}
+
+// ---------------------------------------------------------------- workspace
+
+// Byte layout of the caller's workspace.  Offsets are 256-byte aligned.
+struct WsLayout {
+    size_t hdr;            // WsHeader
+    size_t counts;         // int32 [E]
+    size_t offsets;        // int32 [E + 1]
+    size_t chunk_base;     // int32 [nchunks][E]: chunk counts, then global bases
+    size_t chunk_err;      // uint32 [nchunks]
+    size_t local_rank;     // int32 [T_cap * k]
+    size_t sorted_ids;     // int32 [T_cap * k]
+    size_t sorted_probs;   // float [T_cap * k]
+    size_t perm_src;       // int32 [T_cap * k]
+    size_t dst;            // int32 [T_cap * k]
+    size_t tiles;          // int2 [max_tiles]: (expert, first row)
+    size_t hbuf;           // bf16 [T_cap * k][F] or E4M3 [T_cap * k][F]
+    size_t hscale;         // E8M0 [T_cap * k][F / 32] (mxfp8)
+    size_t obuf;           // float [T_cap * k][H]
+    size_t xq;             // E4M3 [T_cap][H] (mxfp8)
+    size_t xs;             // E8M0 [T_cap][H / 32] (mxfp8)
+    size_t total;
+    int64_t nchunks;
+    int64_t max_tiles;
+};
+
+struct WsHeader {
+    uint32_t fwd_err;      // contract-violation bits of the last forward
+    uint32_t route_err;    // contract-violation bits of the last route
+    int32_t T;             // live tokens of the last forward (clamped)
+    int32_t n_tiles;       // M tiles in the tile table
+    int32_t n_rows;        // routed rows with a valid expert
+    int32_t pad[59];
+};
+
+static_assert(sizeof(WsHeader) == 256, "header is one 256-byte block");
+
+}  // namespace moe

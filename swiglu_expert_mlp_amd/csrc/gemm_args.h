@@ -1,0 +1,44 @@
+// Launch arguments of the grouped expert GEMMs (shared by host and device code).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace moe {
+
+// bf16 operands.
+struct GemmArgs {
+    const uint16_t* A;         // FC1: x [T_cap][H]; FC2: hbuf [rows][F]
+    const uint16_t* W;         // FC1: packed W1 [E][2F][H]; FC2: W2 [E][H][F]
+    const int32_t* perm_src;   // FC1: grouped row -> route (t * k + j)
+    const int2* tiles;         // (expert, first row) per M tile
+    const int32_t* offsets;    // [E + 1]
+    const WsHeader* hdr;       // n_tiles
+    void* out;                 // FC1: hbuf bf16 [rows][F]; FC2: obuf fp32 [rows][H]
+    int N;                     // FC1: 2F; FC2: H
+    int K;                     // FC1: H;  FC2: F
+    int topk;
+    int n_tiles_n;             // N tiles per M tile (4 waves x 64 columns each)
+};
+
+// MXFP8 operands: E4M3 codes with one E8M0 scale byte per 32 elements of K.
+struct MxGemmArgs {
+    const uint8_t* A;          // FC1: xq [T_cap][H]; FC2: hbuf codes [rows][F]
+    const uint8_t* As;         // FC1: xs [T_cap][H/32]; FC2: hbuf scales [rows][F/32]
+    const uint8_t* W;          // FC1: packed W1 codes [E][2F][H]; FC2: W2 codes [E][H][F]
+    const uint8_t* Ws;         // scales [E][N][K/32]
+    const int32_t* perm_src;
+    const int2* tiles;
+    const int32_t* offsets;
+    const WsHeader* hdr;
+    void* out;                 // FC1: hbuf codes [rows][F]; FC2: obuf fp32 [rows][H]
+    uint8_t* out_scale;        // FC1: hbuf scales [rows][F/32]
+    int N;
+    int K;
+    int topk;
+    int n_tiles_n;
+};
+
+}  // namespace moe

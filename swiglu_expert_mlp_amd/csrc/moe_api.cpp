@@ -1,0 +1,377 @@
+// Host side of the C ABI declared in include/moe.h: argument checks, the
+// workspace layout, and the launch sequence of one forward.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/moe.h"
+#include "common.h"
+
+namespace moe {
+hipError_t launch_route(const float* logits, int64_t T_cap, const int32_t* live, int E, int k,
+                        int32_t* ids, float* probs, WsHeader* hdr, int num_cu, hipStream_t s);
+hipError_t launch_prep(const int32_t* ids, const float* probs, int64_t T_cap, const int32_t* live,
+                       int E, int k, int num_cu, char* ws, const WsLayout& L, hipStream_t s);
+hipError_t launch_finalize(const float* O, const int32_t* dst, const float* sorted_probs,
+                           int64_t T_cap, const int32_t* live, int k, int H, float* out, int num_cu,
+                           hipStream_t s);
+hipError_t launch_pack_bf16(const uint16_t* w1, const uint16_t* w2, uint8_t* kbuf, int E, int H,
+                            int F, int num_cu, hipStream_t s);
+hipError_t launch_pack_mxfp8(const uint16_t* w1, const uint16_t* w2, uint8_t* kbuf, int E, int H,
+                             int F, int num_cu, hipStream_t s);
+hipError_t launch_quant_x(const uint16_t* x, int64_t T_cap, const int32_t* live, int H,
+                          uint8_t* codes, uint8_t* scales, int num_cu, hipStream_t s);
+}  // namespace moe
+
+#include "gemm_args.h"
+
+namespace moe {
+hipError_t launch_gemm_bf16(bool fc1, const GemmArgs& g, int num_cu, hipStream_t s);
+hipError_t launch_gemm_mxfp8(bool fc1, const MxGemmArgs& g, int num_cu, hipStream_t s);
+}  // namespace moe
+
+using namespace moe;
+
+struct moe_ctx {
+    int E, H, F, k, precision;
+    const uint8_t* kbuf = nullptr;   // not owned
+    int num_cu = 0;
+    int device = -1;
+};
+
+static thread_local std::string g_err;
+
+static moe_status fail(moe_status st, const char* fmt, ...)
+    __attribute__((format(printf, 2, 3)));
+
+static moe_status fail(moe_status st, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+static moe_status hip_fail(hipError_t e, const char* what)
+{
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static size_t up256(size_t v) { return (v + 255) / 256 * 256; }
+
+static WsLayout layout_of(const moe_ctx* h, int64_t T_cap)
+{
+    WsLayout L;
+    const int64_t E = h->E, H = h->H, F = h->F, k = h->k;
+    const int64_t R = T_cap * k;
+    L.nchunks = (T_cap + kChunkTok - 1) / kChunkTok;
+    if (L.nchunks < 1) L.nchunks = 1;
+    L.max_tiles = E + (R + kBM - 1) / kBM + 1;
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o += up256(bytes > 0 ? bytes : 1); return at; };
+    L.hdr = take(sizeof(WsHeader));
+    L.counts = take(4 * E);
+    L.offsets = take(4 * (E + 1));
+    L.chunk_base = take(4 * E * L.nchunks);
+    L.chunk_err = take(4 * L.nchunks);
+    L.local_rank = take(4 * R);
+    L.sorted_ids = take(4 * R);
+    L.sorted_probs = take(4 * R);
+    L.perm_src = take(4 * R);
+    L.dst = take(4 * R);
+    L.tiles = take(8 * L.max_tiles);
+    if (h->precision == MOE_BF16) {
+        L.hbuf = take(2 * R * F);
+        L.hscale = 0;
+        L.xq = L.xs = 0;
+    } else {
+        L.hbuf = take(R * F);
+        L.hscale = take(R * (F / 32));
+        L.xq = take(T_cap * H);
+        L.xs = take(T_cap * (H / 32));
+    }
+    L.obuf = take(4 * R * H);
+    L.total = o;
+    return L;
+}
+
+static moe_status ensure_device(moe_ctx* h)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (h->device != dev || h->num_cu <= 0) {
+        int cus = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+        h->device = dev;
+        h->num_cu = cus > 0 ? cus : 1;
+    }
+    return MOE_OK;
+}
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+moe_status moe_create(int E, int H, int F, int topk, int precision, moe_handle* out)
+{
+    if (!out) return fail(MOE_ERR_INVALID_ARG, "moe_create: out is NULL");
+    *out = nullptr;
+    if (precision != MOE_BF16 && precision != MOE_MXFP8)
+        return fail(MOE_ERR_UNSUPPORTED, "moe_create: precision %d is not supported (bf16=0, mxfp8=1)",
+                    precision);
+    if (E < 1 || E > kMaxExperts)
+        return fail(MOE_ERR_INVALID_ARG, "moe_create: E=%d outside [1, %d]", E, kMaxExperts);
+    if (topk < 1 || topk > kMaxTopk || topk > E)
+        return fail(MOE_ERR_INVALID_ARG, "moe_create: topk=%d outside [1, min(E, %d)]", topk, kMaxTopk);
+    if (H <= 0 || H % 32 != 0)
+        return fail(MOE_ERR_INVALID_ARG, "moe_create: H=%d must be a positive multiple of 32", H);
+    if (F <= 0 || F % 32 != 0)
+        return fail(MOE_ERR_INVALID_ARG, "moe_create: F=%d must be a positive multiple of 32", F);
+    moe_ctx* h = new moe_ctx();
+    h->E = E; h->H = H; h->F = F; h->k = topk; h->precision = precision;
+    *out = h;
+    g_err.clear();
+    return MOE_OK;
+}
+
+void moe_destroy(moe_handle h) { delete h; }
+
+size_t moe_weight_bytes(moe_handle h)
+{
+    if (!h) return 0;
+    size_t n1 = (size_t)h->E * 2 * h->F * h->H, n2 = (size_t)h->E * h->H * h->F;
+    if (h->precision == MOE_BF16) return 2 * (n1 + n2);
+    return up256(n1) + up256(n2) + up256(n1 / 32) + up256(n2 / 32);
+}
+
+size_t moe_workspace_bytes(moe_handle h, int64_t T_cap)
+{
+    if (!h || T_cap < 0) return 0;
+    return layout_of(h, T_cap).total;
+}
+
+moe_status moe_load_weights(moe_handle h, const void* w1, const void* w2, void* kbuf,
+                            size_t kbuf_bytes, hipStream_t stream)
+{
+    if (!h) return fail(MOE_ERR_INVALID_ARG, "moe_load_weights: NULL handle");
+    if (!w1 || !w2 || !kbuf) return fail(MOE_ERR_INVALID_ARG, "moe_load_weights: NULL pointer");
+    if (!aligned16(w1) || !aligned16(w2) || !aligned16(kbuf))
+        return fail(MOE_ERR_INVALID_ARG, "moe_load_weights: pointers must be 16-byte aligned");
+    if (kbuf_bytes < moe_weight_bytes(h))
+        return fail(MOE_ERR_INVALID_ARG, "moe_load_weights: kbuf_bytes %zu < %zu", kbuf_bytes,
+                    moe_weight_bytes(h));
+    moe_status st = ensure_device(h);
+    if (st != MOE_OK) return st;
+    hipError_t e = h->precision == MOE_BF16
+                       ? launch_pack_bf16((const uint16_t*)w1, (const uint16_t*)w2, (uint8_t*)kbuf,
+                                          h->E, h->H, h->F, h->num_cu, stream)
+                       : launch_pack_mxfp8((const uint16_t*)w1, (const uint16_t*)w2, (uint8_t*)kbuf,
+                                           h->E, h->H, h->F, h->num_cu, stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_load_weights: launch");
+    h->kbuf = (const uint8_t*)kbuf;
+    return MOE_OK;
+}
+
+moe_status moe_route(moe_handle h, const float* logits, int64_t T_cap,
+                     const int32_t* live_rows_dev, int32_t* ids, float* probs, void* ws,
+                     size_t ws_bytes, hipStream_t stream)
+{
+    if (!h) return fail(MOE_ERR_INVALID_ARG, "moe_route: NULL handle");
+    if (T_cap < 0 || T_cap > (int64_t)1 << 26)
+        return fail(MOE_ERR_INVALID_ARG, "moe_route: T_cap=%lld out of range", (long long)T_cap);
+    if (!logits || !live_rows_dev || !ids || !probs || !ws)
+        return fail(MOE_ERR_INVALID_ARG, "moe_route: NULL pointer");
+    if (ws_bytes < sizeof(WsHeader))
+        return fail(MOE_ERR_INVALID_ARG, "moe_route: workspace too small");
+    if (!aligned16(logits) || !aligned16(ids) || !aligned16(probs) || !aligned16(ws))
+        return fail(MOE_ERR_INVALID_ARG, "moe_route: pointers must be 16-byte aligned");
+    moe_status st = ensure_device(h);
+    if (st != MOE_OK) return st;
+    if (T_cap == 0) return MOE_OK;
+    hipError_t e = launch_route(logits, T_cap, live_rows_dev, h->E, h->k, ids, probs,
+                                (WsHeader*)ws, h->num_cu, stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_route: launch");
+    return MOE_OK;
+}
+
+moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
+                       const float* probs, int64_t T_cap, const int32_t* live_rows_dev,
+                       float* out, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (!h) return fail(MOE_ERR_INVALID_ARG, "moe_forward: NULL handle");
+    if (!h->kbuf) return fail(MOE_ERR_NOT_LOADED, "moe_forward: no weights loaded (moe_load_weights)");
+    if (T_cap < 0 || T_cap > (int64_t)1 << 26)
+        return fail(MOE_ERR_INVALID_ARG, "moe_forward: T_cap=%lld out of range", (long long)T_cap);
+    if (!x || !expert_ids || !probs || !live_rows_dev || !out || !ws)
+        return fail(MOE_ERR_INVALID_ARG, "moe_forward: NULL pointer");
+    if (!aligned16(x) || !aligned16(expert_ids) || !aligned16(probs) || !aligned16(out) ||
+        !aligned16(ws))
+        return fail(MOE_ERR_INVALID_ARG, "moe_forward: pointers must be 16-byte aligned");
+    const WsLayout L = layout_of(h, T_cap);
+    if (ws_bytes < L.total)
+        return fail(MOE_ERR_INVALID_ARG, "moe_forward: ws_bytes %zu < %zu for T_cap=%lld", ws_bytes,
+                    L.total, (long long)T_cap);
+    moe_status st = ensure_device(h);
+    if (st != MOE_OK) return st;
+    if (T_cap == 0) return MOE_OK;
+    char* w = (char*)ws;
+    WsHeader* hdr = (WsHeader*)(w + L.hdr);
+    hipError_t e = launch_prep(expert_ids, probs, T_cap, live_rows_dev, h->E, h->k, h->num_cu, w, L,
+                               stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_forward: prep launch");
+    const int E = h->E, H = h->H, F = h->F;
+    if (h->precision == MOE_BF16) {
+        GemmArgs g1;
+        g1.A = (const uint16_t*)x;
+        g1.W = (const uint16_t*)h->kbuf;
+        g1.perm_src = (const int32_t*)(w + L.perm_src);
+        g1.tiles = (const int2*)(w + L.tiles);
+        g1.offsets = (const int32_t*)(w + L.offsets);
+        g1.hdr = hdr;
+        g1.out = w + L.hbuf;
+        g1.N = 2 * F;
+        g1.K = H;
+        g1.topk = h->k;
+        g1.n_tiles_n = ((2 * F / 64) + 3) / 4;
+        e = launch_gemm_bf16(true, g1, h->num_cu, stream);
+        if (e != hipSuccess) return hip_fail(e, "moe_forward: FC1 launch");
+        GemmArgs g2 = g1;
+        g2.A = (const uint16_t*)(w + L.hbuf);
+        g2.W = (const uint16_t*)h->kbuf + (size_t)E * 2 * F * H;
+        g2.perm_src = nullptr;
+        g2.out = w + L.obuf;
+        g2.N = H;
+        g2.K = F;
+        g2.n_tiles_n = ((H + 63) / 64 + 3) / 4;
+        e = launch_gemm_bf16(false, g2, h->num_cu, stream);
+        if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
+    } else {
+        size_t n1 = (size_t)E * 2 * F * H, n2 = (size_t)E * H * F;
+        const uint8_t* c1 = h->kbuf;
+        const uint8_t* c2 = c1 + up256(n1);
+        const uint8_t* s1 = c2 + up256(n2);
+        const uint8_t* s2 = s1 + up256(n1 / 32);
+        e = launch_quant_x((const uint16_t*)x, T_cap, live_rows_dev, H, (uint8_t*)(w + L.xq),
+                           (uint8_t*)(w + L.xs), h->num_cu, stream);
+        if (e != hipSuccess) return hip_fail(e, "moe_forward: quant-x launch");
+        MxGemmArgs g1;
+        g1.A = (const uint8_t*)(w + L.xq);
+        g1.As = (const uint8_t*)(w + L.xs);
+        g1.W = c1;
+        g1.Ws = s1;
+        g1.perm_src = (const int32_t*)(w + L.perm_src);
+        g1.tiles = (const int2*)(w + L.tiles);
+        g1.offsets = (const int32_t*)(w + L.offsets);
+        g1.hdr = hdr;
+        g1.out = w + L.hbuf;
+        g1.out_scale = (uint8_t*)(w + L.hscale);
+        g1.N = 2 * F;
+        g1.K = H;
+        g1.topk = h->k;
+        g1.n_tiles_n = ((2 * F / 64) + 3) / 4;
+        e = launch_gemm_mxfp8(true, g1, h->num_cu, stream);
+        if (e != hipSuccess) return hip_fail(e, "moe_forward: FC1 launch");
+        MxGemmArgs g2 = g1;
+        g2.A = (const uint8_t*)(w + L.hbuf);
+        g2.As = (const uint8_t*)(w + L.hscale);
+        g2.W = c2;
+        g2.Ws = s2;
+        g2.perm_src = nullptr;
+        g2.out = w + L.obuf;
+        g2.out_scale = nullptr;
+        g2.N = H;
+        g2.K = F;
+        g2.n_tiles_n = ((H + 63) / 64 + 3) / 4;
+        e = launch_gemm_mxfp8(false, g2, h->num_cu, stream);
+        if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
+    }
+    e = launch_finalize((const float*)(w + L.obuf), (const int32_t*)(w + L.dst),
+                        (const float*)(w + L.sorted_probs), T_cap, live_rows_dev, h->k, H, out,
+                        h->num_cu, stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_forward: finalize launch");
+    return MOE_OK;
+}
+
+moe_status moe_get_indices(moe_handle h, const void* ws, int64_t T_cap, int32_t* counts,
+                           int32_t* offsets, int32_t* perm_src, int32_t* dst,
+                           int32_t* n_rows_out, int32_t* T_out, hipStream_t stream)
+{
+    if (!h || !ws) return fail(MOE_ERR_INVALID_ARG, "moe_get_indices: NULL handle or workspace");
+    const WsLayout L = layout_of(h, T_cap);
+    const char* w = (const char*)ws;
+    WsHeader hdr;
+    hipError_t e = hipMemcpyAsync(&hdr, w + L.hdr, sizeof(hdr), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_get_indices: header copy");
+    const int64_t R = (int64_t)hdr.T * h->k;
+    if (counts) e = hipMemcpy(counts, w + L.counts, 4 * h->E, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && offsets)
+        e = hipMemcpy(offsets, w + L.offsets, 4 * (h->E + 1), hipMemcpyDeviceToHost);
+    if (e == hipSuccess && perm_src && hdr.n_rows > 0)
+        e = hipMemcpy(perm_src, w + L.perm_src, 4 * (size_t)hdr.n_rows, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && dst && R > 0)
+        e = hipMemcpy(dst, w + L.dst, 4 * (size_t)R, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "moe_get_indices: copy");
+    if (n_rows_out) *n_rows_out = hdr.n_rows;
+    if (T_out) *T_out = hdr.T;
+    return MOE_OK;
+}
+
+moe_status moe_get_rows(moe_handle h, const void* ws, int64_t T_cap, float* fc2_rows,
+                        void* fc1_out_rows, int32_t* sorted_ids, float* sorted_probs,
+                        hipStream_t stream)
+{
+    if (!h || !ws) return fail(MOE_ERR_INVALID_ARG, "moe_get_rows: NULL handle or workspace");
+    const WsLayout L = layout_of(h, T_cap);
+    const char* w = (const char*)ws;
+    WsHeader hdr;
+    hipError_t e = hipMemcpyAsync(&hdr, w + L.hdr, sizeof(hdr), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_get_rows: header copy");
+    const size_t n = (size_t)hdr.n_rows;
+    const size_t R = (size_t)hdr.T * h->k;
+    if (fc2_rows && n) e = hipMemcpy(fc2_rows, w + L.obuf, 4 * n * h->H, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && fc1_out_rows && n) {
+        if (h->precision == MOE_BF16) {
+            e = hipMemcpy(fc1_out_rows, w + L.hbuf, 2 * n * h->F, hipMemcpyDeviceToHost);
+        } else {
+            e = hipMemcpy(fc1_out_rows, w + L.hbuf, n * h->F, hipMemcpyDeviceToHost);
+            if (e == hipSuccess)
+                e = hipMemcpy((char*)fc1_out_rows + n * h->F, w + L.hscale, n * (h->F / 32),
+                              hipMemcpyDeviceToHost);
+        }
+    }
+    if (e == hipSuccess && sorted_ids && R)
+        e = hipMemcpy(sorted_ids, w + L.sorted_ids, 4 * R, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && sorted_probs && R)
+        e = hipMemcpy(sorted_probs, w + L.sorted_probs, 4 * R, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "moe_get_rows: copy");
+    return MOE_OK;
+}
+
+moe_status moe_check(moe_handle h, void* ws, hipStream_t stream, uint32_t* err_bits)
+{
+    if (!h || !ws || !err_bits) return fail(MOE_ERR_INVALID_ARG, "moe_check: NULL argument");
+    uint32_t words[2] = {0, 0};
+    hipError_t e = hipMemcpyAsync(words, ws, sizeof(words), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_check: read");
+    *err_bits = words[0] | words[1];
+    uint32_t zero[2] = {0, 0};
+    e = hipMemcpyAsync(ws, zero, sizeof(zero), hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_check: clear");
+    return MOE_OK;
+}
+
+}  // extern "C"
