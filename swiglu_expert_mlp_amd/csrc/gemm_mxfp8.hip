@@ -12,8 +12,11 @@
 // with the scales of the four 32-blocks, in that order for every row, tile
 // and launch.  A K tail shorter than 128 is padded with zero codes.
 //
-// Lane layout (both operands): lane l holds row (l % 16) and the 32 K values
-// of block (l / 16) of the 128-wide step, plus that block's scale byte.
+// Lane layout of one 128-wide K step (both operands): lane l holds row (l % 16);
+// its first 16 bytes are K = 16 * (l / 16) + [0, 16) and its last 16 bytes are
+// K = 64 + 16 * (l / 16) + [0, 16).  The scale byte of lane l applies to the
+// 32-block (l / 16) of the step, i.e. 32-block q is made of the first halves
+// (q < 2) or second halves (q >= 2) of lane groups 2 (q % 2) and 2 (q % 2) + 1.
 // Work decomposition is the same as the bf16 kernels: persistent grid over
 // (M tile, N tile), 4 waves x 64 columns, up to 64 rows per M tile.
 #include "gemm_args.h"
@@ -35,7 +38,7 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs& g, int e, int row
         if (r >= rows) r = rows - 1;
         int64_t arow = row0 + r;
         if constexpr (FC1) arow = g.perm_src[arow] / g.topk;
-        ap[rg] = g.A + arow * K + 32 * kg;
+        ap[rg] = g.A + arow * K + 16 * kg;
         as[rg] = g.As + arow * KB + kg;
     }
     const uint8_t* bp[4];
@@ -45,7 +48,7 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs& g, int e, int row
         int col = cb * 64 + 16 * ct + r16;
         if (col >= g.N) col = g.N - 1;
         int64_t wrow = (int64_t)e * g.N + col;
-        bp[ct] = g.W + wrow * K + 32 * kg;
+        bp[ct] = g.W + wrow * K + 16 * kg;
         bs[ct] = g.Ws + wrow * KB + kg;
     }
     f32x4 acc[NG][4];
@@ -55,33 +58,28 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs& g, int e, int row
         for (int ct = 0; ct < 4; ++ct) acc[rg][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     for (int k0 = 0; k0 < K; k0 += 128) {
-        // this lane's 32-element block is in range or entirely past K
-        const bool in = k0 + 32 * kg < K;
+        // K is a multiple of 32: each 16-byte half and each 32-block is either
+        // inside K or entirely past it (then zero codes, scale 2^0)
+        const bool lo_in = k0 + 16 * kg < K, hi_in = k0 + 64 + 16 * kg < K;
+        const bool s_in = k0 + 32 * kg < K;
+        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
         i32x8 a[NG], b[4];
         int sa[NG], sb[4];
 #pragma unroll
         for (int rg = 0; rg < NG; ++rg) {
-            if (in) {
-                uint4 lo = *(const uint4*)(ap[rg] + k0), hi = *(const uint4*)(ap[rg] + k0 + 16);
-                a[rg] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                              (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                sa[rg] = as[rg][k0 / 32];
-            } else {
-                a[rg] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-                sa[rg] = 127;
-            }
+            uint4 lo = lo_in ? *(const uint4*)(ap[rg] + k0) : z;
+            uint4 hi = hi_in ? *(const uint4*)(ap[rg] + k0 + 64) : z;
+            a[rg] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                          (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            sa[rg] = s_in ? (int)as[rg][k0 / 32] : 127;
         }
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
-            if (in) {
-                uint4 lo = *(const uint4*)(bp[ct] + k0), hi = *(const uint4*)(bp[ct] + k0 + 16);
-                b[ct] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                              (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                sb[ct] = bs[ct][k0 / 32];
-            } else {
-                b[ct] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-                sb[ct] = 127;
-            }
+            uint4 lo = lo_in ? *(const uint4*)(bp[ct] + k0) : z;
+            uint4 hi = hi_in ? *(const uint4*)(bp[ct] + k0 + 64) : z;
+            b[ct] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                          (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            sb[ct] = s_in ? (int)bs[ct][k0 / 32] : 127;
         }
 #pragma unroll
         for (int rg = 0; rg < NG; ++rg)
