@@ -152,6 +152,14 @@ moe_status moe_get_rows(moe_handle h, const void* ws, int64_t T_cap, float* fc2_
  * in *err_bits, and clear them. */
 moe_status moe_check(moe_handle h, void* ws, hipStream_t stream, uint32_t* err_bits);
 
+/* Stage timing hook (for profiling).  With events != NULL, every later
+ * moe_forward on this handle records, on its stream, events[0] before its
+ * first kernel and events[i] after stage i: 1 permutation (sort, histogram,
+ * scan, scatter), 2 MXFP8 activation quantization (nothing in bf16), 3 FC1 +
+ * SwiGLU, 4 FC2, 5 finalize.  n_events must be 6.  The events are the
+ * caller's; pass NULL to stop recording. */
+moe_status moe_set_stage_events(moe_handle h, hipEvent_t* events, int n_events);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* moe_last_error(void);
 

@@ -46,6 +46,7 @@ _SIGNATURES = {
     "moe_get_indices": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P]),
     "moe_get_rows": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P, _P, _P, _P, _P]),
     "moe_check": (ctypes.c_int, [_P, _P, _P, ctypes.POINTER(ctypes.c_uint32)]),
+    "moe_set_stage_events": (ctypes.c_int, [_P, _P, ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
 }
 
@@ -236,6 +237,19 @@ class MoE:
             res["fc1_scales"] = hr[n_rows * self.F: n_rows * (self.F + self.F // 32)].reshape(
                 n_rows, self.F // 32)
         return res
+
+    STAGES = ("permute", "quant_x", "fc1_swiglu", "fc2", "finalize")
+
+    def set_stage_events(self, events):
+        """Record the 6 torch.cuda.Event objects at the forward's stage boundaries
+        (before the first kernel, then after each of STAGES); None stops."""
+        if events is None:
+            _check(lib().moe_set_stage_events(self._h, None, 0), "moe_set_stage_events")
+            return
+        if len(events) != 6:
+            raise ValueError("need 6 events")
+        arr = (_P * 6)(*[_P(ev.cuda_event) for ev in events])
+        _check(lib().moe_set_stage_events(self._h, arr, 6), "moe_set_stage_events")
 
     def check(self, ws, stream=None) -> int:
         bits = ctypes.c_uint32(0)

@@ -40,7 +40,14 @@ struct moe_ctx {
     const uint8_t* kbuf = nullptr;   // not owned
     int num_cu = 0;
     int device = -1;
+    hipEvent_t stage_events[6] = {};
+    bool record_stages = false;
 };
+
+static hipError_t mark(moe_ctx* h, int i, hipStream_t s)
+{
+    return h->record_stages ? hipEventRecord(h->stage_events[i], s) : hipSuccess;
+}
 
 static thread_local std::string g_err;
 
@@ -226,11 +233,15 @@ moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
     if (T_cap == 0) return MOE_OK;
     char* w = (char*)ws;
     WsHeader* hdr = (WsHeader*)(w + L.hdr);
-    hipError_t e = launch_prep(expert_ids, probs, T_cap, live_rows_dev, h->E, h->k, h->num_cu, w, L,
+    hipError_t e = mark(h, 0, stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_forward: stage event");
+    e = launch_prep(expert_ids, probs, T_cap, live_rows_dev, h->E, h->k, h->num_cu, w, L,
                                stream);
     if (e != hipSuccess) return hip_fail(e, "moe_forward: prep launch");
+    if ((e = mark(h, 1, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     const int E = h->E, H = h->H, F = h->F;
     if (h->precision == MOE_BF16) {
+        if ((e = mark(h, 2, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
         GemmArgs g1;
         g1.A = (const uint16_t*)x;
         g1.W = (const uint16_t*)h->kbuf;
@@ -245,6 +256,7 @@ moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
         g1.n_tiles_n = ((2 * F / 64) + 3) / 4;
         e = launch_gemm_bf16(true, g1, h->num_cu, stream);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC1 launch");
+        if ((e = mark(h, 3, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
         GemmArgs g2 = g1;
         g2.A = (const uint16_t*)(w + L.hbuf);
         g2.W = (const uint16_t*)h->kbuf + (size_t)E * 2 * F * H;
@@ -255,6 +267,7 @@ moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
         g2.n_tiles_n = ((H + 63) / 64 + 3) / 4;
         e = launch_gemm_bf16(false, g2, h->num_cu, stream);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
+        if ((e = mark(h, 4, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     } else {
         size_t n1 = (size_t)E * 2 * F * H, n2 = (size_t)E * H * F;
         const uint8_t* c1 = h->kbuf;
@@ -264,6 +277,7 @@ moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
         e = launch_quant_x((const uint16_t*)x, T_cap, live_rows_dev, H, (uint8_t*)(w + L.xq),
                            (uint8_t*)(w + L.xs), h->num_cu, stream);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: quant-x launch");
+        if ((e = mark(h, 2, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
         MxGemmArgs g1;
         g1.A = (const uint8_t*)(w + L.xq);
         g1.As = (const uint8_t*)(w + L.xs);
@@ -281,6 +295,7 @@ moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
         g1.n_tiles_n = ((2 * F / 64) + 3) / 4;
         e = launch_gemm_mxfp8(true, g1, h->num_cu, stream);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC1 launch");
+        if ((e = mark(h, 3, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
         MxGemmArgs g2 = g1;
         g2.A = (const uint8_t*)(w + L.hbuf);
         g2.As = (const uint8_t*)(w + L.hscale);
@@ -294,11 +309,13 @@ moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
         g2.n_tiles_n = ((H + 63) / 64 + 3) / 4;
         e = launch_gemm_mxfp8(false, g2, h->num_cu, stream);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
+        if ((e = mark(h, 4, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     }
     e = launch_finalize((const float*)(w + L.obuf), (const int32_t*)(w + L.dst),
                         (const float*)(w + L.sorted_probs), T_cap, live_rows_dev, h->k, H, out,
                         h->num_cu, stream);
     if (e != hipSuccess) return hip_fail(e, "moe_forward: finalize launch");
+    if ((e = mark(h, 5, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     return MOE_OK;
 }
 
@@ -356,6 +373,16 @@ moe_status moe_get_rows(moe_handle h, const void* ws, int64_t T_cap, float* fc2_
     if (e == hipSuccess && sorted_probs && R)
         e = hipMemcpy(sorted_probs, w + L.sorted_probs, 4 * R, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "moe_get_rows: copy");
+    return MOE_OK;
+}
+
+moe_status moe_set_stage_events(moe_handle h, hipEvent_t* events, int n_events)
+{
+    if (!h) return fail(MOE_ERR_INVALID_ARG, "moe_set_stage_events: NULL handle");
+    if (!events) { h->record_stages = false; return MOE_OK; }
+    if (n_events != 6) return fail(MOE_ERR_INVALID_ARG, "moe_set_stage_events: n_events must be 6");
+    for (int i = 0; i < 6; ++i) h->stage_events[i] = events[i];
+    h->record_stages = true;
     return MOE_OK;
 }
 
