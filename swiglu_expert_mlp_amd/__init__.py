@@ -248,6 +248,9 @@ class MoE:
             return
         if len(events) != 6:
             raise ValueError("need 6 events")
+        for ev in events:
+            if not ev.cuda_event:        # torch creates the HIP event at its first record
+                ev.record()
         arr = (_P * 6)(*[_P(ev.cuda_event) for ev in events])
         _check(lib().moe_set_stage_events(self._h, arr, 6), "moe_set_stage_events")
 
