@@ -63,6 +63,50 @@ def alg_bytes(w, precision: str, touched: int) -> dict:
     return dict(fc1=fc1, fc2=fc2, step=step)
 
 
+class HipEvents:
+    """HIP timing events created with a device-scope release
+    (hipEventReleaseToDevice), which keeps the record cheap: a default event
+    does a system-scope cache write-back at every record."""
+
+    RELEASE_TO_DEVICE = 0x40000000
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def new(self) -> int:
+        ev = self.ct.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(self.ct.byref(ev), self.RELEASE_TO_DEVICE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.made.append(ev.value)
+        return ev.value
+
+    def record(self, ev: int, stream: int):
+        rc = self.hip.hipEventRecord(ev, stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def ms(self, a: int, b: int) -> float:
+        out = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(out), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(out.value)
+
+    def close(self):
+        for ev in self.made:
+            self.hip.hipEventDestroy(ev)
+        self.made = []
+
+
 def main():
     a = _args()
     if a.gpus != 1:
@@ -76,9 +120,7 @@ def main():
 
     w = WORKLOADS[a.workload]
     dev = torch.device("cuda:0")
-    t_gen = time.time()
     inp = make_inputs(w, seed=a.seed, outliers=(w.precision == "mxfp8"))
-    t_gen = time.time() - t_gen
     bf = lambda arr: torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(
         torch.bfloat16).to(dev)
     x = bf(inp["x_bits"])
@@ -87,6 +129,7 @@ def main():
     logits = torch.from_numpy(inp["logits"]).to(dev)
     live = torch.tensor([w.T], dtype=torch.int32, device=dev)
 
+    # rotate kernel-weight buffers so that their total exceeds twice the MALL
     moe0 = MoE(w.E, w.H, w.F, w.k, w.precision)
     kb = moe0.weight_bytes
     n_rot = max(2, math.ceil(2 * MALL_BYTES / kb) + 1) if kb < 2 * MALL_BYTES else 2
@@ -99,16 +142,13 @@ def main():
     probs = torch.empty((w.T_cap, w.k), dtype=torch.float32, device=dev)
     out = torch.empty((w.T_cap, w.H), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    route_fn = [m.bind_route(logits, live, ids, probs, ws) for m in moes]
+    fwd_fn = [m.bind_forward(x, ids, probs, live, out, ws) for m in moes]
 
-    def step(i, events=None, rev=None):
-        m = moes[i % n_rot]
-        if rev is not None:
-            rev[0].record(stream)
-        m.route(logits, live, ids=ids, probs=probs, ws=ws)
-        if rev is not None:
-            rev[1].record(stream)
-        m.set_stage_events(events)
-        m.forward(x, ids, probs, live, out=out, ws=ws)
+    def step(i):
+        route_fn[i % n_rot]()
+        fwd_fn[i % n_rot]()
 
     for i in range(a.warmup):
         step(i)
@@ -120,24 +160,42 @@ def main():
     touched = int(np.count_nonzero(idx["counts"]))
     loads = idx["counts"].astype(np.int64)
 
-    mk = lambda: torch.cuda.Event(enable_timing=True)
-    stage_ev = [[mk() for _ in range(6)] for _ in range(a.steps)]
-    route_ev = [[mk(), mk()] for _ in range(a.steps)]
-    t0, t1 = mk(), mk()
+    # timed region: K steps; the library records two events around the dominant
+    # kernel (FC1 + SwiGLU) of every step
+    ev = HipEvents()
+    fc1_ev = [(ev.new(), ev.new()) for _ in range(a.steps)]
+    t0, t1 = ev.new(), ev.new()
     torch.cuda.synchronize()
-    t0.record(stream)
+    ev.record(t0, sh)
     for i in range(a.steps):
-        step(i, stage_ev[i], route_ev[i])
-    t1.record(stream)
+        m = moes[i % n_rot]
+        m.set_stage_events([None, None, fc1_ev[i][0], fc1_ev[i][1], None, None])
+        step(i)
+    ev.record(t1, sh)
     torch.cuda.synchronize()
     for m in moes:
         m.set_stage_events(None)
-    ms_step = t0.elapsed_time(t1) / a.steps
+    ms_step = ev.ms(t0, t1) / a.steps
+    fc1_us = float(np.mean([ev.ms(p, q) for p, q in fc1_ev]) * 1e3)
 
+    # stage breakdown (untimed diagnostic pass)
+    n_diag = min(10, a.steps)
+    diag = [[ev.new() for _ in range(8)] for _ in range(n_diag)]
+    for i in range(n_diag):
+        m = moes[i % n_rot]
+        d = diag[i]
+        ev.record(d[6], sh)
+        route_fn[i % n_rot]()
+        ev.record(d[7], sh)
+        m.set_stage_events(d[:6])
+        fwd_fn[i % n_rot]()
+        m.set_stage_events(None)
+    torch.cuda.synchronize()
     names = MoE.STAGES
-    stage_us = {n: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in stage_ev]) * 1e3)
+    stage_us = {n: float(np.mean([ev.ms(d[j], d[j + 1]) for d in diag]) * 1e3)
                 for j, n in enumerate(names)}
-    route_us = float(np.mean([r[0].elapsed_time(r[1]) for r in route_ev]) * 1e3)
+    stage_us = {"route": float(np.mean([ev.ms(d[6], d[7]) for d in diag]) * 1e3), **stage_us}
+    ev.close()
 
     ab = alg_bytes(w, w.precision, touched)
     flops = w.flops()
@@ -145,13 +203,14 @@ def main():
     tflops = flops / (ms_step * 1e-3) / 1e12
     if w.precision == "mxfp8" or w.name in ("bf16_16k",):
         fc1_flops = 4.0 * w.H * w.F * w.R
-        roof = dict(bound="mfma", achieved=fc1_flops / (stage_us["fc1_swiglu"] * 1e-6) / 1e12,
+        roof = dict(bound="mfma", achieved=fc1_flops / (fc1_us * 1e-6) / 1e12,
                     peak=MFMA_PEAK_TFLOPS[w.precision], unit="TFLOP/s")
     else:
-        roof = dict(bound="hbm", achieved=ab["fc1"] / (stage_us["fc1_swiglu"] * 1e-6) / 1e9,
+        roof = dict(bound="hbm", achieved=ab["fc1"] / (fc1_us * 1e-6) / 1e9,
                     peak=HBM_PEAK_GBS, unit="GB/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["kernel"] = "gemm_bf16_kernel<FC1>" if w.precision == "bf16" else "gemm_mxfp8_kernel<FC1>"
+    roof["kernel_us"] = fc1_us
     roof["traffic"] = None
 
     res = {
@@ -166,7 +225,7 @@ def main():
         "mfma_frac": tflops / MFMA_PEAK_TFLOPS[w.precision],
         "hbm_gbs_step": ab["step"] / (ms_step * 1e-3) / 1e9,
         "hbm_frac_step": ab["step"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "stages_us": {"route": route_us, **stage_us},
+        "stages_us": stage_us,
         "expert_load": {"touched": touched, "min": int(loads.min()), "mean": float(loads.mean()),
                         "max": int(loads.max())},
         "weight_buffers_rotated": n_rot,

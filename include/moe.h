@@ -90,12 +90,22 @@ size_t moe_weight_bytes(moe_handle h);
  * PR #7830: caller-owned kernel-weight buffer, refit rewrites it in place).
  *   w1: bf16 [E][2F][H]; rows 0..F-1 of each expert are gate, F..2F-1 up.
  *   w2: bf16 [E][H][F].
- *   kbuf layout (bf16): FC1 [E][2F][H] with packed row 64b+i = gate row 32b+i
- *     (i < 32) or up row F+32b+i-32 (i >= 32), then FC2 [E][H][F] unchanged.
- *   kbuf layout (mxfp8), each section 256-byte aligned: FC1 E4M3 codes
- *     [E][2F][H] (packed row order), FC2 codes [E][H][F], FC1 E8M0 scales
- *     [E][2F][H/32], FC2 scales [E][H][F/32]; scale = power-of-two ceiling of
- *     the block's max magnitude / 448.
+ *   Row order: FC1 packed row 64b+i = gate row 32b+i (i < 32) or up row
+ *     F+32b+i-32 (i >= 32); FC2 rows [H] unchanged.  Rows are K-major and
+ *     tiled into MFMA operand blocks so that one wave's load is 1 KB contiguous.
+ *     For a section with N rows of K elements per expert:
+ *   kbuf layout (bf16): FC1 section (N = 2F, K = H) then FC2 section (N = H,
+ *     K = F); element (e, n, k) at element index
+ *       (((e*(N/16) + n/16)*(K/32) + k/32)*4 + (k%32)/8)*128 + (n%16)*8 + k%8.
+ *   kbuf layout (mxfp8): sections FC1 codes, FC2 codes, FC1 scales, FC2
+ *     scales, each starting at a multiple of 256 bytes.  With KS = ceil(K/128)
+ *     and KQ = ceil(KS/4), code (e, n, k) at byte
+ *       (((e*(N/16) + n/16)*KS + k/128)*2 + (k%128)/64)*1024
+ *         + ((k%64)/16*16 + n%16)*16 + k%16,
+ *     and the E8M0 scale of 32-block b = k/32 of row n at byte
+ *       ((e*(N/16) + n/16)*KQ + (b/4)/4)*256 + ((b%4)*16 + n%16)*4 + (b/4)%4;
+ *     positions past K hold code 0 and scale 127.  Scale = power-of-two
+ *     ceiling of the block's max magnitude / 448 (so no code saturates).
  * The handle remembers kbuf: every later forward reads it.  Calling again
  * (same or another buffer) is the refit; forwards enqueued before it on the
  * same stream read the old contents.  w1/w2 may be freed once the work on
@@ -156,8 +166,8 @@ moe_status moe_check(moe_handle h, void* ws, hipStream_t stream, uint32_t* err_b
  * moe_forward on this handle records, on its stream, events[0] before its
  * first kernel and events[i] after stage i: 1 permutation (sort, histogram,
  * scan, scatter), 2 MXFP8 activation quantization (nothing in bf16), 3 FC1 +
- * SwiGLU, 4 FC2, 5 finalize.  n_events must be 6.  The events are the
- * caller's; pass NULL to stop recording. */
+ * SwiGLU, 4 FC2, 5 finalize.  n_events must be 6; NULL entries are not
+ * recorded.  The events are the caller's; pass events = NULL to stop. */
 moe_status moe_set_stage_events(moe_handle h, hipEvent_t* events, int n_events);
 
 /* Message of the last failed call on this thread ("" if none). */

@@ -75,6 +75,7 @@ def lib() -> ctypes.CDLL:
             "orc_pack_bf16": (None, [ctypes.c_int] * 3 + [P, P, P]),
             "orc_pack_mxfp8": (None, [ctypes.c_int] * 3 + [P, P, P]),
             "orc_pack_bytes": (i64, [ctypes.c_int] * 4),
+            "orc_pack_mx_offsets": (None, [ctypes.c_int] * 3 + [P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -247,6 +248,14 @@ class Model:
 
 def pack_bytes(E, H, F, precision="bf16") -> int:
     return int(lib().orc_pack_bytes(E, H, F, int(precision == "mxfp8")))
+
+
+def pack_mx_offsets(E, H, F) -> list:
+    """Byte offsets of the MXFP8 buffer sections: FC1 codes, FC2 codes, FC1
+    scales, FC2 scales, end (each section's padding is part of the layout)."""
+    off = np.zeros(5, dtype=np.int64)
+    lib().orc_pack_mx_offsets(E, H, F, _p(off))
+    return [int(v) for v in off]
 
 
 def pack(E, H, F, w1_bits, w2_bits, precision="bf16") -> np.ndarray:

@@ -557,64 +557,110 @@ void orc_forward_tokens(void* wp, const uint16_t* x, const int32_t* ids, const f
 
 /* ------------------------------------------------------------------------ */
 /* Kernel-weight buffer layout ([MEGA]: gate/up interleaved in blocks of 32, */
-/* K-major)                                                                  */
+/* K-major), written from the layout's definition (see the C-ABI header):    */
+/* rows interleaved, then tiled into MFMA operand blocks.                    */
 /* ------------------------------------------------------------------------ */
 
 /* Row order of the packed FC1 weight of one expert: packed row 64*b + i is
  * gate row 32*b + i for i < 32 and up row F + 32*b + (i - 32) for i >= 32.
- * Rows stay K(H)-contiguous.  FC2 rows ([H][F], already K(F)-contiguous)
- * keep their order. */
+ * FC2 rows keep their order. */
 static int64_t fc1_logical_row(int64_t packed, int64_t F)
 {
     int64_t b = packed / 64, i = packed % 64;
     return i < 32 ? 32 * b + i : F + 32 * b + (i - 32);
 }
 
-/* bf16 buffer: [E][2F][H] packed FC1 rows, then [E][H][F] FC2 rows, both
- * bf16 bit patterns. */
+/* bf16 section of a weight with N rows of K elements per expert: element
+ * (e, n, k) sits at element index
+ *   (((e*(N/16) + n/16)*(K/32) + k/32)*4 + (k%32)/8)*128 + (n%16)*8 + k%8 . */
+static int64_t bf16_index(int64_t e, int64_t n, int64_t k, int64_t N, int64_t K)
+{
+    return (((e * (N / 16) + n / 16) * (K / 32) + k / 32) * 4 + (k % 32) / 8) * 128 +
+           (n % 16) * 8 + k % 8;
+}
+
+static void pack_bf16_section(int E, int64_t N, int64_t K, int64_t F, int fc1,
+                              const uint16_t* w, uint16_t* out)
+{
+    for (int64_t e = 0; e < E; ++e)
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t src = fc1 ? fc1_logical_row(n, F) : n;
+            for (int64_t k = 0; k < K; ++k)
+                out[bf16_index(e, n, k, N, K)] = w[(e * N + src) * K + k];
+        }
+}
+
+/* bf16 buffer: the FC1 section (N = 2F packed rows, K = H), then the FC2
+ * section (N = H, K = F). */
 void orc_pack_bf16(int E, int H, int F, const uint16_t* w1, const uint16_t* w2, uint8_t* kbuf)
 {
     uint16_t* p1 = (uint16_t*)kbuf;
     uint16_t* p2 = p1 + (int64_t)E * 2 * F * H;
-    for (int64_t e = 0; e < E; ++e)
-        for (int64_t pr = 0; pr < 2 * (int64_t)F; ++pr)
-            memcpy(p1 + (e * 2 * F + pr) * H, w1 + (e * 2 * F + fc1_logical_row(pr, F)) * H,
-                   sizeof(uint16_t) * H);
-    memcpy(p2, w2, sizeof(uint16_t) * (size_t)E * H * F);
+    pack_bf16_section(E, 2 * (int64_t)F, H, F, 1, w1, p1);
+    pack_bf16_section(E, H, F, F, 0, w2, p2);
 }
 
-/* MXFP8 buffer: FC1 codes [E][2F][H] (packed row order), FC2 codes
- * [E][H][F], FC1 scales [E][2F][H/32] (packed row order), FC2 scales
- * [E][H][F/32].  Each section starts at a multiple of 256 bytes. */
 static int64_t up256(int64_t v) { return (v + 255) / 256 * 256; }
+static int64_t ksteps(int64_t K) { return (K + 127) / 128; }
+static int64_t code_bytes(int E, int64_t N, int64_t K) { return (int64_t)E * (N / 16) * ksteps(K) * 2048; }
+static int64_t scale_bytes(int E, int64_t N, int64_t K) { return (int64_t)E * (N / 16) * ((ksteps(K) + 3) / 4) * 256; }
 
+/* MXFP8 codes of a weight with N rows of K elements (KS = ceil(K/128)):
+ *   (((e*(N/16) + n/16)*KS + k/128)*2 + (k%128)/64)*1024
+ *     + ((k%64)/16*16 + n%16)*16 + k%16 ;
+ * scales (KQ = ceil(KS/4)), for the 32-block b = k/32 of row n:
+ *   ((e*(N/16) + n/16)*KQ + (b/4)/4)*256 + ((b%4)*16 + n%16)*4 + (b/4)%4 .
+ * Bytes for k >= K are code 0 and scale 127 (2^0). */
+static void pack_mx_section(int E, int64_t N, int64_t K, int64_t F, int fc1, const uint16_t* w,
+                            uint8_t* codes, uint8_t* scales)
+{
+    int64_t KS = ksteps(K), KQ = (KS + 3) / 4;
+    memset(codes, 0, code_bytes(E, N, K));
+    memset(scales, 127, scale_bytes(E, N, K));
+    float* row = (float*)malloc(sizeof(float) * K);
+    uint8_t* c = (uint8_t*)malloc(K);
+    uint8_t* sc = (uint8_t*)malloc(K / 32);
+    for (int64_t e = 0; e < E; ++e)
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t src = fc1 ? fc1_logical_row(n, F) : n;
+            for (int64_t k = 0; k < K; ++k) row[k] = orc_bf16_value(w[(e * N + src) * K + k]);
+            orc_mx_quantize(row, 1, K, c, sc);
+            int64_t blk = e * (N / 16) + n / 16;
+            for (int64_t k = 0; k < K; ++k)
+                codes[((blk * KS + k / 128) * 2 + (k % 128) / 64) * 1024 +
+                      ((k % 64) / 16 * 16 + n % 16) * 16 + k % 16] = c[k];
+            for (int64_t b = 0; b < K / 32; ++b)
+                scales[(blk * KQ + (b / 4) / 4) * 256 + ((b % 4) * 16 + n % 16) * 4 + (b / 4) % 4] =
+                    sc[b];
+        }
+    free(row); free(c); free(sc);
+}
+
+/* MXFP8 buffer: FC1 codes, FC2 codes, FC1 scales, FC2 scales, each section
+ * starting at a multiple of 256 bytes. */
 void orc_pack_mxfp8(int E, int H, int F, const uint16_t* w1, const uint16_t* w2, uint8_t* kbuf)
 {
-    int64_t n1 = (int64_t)E * 2 * F * H, n2 = (int64_t)E * H * F;
-    uint8_t* c1 = kbuf;
-    uint8_t* c2 = c1 + up256(n1);
-    uint8_t* s1 = c2 + up256(n2);
-    uint8_t* s2 = s1 + up256(n1 / 32);
-    float* f1 = (float*)malloc(sizeof(float) * n1);
-    float* f2 = (float*)malloc(sizeof(float) * n2);
-    uint8_t* qc1 = (uint8_t*)malloc(n1);
-    uint8_t* qs1 = (uint8_t*)malloc(n1 / 32);
-    for (int64_t i = 0; i < n1; ++i) f1[i] = orc_bf16_value(w1[i]);
-    for (int64_t i = 0; i < n2; ++i) f2[i] = orc_bf16_value(w2[i]);
-    orc_mx_quantize(f1, (int64_t)E * 2 * F, H, qc1, qs1);
-    orc_mx_quantize(f2, (int64_t)E * H, F, c2, s2);
-    for (int64_t e = 0; e < E; ++e)
-        for (int64_t pr = 0; pr < 2 * (int64_t)F; ++pr) {
-            int64_t lr = e * 2 * F + fc1_logical_row(pr, F);
-            memcpy(c1 + (e * 2 * F + pr) * H, qc1 + lr * H, H);
-            memcpy(s1 + (e * 2 * F + pr) * (H / 32), qs1 + lr * (H / 32), H / 32);
-        }
-    free(f1); free(f2); free(qc1); free(qs1);
+    int64_t c1 = up256(code_bytes(E, 2 * (int64_t)F, H)), c2 = up256(code_bytes(E, H, F));
+    int64_t s1 = up256(scale_bytes(E, 2 * (int64_t)F, H));
+    pack_mx_section(E, 2 * (int64_t)F, H, F, 1, w1, kbuf, kbuf + c1 + c2);
+    pack_mx_section(E, H, F, F, 0, w2, kbuf + c1, kbuf + c1 + c2 + s1);
 }
 
 int64_t orc_pack_bytes(int E, int H, int F, int mx)
 {
     int64_t n1 = (int64_t)E * 2 * F * H, n2 = (int64_t)E * H * F;
     if (!mx) return 2 * (n1 + n2);
-    return up256(n1) + up256(n2) + up256(n1 / 32) + up256(n2 / 32);
+    return up256(code_bytes(E, 2 * (int64_t)F, H)) + up256(code_bytes(E, H, F)) +
+           up256(scale_bytes(E, 2 * (int64_t)F, H)) + up256(scale_bytes(E, H, F));
+}
+
+/* Section offsets of the MXFP8 buffer: FC1 codes, FC2 codes, FC1 scales,
+ * FC2 scales, and the end. */
+void orc_pack_mx_offsets(int E, int H, int F, int64_t* off)
+{
+    off[0] = 0;
+    off[1] = up256(code_bytes(E, 2 * (int64_t)F, H));
+    off[2] = off[1] + up256(code_bytes(E, H, F));
+    off[3] = off[2] + up256(scale_bytes(E, 2 * (int64_t)F, H));
+    off[4] = off[3] + up256(scale_bytes(E, H, F));
 }

@@ -241,18 +241,61 @@ class MoE:
     STAGES = ("permute", "quant_x", "fc1_swiglu", "fc2", "finalize")
 
     def set_stage_events(self, events):
-        """Record the 6 torch.cuda.Event objects at the forward's stage boundaries
-        (before the first kernel, then after each of STAGES); None stops."""
+        """Record 6 events at the forward's stage boundaries (before the first
+        kernel, then after each of STAGES); entries may be None (skipped), raw
+        hipEvent_t handles (int) or torch.cuda.Event objects.  None stops."""
         if events is None:
             _check(lib().moe_set_stage_events(self._h, None, 0), "moe_set_stage_events")
             return
         if len(events) != 6:
             raise ValueError("need 6 events")
+        handles = []
         for ev in events:
+            if ev is None or isinstance(ev, int):
+                handles.append(_P(ev or 0))
+                continue
             if not ev.cuda_event:        # torch creates the HIP event at its first record
                 ev.record()
-        arr = (_P * 6)(*[_P(ev.cuda_event) for ev in events])
+            handles.append(_P(ev.cuda_event))
+        arr = (_P * 6)(*handles)
         _check(lib().moe_set_stage_events(self._h, arr, 6), "moe_set_stage_events")
+
+    def bind_forward(self, x, ids, probs, live, out, ws, stream=None):
+        """Check the arguments once and return a no-argument callable that
+        enqueues this forward (for launch loops where per-call checks would
+        cost more host time than the GPU work)."""
+        torch = _torch()
+        T_cap = x.shape[0]
+        args = (self._h, _dev(x, "x", (torch.bfloat16, torch.int16, torch.uint16), (T_cap, self.H)),
+                _dev(ids, "expert_ids", (torch.int32,), (T_cap, self.topk)),
+                _dev(probs, "probs", (torch.float32,), (T_cap, self.topk)), T_cap,
+                _dev(live, "live", (torch.int32,)),
+                _dev(out, "out", (torch.float32,), (T_cap, self.H)),
+                _dev(ws, "ws", (torch.uint8,)), ws.numel(), _stream(stream))
+        fn = lib().moe_forward
+        keep = (x, ids, probs, live, out, ws)
+
+        def call():
+            _check(fn(*args), "moe_forward")
+        call.keep = keep
+        return call
+
+    def bind_route(self, logits, live, ids, probs, ws, stream=None):
+        """As bind_forward, for the router."""
+        torch = _torch()
+        T_cap = logits.shape[0]
+        args = (self._h, _dev(logits, "logits", (torch.float32,), (T_cap, self.E)), T_cap,
+                _dev(live, "live", (torch.int32,)),
+                _dev(ids, "ids", (torch.int32,), (T_cap, self.topk)),
+                _dev(probs, "probs", (torch.float32,), (T_cap, self.topk)),
+                _dev(ws, "ws", (torch.uint8,)), ws.numel(), _stream(stream))
+        fn = lib().moe_route
+        keep = (logits, live, ids, probs, ws)
+
+        def call():
+            _check(fn(*args), "moe_route")
+        call.keep = keep
+        return call
 
     def check(self, ws, stream=None) -> int:
         bits = ctypes.c_uint32(0)

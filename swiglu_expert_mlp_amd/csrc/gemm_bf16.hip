@@ -46,12 +46,16 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, int e, int row0, in
             ap[rg] = g.A + (int64_t)row * K + 8 * kg;
         }
     }
+    // B fragments: the weight is stored as 1 KB blocks of 16 rows x 32 K in
+    // lane order, [expert][row / 16][k / 32]; a lane reads its 16 bytes at
+    // block + 16 * lane, so one load instruction of a wave is 1 KB contiguous.
+    const int nt16 = g.N / 16;
     const uint16_t* bp[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-        int col = cb * 64 + 16 * ct + r16;
-        if (col >= g.N) col = g.N - 1;
-        bp[ct] = g.W + ((int64_t)e * g.N + col) * K + 8 * kg;
+        int c16 = cb * 4 + ct;
+        if (c16 >= nt16) c16 = nt16 - 1;
+        bp[ct] = g.W + ((int64_t)e * nt16 + c16) * (int64_t)(K / 32) * 512 + 8 * lane;
     }
     f32x4 acc[NG][4];
 #pragma unroll
@@ -59,29 +63,53 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, int e, int row0, in
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) acc[rg][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    uint4 an[NG], bn[4];
+    // Ring of D K-steps in flight: step s lives in slot s % D.  The MFMA order
+    // is still k0 = 0, 32, 64, ... for every element; only the load schedule
+    // runs ahead.
+    constexpr int D = 4;
+    const int nsteps = K / 32;
+    uint4 ar[D][NG], br[D][4];
+    auto load = [&](int d, int s) {
 #pragma unroll
-    for (int rg = 0; rg < NG; ++rg) an[rg] = *(const uint4*)(ap[rg]);
+        for (int rg = 0; rg < NG; ++rg) ar[d][rg] = *(const uint4*)(ap[rg] + 32 * s);
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) bn[ct] = *(const uint4*)(bp[ct]);
-    for (int k0 = 0; k0 < K; k0 += 32) {
-        uint4 ac[NG], bc[4];
-#pragma unroll
-        for (int rg = 0; rg < NG; ++rg) ac[rg] = an[rg];
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) bc[ct] = bn[ct];
-        if (k0 + 32 < K) {
-#pragma unroll
-            for (int rg = 0; rg < NG; ++rg) an[rg] = *(const uint4*)(ap[rg] + k0 + 32);
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) bn[ct] = *(const uint4*)(bp[ct] + k0 + 32);
-        }
+        for (int ct = 0; ct < 4; ++ct) br[d][ct] = *(const uint4*)(bp[ct] + 512 * s);
+    };
+    auto mfma = [&](int d) {
 #pragma unroll
         for (int rg = 0; rg < NG; ++rg)
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct)
                 acc[rg][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    as_bf16x8(ac[rg]), as_bf16x8(bc[ct]), acc[rg][ct], 0, 0, 0);
+                    as_bf16x8(ar[d][rg]), as_bf16x8(br[d][ct]), acc[rg][ct], 0, 0, 0);
+    };
+    int s0 = 0;
+    if (nsteps >= D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) load(d, d);
+        // steady state: every slot is consumed and refilled D steps ahead
+        for (; s0 + 2 * D <= nsteps; s0 += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                mfma(d);
+                load(d, s0 + D + d);
+            }
+        }
+        // drain the ring, refilling only with steps that exist
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            mfma(d);
+            if (s0 + D + d < nsteps) load(d, s0 + D + d);
+        }
+        s0 += D;
+    }
+    // remaining steps (fewer than D), one at a time
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        if (s0 + d < nsteps) {
+            if (nsteps < D) load(d, s0 + d);
+            mfma(d);
+        }
     }
 
     // epilogue: lane holds rows 4 * kg + i (i < 4) of each group, column r16 of each tile

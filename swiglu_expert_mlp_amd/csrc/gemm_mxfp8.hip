@@ -12,7 +12,8 @@
 // with the scales of the four 32-blocks, in that order for every row, tile
 // and launch.  A K tail shorter than 128 is padded with zero codes.
 //
-// Lane layout of one 128-wide K step (both operands): lane l holds row (l % 16);
+// Lane layout of one 128-wide K step (both operands; the weights are stored
+// pre-arranged in it, the activations are gathered from row-major rows): lane l holds row (l % 16);
 // its first 16 bytes are K = 16 * (l / 16) + [0, 16) and its last 16 bytes are
 // K = 64 + 16 * (l / 16) + [0, 16).  The scale byte of lane l applies to the
 // 32-block (l / 16) of the step, i.e. 32-block q is made of the first halves
@@ -41,15 +42,19 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs& g, int e, int row
         ap[rg] = g.A + arow * K + 16 * kg;
         as[rg] = g.As + arow * KB + kg;
     }
+    // B fragments: 2 KB blocks of 16 rows x 128 K, [expert][row / 16][k / 128],
+    // each block two 1 KB halves in lane order (16 codes per lane); scales in
+    // 256-byte groups of 4 K-steps, one dword per lane (byte = step % 4).
+    const int nt16 = g.N / 16, KS = (K + 127) / 128, KQ = (KS + 3) / 4;
     const uint8_t* bp[4];
-    const uint8_t* bs[4];
+    const uint32_t* bs[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-        int col = cb * 64 + 16 * ct + r16;
-        if (col >= g.N) col = g.N - 1;
-        int64_t wrow = (int64_t)e * g.N + col;
-        bp[ct] = g.W + wrow * K + 16 * kg;
-        bs[ct] = g.Ws + wrow * KB + kg;
+        int c16 = cb * 4 + ct;
+        if (c16 >= nt16) c16 = nt16 - 1;
+        const int64_t blk = (int64_t)e * nt16 + c16;
+        bp[ct] = g.W + blk * KS * 2048 + 16 * lane;
+        bs[ct] = (const uint32_t*)(g.Ws + blk * KQ * 256) + lane;
     }
     f32x4 acc[NG][4];
 #pragma unroll
@@ -73,13 +78,15 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs& g, int e, int row
                           (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
             sa[rg] = s_in ? (int)as[rg][k0 / 32] : 127;
         }
+        const int step = k0 / 128;
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
-            uint4 lo = lo_in ? *(const uint4*)(bp[ct] + k0) : z;
-            uint4 hi = hi_in ? *(const uint4*)(bp[ct] + k0 + 64) : z;
+            // padded blocks hold zero codes and scale 2^0, so no K check here
+            uint4 lo = *(const uint4*)(bp[ct] + step * 2048);
+            uint4 hi = *(const uint4*)(bp[ct] + step * 2048 + 1024);
             b[ct] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                           (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            sb[ct] = s_in ? (int)bs[ct][k0 / 32] : 127;
+            sb[ct] = (int)((bs[ct][(step >> 2) * 64] >> (8 * (step & 3))) & 0xffu);
         }
 #pragma unroll
         for (int rg = 0; rg < NG; ++rg)

@@ -22,6 +22,7 @@ hipError_t launch_pack_bf16(const uint16_t* w1, const uint16_t* w2, uint8_t* kbu
                             int F, int num_cu, hipStream_t s);
 hipError_t launch_pack_mxfp8(const uint16_t* w1, const uint16_t* w2, uint8_t* kbuf, int E, int H,
                              int F, int num_cu, hipStream_t s);
+void mx_section_bytes(int E, int H, int F, size_t* c1, size_t* c2, size_t* s1, size_t* s2);
 hipError_t launch_quant_x(const uint16_t* x, int64_t T_cap, const int32_t* live, int H,
                           uint8_t* codes, uint8_t* scales, int num_cu, hipStream_t s);
 }  // namespace moe
@@ -46,7 +47,8 @@ struct moe_ctx {
 
 static hipError_t mark(moe_ctx* h, int i, hipStream_t s)
 {
-    return h->record_stages ? hipEventRecord(h->stage_events[i], s) : hipSuccess;
+    return (h->record_stages && h->stage_events[i]) ? hipEventRecord(h->stage_events[i], s)
+                                                     : hipSuccess;
 }
 
 static thread_local std::string g_err;
@@ -158,7 +160,9 @@ size_t moe_weight_bytes(moe_handle h)
     if (!h) return 0;
     size_t n1 = (size_t)h->E * 2 * h->F * h->H, n2 = (size_t)h->E * h->H * h->F;
     if (h->precision == MOE_BF16) return 2 * (n1 + n2);
-    return up256(n1) + up256(n2) + up256(n1 / 32) + up256(n2 / 32);
+    size_t c1, c2, s1, s2;
+    mx_section_bytes(h->E, h->H, h->F, &c1, &c2, &s1, &s2);
+    return c1 + c2 + s1 + s2;
 }
 
 size_t moe_workspace_bytes(moe_handle h, int64_t T_cap)
@@ -269,11 +273,12 @@ moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
         if ((e = mark(h, 4, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     } else {
-        size_t n1 = (size_t)E * 2 * F * H, n2 = (size_t)E * H * F;
+        size_t b1, b2, b3, b4;
+        mx_section_bytes(E, H, F, &b1, &b2, &b3, &b4);
         const uint8_t* c1 = h->kbuf;
-        const uint8_t* c2 = c1 + up256(n1);
-        const uint8_t* s1 = c2 + up256(n2);
-        const uint8_t* s2 = s1 + up256(n1 / 32);
+        const uint8_t* c2 = c1 + b1;
+        const uint8_t* s1 = c2 + b2;
+        const uint8_t* s2 = s1 + b3;
         e = launch_quant_x((const uint16_t*)x, T_cap, live_rows_dev, H, (uint8_t*)(w + L.xq),
                            (uint8_t*)(w + L.xs), h->num_cu, stream);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: quant-x launch");

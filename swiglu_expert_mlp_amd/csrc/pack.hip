@@ -12,6 +12,16 @@
 // row F + 32 b + (i - 32) (i >= 32); FC2 rows keep their order.  MXFP8 blocks
 // run along K (H for FC1 rows, F for FC2 rows), so the interleave moves whole
 // rows and never splits a block.
+//
+// The rows are then tiled into MFMA operand blocks so that one wave's operand
+// load is one contiguous 1 KB read (layout formulas in include/moe.h):
+//   bf16:  16 rows x 32 K per 1 KB block, lane order (lane = 16 * (k%32 / 8)
+//          + n%16, 8 elements per lane); blocks [expert][n/16][k/32].
+//   MXFP8: 16 rows x 128 K per 2 KB block = two 1 KB halves (K%128 < 64 and
+//          >= 64), lane = 16 * (k%64 / 16) + n%16, 16 codes per lane; blocks
+//          [expert][n/16][k/128]; E8M0 scales 4 K-steps per lane dword:
+//          256 B groups [expert][n/16][k/512], byte (k/128)%4 of lane
+//          16 * ((k/32)%4) + n%16.
 #include "common.h"
 
 namespace moe {
@@ -22,19 +32,25 @@ __device__ __forceinline__ int64_t fc1_src_row(int64_t packed, int64_t F)
     return i < 32 ? 32 * b + i : F + 32 * b + (i - 32);
 }
 
-// bf16: copy 16-byte pieces of rows into their packed position.
-__global__ void __launch_bounds__(256) pack_fc1_bf16_kernel(const uint16_t* __restrict__ w1,
-                                                            uint16_t* __restrict__ p1, int E,
-                                                            int H, int F)
+// bf16 tiled layout: one thread writes one lane's 16 bytes (8 elements) of a
+// block.  N rows of K elements per expert; fc1 selects the interleaved order.
+__global__ void __launch_bounds__(256) pack_bf16_kernel(const uint16_t* __restrict__ src,
+                                                        uint16_t* __restrict__ dst, int E, int N,
+                                                        int K, int F, int fc1)
 {
-    const int64_t per_row = H / 8;
-    const int64_t n = (int64_t)E * 2 * F * per_row;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+    const int64_t ks = K / 32, nt = N / 16;
+    const int64_t n_pieces = (int64_t)E * nt * ks * 64;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_pieces;
          i += (int64_t)gridDim.x * blockDim.x) {
-        int64_t prow = i / per_row, piece = i - prow * per_row;
-        int64_t e = prow / (2 * F), pr = prow - e * 2 * F;
-        int64_t src = (e * 2 * F + fc1_src_row(pr, F)) * per_row + piece;
-        ((uint4*)p1)[i] = ((const uint4*)w1)[src];
+        const int lane = (int)(i & 63);
+        int64_t blk = i >> 6;                       // (e * nt + n16) * ks + s
+        const int64_t s = blk % ks;
+        blk /= ks;
+        const int64_t n16 = blk % nt, e = blk / nt;
+        const int64_t n = n16 * 16 + (lane & 15);
+        const int64_t k = s * 32 + (lane >> 4) * 8;
+        const int64_t srow = fc1 ? fc1_src_row(n, F) : n;
+        ((uint4*)dst)[i] = *(const uint4*)(src + ((e * N + srow) * K + k));
     }
 }
 
@@ -74,26 +90,46 @@ __device__ __forceinline__ void quant_block32(const uint16_t* __restrict__ src,
     *scale = (uint8_t)(e8 + 127);
 }
 
-// Weight rows: one thread per 32-element block; FC1 rows are taken in the
-// packed (interleaved) order.
-template <bool FC1_ORDER>
-__global__ void __launch_bounds__(256) quant_rows_mx_kernel(const uint16_t* __restrict__ src,
-                                                            uint8_t* __restrict__ codes,
-                                                            uint8_t* __restrict__ scales,
-                                                            int64_t rows, int cols, int F)
+// MXFP8 weights, tiled layout.  One thread quantizes one 32-element block
+// (row n, block q of K) and writes its 32 codes as two 16-byte pieces (the
+// block's halves go to lanes kg = 2 (q%2) and 2 (q%2) + 1 of one half of the
+// K-step) and its scale byte.  Padding past K (codes 0, scale 2^0) is written
+// by the threads of the blocks q >= K/32 up to the padded size.
+__global__ void __launch_bounds__(256) pack_mx_kernel(const uint16_t* __restrict__ src,
+                                                      uint8_t* __restrict__ codes,
+                                                      uint8_t* __restrict__ scales, int E, int N,
+                                                      int K, int F, int fc1)
 {
-    const int nb = cols / 32;
-    const int64_t n = rows * nb;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+    const int64_t KS = (K + 127) / 128, KQ = (KS + 3) / 4, nt = N / 16;
+    const int64_t nbk = KQ * 16;                  // padded 32-blocks per row
+    const int64_t n_items = (int64_t)E * N * nbk;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_items;
          i += (int64_t)gridDim.x * blockDim.x) {
-        int64_t r = i / nb;
-        int b = (int)(i - r * nb);
-        int64_t sr = r;
-        if constexpr (FC1_ORDER) {
-            int64_t e = r / (2 * F), pr = r - e * 2 * F;
-            sr = e * 2 * F + fc1_src_row(pr, F);
+        const int64_t q = i % nbk;
+        const int64_t row = i / nbk;               // e * N + n
+        const int64_t e = row / N, n = row - e * N;
+        const int64_t n16 = n >> 4, r16 = n & 15;
+        const int64_t step = q >> 2, kg = q & 3;
+        uint8_t* sc = scales + ((e * nt + n16) * KQ + (step >> 2)) * 256 +
+                      ((kg * 16 + r16) * 4) + (step & 3);
+        if (q >= K / 32) {
+            *sc = 127;
+            if (step < KS) {
+                // the two 16-byte pieces of this (padded) block
+                const int64_t half = (kg >> 1), lg = (kg & 1) * 2;
+                uint8_t* base = codes + (((e * nt + n16) * KS + step) * 2 + half) * 1024;
+                *(uint4*)(base + ((lg + 0) * 16 + r16) * 16) = make_uint4(0, 0, 0, 0);
+                *(uint4*)(base + ((lg + 1) * 16 + r16) * 16) = make_uint4(0, 0, 0, 0);
+            }
+            continue;
         }
-        quant_block32(src + sr * cols + b * 32, codes + r * cols + b * 32, scales + r * nb + b);
+        const int64_t srow = fc1 ? fc1_src_row(n, F) : n;
+        alignas(16) uint8_t c32[32];
+        quant_block32(src + (e * N + srow) * K + q * 32, c32, sc);
+        const int64_t half = kg >> 1, lg = (kg & 1) * 2;   // K%128 = 32 kg + [0, 32)
+        uint8_t* base = codes + (((e * nt + n16) * KS + step) * 2 + half) * 1024;
+        *(uint4*)(base + ((lg + 0) * 16 + r16) * 16) = *(const uint4*)(c32);
+        *(uint4*)(base + ((lg + 1) * 16 + r16) * 16) = *(const uint4*)(c32 + 16);
     }
 }
 
@@ -128,26 +164,38 @@ hipError_t launch_pack_bf16(const uint16_t* w1, const uint16_t* w2, uint8_t* kbu
 {
     uint16_t* p1 = (uint16_t*)kbuf;
     uint16_t* p2 = p1 + (int64_t)E * 2 * F * H;
-    hipLaunchKernelGGL(pack_fc1_bf16_kernel, dim3(num_cu * 8), dim3(256), 0, s, w1, p1, E, H, F);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    return hipMemcpyAsync(p2, w2, sizeof(uint16_t) * (size_t)E * H * F, hipMemcpyDeviceToDevice, s);
+    hipLaunchKernelGGL(pack_bf16_kernel, dim3(num_cu * 8), dim3(256), 0, s, w1, p1, E, 2 * F, H, F, 1);
+    hipLaunchKernelGGL(pack_bf16_kernel, dim3(num_cu * 8), dim3(256), 0, s, w2, p2, E, H, F, F, 0);
+    return hipGetLastError();
 }
 
 static size_t up256(size_t v) { return (v + 255) / 256 * 256; }
 
+// Section sizes of the MXFP8 buffer (codes and scales of FC1, then FC2).
+void mx_section_bytes(int E, int H, int F, size_t* c1, size_t* c2, size_t* s1, size_t* s2)
+{
+    auto codes = [&](int64_t N, int64_t K) { return (size_t)E * (N / 16) * ((K + 127) / 128) * 2048; };
+    auto scl = [&](int64_t N, int64_t K) {
+        int64_t KS = (K + 127) / 128;
+        return (size_t)E * (N / 16) * ((KS + 3) / 4) * 256;
+    };
+    *c1 = up256(codes(2 * F, H));
+    *c2 = up256(codes(H, F));
+    *s1 = up256(scl(2 * F, H));
+    *s2 = up256(scl(H, F));
+}
+
 hipError_t launch_pack_mxfp8(const uint16_t* w1, const uint16_t* w2, uint8_t* kbuf, int E, int H,
                              int F, int num_cu, hipStream_t s)
 {
-    size_t n1 = (size_t)E * 2 * F * H, n2 = (size_t)E * H * F;
-    uint8_t* c1 = kbuf;
-    uint8_t* c2 = c1 + up256(n1);
-    uint8_t* s1 = c2 + up256(n2);
-    uint8_t* s2 = s1 + up256(n1 / 32);
-    hipLaunchKernelGGL(quant_rows_mx_kernel<true>, dim3(num_cu * 8), dim3(256), 0, s, w1, c1, s1,
-                       (int64_t)E * 2 * F, H, F);
-    hipLaunchKernelGGL(quant_rows_mx_kernel<false>, dim3(num_cu * 8), dim3(256), 0, s, w2, c2, s2,
-                       (int64_t)E * H, F, F);
+    size_t c1, c2, s1, s2;
+    mx_section_bytes(E, H, F, &c1, &c2, &s1, &s2);
+    uint8_t* pc1 = kbuf;
+    uint8_t* pc2 = pc1 + c1;
+    uint8_t* ps1 = pc2 + c2;
+    uint8_t* ps2 = ps1 + s1;
+    hipLaunchKernelGGL(pack_mx_kernel, dim3(num_cu * 8), dim3(256), 0, s, w1, pc1, ps1, E, 2 * F, H, F, 1);
+    hipLaunchKernelGGL(pack_mx_kernel, dim3(num_cu * 8), dim3(256), 0, s, w2, pc2, ps2, E, H, F, F, 0);
     return hipGetLastError();
 }
 

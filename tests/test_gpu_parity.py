@@ -115,16 +115,18 @@ def test_pack_bytes_bitwise(name, precision):
     ref = oracle.pack(w.E, w.H, w.F, c.inp["w1_bits"], c.inp["w2_bits"], precision)
     got = kbuf.cpu().numpy()
     assert got.shape == ref.shape
-    # every defined section bit for bit (padding between sections is unspecified)
+    # every defined section bit for bit, its K padding included (the bytes that
+    # round a section up to 256 are unspecified)
     n1, n2 = w.E * 2 * w.F * w.H, w.E * w.H * w.F
     if precision == "bf16":
         sections = [(0, 2 * (n1 + n2))]
     else:
-        up = lambda v: (v + 255) // 256 * 256
-        o2 = up(n1)
-        o3 = o2 + up(n2)
-        o4 = o3 + up(n1 // 32)
-        sections = [(0, n1), (o2, o2 + n2), (o3, o3 + n1 // 32), (o4, o4 + n2 // 32)]
+        off = oracle.pack_mx_offsets(w.E, w.H, w.F)
+        KS = lambda K: (K + 127) // 128
+        sizes = [w.E * (2 * w.F // 16) * KS(w.H) * 2048, w.E * (w.H // 16) * KS(w.F) * 2048,
+                 w.E * (2 * w.F // 16) * ((KS(w.H) + 3) // 4) * 256,
+                 w.E * (w.H // 16) * ((KS(w.F) + 3) // 4) * 256]
+        sections = [(off[i], off[i] + sizes[i]) for i in range(4)]
     for a, b in sections:
         assert np.array_equal(got[a:b], ref[a:b]), (a, b)
 

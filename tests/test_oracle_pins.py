@@ -434,43 +434,67 @@ def test_forward_live_prefix_and_capacity():
 
 # ------------------------------------------------------------------ packer
 
-def test_pack_layout_definition():
-    """Packed FC1 row 64b+i = gate row 32b+i (i<32) or up row F+32b+i-32; FC2 verbatim."""
+def _interleave(w, F):
+    """Packed FC1 row 64b+i = gate row 32b+i (i<32) or up row F+32b+i-32."""
+    E, N2, H = w.shape
+    rows = [32 * b + i if i < 32 else F + 32 * b + i - 32 for b in range(F // 32) for i in range(64)]
+    return w[:, rows]
+
+
+def _unswizzle_bf16(buf, E, N, K):
+    """Inverse of the bf16 tiled layout by array reshapes: blocks
+    [E][N/16][K/32] of [4 (k%32 / 8)][16 (n%16)][8 (k%8)]."""
+    t = buf.reshape(E, N // 16, K // 32, 4, 16, 8)
+    return t.transpose(0, 1, 4, 2, 3, 5).reshape(E, N, K)
+
+
+def _unswizzle_mx(codes, scales, E, N, K):
+    KS = (K + 127) // 128
+    KQ = (KS + 3) // 4
+    c = codes.reshape(E, N // 16, KS, 2, 4, 16, 16)            # e n16 step half kg r16 byte
+    c = c.transpose(0, 1, 5, 2, 3, 4, 6).reshape(E, N, KS * 128)
+    sc = scales.reshape(E, N // 16, KQ, 4, 16, 4)               # e n16 group kg r16 step%4
+    sc = sc.transpose(0, 1, 4, 2, 5, 3).reshape(E, N, KQ * 16)
+    return c, sc
+
+
+def test_pack_bf16_layout_definition():
+    """Unswizzled by reshapes, the packed buffer is the interleaved weight."""
     E, H, F = 2, 64, 96
     rng = np.random.default_rng(4)
     w1 = rng.integers(0, 65535, (E, 2 * F, H)).astype(np.uint16)
     w2 = rng.integers(0, 65535, (E, H, F)).astype(np.uint16)
     buf = oracle.pack(E, H, F, w1, w2, "bf16").view(np.uint16)
-    p1 = buf[: E * 2 * F * H].reshape(E, 2 * F, H)
-    p2 = buf[E * 2 * F * H:].reshape(E, H, F)
-    for b in range(F // 32):
-        for i in range(64):
-            src = 32 * b + i if i < 32 else F + 32 * b + i - 32
-            assert np.array_equal(p1[:, 64 * b + i], w1[:, src])
+    p1 = _unswizzle_bf16(buf[: E * 2 * F * H], E, 2 * F, H)
+    p2 = _unswizzle_bf16(buf[E * 2 * F * H:], E, H, F)
+    assert np.array_equal(p1, _interleave(w1, F))
     assert np.array_equal(p2, w2)
+    # one spot check of the lane order: element (e=1, n=17, k=45)
+    idx = (((1 * (2 * F // 16) + 1) * (H // 32) + 1) * 4 + 13 // 8) * 128 + 1 * 8 + 45 % 8
+    assert buf[idx] == _interleave(w1, F)[1, 17, 45]
 
 
-def test_pack_mxfp8_sections():
-    E, H, F = 2, 64, 96
-    w = make_inputs(WORKLOADS["tiny"], seed=4)
+@pytest.mark.parametrize("H,F", [(64, 96), (160, 96)])
+def test_pack_mxfp8_layout_definition(H, F):
+    """Codes and scales, unswizzled, are the per-row quantization of the
+    interleaved bf16 weight; padding past K is code 0 and scale 127."""
+    E = 2
     rng = np.random.default_rng(4)
     w1 = oracle.bf16_bits(rng.standard_normal((E, 2 * F, H)).astype(np.float32))
     w2 = oracle.bf16_bits(rng.standard_normal((E, H, F)).astype(np.float32))
     buf = oracle.pack(E, H, F, w1, w2, "mxfp8")
-    up = lambda v: (v + 255) // 256 * 256
-    n1, n2 = E * 2 * F * H, E * H * F
-    c1 = buf[:n1].reshape(E, 2 * F, H)
-    c2 = buf[up(n1):up(n1) + n2].reshape(E, H, F)
-    s1 = buf[up(n1) + up(n2):up(n1) + up(n2) + n1 // 32].reshape(E, 2 * F, H // 32)
-    o2 = up(n1) + up(n2) + up(n1 // 32)
-    s2 = buf[o2:o2 + n2 // 32].reshape(E, H, F // 32)
-    qc1, qs1 = oracle.mx_quantize(oracle.bf16_value(w1).reshape(-1, H))
-    qc2, qs2 = oracle.mx_quantize(oracle.bf16_value(w2).reshape(-1, F))
-    qc1, qs1 = qc1.reshape(E, 2 * F, H), qs1.reshape(E, 2 * F, H // 32)
-    for b in range(F // 32):
-        for i in range(64):
-            src = 32 * b + i if i < 32 else F + 32 * b + i - 32
-            assert np.array_equal(c1[:, 64 * b + i], qc1[:, src])
-            assert np.array_equal(s1[:, 64 * b + i], qs1[:, src])
-    assert np.array_equal(c2.reshape(-1, F), qc2) and np.array_equal(s2.reshape(-1, F // 32), qs2)
-    assert len(buf) == oracle.pack_bytes(E, H, F, "mxfp8")
+    off = oracle.pack_mx_offsets(E, H, F)
+    assert len(buf) == off[4] == oracle.pack_bytes(E, H, F, "mxfp8")
+    for (codes_at, scales_at, w, N, K, fc1) in ((0, 2, w1, 2 * F, H, True),
+                                                (1, 3, w2, H, F, False)):
+        KS = (K + 127) // 128
+        KQ = (KS + 3) // 4
+        nc = E * (N // 16) * KS * 2048
+        ns = E * (N // 16) * KQ * 256
+        c, sc = _unswizzle_mx(buf[off[codes_at]:off[codes_at] + nc],
+                              buf[off[scales_at]:off[scales_at] + ns], E, N, K)
+        logical = _interleave(w, F) if fc1 else w
+        qc, qs = oracle.mx_quantize(oracle.bf16_value(logical).reshape(-1, K))
+        assert np.array_equal(c[:, :, :K].reshape(-1, K), qc)
+        assert np.array_equal(sc[:, :, :K // 32].reshape(-1, K // 32), qs)
+        assert np.all(c[:, :, K:] == 0) and np.all(sc[:, :, K // 32:] == 127)
