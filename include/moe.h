@@ -68,7 +68,7 @@ typedef enum {
 
 /* Device-side contract-violation bits reported by moe_check. */
 #define MOE_DEVERR_BAD_EXPERT_ID 1u   /* id outside [0, E) in a live token: route dropped */
-#define MOE_DEVERR_DUP_EXPERT_ID 2u   /* same id twice in a live token: both rows summed  */
+#define MOE_DEVERR_DUP_EXPERT_ID 2u   /* same id twice in a live token: repeat dropped    */
 #define MOE_DEVERR_LIVE_ABOVE_CAP 4u  /* live > T_cap: clamped to T_cap                  */
 #define MOE_DEVERR_LIVE_NEGATIVE 8u   /* live < 0: treated as 0                          */
 

@@ -244,8 +244,10 @@ uint32_t orc_route(const float* logits, int64_t T_cap, int32_t live, int E, int 
  * sort of the routes r = t*k + j by expert: counts, exclusive offsets,
  * position of route r = offsets[e_r] + number of earlier routes (in r order)
  * to the same expert.  perm_src[pos] = r, dst[r] = pos.  A route whose id is
- * outside [0, E) is dropped: dst = -1, not counted.  Outputs beyond the
- * live routes are not written.  Returns error bits. */
+ * outside [0, E), or repeats the id of the route before it in canonical
+ * order (the same expert listed twice for one token), is dropped: dst = -1,
+ * not counted.  Outputs beyond the live routes are not written.  Returns
+ * error bits. */
 uint32_t orc_prepare(const int32_t* ids, const float* probs, int64_t T_cap, int32_t live,
                      int E, int k, int32_t* sorted_ids, float* sorted_probs,
                      int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* dst,
@@ -273,21 +275,24 @@ uint32_t orc_prepare(const int32_t* ids, const float* probs, int64_t T_cap, int3
     }
     for (int e = 0; e < E; ++e) counts[e] = 0;
     int64_t R = (int64_t)T * k;
+    char* drop = (char*)calloc((size_t)(R > 0 ? R : 1), 1);
     for (int64_t r = 0; r < R; ++r) {
         int32_t e = sorted_ids[r];
-        if (e >= 0 && e < E) counts[e] += 1;
+        if (e < 0 || e >= E || (r % k > 0 && sorted_ids[r - 1] == e)) { drop[r] = 1; continue; }
+        counts[e] += 1;
     }
     offsets[0] = 0;
     for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
     int32_t* fill = (int32_t*)calloc((size_t)(E > 0 ? E : 1), sizeof(int32_t));
     for (int64_t r = 0; r < R; ++r) {
         int32_t e = sorted_ids[r];
-        if (e < 0 || e >= E) { dst[r] = -1; continue; }
+        if (drop[r]) { dst[r] = -1; continue; }
         int32_t pos = offsets[e] + fill[e]++;
         perm_src[pos] = (int32_t)r;
         dst[r] = pos;
     }
     free(fill);
+    free(drop);
     return err;
 }
 
@@ -542,12 +547,15 @@ void orc_forward_tokens(void* wp, const uint16_t* x, const int32_t* ids, const f
                     int32_t ti = id[b]; id[b] = id[b - 1]; id[b - 1] = ti;
                     float tp = p[b]; p[b] = p[b - 1]; p[b - 1] = tp;
                 }
+            int use[64];
             for (int j = 0; j < k; ++j)
-                if (id[j] >= 0 && id[j] < E) expert_row(m, id[j], xr, o + (int64_t)j * H, a32, hrow);
+                use[j] = id[j] >= 0 && id[j] < E && !(j > 0 && id[j] == id[j - 1]);
+            for (int j = 0; j < k; ++j)
+                if (use[j]) expert_row(m, id[j], xr, o + (int64_t)j * H, a32, hrow);
             for (int64_t mo = 0; mo < H; ++mo) {
                 float acc = 0.0f;
                 for (int j = 0; j < k; ++j)
-                    if (id[j] >= 0 && id[j] < E) acc = fmaf(p[j], o[(int64_t)j * H + mo], acc);
+                    if (use[j]) acc = fmaf(p[j], o[(int64_t)j * H + mo], acc);
                 out_rows[q * H + mo] = acc;
             }
         }

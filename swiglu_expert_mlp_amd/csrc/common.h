@@ -117,7 +117,8 @@ struct WsHeader {
     int32_t T;             // live tokens of the last forward (clamped)
     int32_t n_tiles;       // M tiles in the tile table
     int32_t n_rows;        // routed rows with a valid expert
-    int32_t pad[59];
+    uint32_t ticket;       // prep workgroups finished (the last one resets it to 0)
+    int32_t pad[58];
 };
 
 static_assert(sizeof(WsHeader) == 256, "header is one 256-byte block");

@@ -8,15 +8,19 @@
 // Megatron-LM PR #8367, "Problem": the token count is a device-side value,
 // so every kernel here reads it from device memory.
 //
-// Three launches, each with a grid that never depends on the live count:
-//   prep_count   one workgroup per 256-token chunk (chunks past the live
-//                count exit at once): canonical sort, per-chunk expert counts
-//                and each route's stable rank inside its chunk (wave ballots,
-//                so the ranks are deterministic, not atomic-order dependent);
-//   prep_scan    one workgroup: chunk prefix per expert, exclusive scan over
-//                experts, M-tile table, error word;
-//   prep_scatter one thread per route: position = expert offset + chunk base
-//                + rank; perm_src[position] = route, dst[route] = position.
+// Two launches, with grids that never depend on the live count:
+//   prep_kernel    one workgroup per 256-token chunk (chunks past the live
+//                  count exit at once): canonical sort, then per expert a
+//                  256-bit map of the chunk's tokens that route to it (LDS
+//                  atomic OR, order-independent); a route's stable rank inside
+//                  the chunk is the number of set bits below its token, and
+//                  the chunk's count the bits set in all.  The workgroup that
+//                  finishes last (atomic ticket, no waiting) does the prefix
+//                  over chunks and experts, the M-tile table and the error word.
+//   prep_scatter   one thread per route: position = expert offset + chunk
+//                  base + rank; perm_src[position] = route, dst[route] = position.
+// A route whose id is outside [0, E), or repeats an id already listed for the
+// token (contract violations), is dropped: it has no row and dst = -1.
 #include "common.h"
 
 namespace moe {
@@ -52,148 +56,176 @@ __device__ int block_exclusive_scan(int v, int* total, int* lds /* >= 32 ints */
     return excl;
 }
 
-template <int K>
-__global__ void __launch_bounds__(256) prep_count_kernel(
-    const int32_t* __restrict__ ids, const float* __restrict__ probs, int64_t T_cap,
-    const int32_t* __restrict__ live_ptr, int E, int32_t* __restrict__ sorted_ids,
-    float* __restrict__ sorted_probs, int32_t* __restrict__ local_rank,
-    int32_t* __restrict__ chunk_counts, uint32_t* __restrict__ chunk_err)
+struct PrepArgs {
+    const int32_t* ids;
+    const float* probs;
+    int64_t T_cap;
+    const int32_t* live;
+    int E;
+    int32_t* sorted_ids;
+    float* sorted_probs;
+    int32_t* local_rank;
+    int32_t* chunk_base;     // [nchunks][E]: chunk counts, then global bases
+    uint32_t* chunk_err;
+    int32_t* counts;
+    int32_t* offsets;
+    int2* tiles;
+    WsHeader* hdr;
+};
+
+// Prefix over chunks and experts, tile table, header (one workgroup).
+__device__ void prep_finish(const PrepArgs& a, int T, int nch, int k, int32_t live, int* lds)
 {
-    __shared__ int wcnt[4][kMaxExperts];
-    const int T = clamp_live(*live_ptr, T_cap);
+    const int E = a.E;
+    constexpr int PER = kMaxExperts / 256;          // experts per thread
+    int cnt[PER];
+    int mine = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int e = threadIdx.x * PER + q;
+        int run = 0;
+        if (e < E) {
+            for (int c = 0; c < nch; ++c) {
+                int v = __builtin_nontemporal_load(&a.chunk_base[(int64_t)c * E + e]);
+                a.chunk_base[(int64_t)c * E + e] = run;
+                run += v;
+            }
+        }
+        cnt[q] = run;
+        mine += run;
+    }
+    int total;
+    int off = block_exclusive_scan(mine, &total, lds);
+    int ntile_mine = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) ntile_mine += (cnt[q] + kBM - 1) / kBM;
+    int ntotal;
+    int tfirst = block_exclusive_scan(ntile_mine, &ntotal, lds);
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int e = threadIdx.x * PER + q;
+        if (e < E) {
+            a.counts[e] = cnt[q];
+            a.offsets[e] = off;
+            for (int c = 0; c < nch; ++c) a.chunk_base[(int64_t)c * E + e] += off;
+            const int nt = (cnt[q] + kBM - 1) / kBM;
+            for (int i = 0; i < nt; ++i) a.tiles[tfirst + i] = make_int2(e, off + i * kBM);
+            tfirst += nt;
+        }
+        off += cnt[q];
+    }
+    if (threadIdx.x == 0) a.offsets[E] = total;
+    uint32_t err = 0;
+    for (int c = threadIdx.x; c < nch; c += blockDim.x) err |= __builtin_nontemporal_load(&a.chunk_err[c]);
+    uint64_t b1 = __ballot(err & kErrBadId), b2 = __ballot(err & kErrDupId);
+    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = (b1 ? kErrBadId : 0) | (b2 ? kErrDupId : 0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t all = (live < 0 ? kErrLiveNeg : 0u) | (live > a.T_cap ? kErrLiveHigh : 0u);
+        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) all |= (uint32_t)lds[w];
+        a.hdr->fwd_err = all;
+        a.hdr->T = T;
+        a.hdr->n_tiles = ntotal;
+        a.hdr->n_rows = total;
+    }
+}
+
+template <int K>
+__global__ void __launch_bounds__(256) prep_kernel(PrepArgs a)
+{
+    __shared__ uint32_t bm[kMaxExperts * (kChunkTok / 32)];
+    __shared__ int lds[32];
+    __shared__ int s_last;
+    const int32_t live = *a.live;
+    const int T = clamp_live(live, a.T_cap);
+    const int nch = (T + kChunkTok - 1) / kChunkTok;
     const int c = blockIdx.x;
-    const int t0 = c * kChunkTok;
-    if (t0 >= T) return;
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const int t = t0 + threadIdx.x;
+    const int E = a.E;
+    if (nch == 0) {
+        if (c == 0) prep_finish(a, T, 0, K, live, lds);
+        return;
+    }
+    if (c >= nch) return;
+    for (int i = threadIdx.x; i < E * (kChunkTok / 32); i += blockDim.x) bm[i] = 0;
+    const int t = c * kChunkTok + threadIdx.x;
     const bool valid = t < T;
 
-    // canonical sort of this token's (id, prob) pairs: insertion sort keeps
-    // equal ids (a contract violation) in their listed order
+    // canonical sort of this token's (id, prob) pairs (stable insertion sort)
     int id[K];
     float p[K];
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-        id[j] = valid ? ids[(int64_t)t * K + j] : -1;
-        p[j] = valid ? probs[(int64_t)t * K + j] : 0.0f;
+        id[j] = valid ? a.ids[(int64_t)t * K + j] : -1;
+        p[j] = valid ? a.probs[(int64_t)t * K + j] : 0.0f;
     }
 #pragma unroll
-    for (int a = 1; a < K; ++a)
+    for (int x = 1; x < K; ++x)
 #pragma unroll
-        for (int b = a; b > 0; --b)
-            if (id[b - 1] > id[b]) {
-                int ti = id[b]; id[b] = id[b - 1]; id[b - 1] = ti;
-                float tp = p[b]; p[b] = p[b - 1]; p[b - 1] = tp;
+        for (int y = x; y > 0; --y)
+            if (id[y - 1] > id[y]) {
+                int ti = id[y]; id[y] = id[y - 1]; id[y - 1] = ti;
+                float tp = p[y]; p[y] = p[y - 1]; p[y - 1] = tp;
             }
     uint32_t err = 0;
-    if (valid) {
-#pragma unroll
-        for (int j = 0; j < K; ++j) {
-            sorted_ids[(int64_t)t * K + j] = id[j];
-            sorted_probs[(int64_t)t * K + j] = p[j];
-            if (id[j] < 0 || id[j] >= E) err |= kErrBadId;
-            if (j > 0 && id[j] == id[j - 1]) err |= kErrDupId;
-        }
-    }
-    // in-wave stable ranks: route (t, j) precedes (t', j') iff t < t' or
-    // (t == t' and j < j'); rank = earlier routes of this wave with the same id
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int rank[K];
-#pragma unroll
-    for (int j = 0; j < K; ++j) rank[j] = -1;
-    for (int e = 0; e < E; ++e) {
-        uint64_t m[K];
-        int tot = 0;
-#pragma unroll
-        for (int j = 0; j < K; ++j) {
-            m[j] = __ballot(valid && id[j] == e);
-            tot += __popcll(m[j]);
-        }
-        if (tot == 0) {
-            if (lane == 0) wcnt[wid][e] = 0;
-            continue;
-        }
-        int before = 0;
-#pragma unroll
-        for (int j = 0; j < K; ++j) before += __popcll(m[j] & lt);
-        int same_tok = 0;
-#pragma unroll
-        for (int j = 0; j < K; ++j)
-            if (valid && id[j] == e) { rank[j] = before + same_tok; ++same_tok; }
-        if (lane == 0) wcnt[wid][e] = tot;
-    }
-    __syncthreads();
-    // chunk counts and the wave's base inside the chunk
+    bool keep[K];
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-        if (rank[j] >= 0) {
-            int e = id[j];
-            int base = 0;
-            for (int w = 0; w < wid; ++w) base += wcnt[w][e];
-            rank[j] += base;
+        const bool in = id[j] >= 0 && id[j] < E;
+        const bool dup = j > 0 && id[j] == id[j - 1];
+        keep[j] = valid && in && !dup;
+        if (valid && !in) err |= kErrBadId;
+        if (valid && dup) err |= kErrDupId;
+        if (valid) {
+            a.sorted_ids[(int64_t)t * K + j] = id[j];
+            a.sorted_probs[(int64_t)t * K + j] = p[j];
         }
-        if (valid) local_rank[(int64_t)t * K + j] = rank[j];
     }
-    for (int e = threadIdx.x; e < E; e += blockDim.x)
-        chunk_counts[(int64_t)c * E + e] = wcnt[0][e] + wcnt[1][e] + wcnt[2][e] + wcnt[3][e];
-    // OR of the error bits of the chunk
-    uint64_t any_bad = __ballot(err & kErrBadId), any_dup = __ballot(err & kErrDupId);
-    __shared__ uint32_t werr[4];
-    if (lane == 0) werr[wid] = (any_bad ? kErrBadId : 0u) | (any_dup ? kErrDupId : 0u);
     __syncthreads();
-    if (threadIdx.x == 0) chunk_err[c] = werr[0] | werr[1] | werr[2] | werr[3];
-}
-
-// One workgroup of 1024 threads.
-__global__ void __launch_bounds__(1024) prep_scan_kernel(
-    int64_t T_cap, const int32_t* __restrict__ live_ptr, int E, int k,
-    int32_t* __restrict__ chunk_base, const uint32_t* __restrict__ chunk_err,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int2* __restrict__ tiles,
-    WsHeader* __restrict__ hdr)
-{
-    __shared__ int lds[32];
-    const int32_t live = *live_ptr;
-    const int T = clamp_live(live, T_cap);
-    const int nch = (T + kChunkTok - 1) / kChunkTok;
-    const int e = threadIdx.x;
-    // per-expert prefix over chunks (chunk order = token order)
-    int run = 0;
-    if (e < E) {
-        for (int c = 0; c < nch; ++c) {
-            int v = chunk_base[(int64_t)c * E + e];
-            chunk_base[(int64_t)c * E + e] = run;
-            run += v;
+    const int word = threadIdx.x >> 5, bit = threadIdx.x & 31;
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+        if (keep[j]) atomicOr(&bm[id[j] * 8 + word], 1u << bit);
+    __syncthreads();
+    // stable rank = tokens of this chunk below t that route to the same expert
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        int rank = -1;
+        if (keep[j]) {
+            const uint32_t* m = &bm[id[j] * 8];
+            rank = __popc(m[word] & ((1u << bit) - 1u));
+            for (int w = 0; w < word; ++w) rank += __popc(m[w]);
         }
+        if (valid) a.local_rank[(int64_t)t * K + j] = rank;
     }
-    int cnt = e < E ? run : 0;
-    int total;
-    int off = block_exclusive_scan(cnt, &total, lds);
-    if (e < E) {
-        counts[e] = cnt;
-        offsets[e] = off;
-        for (int c = 0; c < nch; ++c) chunk_base[(int64_t)c * E + e] += off;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        int n = 0;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) n += __popc(bm[e * 8 + w]);
+        a.chunk_base[(int64_t)c * E + e] = n;
     }
-    if (e == 0) offsets[E] = total;
-    // M-tile table: expert e owns ceil(count / kBM) tiles
-    int nt = (cnt + kBM - 1) / kBM;
-    int ntotal;
-    int tfirst = block_exclusive_scan(nt, &ntotal, lds);
-    for (int i = 0; i < nt; ++i) tiles[tfirst + i] = make_int2(e, off + i * kBM);
-    // error word: OR over the live chunks plus the live-count checks
-    uint32_t err = 0;
-    for (int c = e; c < nch; c += blockDim.x) err |= chunk_err[c];
-    uint64_t b1 = __ballot(err & kErrBadId), b2 = __ballot(err & kErrDupId);
-    __shared__ uint32_t werr[16];
-    if ((threadIdx.x & 63) == 0) werr[threadIdx.x >> 6] = (b1 ? kErrBadId : 0u) | (b2 ? kErrDupId : 0u);
+    uint64_t any_bad = __ballot(err & kErrBadId), any_dup = __ballot(err & kErrDupId);
+    if ((threadIdx.x & 63) == 0)
+        lds[threadIdx.x >> 6] = (any_bad ? kErrBadId : 0) | (any_dup ? kErrDupId : 0);
     __syncthreads();
     if (threadIdx.x == 0) {
-        uint32_t all = (live < 0 ? kErrLiveNeg : 0u) | (live > T_cap ? kErrLiveHigh : 0u);
-        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) all |= werr[w];
-        hdr->fwd_err = all;
-        hdr->T = T;
-        hdr->n_tiles = ntotal;
-        hdr->n_rows = total;
+        uint32_t ce = 0;
+        for (int w = 0; w < 4; ++w) ce |= (uint32_t)lds[w];
+        a.chunk_err[c] = ce;
     }
+    // the last workgroup to finish does the scan: publish this chunk's data
+    // (device-scope release), take a ticket, and only the last ticket holder
+    // reads every chunk's data (acquire).  Nobody waits.
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t prev = atomicAdd(&a.hdr->ticket, 1u);
+        s_last = (prev == (uint32_t)(nch - 1));
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    prep_finish(a, T, nch, K, live, lds);
+    if (threadIdx.x == 0) atomicExch(&a.hdr->ticket, 0u);
 }
 
 __global__ void __launch_bounds__(256) prep_scatter_kernel(
@@ -206,9 +238,9 @@ __global__ void __launch_bounds__(256) prep_scatter_kernel(
     const int64_t R = (int64_t)T * k;
     for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < R;
          r += (int64_t)gridDim.x * blockDim.x) {
-        int e = sorted_ids[r];
         int rk = local_rank[r];
-        if (rk < 0 || e < 0 || e >= E) { dst[r] = -1; continue; }
+        if (rk < 0) { dst[r] = -1; continue; }
+        int e = sorted_ids[r];
         int c = (int)((r / k) / kChunkTok);
         int pos = chunk_base[(int64_t)c * E + e] + rk;
         perm_src[pos] = (int32_t)r;
@@ -219,16 +251,25 @@ __global__ void __launch_bounds__(256) prep_scatter_kernel(
 hipError_t launch_prep(const int32_t* ids, const float* probs, int64_t T_cap, const int32_t* live,
                        int E, int k, int num_cu, char* ws, const WsLayout& L, hipStream_t s)
 {
-    int32_t* sorted_ids = (int32_t*)(ws + L.sorted_ids);
-    float* sorted_probs = (float*)(ws + L.sorted_probs);
-    int32_t* local_rank = (int32_t*)(ws + L.local_rank);
-    int32_t* chunk_base = (int32_t*)(ws + L.chunk_base);
-    uint32_t* chunk_err = (uint32_t*)(ws + L.chunk_err);
+    PrepArgs a;
+    a.ids = ids;
+    a.probs = probs;
+    a.T_cap = T_cap;
+    a.live = live;
+    a.E = E;
+    a.sorted_ids = (int32_t*)(ws + L.sorted_ids);
+    a.sorted_probs = (float*)(ws + L.sorted_probs);
+    a.local_rank = (int32_t*)(ws + L.local_rank);
+    a.chunk_base = (int32_t*)(ws + L.chunk_base);
+    a.chunk_err = (uint32_t*)(ws + L.chunk_err);
+    a.counts = (int32_t*)(ws + L.counts);
+    a.offsets = (int32_t*)(ws + L.offsets);
+    a.tiles = (int2*)(ws + L.tiles);
+    a.hdr = (WsHeader*)(ws + L.hdr);
     dim3 g1((unsigned)L.nchunks), b1(256);
-#define PREP_CASE(KK)                                                                        \
-    case KK:                                                                                 \
-        hipLaunchKernelGGL(prep_count_kernel<KK>, g1, b1, 0, s, ids, probs, T_cap, live, E,  \
-                           sorted_ids, sorted_probs, local_rank, chunk_base, chunk_err);     \
+#define PREP_CASE(KK)                                                        \
+    case KK:                                                                 \
+        hipLaunchKernelGGL(prep_kernel<KK>, g1, b1, 0, s, a);                \
         break;
     switch (k) {
         PREP_CASE(1) PREP_CASE(2) PREP_CASE(3) PREP_CASE(4) PREP_CASE(5) PREP_CASE(6)
@@ -237,15 +278,12 @@ hipError_t launch_prep(const int32_t* ids, const float* probs, int64_t T_cap, co
         default: return hipErrorInvalidValue;
     }
 #undef PREP_CASE
-    hipLaunchKernelGGL(prep_scan_kernel, dim3(1), dim3(1024), 0, s, T_cap, live, E, k, chunk_base,
-                       chunk_err, (int32_t*)(ws + L.counts), (int32_t*)(ws + L.offsets),
-                       (int2*)(ws + L.tiles), (WsHeader*)(ws + L.hdr));
     int64_t R = T_cap * k;
     int64_t blocks = (R + 255) / 256;
     if (blocks > (int64_t)num_cu * 4) blocks = (int64_t)num_cu * 4;
     if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL(prep_scatter_kernel, dim3((unsigned)blocks), dim3(256), 0, s, T_cap, live, E,
-                       k, sorted_ids, local_rank, chunk_base, (int32_t*)(ws + L.perm_src),
+                       k, a.sorted_ids, a.local_rank, a.chunk_base, (int32_t*)(ws + L.perm_src),
                        (int32_t*)(ws + L.dst));
     return hipGetLastError();
 }

@@ -1,0 +1,229 @@
+"""Batch invariance, determinism, live-row bounds, refit and error reporting of
+the HIP path (through the C ABI), on the GPU.
+
+Megatron-LM PR #7830, "Tests": a token's output does not depend on how many
+tokens shared the launch; repeated launches return identical bits; a refit
+without refreshing the kernel weights is stale (negative control); per-layer
+buffers are independent.  Megatron-LM PR #8367, "Problem": only the live
+rows are touched.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import WORKLOADS, Workload
+from gpu_common import Case, assert_close, live_tensor, sentinel_out, to_dev_bits, SENTINEL_BITS
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import swiglu_expert_mlp_amd  # noqa: F401
+
+
+INV = {
+    "decode_T300": WORKLOADS["decode"].with_tokens(300),
+    "logprob_T300": WORKLOADS["logprob"].with_tokens(300),
+    "mxfp8_T300": WORKLOADS["mxfp8_16k"].with_tokens(300),
+    "odd_mxfp8_T300": Workload("odd_mxfp8", 300, 300, 96, 160, 5, 3, "mxfp8"),
+}
+_cases = {}
+
+
+def case(name):
+    if name not in _cases:
+        _cases[name] = Case(INV[name], seed=12, outliers=INV[name].precision == "mxfp8")
+    return _cases[name]
+
+
+_handles = {}
+
+
+def handle(name):
+    if name not in _handles:
+        from swiglu_expert_mlp_amd import MoE
+        c = case(name)
+        w = c.w
+        m = MoE(w.E, w.H, w.F, w.k, w.precision)
+        w1, w2 = c.weights_dev()
+        m.load_weights(w1, w2)
+        _handles[name] = m
+    return _handles[name]
+
+
+def forward(m, x, ids, probs, live, T_cap=None, stream=None):
+    T_cap = x.shape[0] if T_cap is None else T_cap
+    out = sentinel_out(T_cap, m.H)
+    ws = m.new_workspace(T_cap)
+    m.forward(x, ids, probs, live_tensor(live), out=out, ws=ws, stream=stream)
+    return out, ws
+
+
+def bits(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+@pytest.mark.parametrize("name", list(INV))
+def test_wide_equals_chunks_of_8(name):
+    c, m = case(name), handle(name)
+    x, ids, probs = c.dev()
+    T = c.w.T
+    wide, _ = forward(m, x, ids, probs, T)
+    wide = bits(wide)
+    for t0 in range(0, T, 8):
+        t1 = min(T, t0 + 8)
+        part, _ = forward(m, x[t0:t1].contiguous(), ids[t0:t1].contiguous(),
+                          probs[t0:t1].contiguous(), t1 - t0)
+        assert np.array_equal(bits(part), wide[t0:t1]), f"tokens {t0}..{t1}"
+
+
+@pytest.mark.parametrize("name", ["decode_T300", "mxfp8_T300"])
+def test_capacity_and_live_count_invariance(name):
+    """Same tokens: capacity T vs 4T (rows past live are NaN), and live counts
+    T, 171, 1, 0 at a fixed capacity give the same bits for the live tokens and
+    leave every other output row untouched."""
+    c, m = case(name), handle(name)
+    x, ids, probs = c.dev()
+    T = c.w.T
+    ref = bits(forward(m, x, ids, probs, T)[0])
+    cap = 4 * T
+    xb = torch.full((cap, c.w.H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    xb[:T] = x
+    ib = torch.full((cap, c.w.k), 0x7FC00000, dtype=torch.int32, device="cuda")
+    ib[:T] = ids
+    pb = torch.full((cap, c.w.k), float("nan"), dtype=torch.float32, device="cuda")
+    pb[:T] = probs
+    got = bits(forward(m, xb, ib, pb, T)[0])
+    assert np.array_equal(got[:T], ref)
+    assert np.all(got[T:] == SENTINEL_BITS)
+    for live in (T, 171, 1, 0):
+        got = bits(forward(m, x, ids, probs, live)[0])
+        assert np.array_equal(got[:live], ref[:live]), live
+        assert np.all(got[live:] == SENTINEL_BITS), live
+
+
+@pytest.mark.parametrize("name", ["decode_T300", "mxfp8_T300"])
+def test_token_order_invariance(name):
+    c, m = case(name), handle(name)
+    x, ids, probs = c.dev()
+    T = c.w.T
+    ref = bits(forward(m, x, ids, probs, T)[0])
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(T)).cuda()
+    got = bits(forward(m, x[perm].contiguous(), ids[perm].contiguous(),
+                       probs[perm].contiguous(), T)[0])
+    assert np.array_equal(got, ref[perm.cpu().numpy()])
+    # a token's routes listed in a different order: the same bits
+    rev = bits(forward(m, x, ids.flip(1).contiguous(), probs.flip(1).contiguous(), T)[0])
+    assert np.array_equal(rev, ref)
+
+
+@pytest.mark.parametrize("name", ["decode_T300", "odd_mxfp8_T300"])
+def test_repeat_and_racing_stream(name):
+    """Identical bits across repeated launches, also while a second stream
+    (default priority) moves ~1 GB through HBM at the same time."""
+    c, m = case(name), handle(name)
+    x, ids, probs = c.dev()
+    T = c.w.T
+    ref = bits(forward(m, x, ids, probs, T)[0])
+    for _ in range(3):
+        assert np.array_equal(bits(forward(m, x, ids, probs, T)[0]), ref)
+    src = torch.empty(256 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    with torch.cuda.stream(side):
+        for _ in range(4):
+            dst.copy_(src)
+    for _ in range(4):
+        outs.append(forward(m, x, ids, probs, T)[0])
+    torch.cuda.synchronize()
+    for o in outs:
+        assert np.array_equal(bits(o), ref)
+
+
+def test_refit_stale_then_fresh():
+    """Changing the parameters without reloading leaves the kernel weights (and
+    outputs) unchanged; reloading into the same buffer equals a fresh handle."""
+    from swiglu_expert_mlp_amd import MoE
+    c = case("decode_T300")
+    w = c.w
+    x, ids, probs = c.dev()
+    w1, w2 = c.weights_dev()
+    m = MoE(w.E, w.H, w.F, w.k, w.precision)
+    kbuf = m.load_weights(w1, w2)
+    before = bits(forward(m, x, ids, probs, w.T)[0])
+    w1.mul_(-0.5)                      # in-place parameter update, no refresh
+    stale = bits(forward(m, x, ids, probs, w.T)[0])
+    assert np.array_equal(stale, before), "the kernel weights changed without a refresh"
+    m.load_weights(w1, w2, kbuf=kbuf)  # the refit: rewrite the same buffer in place
+    refit = bits(forward(m, x, ids, probs, w.T)[0])
+    fresh_m = MoE(w.E, w.H, w.F, w.k, w.precision)
+    fresh_m.load_weights(w1, w2)
+    fresh = bits(forward(fresh_m, x, ids, probs, w.T)[0])
+    assert np.array_equal(refit, fresh)
+    assert not np.array_equal(refit, before)
+    # the reference: oracle with the updated weights
+    m_or = oracle.Model(w.E, w.H, w.F, w.k,
+                        w1.view(torch.int16).cpu().numpy().view(np.uint16),
+                        c.inp["w2_bits"])
+    ref, _, _ = m_or.forward(c.inp["x_bits"], c.ids, c.probs, w.T)
+    assert_close(refit.view(np.float32)[: w.T], ref[: w.T], "refit")
+
+
+def test_two_handles_are_independent():
+    from swiglu_expert_mlp_amd import MoE
+    c = case("decode_T300")
+    w = c.w
+    x, ids, probs = c.dev()
+    w1, w2 = c.weights_dev()
+    a = MoE(w.E, w.H, w.F, w.k, w.precision)
+    b = MoE(w.E, w.H, w.F, w.k, w.precision)
+    a.load_weights(w1, w2)
+    b.load_weights((w1 * 2).contiguous(), w2)
+    ra = bits(forward(a, x, ids, probs, w.T)[0])
+    rb = bits(forward(b, x, ids, probs, w.T)[0])
+    assert np.array_equal(ra, bits(forward(handle("decode_T300"), x, ids, probs, w.T)[0]))
+    assert not np.array_equal(ra, rb)
+
+
+@pytest.mark.parametrize("precision", ["bf16", "mxfp8"])
+def test_contract_violations_flagged_and_match_oracle(precision):
+    """An out-of-range id drops that route, a repeated id drops the repeat, and
+    both set their bit; live above capacity is clamped, below zero writes
+    nothing.  The outputs match the oracle's rules for the same cases."""
+    from swiglu_expert_mlp_amd import MoE
+    w = Workload("viol", 40, 40, 64, 96, 6, 3, precision)
+    c = Case(w, seed=13)
+    ids = c.ids.copy()
+    ids[3, 1] = 6            # out of range
+    ids[5, 2] = -1           # out of range
+    ids[7, 2] = ids[7, 0]    # duplicate
+    m = MoE(w.E, w.H, w.F, w.k, precision)
+    w1, w2 = c.weights_dev()
+    m.load_weights(w1, w2)
+    x = to_dev_bits(c.inp["x_bits"])
+    out, ws = forward(m, x, torch.from_numpy(ids).cuda(), torch.from_numpy(c.probs).cuda(), w.T)
+    assert m.check(ws) == 3
+    assert m.check(ws) == 0, "check clears the bits"
+    ref, err, _ = c.oracle_model().forward(c.inp["x_bits"], ids, c.probs, w.T)
+    assert err == 3
+    assert_close(out.cpu().numpy()[: w.T], ref[: w.T], "violations")
+    # live above capacity: clamped, bit 4
+    out, ws = forward(m, x, torch.from_numpy(c.ids).cuda(), torch.from_numpy(c.probs).cuda(),
+                      w.T + 5)
+    assert m.check(ws) == 4
+    assert not np.any(bits(out) == SENTINEL_BITS)
+    # live below zero: nothing written, bit 8
+    out, ws = forward(m, x, torch.from_numpy(c.ids).cuda(), torch.from_numpy(c.probs).cuda(), -3)
+    assert m.check(ws) == 8
+    assert np.all(bits(out) == SENTINEL_BITS)
+    # the router reports its live-count bits too
+    logits = torch.from_numpy(c.inp["logits"]).cuda()
+    ws = m.new_workspace(w.T_cap)
+    m.route(logits, live_tensor(w.T + 1), ws=ws)
+    assert m.check(ws) == 4

@@ -181,7 +181,10 @@ def _prepare_reference(ids, probs, live, E):
         for j, (e, _) in enumerate(pairs):
             sorted_ids[t, j] = e
             routes.append((e, t * k + j))
-    valid = [(e, r) for e, r in routes if 0 <= e < E]
+    # a route is dropped if its id is out of range or repeats the id of the
+    # route before it in canonical order (the same expert listed twice)
+    valid = [(e, r) for e, r in routes
+             if 0 <= e < E and not (r % k > 0 and sorted_ids.reshape(-1)[r - 1] == e)]
     perm = [r for e, r in sorted(valid, key=lambda q: q[0])]
     counts = np.bincount([e for e, _ in valid], minlength=E)
     dst = -np.ones(T * k, np.int64)
