@@ -47,7 +47,22 @@ def _args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device copy 5 times (to scale HBM counters)")
     return p.parse_args()
+
+
+def copy_calibration():
+    """A plain copy of known size: 1 GiB read + 1 GiB written per launch, the
+    reference that converts FETCH_SIZE / WRITE_SIZE counter readings to bytes."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}))
 
 
 def alg_bytes(w, precision: str, touched: int) -> dict:
@@ -113,6 +128,9 @@ def main():
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
               f"(--gpus {a.gpus} requested)", file=sys.stderr)
         sys.exit(2)
+    if a.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
     from workloads import WORKLOADS, make_inputs
