@@ -65,6 +65,29 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}))
 
 
+GEMM_SOURCES = ["swiglu_expert_mlp_amd/csrc/gemm_bf16.hip", "swiglu_expert_mlp_amd/csrc/gemm_mxfp8.hip",
+                "swiglu_expert_mlp_amd/csrc/gemm_args.h", "swiglu_expert_mlp_amd/csrc/common.h"]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    runs (profiles/traffic.json), or None when the GEMM sources changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    entry = json.load(open(path)).get(workload)
+    if not entry:
+        return None
+    h = hashlib.sha256()
+    for s in GEMM_SOURCES:
+        with open(os.path.join(ROOT, s), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != entry.get("gemm_source_sha256"):
+        return None
+    return entry["fetch_bytes_per_launch"] + entry["write_bytes_per_launch"]
+
+
 def alg_bytes(w, precision: str, touched: int) -> dict:
     """Algorithmic bytes: each touched expert's weights once, each live token's
     x row once, routed rows written/read once where a stage must (FC1 writes
@@ -229,7 +252,7 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["kernel"] = "gemm_bf16_kernel<FC1>" if w.precision == "bf16" else "gemm_mxfp8_kernel<FC1>"
     roof["kernel_us"] = fc1_us
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(w.name)
 
     res = {
         "metric": METRIC, "value": tokens_s, "unit": "tokens/s", "n_gpus": 1,
