@@ -19,7 +19,9 @@ constexpr int kWave = 64;            // CDNA wavefront width
 constexpr int kMaxTopk = 16;
 constexpr int kMaxExperts = 1024;
 constexpr int kChunkTok = 256;       // tokens per prep workgroup
-constexpr int kBM = 64;              // rows per M tile of the grouped GEMMs
+constexpr int kBM = 64;              // rows per M tile of the streaming GEMMs
+constexpr int kBigBMRows = 256;      // rows per M tile of the LDS-staged GEMMs
+constexpr int kBigMin = 128;         // experts with more rows than this use the LDS-staged GEMMs
 
 // Error bits reported by moe_check (same values as the header's MOE_DEVERR_*).
 constexpr uint32_t kErrBadId = 1u;
@@ -100,7 +102,8 @@ struct WsLayout {
     size_t sorted_probs;   // float [T_cap * k]
     size_t perm_src;       // int32 [T_cap * k]
     size_t dst;            // int32 [T_cap * k]
-    size_t tiles;          // int2 [max_tiles]: (expert, first row)
+    size_t tiles;          // int2 [max_tiles]: (expert, first row), streaming GEMM tiles
+    size_t tiles_big;      // int2 [max_tiles_big]: (expert, first row), LDS-staged GEMM tiles
     size_t hbuf;           // bf16 [T_cap * k][F] or E4M3 [T_cap * k][F]
     size_t hscale;         // E8M0 [T_cap * k][F / 32] (mxfp8)
     size_t obuf;           // float [T_cap * k][H]
@@ -109,6 +112,7 @@ struct WsLayout {
     size_t total;
     int64_t nchunks;
     int64_t max_tiles;
+    int64_t max_tiles_big;
 };
 
 struct WsHeader {
@@ -118,7 +122,8 @@ struct WsHeader {
     int32_t n_tiles;       // M tiles in the tile table
     int32_t n_rows;        // routed rows with a valid expert
     uint32_t ticket;       // prep workgroups finished (the last one resets it to 0)
-    int32_t pad[58];
+    int32_t n_tiles_big;   // M tiles in the LDS-staged table
+    int32_t pad[57];
 };
 
 static_assert(sizeof(WsHeader) == 256, "header is one 256-byte block");

@@ -13,9 +13,10 @@ struct GemmArgs {
     const uint16_t* A;         // FC1: x [T_cap][H]; FC2: hbuf [rows][F]
     const uint16_t* W;         // FC1: packed W1 [E][2F][H]; FC2: W2 [E][H][F]
     const int32_t* perm_src;   // FC1: grouped row -> route (t * k + j)
-    const int2* tiles;         // (expert, first row) per M tile
+    const int2* tiles;         // (expert, first row) per M tile (streaming kernel)
+    const int2* tiles_big;     // (expert, first row) per 256-row M tile (LDS-staged kernel)
     const int32_t* offsets;    // [E + 1]
-    const WsHeader* hdr;       // n_tiles
+    const WsHeader* hdr;       // n_tiles, n_tiles_big
     void* out;                 // FC1: hbuf bf16 [rows][F]; FC2: obuf fp32 [rows][H]
     int N;                     // FC1: 2F; FC2: H
     int K;                     // FC1: H;  FC2: F
@@ -31,6 +32,7 @@ struct MxGemmArgs {
     const uint8_t* Ws;         // scales [E][N][K/32]
     const int32_t* perm_src;
     const int2* tiles;
+    const int2* tiles_big;
     const int32_t* offsets;
     const WsHeader* hdr;
     void* out;                 // FC1: hbuf codes [rows][F]; FC2: obuf fp32 [rows][H]

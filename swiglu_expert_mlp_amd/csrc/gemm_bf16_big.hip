@@ -1,0 +1,194 @@
+// K3 / K4 for experts with many rows: LDS-staged grouped GEMM on CDNA4 MFMA,
+// bf16 operands, fp32 accumulate.
+//
+// Same arithmetic contract as gemm_bf16.hip (and therefore bitwise the same
+// results for a row): every output element is acc = 0; for k0 = 0, 32, ... :
+// acc = MFMA_16x16x32_bf16(A[row, k0:k0+32], B[col, k0:k0+32], acc).  Only
+// the decomposition differs: a workgroup computes a 256 x 256 tile, each of
+// its 8 waves a 128 x 64 part (8 x 4 MFMA blocks, accumulators in registers;
+// for FC1 the 64 columns are one gate/up interleave block), with both
+// operands staged through LDS in 64-wide K stages,
+// double-buffered.  Stages are filled with direct global->LDS loads
+// (global_load_lds_dwordx4): one wave instruction moves one 16 x 32 operand
+// block (1 KB) into LDS already in MFMA lane order, so every LDS read of a
+// fragment is a conflict-free 16-byte-per-lane read.  The weight blocks are
+// stored in exactly that order in the kernel-weight buffer (1 KB contiguous
+// per block); activation blocks are gathered 16 rows x 64 bytes at a time.
+//
+// Tiles: the device-built table of 256-row M tiles (experts with more rows
+// than the streaming kernel takes) x 256-column N tiles.  The persistent grid
+// is one workgroup per CU; tiles are split into 8 contiguous ranges, one per
+// XCD (workgroups are dispatched round-robin over the XCDs), so the tiles of
+// one expert, which share activation and weight slices, run on one XCD and
+// share its L2.
+#include "gemm_args.h"
+
+namespace moe {
+
+constexpr int kBigBM = 256;
+constexpr int kBigBN = 256;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void load_block_to_lds(const void* gsrc, void* lds_dst)
+{
+    __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)lds_dst, 16, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 lds_frag(const char* base, int lane)
+{
+    return __builtin_bit_cast(bf16x8, *(const uint4*)(base + 16 * lane));
+}
+
+template <bool FC1>
+__global__ void __launch_bounds__(512, 1) gemm_bf16_big_kernel(GemmArgs g)
+{
+    // [stage][A 32 blocks | B 32 blocks] of 1 KB; block (group, ks) at 2 group + ks
+    __shared__ __attribute__((aligned(1024))) char smem[2][64 * 1024];
+    const int n_mt = g.hdr->n_tiles_big;
+    const int NT = (g.N + kBigBN - 1) / kBigBN;
+    const int total = n_mt * NT;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;   // 8 waves
+    const int wm = wid >> 2, wn = wid & 3;                        // 2 x 4 waves
+    const int K = g.K;
+    const int nsteps = K / 32;                                    // 32-wide K steps
+    const int nstages = (nsteps + 1) / 2;
+    const int nt16 = g.N / 16;
+
+    // contiguous range of tiles for this XCD, strided over its workgroups
+    const int xcd = blockIdx.x & 7, per_xcd = gridDim.x >> 3;
+    const int chunk = (total + 7) / 8;
+    const int t_begin = xcd * chunk;
+    const int t_end = min(total, t_begin + chunk);
+    for (int tile = t_begin + (blockIdx.x >> 3); tile < t_end; tile += per_xcd) {
+        const int mt = tile / NT, nt = tile - mt * NT;
+        const int2 te = g.tiles_big[mt];
+        const int e = te.x, row0 = te.y;
+        int rows = g.offsets[e + 1] - row0;
+        if (rows > kBigBM) rows = kBigBM;
+        const int n0 = nt * kBigBN;
+
+        // loads: wave w moves A blocks of row groups 2w, 2w+1 and B blocks of
+        // column groups 2w, 2w+1, both K halves of the stage (8 blocks)
+        const uint16_t* arow[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            int r = 16 * (2 * wid + i) + (lane & 15);
+            if (r >= rows) r = rows - 1;
+            const int row = row0 + r;
+            int64_t src_row = row;
+            if constexpr (FC1) src_row = g.perm_src[row] / g.topk;
+            arow[i] = g.A + src_row * K + 8 * (lane >> 4);
+        }
+        const uint16_t* bblk[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            int c16 = n0 / 16 + 2 * wid + i;
+            if (c16 >= nt16) c16 = nt16 - 1;
+            bblk[i] = g.W + ((int64_t)e * nt16 + c16) * (int64_t)nsteps * 512 + 8 * lane;
+        }
+        auto issue_stage = [&](int st, int buf) {
+            const int s0 = 2 * st;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i = q >> 1, ks = q & 1;
+                if (s0 + ks < nsteps) {
+                    load_block_to_lds(arow[i] + 32 * (s0 + ks),
+                                      &smem[buf][((2 * wid + i) * 2 + ks) * 1024]);
+                    load_block_to_lds(bblk[i] + 512 * (s0 + ks),
+                                      &smem[buf][32 * 1024 + ((2 * wid + i) * 2 + ks) * 1024]);
+                }
+            }
+        };
+
+        f32x4 acc[8][4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        issue_stage(0, 0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        for (int st = 0; st < nstages; ++st) {
+            const int buf = st & 1;
+            if (st + 1 < nstages) issue_stage(st + 1, buf ^ 1);
+            const char* As = &smem[buf][0];
+            const char* Bs = &smem[buf][32 * 1024];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                if (2 * st + ks < nsteps) {
+                    bf16x8 a[8], b[4];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) a[i] = lds_frag(As + ((8 * wm + i) * 2 + ks) * 1024, lane);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) b[j] = lds_frag(Bs + ((4 * wn + j) * 2 + ks) * 1024, lane);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j],
+                                                                                0, 0, 0);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+
+        // epilogue: lane holds rows 4 (lane / 16) + v of each 16-row group, column lane % 16
+        const int r16 = lane & 15, kg = lane >> 4;
+        const int c0 = n0 + 64 * wn;                 // this wave's 64 columns
+        if constexpr (FC1) {
+            // one interleave block: tiles 0, 1 gate and 2, 3 up of the same 32 outputs
+            const int F = g.N / 2;
+            const int cb = c0 / 64;
+            uint16_t* hb = (uint16_t*)g.out;
+            if (c0 < g.N) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int r = 128 * wm + 16 * i + 4 * kg + v;
+                        if (r < rows) {
+                            const int64_t row = row0 + r;
+#pragma unroll
+                            for (int ct = 0; ct < 2; ++ct) {
+                                const float gt = acc[i][ct][v];
+                                const float up = acc[i][ct + 2][v];
+                                const float h = gt / (1.0f + __expf(-gt)) * up;
+                                hb[row * F + cb * 32 + 16 * ct + r16] = f32_to_bf16_bits(h);
+                            }
+                        }
+                    }
+            }
+        } else {
+            float* ob = (float*)g.out;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = 128 * wm + 16 * i + 4 * kg + v;
+                    if (r < rows) {
+                        const int64_t row = row0 + r;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int col = c0 + 16 * j + r16;
+                            if (col < g.N) ob[row * g.N + col] = acc[i][j][v];
+                        }
+                    }
+                }
+        }
+    }
+}
+
+hipError_t launch_gemm_bf16_big(bool fc1, const GemmArgs& g, int num_cu, hipStream_t s)
+{
+    dim3 grid((unsigned)(num_cu >= 8 ? num_cu / 8 * 8 : 8)), block(512);
+    if (fc1)
+        hipLaunchKernelGGL(gemm_bf16_big_kernel<true>, grid, block, 0, s, g);
+    else
+        hipLaunchKernelGGL(gemm_bf16_big_kernel<false>, grid, block, 0, s, g);
+    return hipGetLastError();
+}
+
+}  // namespace moe

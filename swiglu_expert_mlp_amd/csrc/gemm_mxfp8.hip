@@ -148,14 +148,24 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs& g, int e, int row
 template <bool FC1>
 __global__ void __launch_bounds__(256) gemm_mxfp8_kernel(MxGemmArgs g)
 {
-    const int n_mt = g.hdr->n_tiles;
+    // 64-row tiles: the streaming table, then each 256-row tile of the large-
+    // expert table as four 64-row tiles
+    const int n_small = g.hdr->n_tiles;
+    const int n_mt = n_small + 4 * g.hdr->n_tiles_big;
     const int total = n_mt * g.n_tiles_n;
     const int wid = threadIdx.x >> 6;
     const int n_cb = g.N / 64 + ((g.N % 64) ? 1 : 0);
     for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
         const int mt = tile / g.n_tiles_n;
         const int nt = tile - mt * g.n_tiles_n;
-        const int2 te = g.tiles[mt];
+        int2 te;
+        if (mt < n_small) {
+            te = g.tiles[mt];
+        } else {
+            const int b = mt - n_small;
+            te = g.tiles_big[b >> 2];
+            te.y += kBM * (b & 3);
+        }
         const int e = te.x, row0 = te.y;
         int rows = g.offsets[e + 1] - row0;
         if (rows > kBM) rows = kBM;

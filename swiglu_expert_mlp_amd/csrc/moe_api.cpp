@@ -31,6 +31,7 @@ hipError_t launch_quant_x(const uint16_t* x, int64_t T_cap, const int32_t* live,
 
 namespace moe {
 hipError_t launch_gemm_bf16(bool fc1, const GemmArgs& g, int num_cu, hipStream_t s);
+hipError_t launch_gemm_bf16_big(bool fc1, const GemmArgs& g, int num_cu, hipStream_t s);
 hipError_t launch_gemm_mxfp8(bool fc1, const MxGemmArgs& g, int num_cu, hipStream_t s);
 }  // namespace moe
 
@@ -84,6 +85,7 @@ static WsLayout layout_of(const moe_ctx* h, int64_t T_cap)
     L.nchunks = (T_cap + kChunkTok - 1) / kChunkTok;
     if (L.nchunks < 1) L.nchunks = 1;
     L.max_tiles = E + (R + kBM - 1) / kBM + 1;
+    L.max_tiles_big = E + (R + kBigBMRows - 1) / kBigBMRows + 1;
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += up256(bytes > 0 ? bytes : 1); return at; };
     L.hdr = take(sizeof(WsHeader));
@@ -97,6 +99,7 @@ static WsLayout layout_of(const moe_ctx* h, int64_t T_cap)
     L.perm_src = take(4 * R);
     L.dst = take(4 * R);
     L.tiles = take(8 * L.max_tiles);
+    L.tiles_big = take(8 * L.max_tiles_big);
     if (h->precision == MOE_BF16) {
         L.hbuf = take(2 * R * F);
         L.hscale = 0;
@@ -251,6 +254,7 @@ moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
         g1.W = (const uint16_t*)h->kbuf;
         g1.perm_src = (const int32_t*)(w + L.perm_src);
         g1.tiles = (const int2*)(w + L.tiles);
+        g1.tiles_big = (const int2*)(w + L.tiles_big);
         g1.offsets = (const int32_t*)(w + L.offsets);
         g1.hdr = hdr;
         g1.out = w + L.hbuf;
@@ -259,6 +263,7 @@ moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
         g1.topk = h->k;
         g1.n_tiles_n = ((2 * F / 64) + 3) / 4;
         e = launch_gemm_bf16(true, g1, h->num_cu, stream);
+        if (e == hipSuccess) e = launch_gemm_bf16_big(true, g1, h->num_cu, stream);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC1 launch");
         if ((e = mark(h, 3, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
         GemmArgs g2 = g1;
@@ -270,6 +275,7 @@ moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
         g2.K = F;
         g2.n_tiles_n = ((H + 63) / 64 + 3) / 4;
         e = launch_gemm_bf16(false, g2, h->num_cu, stream);
+        if (e == hipSuccess) e = launch_gemm_bf16_big(false, g2, h->num_cu, stream);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
         if ((e = mark(h, 4, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     } else {
@@ -290,6 +296,7 @@ moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
         g1.Ws = s1;
         g1.perm_src = (const int32_t*)(w + L.perm_src);
         g1.tiles = (const int2*)(w + L.tiles);
+        g1.tiles_big = (const int2*)(w + L.tiles_big);
         g1.offsets = (const int32_t*)(w + L.offsets);
         g1.hdr = hdr;
         g1.out = w + L.hbuf;

@@ -70,6 +70,7 @@ struct PrepArgs {
     int32_t* counts;
     int32_t* offsets;
     int2* tiles;
+    int2* tiles_big;
     WsHeader* hdr;
 };
 
@@ -96,11 +97,17 @@ __device__ void prep_finish(const PrepArgs& a, int T, int nch, int k, int32_t li
     }
     int total;
     int off = block_exclusive_scan(mine, &total, lds);
-    int ntile_mine = 0;
+    // M tiles: an expert with at most kBigMin rows goes to the streaming GEMM
+    // (64-row tiles), a larger one to the LDS-staged GEMM (256-row tiles)
+    int ntile_mine = 0, nbig_mine = 0;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) ntile_mine += (cnt[q] + kBM - 1) / kBM;
-    int ntotal;
+    for (int q = 0; q < PER; ++q) {
+        if (cnt[q] > kBigMin) nbig_mine += (cnt[q] + kBigBMRows - 1) / kBigBMRows;
+        else ntile_mine += (cnt[q] + kBM - 1) / kBM;
+    }
+    int ntotal, nbig;
     int tfirst = block_exclusive_scan(ntile_mine, &ntotal, lds);
+    int bfirst = block_exclusive_scan(nbig_mine, &nbig, lds);
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
         const int e = threadIdx.x * PER + q;
@@ -108,9 +115,15 @@ __device__ void prep_finish(const PrepArgs& a, int T, int nch, int k, int32_t li
             a.counts[e] = cnt[q];
             a.offsets[e] = off;
             for (int c = 0; c < nch; ++c) a.chunk_base[(int64_t)c * E + e] += off;
-            const int nt = (cnt[q] + kBM - 1) / kBM;
-            for (int i = 0; i < nt; ++i) a.tiles[tfirst + i] = make_int2(e, off + i * kBM);
-            tfirst += nt;
+            if (cnt[q] > kBigMin) {
+                const int nt = (cnt[q] + kBigBMRows - 1) / kBigBMRows;
+                for (int i = 0; i < nt; ++i) a.tiles_big[bfirst + i] = make_int2(e, off + i * kBigBMRows);
+                bfirst += nt;
+            } else {
+                const int nt = (cnt[q] + kBM - 1) / kBM;
+                for (int i = 0; i < nt; ++i) a.tiles[tfirst + i] = make_int2(e, off + i * kBM);
+                tfirst += nt;
+            }
         }
         off += cnt[q];
     }
@@ -126,6 +139,7 @@ __device__ void prep_finish(const PrepArgs& a, int T, int nch, int k, int32_t li
         a.hdr->fwd_err = all;
         a.hdr->T = T;
         a.hdr->n_tiles = ntotal;
+        a.hdr->n_tiles_big = nbig;
         a.hdr->n_rows = total;
     }
 }
@@ -265,6 +279,7 @@ hipError_t launch_prep(const int32_t* ids, const float* probs, int64_t T_cap, co
     a.counts = (int32_t*)(ws + L.counts);
     a.offsets = (int32_t*)(ws + L.offsets);
     a.tiles = (int2*)(ws + L.tiles);
+    a.tiles_big = (int2*)(ws + L.tiles_big);
     a.hdr = (WsHeader*)(ws + L.hdr);
     dim3 g1((unsigned)L.nchunks), b1(256);
 #define PREP_CASE(KK)                                                        \
