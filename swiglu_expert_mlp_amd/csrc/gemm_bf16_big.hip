@@ -7,8 +7,8 @@
 // the decomposition differs: a workgroup computes a 256 x 256 tile, each of
 // its 8 waves a 128 x 64 part (8 x 4 MFMA blocks, accumulators in registers;
 // for FC1 the 64 columns are one gate/up interleave block), with both
-// operands staged through LDS in 64-wide K stages,
-// double-buffered.  Stages are filled with direct global->LDS loads
+// operands staged through LDS in 32-wide K stages,
+// a ring of 4 stages with 3 in flight.  Stages are filled with direct global->LDS loads
 // (global_load_lds_dwordx4): one wave instruction moves one 16 x 32 operand
 // block (1 KB) into LDS already in MFMA lane order, so every LDS read of a
 // fragment is a conflict-free 16-byte-per-lane read.  The weight blocks are
@@ -40,11 +40,17 @@ __device__ __forceinline__ bf16x8 lds_frag(const char* base, int lane)
     return __builtin_bit_cast(bf16x8, *(const uint4*)(base + 16 * lane));
 }
 
+constexpr int kRing = 4;          // LDS stages (one 32-wide K step each)
+constexpr int kStageBytes = 32 * 1024;
+
+// s_waitcnt with only a vector-memory bound (expcnt and lgkmcnt left at max).
+#define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+
 template <bool FC1>
 __global__ void __launch_bounds__(512, 1) gemm_bf16_big_kernel(GemmArgs g)
 {
-    // [stage][A 32 blocks | B 32 blocks] of 1 KB; block (group, ks) at 2 group + ks
-    __shared__ __attribute__((aligned(1024))) char smem[2][64 * 1024];
+    // [stage][A 16 blocks | B 16 blocks] of 1 KB (16 rows or columns x 32 K)
+    __shared__ __attribute__((aligned(1024))) char smem[kRing][kStageBytes];
     const int n_mt = g.hdr->n_tiles_big;
     const int NT = (g.N + kBigBN - 1) / kBigBN;
     const int total = n_mt * NT;
@@ -52,7 +58,6 @@ __global__ void __launch_bounds__(512, 1) gemm_bf16_big_kernel(GemmArgs g)
     const int wm = wid >> 2, wn = wid & 3;                        // 2 x 4 waves
     const int K = g.K;
     const int nsteps = K / 32;                                    // 32-wide K steps
-    const int nstages = (nsteps + 1) / 2;
     const int nt16 = g.N / 16;
 
     // contiguous range of tiles for this XCD, strided over its workgroups
@@ -68,8 +73,8 @@ __global__ void __launch_bounds__(512, 1) gemm_bf16_big_kernel(GemmArgs g)
         if (rows > kBigBM) rows = kBigBM;
         const int n0 = nt * kBigBN;
 
-        // loads: wave w moves A blocks of row groups 2w, 2w+1 and B blocks of
-        // column groups 2w, 2w+1, both K halves of the stage (8 blocks)
+        // loads: wave w moves the A blocks of row groups 2w, 2w+1 and the B
+        // blocks of column groups 2w, 2w+1 of each K step (4 instructions)
         const uint16_t* arow[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -87,17 +92,12 @@ __global__ void __launch_bounds__(512, 1) gemm_bf16_big_kernel(GemmArgs g)
             if (c16 >= nt16) c16 = nt16 - 1;
             bblk[i] = g.W + ((int64_t)e * nt16 + c16) * (int64_t)nsteps * 512 + 8 * lane;
         }
-        auto issue_stage = [&](int st, int buf) {
-            const int s0 = 2 * st;
+        auto issue = [&](int s) {
+            char* st = smem[s % kRing];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int i = q >> 1, ks = q & 1;
-                if (s0 + ks < nsteps) {
-                    load_block_to_lds(arow[i] + 32 * (s0 + ks),
-                                      &smem[buf][((2 * wid + i) * 2 + ks) * 1024]);
-                    load_block_to_lds(bblk[i] + 512 * (s0 + ks),
-                                      &smem[buf][32 * 1024 + ((2 * wid + i) * 2 + ks) * 1024]);
-                }
+            for (int i = 0; i < 2; ++i) {
+                load_block_to_lds(arow[i] + 32 * s, st + (2 * wid + i) * 1024);
+                load_block_to_lds(bblk[i] + 512 * s, st + 16 * 1024 + (2 * wid + i) * 1024);
             }
         };
 
@@ -107,32 +107,34 @@ __global__ void __launch_bounds__(512, 1) gemm_bf16_big_kernel(GemmArgs g)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        issue_stage(0, 0);
-        __builtin_amdgcn_s_waitcnt(0);
+        // every wave finished the previous tile's reads before the ring is refilled
         __syncthreads();
-        for (int st = 0; st < nstages; ++st) {
-            const int buf = st & 1;
-            if (st + 1 < nstages) issue_stage(st + 1, buf ^ 1);
-            const char* As = &smem[buf][0];
-            const char* Bs = &smem[buf][32 * 1024];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                if (2 * st + ks < nsteps) {
-                    bf16x8 a[8], b[4];
+        for (int s = 0; s < kRing - 1; ++s)
+            if (s < nsteps) issue(s);
+        for (int s = 0; s < nsteps; ++s) {
+            // step s landed when at most the later in-flight steps remain
+            const int later = min(kRing - 2, nsteps - 1 - s);
+            if (later >= 2) WAIT_VMCNT(8);
+            else if (later == 1) WAIT_VMCNT(4);
+            else WAIT_VMCNT(0);
+            // a bare barrier: each wave has waited for its own loads of step s,
+            // and __syncthreads() would also wait for the steps still in flight
+            __builtin_amdgcn_s_barrier();
+            // refill the slot every wave finished reading in the previous step
+            if (s + kRing - 1 < nsteps) issue(s + kRing - 1);
+            const char* As = smem[s % kRing];
+            const char* Bs = As + 16 * 1024;
+            bf16x8 a[8], b[4];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) a[i] = lds_frag(As + ((8 * wm + i) * 2 + ks) * 1024, lane);
+            for (int i = 0; i < 8; ++i) a[i] = lds_frag(As + (8 * wm + i) * 1024, lane);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) b[j] = lds_frag(Bs + ((4 * wn + j) * 2 + ks) * 1024, lane);
+            for (int j = 0; j < 4; ++j) b[j] = lds_frag(Bs + (4 * wn + j) * 1024, lane);
 #pragma unroll
-                    for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < 8; ++i)
 #pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j],
-                                                                                0, 0, 0);
-                }
-            }
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
 
         // epilogue: lane holds rows 4 (lane / 16) + v of each 16-row group, column lane % 16

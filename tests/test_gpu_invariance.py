@@ -81,6 +81,26 @@ def test_wide_equals_chunks_of_8(name):
         assert np.array_equal(bits(part), wide[t0:t1]), f"tokens {t0}..{t1}"
 
 
+def test_streaming_and_lds_staged_gemms_agree_bitwise():
+    """Experts with more than 128 rows run on the LDS-staged GEMM, the others on
+    the streaming GEMM; a token's bits must not depend on which one ran."""
+    from swiglu_expert_mlp_amd import MoE
+    w = WORKLOADS["logprob"].with_tokens(2048)
+    c = Case(w, seed=11)
+    m = MoE(w.E, w.H, w.F, w.k, w.precision)
+    w1, w2 = c.weights_dev()
+    m.load_weights(w1, w2)
+    x, ids, probs = c.dev()
+    wide, ws = forward(m, x, ids, probs, w.T)
+    counts = m.get_indices(ws, w.T)["counts"]
+    assert (counts > 128).sum() > 10 and (counts <= 128).sum() > 10, counts
+    wide = bits(wide)
+    for t0 in range(0, w.T, 128):
+        part, _ = forward(m, x[t0:t0 + 128].contiguous(), ids[t0:t0 + 128].contiguous(),
+                          probs[t0:t0 + 128].contiguous(), 128)
+        assert np.array_equal(bits(part), wide[t0:t0 + 128]), f"tokens {t0}.."
+
+
 @pytest.mark.parametrize("name", ["decode_T300", "mxfp8_T300"])
 def test_capacity_and_live_count_invariance(name):
     """Same tokens: capacity T vs 4T (rows past live are NaN), and live counts
