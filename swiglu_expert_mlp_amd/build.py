@@ -35,9 +35,17 @@ def _hipcc() -> str:
     return "hipcc"
 
 
+# per-file code generation options: the LDS-staged GEMMs keep MFMA accumulators
+# and operands in the VGPR form (the default split between VGPRs and AGPRs spills
+# their 128 x 128 per-wave tiles)
+FILE_FLAGS = {
+    "gemm_bf16_big.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [_hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + FLAGS
+    cmd = [_hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + FLAGS + FILE_FLAGS.get(src, [])
     if src.endswith(".cpp"):
         cmd = [_hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + FLAGS
     r = subprocess.run(cmd, capture_output=True, text=True)
