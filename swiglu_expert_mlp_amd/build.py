@@ -35,12 +35,8 @@ def _hipcc() -> str:
     return "hipcc"
 
 
-# per-file code generation options: the LDS-staged GEMMs keep MFMA accumulators
-# and operands in the VGPR form (the default split between VGPRs and AGPRs spills
-# their 128 x 128 per-wave tiles)
-FILE_FLAGS = {
-    "gemm_bf16_big.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-}
+# per-file code generation options
+FILE_FLAGS = {}
 
 
 def _compile(src: str) -> str:

@@ -5,11 +5,10 @@
 // results for a row): every output element is acc = 0; for k0 = 0, 32, ... :
 // acc = MFMA_16x16x32_bf16(A[row, k0:k0+32], B[col, k0:k0+32], acc).  Only
 // the decomposition differs: a workgroup computes a 256 x 256 tile, each of
-// its 4 waves a 128 x 128 quarter (8 x 8 MFMA blocks, accumulators in
-// registers; for FC1 the 128 columns are two gate/up interleave blocks), with
-// both operands staged through LDS in 32-wide K stages, a ring of 4 stages
-// with 3 in flight, and each wave's operand fragments for the next K step
-// read from LDS while the MFMAs of the current step run.  Stages are filled with direct global->LDS loads
+// its 8 waves a 128 x 64 part (8 x 4 MFMA blocks, accumulators in registers;
+// for FC1 the 64 columns are one gate/up interleave block), with both
+// operands staged through LDS in 32-wide K stages,
+// a ring of 4 stages with 3 in flight.  Stages are filled with direct global->LDS loads
 // (global_load_lds_dwordx4): one wave instruction moves one 16 x 32 operand
 // block (1 KB) into LDS already in MFMA lane order, so every LDS read of a
 // fragment is a conflict-free 16-byte-per-lane read.  The weight blocks are
@@ -36,7 +35,10 @@ __device__ __forceinline__ void load_block_to_lds(const void* gsrc, void* lds_ds
     __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)lds_dst, 16, 0, 0);
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8_big(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ bf16x8 lds_frag(const char* base, int lane)
+{
+    return __builtin_bit_cast(bf16x8, *(const uint4*)(base + 16 * lane));
+}
 
 constexpr int kRing = 4;          // LDS stages (one 32-wide K step each)
 constexpr int kStageBytes = 32 * 1024;
@@ -45,15 +47,15 @@ constexpr int kStageBytes = 32 * 1024;
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 
 template <bool FC1>
-__global__ void __launch_bounds__(256, 1) gemm_bf16_big_kernel(GemmArgs g)
+__global__ void __launch_bounds__(512, 1) gemm_bf16_big_kernel(GemmArgs g)
 {
     // [stage][A 16 blocks | B 16 blocks] of 1 KB (16 rows or columns x 32 K)
     __shared__ __attribute__((aligned(1024))) char smem[kRing][kStageBytes];
     const int n_mt = g.hdr->n_tiles_big;
     const int NT = (g.N + kBigBN - 1) / kBigBN;
     const int total = n_mt * NT;
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;   // 4 waves
-    const int wm = wid >> 1, wn = wid & 1;                        // 2 x 2 waves
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;   // 8 waves
+    const int wm = wid >> 2, wn = wid & 3;                        // 2 x 4 waves
     const int K = g.K;
     const int nsteps = K / 32;                                    // 32-wide K steps
     const int nt16 = g.N / 16;
@@ -71,124 +73,95 @@ __global__ void __launch_bounds__(256, 1) gemm_bf16_big_kernel(GemmArgs g)
         if (rows > kBigBM) rows = kBigBM;
         const int n0 = nt * kBigBN;
 
-        // loads: wave w moves the A blocks of row groups 4w..4w+3 and the B
-        // blocks of column groups 4w..4w+3 of each K step (8 instructions)
-        const uint16_t* arow[4];
+        // loads: wave w moves the A blocks of row groups 2w, 2w+1 and the B
+        // blocks of column groups 2w, 2w+1 of each K step (4 instructions)
+        const uint16_t* arow[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int r = 16 * (4 * wid + i) + (lane & 15);
+        for (int i = 0; i < 2; ++i) {
+            int r = 16 * (2 * wid + i) + (lane & 15);
             if (r >= rows) r = rows - 1;
             const int row = row0 + r;
             int64_t src_row = row;
             if constexpr (FC1) src_row = g.perm_src[row] / g.topk;
             arow[i] = g.A + src_row * K + 8 * (lane >> 4);
         }
-        const uint16_t* bblk[4];
+        const uint16_t* bblk[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int c16 = n0 / 16 + 4 * wid + i;
+        for (int i = 0; i < 2; ++i) {
+            int c16 = n0 / 16 + 2 * wid + i;
             if (c16 >= nt16) c16 = nt16 - 1;
             bblk[i] = g.W + ((int64_t)e * nt16 + c16) * (int64_t)nsteps * 512 + 8 * lane;
         }
         auto issue = [&](int s) {
             char* st = smem[s % kRing];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                load_block_to_lds(arow[i] + 32 * s, st + (4 * wid + i) * 1024);
-                load_block_to_lds(bblk[i] + 512 * s, st + 16 * 1024 + (4 * wid + i) * 1024);
+            for (int i = 0; i < 2; ++i) {
+                load_block_to_lds(arow[i] + 32 * s, st + (2 * wid + i) * 1024);
+                load_block_to_lds(bblk[i] + 512 * s, st + 16 * 1024 + (2 * wid + i) * 1024);
             }
         };
-        // a wave's fragments of one K step: 8 A (its row groups) and 8 B
-        auto read_frags = [&](int s, uint4* fr) {
-            const char* As = smem[s % kRing];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) fr[i] = *(const uint4*)(As + (8 * wm + i) * 1024 + 16 * lane);
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                fr[8 + j] = *(const uint4*)(As + 16 * 1024 + (8 * wn + j) * 1024 + 16 * lane);
-        };
 
-        f32x4 acc[8][8];
+        f32x4 acc[8][4];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        auto mfma_step = [&](const uint4* fr) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        as_bf16x8_big(fr[i]), as_bf16x8_big(fr[8 + j]), acc[i][j], 0, 0, 0);
-        };
-        // a wave has landed step t once at most `later` of its steps issued after
-        // t are still in flight (8 loads each)
-        auto wait_landed = [&](int later) {
-            if (later >= 2) WAIT_VMCNT(16);
-            else if (later == 1) WAIT_VMCNT(8);
-            else WAIT_VMCNT(0);
-        };
+            for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         // every wave finished the previous tile's reads before the ring is refilled
         __syncthreads();
 #pragma unroll
         for (int s = 0; s < kRing - 1; ++s)
             if (s < nsteps) issue(s);
-        wait_landed(min(kRing - 2, nsteps - 1));
-        __builtin_amdgcn_s_barrier();
-        uint4 fa[16], fb[16];
-        read_frags(0, fa);
-        // two K steps per iteration so the fragment buffers alternate statically
-        for (int s = 0; s < nsteps; s += 2) {
+        for (int s = 0; s < nsteps; ++s) {
+            // step s landed when at most the later in-flight steps remain
+            const int later = min(kRing - 2, nsteps - 1 - s);
+            if (later >= 2) WAIT_VMCNT(8);
+            else if (later == 1) WAIT_VMCNT(4);
+            else WAIT_VMCNT(0);
+            // a bare barrier: each wave has waited for its own loads of step s,
+            // and __syncthreads() would also wait for the steps still in flight
+            __builtin_amdgcn_s_barrier();
+            // refill the slot every wave finished reading in the previous step
+            if (s + kRing - 1 < nsteps) issue(s + kRing - 1);
+            const char* As = smem[s % kRing];
+            const char* Bs = As + 16 * 1024;
+            bf16x8 a[8], b[4];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int t = s + h;
-                if (t < nsteps) {
-                    // make step t+1 visible to every wave, refill the slot of step t-1
-                    // (read by every wave before this barrier), prefetch t+1's
-                    // fragments, then run step t's MFMAs
-                    if (t + 1 < nsteps) wait_landed(min(1, nsteps - 2 - t));
-                    __builtin_amdgcn_s_barrier();
-                    if (t + kRing - 1 < nsteps) issue(t + kRing - 1);
-                    if (h == 0) {
-                        if (t + 1 < nsteps) read_frags(t + 1, fb);
-                        mfma_step(fa);
-                    } else {
-                        if (t + 1 < nsteps) read_frags(t + 1, fa);
-                        mfma_step(fb);
-                    }
-                }
-            }
+            for (int i = 0; i < 8; ++i) a[i] = lds_frag(As + (8 * wm + i) * 1024, lane);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = lds_frag(Bs + (4 * wn + j) * 1024, lane);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
 
         // epilogue: lane holds rows 4 (lane / 16) + v of each 16-row group, column lane % 16
         const int r16 = lane & 15, kg = lane >> 4;
-        const int c0 = n0 + 128 * wn;                // this wave's 128 columns
+        const int c0 = n0 + 64 * wn;                 // this wave's 64 columns
         if constexpr (FC1) {
+            // one interleave block: tiles 0, 1 gate and 2, 3 up of the same 32 outputs
             const int F = g.N / 2;
+            const int cb = c0 / 64;
             uint16_t* hb = (uint16_t*)g.out;
+            if (c0 < g.N) {
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-                // interleave block of 64 columns: tiles 4 blk + {0, 1} gate, + {2, 3} up
-                const int cb = c0 / 64 + blk;
-                if (cb * 64 < g.N) {
+                for (int i = 0; i < 8; ++i)
 #pragma unroll
-                    for (int i = 0; i < 8; ++i)
+                    for (int v = 0; v < 4; ++v) {
+                        const int r = 128 * wm + 16 * i + 4 * kg + v;
+                        if (r < rows) {
+                            const int64_t row = row0 + r;
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            const int r = 128 * wm + 16 * i + 4 * kg + v;
-                            if (r < rows) {
-                                const int64_t row = row0 + r;
-#pragma unroll
-                                for (int ct = 0; ct < 2; ++ct) {
-                                    const float gt = acc[i][4 * blk + ct][v];
-                                    const float up = acc[i][4 * blk + ct + 2][v];
-                                    const float h = gt / (1.0f + __expf(-gt)) * up;
-                                    hb[row * F + cb * 32 + 16 * ct + r16] = f32_to_bf16_bits(h);
-                                }
+                            for (int ct = 0; ct < 2; ++ct) {
+                                const float gt = acc[i][ct][v];
+                                const float up = acc[i][ct + 2][v];
+                                const float h = gt / (1.0f + __expf(-gt)) * up;
+                                hb[row * F + cb * 32 + 16 * ct + r16] = f32_to_bf16_bits(h);
                             }
                         }
-                }
+                    }
             }
         } else {
             float* ob = (float*)g.out;
@@ -200,7 +173,7 @@ __global__ void __launch_bounds__(256, 1) gemm_bf16_big_kernel(GemmArgs g)
                     if (r < rows) {
                         const int64_t row = row0 + r;
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) {
+                        for (int j = 0; j < 4; ++j) {
                             const int col = c0 + 16 * j + r16;
                             if (col < g.N) ob[row * g.N + col] = acc[i][j][v];
                         }
@@ -212,7 +185,7 @@ __global__ void __launch_bounds__(256, 1) gemm_bf16_big_kernel(GemmArgs g)
 
 hipError_t launch_gemm_bf16_big(bool fc1, const GemmArgs& g, int num_cu, hipStream_t s)
 {
-    dim3 grid((unsigned)(num_cu >= 8 ? num_cu / 8 * 8 : 8)), block(256);
+    dim3 grid((unsigned)(num_cu >= 8 ? num_cu / 8 * 8 : 8)), block(512);
     if (fc1)
         hipLaunchKernelGGL(gemm_bf16_big_kernel<true>, grid, block, 0, s, g);
     else
