@@ -1,0 +1,73 @@
+// Finalize fused into the FC2 epilogue.
+//
+// Megatron-LM PR #7798, "What is changed": a token's routes are added as fp32
+// fused multiply-adds of probability and row, from zero, in the listed order;
+// Megatron-LM PR #7830, "1. Mega backend for generation": the listed order is
+// ascending expert id.  Megatron-LM PR #8367, "Problem": fp32 result, only
+// live tokens.
+//
+// The k FC2 rows of a token come from k different expert tiles.  Each FC2
+// workgroup, after storing its unweighted fp32 rows for one 256-column slice,
+// counts one arrival per row on (token, slice); the workgroup whose arrival
+// completes the token's count publishes nothing more and sums the token's
+// rows for that slice itself:
+//   out[t][c] = fma(p_{k-1}, O[dst[t,k-1]][c], ... fma(p_0, O[dst[t,0]][c], +0.0f))
+// The atomics only decide WHO sums; the sum is always the same fixed-order
+// chain, so the result bits do not depend on the arrival order.  Stores are
+// published with a device-scope release fence before the arrival and read
+// after a device-scope acquire fence (the L2 of each XCD is written back /
+// invalidated), so rows written on another XCD are seen.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+struct FinArgs {
+    int32_t* cnt;              // [T_cap][ns_per_token] arrivals, zeroed by the prep kernel
+    const int32_t* kvalid;     // [T_cap] kept routes of each token
+    const int32_t* perm_src;   // grouped row -> route
+    const int32_t* dst;        // route -> grouped row (-1 if dropped)
+    const float* sorted_probs; // [T_cap][k] in canonical order
+    const float* O;            // fp32 FC2 rows [rows][H]
+    float* out;                // [T_cap][H]
+    int H;
+    int k;
+    int ns_per_token;          // ceil(H / 256)
+};
+
+// All threads of the workgroup call this after storing the O values of rows
+// [row0, row0 + rows) and columns [256 ns, 256 ns + 256).  list: LDS scratch of
+// at least rows + 1 ints.
+__device__ __forceinline__ void fused_finalize(const FinArgs& f, int row0, int rows, int ns, int* list)
+{
+    __syncthreads();                       // every wave's stores of this tile are done
+    if (threadIdx.x == 0) list[0] = 0;
+    __syncthreads();
+    for (int r = threadIdx.x; r < rows; r += blockDim.x) {
+        const int route = f.perm_src[row0 + r];
+        const int t = route / f.k;
+        __threadfence();                   // release this tile's rows before the arrival
+        const int old = atomicAdd(&f.cnt[(int64_t)t * f.ns_per_token + ns], 1);
+        if (old == f.kvalid[t] - 1) list[1 + atomicAdd(&list[0], 1)] = t;
+    }
+    __syncthreads();
+    const int nl = list[0];
+    if (nl == 0) return;
+    __threadfence();                       // acquire the other routes' rows
+    const int c0 = ns * 256;
+    for (int q = threadIdx.x; q < nl * 256; q += blockDim.x) {
+        const int i = q >> 8, c = c0 + (q & 255);
+        if (c >= f.H) continue;
+        const int t = list[1 + i];
+        float acc = 0.0f;
+        for (int j = 0; j < f.k; ++j) {
+            const int d = f.dst[(int64_t)t * f.k + j];
+            if (d < 0) continue;
+            acc = __builtin_fmaf(f.sorted_probs[(int64_t)t * f.k + j], f.O[(int64_t)d * f.H + c], acc);
+        }
+        f.out[(int64_t)t * f.H + c] = acc;
+    }
+}
+
+}  // namespace moe

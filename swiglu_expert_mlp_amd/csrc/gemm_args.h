@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "common.h"
+#include "finalize_fused.h"
 
 namespace moe {
 
@@ -22,6 +23,7 @@ struct GemmArgs {
     int K;                     // FC1: H;  FC2: F
     int topk;
     int n_tiles_n;             // N tiles per M tile (4 waves x 64 columns each)
+    FinArgs fin;               // FC2: the fused finalize
 };
 
 // MXFP8 operands: E4M3 codes with one E8M0 scale byte per 32 elements of K.
@@ -41,6 +43,7 @@ struct MxGemmArgs {
     int K;
     int topk;
     int n_tiles_n;
+    FinArgs fin;               // FC2: the fused finalize
 };
 
 }  // namespace moe

@@ -51,6 +51,7 @@ __global__ void __launch_bounds__(512, 1) gemm_bf16_big_kernel(GemmArgs g)
 {
     // [stage][A 16 blocks | B 16 blocks] of 1 KB (16 rows or columns x 32 K)
     __shared__ __attribute__((aligned(1024))) char smem[kRing][kStageBytes];
+    __shared__ int fin_list[kBigBM + 1];
     const int n_mt = g.hdr->n_tiles_big;
     const int NT = (g.N + kBigBN - 1) / kBigBN;
     const int total = n_mt * NT;
@@ -179,6 +180,7 @@ __global__ void __launch_bounds__(512, 1) gemm_bf16_big_kernel(GemmArgs g)
                         }
                     }
                 }
+            fused_finalize(g.fin, row0, rows, nt, fin_list);
         }
     }
 }
