@@ -13,10 +13,15 @@
 // rows for that slice itself:
 //   out[t][c] = fma(p_{k-1}, O[dst[t,k-1]][c], ... fma(p_0, O[dst[t,0]][c], +0.0f))
 // The atomics only decide WHO sums; the sum is always the same fixed-order
-// chain, so the result bits do not depend on the arrival order.  Stores are
-// published with a device-scope release fence before the arrival and read
-// after a device-scope acquire fence (the L2 of each XCD is written back /
-// invalidated), so rows written on another XCD are seen.
+// chain, so the result bits do not depend on the arrival order.
+//
+// Visibility across XCDs (each XCD has its own L2): the FC2 rows are stored
+// with device-scope atomic stores (write-through past the XCD's L2), the
+// workgroup waits for their completion and issues one device-scope release
+// fence before its arrivals, and the summing workgroup reads the rows with
+// device-scope atomic loads (which do not return lines cached in its own
+// L2).  No L2 invalidation is needed, so the other workgroups of the XCD keep
+// their cached GEMM operands.
 #pragma once
 
 #include "common.h"
@@ -29,7 +34,7 @@ struct FinArgs {
     const int32_t* perm_src;   // grouped row -> route
     const int32_t* dst;        // route -> grouped row (-1 if dropped)
     const float* sorted_probs; // [T_cap][k] in canonical order
-    const float* O;            // fp32 FC2 rows [rows][H]
+    float* O;                  // fp32 FC2 rows [rows][H]
     float* out;                // [T_cap][H]
     int H;
     int k;
@@ -39,22 +44,30 @@ struct FinArgs {
 // All threads of the workgroup call this after storing the O values of rows
 // [row0, row0 + rows) and columns [256 ns, 256 ns + 256).  list: LDS scratch of
 // at least rows + 1 ints.
+// Device-scope atomic (write-through) store of one FC2 value.
+__device__ __forceinline__ void store_fc2(float* p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ void fused_finalize(const FinArgs& f, int row0, int rows, int ns, int* list)
 {
-    __syncthreads();                       // every wave's stores of this tile are done
-    if (threadIdx.x == 0) list[0] = 0;
-    __syncthreads();
-    for (int r = threadIdx.x; r < rows; r += blockDim.x) {
-        const int route = f.perm_src[row0 + r];
-        const int t = route / f.k;
-        __threadfence();                   // release this tile's rows before the arrival
-        const int old = atomicAdd(&f.cnt[(int64_t)t * f.ns_per_token + ns], 1);
-        if (old == f.kvalid[t] - 1) list[1 + atomicAdd(&list[0], 1)] = t;
+    __builtin_amdgcn_s_waitcnt(0);         // this wave's FC2 stores have completed
+    __syncthreads();                       // ... and every other wave's
+    if (threadIdx.x < 64) {
+        if (threadIdx.x == 0) list[0] = 0;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        for (int r = threadIdx.x; r < rows; r += 64) {
+            const int route = f.perm_src[row0 + r];
+            const int t = route / f.k;
+            const int old = __hip_atomic_fetch_add(&f.cnt[(int64_t)t * f.ns_per_token + ns], 1,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (old == f.kvalid[t] - 1) list[1 + atomicAdd(&list[0], 1)] = t;
+        }
     }
     __syncthreads();
     const int nl = list[0];
     if (nl == 0) return;
-    __threadfence();                       // acquire the other routes' rows
     const int c0 = ns * 256;
     for (int q = threadIdx.x; q < nl * 256; q += blockDim.x) {
         const int i = q >> 8, c = c0 + (q & 255);
@@ -64,7 +77,9 @@ __device__ __forceinline__ void fused_finalize(const FinArgs& f, int row0, int r
         for (int j = 0; j < f.k; ++j) {
             const int d = f.dst[(int64_t)t * f.k + j];
             if (d < 0) continue;
-            acc = __builtin_fmaf(f.sorted_probs[(int64_t)t * f.k + j], f.O[(int64_t)d * f.H + c], acc);
+            const float o = __hip_atomic_load(&f.O[(int64_t)d * f.H + c], __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+            acc = __builtin_fmaf(f.sorted_probs[(int64_t)t * f.k + j], o, acc);
         }
         f.out[(int64_t)t * f.H + c] = acc;
     }

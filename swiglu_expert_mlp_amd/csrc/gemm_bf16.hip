@@ -144,7 +144,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, int e, int row0, in
 #pragma unroll
                     for (int ct = 0; ct < 4; ++ct) {
                         int col = cb * 64 + 16 * ct + r16;
-                        if (col < g.N) ob[row * g.N + col] = acc[rg][ct][i];
+                        if (col < g.N) store_fc2(&ob[row * g.N + col], acc[rg][ct][i]);
                     }
                 }
             }

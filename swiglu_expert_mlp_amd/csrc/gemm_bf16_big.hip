@@ -176,7 +176,7 @@ __global__ void __launch_bounds__(512, 1) gemm_bf16_big_kernel(GemmArgs g)
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
                             const int col = c0 + 16 * j + r16;
-                            if (col < g.N) ob[row * g.N + col] = acc[i][j][v];
+                            if (col < g.N) store_fc2(&ob[row * g.N + col], acc[i][j][v]);
                         }
                     }
                 }

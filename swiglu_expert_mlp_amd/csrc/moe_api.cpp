@@ -253,7 +253,7 @@ moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
     fin.perm_src = (const int32_t*)(w + L.perm_src);
     fin.dst = (const int32_t*)(w + L.dst);
     fin.sorted_probs = (const float*)(w + L.sorted_probs);
-    fin.O = (const float*)(w + L.obuf);
+    fin.O = (float*)(w + L.obuf);
     fin.out = out;
     fin.H = H;
     fin.k = h->k;
