@@ -15,13 +15,12 @@
 // The atomics only decide WHO sums; the sum is always the same fixed-order
 // chain, so the result bits do not depend on the arrival order.
 //
-// Visibility across XCDs (each XCD has its own L2): the FC2 rows are stored
-// with device-scope atomic stores (write-through past the XCD's L2), the
-// workgroup waits for their completion and issues one device-scope release
-// fence before its arrivals, and the summing workgroup reads the rows with
-// device-scope atomic loads (which do not return lines cached in its own
-// L2).  No L2 invalidation is needed, so the other workgroups of the XCD keep
-// their cached GEMM operands.
+// Visibility across XCDs (each XCD has its own L2): after storing its FC2
+// rows the workgroup issues one device-scope release fence (the XCD's L2
+// writes its dirty lines back) before its arrivals, and the summing workgroup
+// reads the rows with device-scope atomic loads, which do not return lines
+// cached in its own L2.  No L2 invalidation is needed, so the other
+// workgroups of the XCD keep their cached GEMM operands.
 #pragma once
 
 #include "common.h"
@@ -44,11 +43,8 @@ struct FinArgs {
 // All threads of the workgroup call this after storing the O values of rows
 // [row0, row0 + rows) and columns [256 ns, 256 ns + 256).  list: LDS scratch of
 // at least rows + 1 ints.
-// Device-scope atomic (write-through) store of one FC2 value.
-__device__ __forceinline__ void store_fc2(float* p, float v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// Store of one FC2 value (write-back; published by the release fence below).
+__device__ __forceinline__ void store_fc2(float* p, float v) { *p = v; }
 
 __device__ __forceinline__ void fused_finalize(const FinArgs& f, int row0, int rows, int ns, int* list)
 {
