@@ -210,7 +210,7 @@ def main():
     ev.record(t0, sh)
     for i in range(a.steps):
         m = moes[i % n_rot]
-        m.set_stage_events([None, None, fc1_ev[i][0], fc1_ev[i][1], None])
+        m.set_stage_events([None, None, fc1_ev[i][0], fc1_ev[i][1], None, None])
         step(i)
     ev.record(t1, sh)
     torch.cuda.synchronize()
@@ -221,21 +221,21 @@ def main():
 
     # stage breakdown (untimed diagnostic pass)
     n_diag = min(10, a.steps)
-    diag = [[ev.new() for _ in range(7)] for _ in range(n_diag)]
+    diag = [[ev.new() for _ in range(8)] for _ in range(n_diag)]
     for i in range(n_diag):
         m = moes[i % n_rot]
         d = diag[i]
-        ev.record(d[5], sh)
-        route_fn[i % n_rot]()
         ev.record(d[6], sh)
-        m.set_stage_events(d[:5])
+        route_fn[i % n_rot]()
+        ev.record(d[7], sh)
+        m.set_stage_events(d[:6])
         fwd_fn[i % n_rot]()
         m.set_stage_events(None)
     torch.cuda.synchronize()
     names = MoE.STAGES
     stage_us = {n: float(np.mean([ev.ms(d[j], d[j + 1]) for d in diag]) * 1e3)
                 for j, n in enumerate(names)}
-    stage_us = {"route": float(np.mean([ev.ms(d[5], d[6]) for d in diag]) * 1e3), **stage_us}
+    stage_us = {"route": float(np.mean([ev.ms(d[6], d[7]) for d in diag]) * 1e3), **stage_us}
     ev.close()
 
     ab = alg_bytes(w, w.precision, touched)

@@ -166,8 +166,8 @@ moe_status moe_check(moe_handle h, void* ws, hipStream_t stream, uint32_t* err_b
  * moe_forward on this handle records, on its stream, events[0] before its
  * first kernel and events[i] after stage i: 1 permutation (sort, histogram,
  * scan, scatter), 2 MXFP8 activation quantization (nothing in bf16), 3 FC1 +
- * SwiGLU, 4 FC2 with the fused finalize.  n_events must be 5; NULL entries
- * are not recorded.  The events are the caller's; pass events = NULL to stop. */
+ * SwiGLU, 4 FC2, 5 finalize.  n_events must be 6; NULL entries are not
+ * recorded.  The events are the caller's; pass events = NULL to stop. */
 moe_status moe_set_stage_events(moe_handle h, hipEvent_t* events, int n_events);
 
 /* Message of the last failed call on this thread ("" if none). */

@@ -238,17 +238,17 @@ class MoE:
                 n_rows, self.F // 32)
         return res
 
-    STAGES = ("permute", "quant_x", "fc1_swiglu", "fc2_finalize")
+    STAGES = ("permute", "quant_x", "fc1_swiglu", "fc2", "finalize")
 
     def set_stage_events(self, events):
-        """Record 5 events at the forward's stage boundaries (before the first
+        """Record 6 events at the forward's stage boundaries (before the first
         kernel, then after each of STAGES); entries may be None (skipped), raw
         hipEvent_t handles (int) or torch.cuda.Event objects.  None stops."""
         if events is None:
             _check(lib().moe_set_stage_events(self._h, None, 0), "moe_set_stage_events")
             return
-        if len(events) != 5:
-            raise ValueError("need 5 events")
+        if len(events) != 6:
+            raise ValueError("need 6 events")
         handles = []
         for ev in events:
             if ev is None or isinstance(ev, int):
@@ -257,8 +257,8 @@ class MoE:
             if not ev.cuda_event:        # torch creates the HIP event at its first record
                 ev.record()
             handles.append(_P(ev.cuda_event))
-        arr = (_P * 5)(*handles)
-        _check(lib().moe_set_stage_events(self._h, arr, 5), "moe_set_stage_events")
+        arr = (_P * 6)(*handles)
+        _check(lib().moe_set_stage_events(self._h, arr, 6), "moe_set_stage_events")
 
     def bind_forward(self, x, ids, probs, live, out, ws, stream=None):
         """Check the arguments once and return a no-argument callable that

@@ -22,7 +22,7 @@ ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["moe_api.cpp", "route.hip", "prep.hip", "gemm_bf16.hip", "gemm_bf16_big.hip",
            "gemm_mxfp8.hip",
-           "pack.hip"]
+           "finalize.hip", "pack.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include")]

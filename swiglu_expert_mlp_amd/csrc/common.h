@@ -109,8 +109,6 @@ struct WsLayout {
     size_t obuf;           // float [T_cap * k][H]
     size_t xq;             // E4M3 [T_cap][H] (mxfp8)
     size_t xs;             // E8M0 [T_cap][H / 32] (mxfp8)
-    size_t fin_cnt;        // int32 [T_cap][ceil(H / 256)]: finalize arrivals
-    size_t kvalid;         // int32 [T_cap]: kept routes per token
     size_t total;
     int64_t nchunks;
     int64_t max_tiles;

@@ -5,7 +5,6 @@
 #include <stdint.h>
 
 #include "common.h"
-#include "finalize_fused.h"
 
 namespace moe {
 
@@ -23,7 +22,6 @@ struct GemmArgs {
     int K;                     // FC1: H;  FC2: F
     int topk;
     int n_tiles_n;             // N tiles per M tile (4 waves x 64 columns each)
-    FinArgs fin;               // FC2: the fused finalize
 };
 
 // MXFP8 operands: E4M3 codes with one E8M0 scale byte per 32 elements of K.
@@ -43,7 +41,6 @@ struct MxGemmArgs {
     int K;
     int topk;
     int n_tiles_n;
-    FinArgs fin;               // FC2: the fused finalize
 };
 
 }  // namespace moe

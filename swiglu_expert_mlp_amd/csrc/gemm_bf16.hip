@@ -144,7 +144,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, int e, int row0, in
 #pragma unroll
                     for (int ct = 0; ct < 4; ++ct) {
                         int col = cb * 64 + 16 * ct + r16;
-                        if (col < g.N) store_fc2(&ob[row * g.N + col], acc[rg][ct][i]);
+                        if (col < g.N) ob[row * g.N + col] = acc[rg][ct][i];
                     }
                 }
             }
@@ -154,7 +154,6 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, int e, int row0, in
 template <bool FC1>
 __global__ void __launch_bounds__(256) gemm_bf16_kernel(GemmArgs g)
 {
-    __shared__ int fin_list[kBM + 1];
     const int n_mt = g.hdr->n_tiles;
     const int total = n_mt * g.n_tiles_n;
     const int wid = threadIdx.x >> 6;
@@ -166,19 +165,15 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(GemmArgs g)
         const int e = te.x, row0 = te.y;
         int rows = g.offsets[e + 1] - row0;
         if (rows > kBM) rows = kBM;
-        if (rows <= 0) continue;                     // the same for the whole workgroup
         const int cb = nt * 4 + wid;
-        if (cb < n_cb) {
-            const int ng = (rows + 15) >> 4;
-            switch (ng) {
-                case 1: tile_body<FC1, 1>(g, e, row0, rows, cb); break;
-                case 2: tile_body<FC1, 2>(g, e, row0, rows, cb); break;
-                case 3: tile_body<FC1, 3>(g, e, row0, rows, cb); break;
-                default: tile_body<FC1, 4>(g, e, row0, rows, cb); break;
-            }
+        if (cb >= n_cb || rows <= 0) continue;
+        const int ng = (rows + 15) >> 4;
+        switch (ng) {
+            case 1: tile_body<FC1, 1>(g, e, row0, rows, cb); break;
+            case 2: tile_body<FC1, 2>(g, e, row0, rows, cb); break;
+            case 3: tile_body<FC1, 3>(g, e, row0, rows, cb); break;
+            default: tile_body<FC1, 4>(g, e, row0, rows, cb); break;
         }
-        // FC2: the workgroup's 4 x 64 columns are the 256-column slice nt
-        if constexpr (!FC1) fused_finalize(g.fin, row0, rows, nt, fin_list);
     }
 }
 

@@ -51,7 +51,6 @@ __global__ void __launch_bounds__(512, 1) gemm_bf16_big_kernel(GemmArgs g)
 {
     // [stage][A 16 blocks | B 16 blocks] of 1 KB (16 rows or columns x 32 K)
     __shared__ __attribute__((aligned(1024))) char smem[kRing][kStageBytes];
-    __shared__ int fin_list[kBigBM + 1];
     const int n_mt = g.hdr->n_tiles_big;
     const int NT = (g.N + kBigBN - 1) / kBigBN;
     const int total = n_mt * NT;
@@ -176,11 +175,10 @@ __global__ void __launch_bounds__(512, 1) gemm_bf16_big_kernel(GemmArgs g)
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
                             const int col = c0 + 16 * j + r16;
-                            if (col < g.N) store_fc2(&ob[row * g.N + col], acc[i][j][v]);
+                            if (col < g.N) ob[row * g.N + col] = acc[i][j][v];
                         }
                     }
                 }
-            fused_finalize(g.fin, row0, rows, nt, fin_list);
         }
     }
 }

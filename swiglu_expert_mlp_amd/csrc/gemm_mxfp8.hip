@@ -138,7 +138,7 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs& g, int e, int row
 #pragma unroll
                     for (int ct = 0; ct < 4; ++ct) {
                         int col = cb * 64 + 16 * ct + r16;
-                        if (col < g.N) store_fc2(&ob[row * g.N + col], acc[rg][ct][i]);
+                        if (col < g.N) ob[row * g.N + col] = acc[rg][ct][i];
                     }
                 }
             }
@@ -150,7 +150,6 @@ __global__ void __launch_bounds__(256) gemm_mxfp8_kernel(MxGemmArgs g)
 {
     // 64-row tiles: the streaming table, then each 256-row tile of the large-
     // expert table as four 64-row tiles
-    __shared__ int fin_list[kBM + 1];
     const int n_small = g.hdr->n_tiles;
     const int n_mt = n_small + 4 * g.hdr->n_tiles_big;
     const int total = n_mt * g.n_tiles_n;
@@ -170,18 +169,15 @@ __global__ void __launch_bounds__(256) gemm_mxfp8_kernel(MxGemmArgs g)
         const int e = te.x, row0 = te.y;
         int rows = g.offsets[e + 1] - row0;
         if (rows > kBM) rows = kBM;
-        if (rows <= 0) continue;                     // the same for the whole workgroup
         const int cb = nt * 4 + wid;
-        if (cb < n_cb) {
-            const int ng = (rows + 15) >> 4;
-            switch (ng) {
-                case 1: mx_tile_body<FC1, 1>(g, e, row0, rows, cb); break;
-                case 2: mx_tile_body<FC1, 2>(g, e, row0, rows, cb); break;
-                case 3: mx_tile_body<FC1, 3>(g, e, row0, rows, cb); break;
-                default: mx_tile_body<FC1, 4>(g, e, row0, rows, cb); break;
-            }
+        if (cb >= n_cb || rows <= 0) continue;
+        const int ng = (rows + 15) >> 4;
+        switch (ng) {
+            case 1: mx_tile_body<FC1, 1>(g, e, row0, rows, cb); break;
+            case 2: mx_tile_body<FC1, 2>(g, e, row0, rows, cb); break;
+            case 3: mx_tile_body<FC1, 3>(g, e, row0, rows, cb); break;
+            default: mx_tile_body<FC1, 4>(g, e, row0, rows, cb); break;
         }
-        if constexpr (!FC1) fused_finalize(g.fin, row0, rows, nt, fin_list);
     }
 }
 

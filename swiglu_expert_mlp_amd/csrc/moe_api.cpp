@@ -14,8 +14,10 @@ namespace moe {
 hipError_t launch_route(const float* logits, int64_t T_cap, const int32_t* live, int E, int k,
                         int32_t* ids, float* probs, WsHeader* hdr, int num_cu, hipStream_t s);
 hipError_t launch_prep(const int32_t* ids, const float* probs, int64_t T_cap, const int32_t* live,
-                       int E, int k, int H, float* out, int num_cu, char* ws, const WsLayout& L,
-                       hipStream_t s);
+                       int E, int k, int num_cu, char* ws, const WsLayout& L, hipStream_t s);
+hipError_t launch_finalize(const float* O, const int32_t* dst, const float* sorted_probs,
+                           int64_t T_cap, const int32_t* live, int k, int H, float* out, int num_cu,
+                           hipStream_t s);
 hipError_t launch_pack_bf16(const uint16_t* w1, const uint16_t* w2, uint8_t* kbuf, int E, int H,
                             int F, int num_cu, hipStream_t s);
 hipError_t launch_pack_mxfp8(const uint16_t* w1, const uint16_t* w2, uint8_t* kbuf, int E, int H,
@@ -40,7 +42,7 @@ struct moe_ctx {
     const uint8_t* kbuf = nullptr;   // not owned
     int num_cu = 0;
     int device = -1;
-    hipEvent_t stage_events[5] = {};
+    hipEvent_t stage_events[6] = {};
     bool record_stages = false;
 };
 
@@ -109,8 +111,6 @@ static WsLayout layout_of(const moe_ctx* h, int64_t T_cap)
         L.xs = take(T_cap * (H / 32));
     }
     L.obuf = take(4 * R * H);
-    L.fin_cnt = take(4 * T_cap * ((H + 255) / 256));
-    L.kvalid = take(4 * T_cap);
     L.total = o;
     return L;
 }
@@ -242,22 +242,11 @@ moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
     WsHeader* hdr = (WsHeader*)(w + L.hdr);
     hipError_t e = mark(h, 0, stream);
     if (e != hipSuccess) return hip_fail(e, "moe_forward: stage event");
-    e = launch_prep(expert_ids, probs, T_cap, live_rows_dev, h->E, h->k, h->H, out, h->num_cu, w,
-                    L, stream);
+    e = launch_prep(expert_ids, probs, T_cap, live_rows_dev, h->E, h->k, h->num_cu, w, L,
+                               stream);
     if (e != hipSuccess) return hip_fail(e, "moe_forward: prep launch");
     if ((e = mark(h, 1, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     const int E = h->E, H = h->H, F = h->F;
-    FinArgs fin;
-    fin.cnt = (int32_t*)(w + L.fin_cnt);
-    fin.kvalid = (const int32_t*)(w + L.kvalid);
-    fin.perm_src = (const int32_t*)(w + L.perm_src);
-    fin.dst = (const int32_t*)(w + L.dst);
-    fin.sorted_probs = (const float*)(w + L.sorted_probs);
-    fin.O = (float*)(w + L.obuf);
-    fin.out = out;
-    fin.H = H;
-    fin.k = h->k;
-    fin.ns_per_token = (H + 255) / 256;
     if (h->precision == MOE_BF16) {
         if ((e = mark(h, 2, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
         GemmArgs g1;
@@ -285,7 +274,6 @@ moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
         g2.N = H;
         g2.K = F;
         g2.n_tiles_n = ((H + 63) / 64 + 3) / 4;
-        g2.fin = fin;
         e = launch_gemm_bf16(false, g2, h->num_cu, stream);
         if (e == hipSuccess) e = launch_gemm_bf16_big(false, g2, h->num_cu, stream);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
@@ -331,11 +319,15 @@ moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
         g2.N = H;
         g2.K = F;
         g2.n_tiles_n = ((H + 63) / 64 + 3) / 4;
-        g2.fin = fin;
         e = launch_gemm_mxfp8(false, g2, h->num_cu, stream);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
         if ((e = mark(h, 4, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     }
+    e = launch_finalize((const float*)(w + L.obuf), (const int32_t*)(w + L.dst),
+                        (const float*)(w + L.sorted_probs), T_cap, live_rows_dev, h->k, H, out,
+                        h->num_cu, stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_forward: finalize launch");
+    if ((e = mark(h, 5, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     return MOE_OK;
 }
 
@@ -400,8 +392,8 @@ moe_status moe_set_stage_events(moe_handle h, hipEvent_t* events, int n_events)
 {
     if (!h) return fail(MOE_ERR_INVALID_ARG, "moe_set_stage_events: NULL handle");
     if (!events) { h->record_stages = false; return MOE_OK; }
-    if (n_events != 5) return fail(MOE_ERR_INVALID_ARG, "moe_set_stage_events: n_events must be 5");
-    for (int i = 0; i < 5; ++i) h->stage_events[i] = events[i];
+    if (n_events != 6) return fail(MOE_ERR_INVALID_ARG, "moe_set_stage_events: n_events must be 6");
+    for (int i = 0; i < 6; ++i) h->stage_events[i] = events[i];
     h->record_stages = true;
     return MOE_OK;
 }

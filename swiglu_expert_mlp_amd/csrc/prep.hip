@@ -72,11 +72,6 @@ struct PrepArgs {
     int2* tiles;
     int2* tiles_big;
     WsHeader* hdr;
-    int32_t* fin_cnt;        // [T_cap][ns_per_token], zeroed here for live tokens
-    int32_t* kvalid;         // [T_cap]
-    int ns_per_token;
-    float* out;              // tokens without a kept route get a zero row here
-    int H;
 };
 
 // Prefix over chunks and experts, tile table, header (one workgroup).
@@ -199,15 +194,6 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a)
             a.sorted_probs[(int64_t)t * K + j] = p[j];
         }
     }
-    if (valid) {
-        int nk = 0;
-#pragma unroll
-        for (int j = 0; j < K; ++j) nk += keep[j] ? 1 : 0;
-        a.kvalid[t] = nk;
-        for (int q = 0; q < a.ns_per_token; ++q) a.fin_cnt[(int64_t)t * a.ns_per_token + q] = 0;
-        if (nk == 0)   // no FC2 tile will finalize this token: its output is the empty sum
-            for (int c = 0; c < a.H; ++c) a.out[(int64_t)t * a.H + c] = 0.0f;
-    }
     __syncthreads();
     const int word = threadIdx.x >> 5, bit = threadIdx.x & 31;
 #pragma unroll
@@ -277,15 +263,9 @@ __global__ void __launch_bounds__(256) prep_scatter_kernel(
 }
 
 hipError_t launch_prep(const int32_t* ids, const float* probs, int64_t T_cap, const int32_t* live,
-                       int E, int k, int H, float* out, int num_cu, char* ws, const WsLayout& L,
-                       hipStream_t s)
+                       int E, int k, int num_cu, char* ws, const WsLayout& L, hipStream_t s)
 {
     PrepArgs a;
-    a.fin_cnt = (int32_t*)(ws + L.fin_cnt);
-    a.kvalid = (int32_t*)(ws + L.kvalid);
-    a.ns_per_token = (H + 255) / 256;
-    a.out = out;
-    a.H = H;
     a.ids = ids;
     a.probs = probs;
     a.T_cap = T_cap;
