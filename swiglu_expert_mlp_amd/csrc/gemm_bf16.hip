@@ -65,8 +65,9 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, int e, int row0, in
 
     // Ring of D K-steps in flight: step s lives in slot s % D.  The MFMA order
     // is still k0 = 0, 32, 64, ... for every element; only the load schedule
-    // runs ahead.
-    constexpr int D = 4;
+    // runs ahead.  D shrinks as the row groups grow, so that every variant
+    // fits two workgroups per CU (the grid is two per CU, all resident).
+    constexpr int D = NG <= 2 ? 4 : (NG == 3 ? 3 : 2);
     const int nsteps = K / 32;
     uint4 ar[D][NG], br[D][4];
     auto load = [&](int d, int s) {
@@ -152,7 +153,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, int e, int row0, in
 }
 
 template <bool FC1>
-__global__ void __launch_bounds__(256) gemm_bf16_kernel(GemmArgs g)
+__global__ void __launch_bounds__(256, 2) gemm_bf16_kernel(GemmArgs g)
 {
     const int n_mt = g.hdr->n_tiles;
     const int total = n_mt * g.n_tiles_n;
@@ -179,7 +180,7 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(GemmArgs g)
 
 hipError_t launch_gemm_bf16(bool fc1, const GemmArgs& g, int num_cu, hipStream_t s)
 {
-    dim3 grid((unsigned)(num_cu * 3)), block(256);
+    dim3 grid((unsigned)(num_cu * 2)), block(256);
     if (fc1)
         hipLaunchKernelGGL(gemm_bf16_kernel<true>, grid, block, 0, s, g);
     else

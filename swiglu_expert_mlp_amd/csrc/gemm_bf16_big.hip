@@ -107,8 +107,11 @@ __global__ void __launch_bounds__(512, 1) gemm_bf16_big_kernel(GemmArgs g)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        // every wave finished the previous tile's reads before the ring is refilled
-        __syncthreads();
+        // every wave finished the previous tile's LDS reads before the ring is
+        // refilled; a bare barrier (no vmcnt drain) lets the previous tile's
+        // output stores overlap the first loads of this tile
+        __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
 #pragma unroll
         for (int s = 0; s < kRing - 1; ++s)
             if (s < nsteps) issue(s);

@@ -19,6 +19,10 @@
 //                  over chunks and experts, the M-tile table and the error word.
 //   prep_scatter   one thread per route: position = expert offset + chunk
 //                  base + rank; perm_src[position] = route, dst[route] = position.
+// A launch whose capacity fits one chunk (T_cap <= 256 tokens, the decode
+// sizes) runs as a single workgroup that keeps the counts in LDS, finishes
+// without device-scope fences or a ticket, and scatters its own routes; the
+// host then skips the scatter launch.
 // A route whose id is outside [0, E), or repeats an id already listed for the
 // token (contract violations), is dropped: it has no row and dst = -1.
 #include "common.h"
@@ -72,10 +76,17 @@ struct PrepArgs {
     int2* tiles;
     int2* tiles_big;
     WsHeader* hdr;
+    int32_t* perm_src;
+    int32_t* dst;
 };
 
 // Prefix over chunks and experts, tile table, header (one workgroup).
-__device__ void prep_finish(const PrepArgs& a, int T, int nch, int k, int32_t live, int* lds)
+// With local_cnt (single-chunk launch) the per-expert counts come from LDS,
+// the expert offsets go to local_off (LDS) instead of the chunk bases, and
+// local_err is the chunk's error bits.
+__device__ void prep_finish(const PrepArgs& a, int T, int nch, int k, int32_t live, int* lds,
+                            const int* local_cnt = nullptr, int* local_off = nullptr,
+                            uint32_t local_err = 0)
 {
     const int E = a.E;
     constexpr int PER = kMaxExperts / 256;          // experts per thread
@@ -86,10 +97,14 @@ __device__ void prep_finish(const PrepArgs& a, int T, int nch, int k, int32_t li
         const int e = threadIdx.x * PER + q;
         int run = 0;
         if (e < E) {
-            for (int c = 0; c < nch; ++c) {
-                int v = __builtin_nontemporal_load(&a.chunk_base[(int64_t)c * E + e]);
-                a.chunk_base[(int64_t)c * E + e] = run;
-                run += v;
+            if (local_cnt) {
+                run = local_cnt[e];
+            } else {
+                for (int c = 0; c < nch; ++c) {
+                    int v = __builtin_nontemporal_load(&a.chunk_base[(int64_t)c * E + e]);
+                    a.chunk_base[(int64_t)c * E + e] = run;
+                    run += v;
+                }
             }
         }
         cnt[q] = run;
@@ -114,7 +129,9 @@ __device__ void prep_finish(const PrepArgs& a, int T, int nch, int k, int32_t li
         if (e < E) {
             a.counts[e] = cnt[q];
             a.offsets[e] = off;
-            for (int c = 0; c < nch; ++c) a.chunk_base[(int64_t)c * E + e] += off;
+            if (local_off) local_off[e] = off;
+            else
+                for (int c = 0; c < nch; ++c) a.chunk_base[(int64_t)c * E + e] += off;
             if (cnt[q] > kBigMin) {
                 const int nt = (cnt[q] + kBigBMRows - 1) / kBigBMRows;
                 for (int i = 0; i < nt; ++i) a.tiles_big[bfirst + i] = make_int2(e, off + i * kBigBMRows);
@@ -129,7 +146,10 @@ __device__ void prep_finish(const PrepArgs& a, int T, int nch, int k, int32_t li
     }
     if (threadIdx.x == 0) a.offsets[E] = total;
     uint32_t err = 0;
-    for (int c = threadIdx.x; c < nch; c += blockDim.x) err |= __builtin_nontemporal_load(&a.chunk_err[c]);
+    if (local_cnt) err = threadIdx.x == 0 ? local_err : 0u;
+    else
+        for (int c = threadIdx.x; c < nch; c += blockDim.x)
+            err |= __builtin_nontemporal_load(&a.chunk_err[c]);
     uint64_t b1 = __ballot(err & kErrBadId), b2 = __ballot(err & kErrDupId);
     if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = (b1 ? kErrBadId : 0) | (b2 ? kErrDupId : 0);
     __syncthreads();
@@ -150,16 +170,18 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a)
     __shared__ uint32_t bm[kMaxExperts * (kChunkTok / 32)];
     __shared__ int lds[32];
     __shared__ int s_last;
+    __shared__ int loc[2 * kMaxExperts];         // single-chunk launch: counts, offsets
     const int32_t live = *a.live;
     const int T = clamp_live(live, a.T_cap);
     const int nch = (T + kChunkTok - 1) / kChunkTok;
     const int c = blockIdx.x;
     const int E = a.E;
-    if (nch == 0) {
+    const bool single = gridDim.x == 1;          // T_cap <= one chunk
+    if (nch == 0 && !single) {
         if (c == 0) prep_finish(a, T, 0, K, live, lds);
         return;
     }
-    if (c >= nch) return;
+    if (c >= nch && !single) return;
     for (int i = threadIdx.x; i < E * (kChunkTok / 32); i += blockDim.x) bm[i] = 0;
     const int t = c * kChunkTok + threadIdx.x;
     const bool valid = t < T;
@@ -201,31 +223,51 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a)
         if (keep[j]) atomicOr(&bm[id[j] * 8 + word], 1u << bit);
     __syncthreads();
     // stable rank = tokens of this chunk below t that route to the same expert
+    int rank[K];
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-        int rank = -1;
+        rank[j] = -1;
         if (keep[j]) {
             const uint32_t* m = &bm[id[j] * 8];
-            rank = __popc(m[word] & ((1u << bit) - 1u));
-            for (int w = 0; w < word; ++w) rank += __popc(m[w]);
+            rank[j] = __popc(m[word] & ((1u << bit) - 1u));
+            for (int w = 0; w < word; ++w) rank[j] += __popc(m[w]);
         }
-        if (valid) a.local_rank[(int64_t)t * K + j] = rank;
+        if (valid && !single) a.local_rank[(int64_t)t * K + j] = rank[j];
     }
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
         int n = 0;
 #pragma unroll
         for (int w = 0; w < 8; ++w) n += __popc(bm[e * 8 + w]);
-        a.chunk_base[(int64_t)c * E + e] = n;
+        if (single) loc[e] = n;
+        else a.chunk_base[(int64_t)c * E + e] = n;
     }
     uint64_t any_bad = __ballot(err & kErrBadId), any_dup = __ballot(err & kErrDupId);
     if ((threadIdx.x & 63) == 0)
         lds[threadIdx.x >> 6] = (any_bad ? kErrBadId : 0) | (any_dup ? kErrDupId : 0);
     __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t ce = 0;
-        for (int w = 0; w < 4; ++w) ce |= (uint32_t)lds[w];
-        a.chunk_err[c] = ce;
+    uint32_t ce = 0;
+    for (int w = 0; w < 4; ++w) ce |= (uint32_t)lds[w];
+    if (single) {
+        // the only chunk: finish from LDS, then each thread places its own routes
+        __syncthreads();
+        prep_finish(a, T, nch, K, live, lds, loc, loc + kMaxExperts, ce);
+        __syncthreads();
+        if (valid) {
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                const int64_t r = (int64_t)t * K + j;
+                if (keep[j]) {
+                    const int pos = loc[kMaxExperts + id[j]] + rank[j];
+                    a.perm_src[pos] = (int32_t)r;
+                    a.dst[r] = pos;
+                } else {
+                    a.dst[r] = -1;
+                }
+            }
+        }
+        return;
     }
+    if (threadIdx.x == 0) a.chunk_err[c] = ce;
     // the last workgroup to finish does the scan: publish this chunk's data
     // (device-scope release), take a ticket, and only the last ticket holder
     // reads every chunk's data (acquire).  Nobody waits.
@@ -281,6 +323,8 @@ hipError_t launch_prep(const int32_t* ids, const float* probs, int64_t T_cap, co
     a.tiles = (int2*)(ws + L.tiles);
     a.tiles_big = (int2*)(ws + L.tiles_big);
     a.hdr = (WsHeader*)(ws + L.hdr);
+    a.perm_src = (int32_t*)(ws + L.perm_src);
+    a.dst = (int32_t*)(ws + L.dst);
     dim3 g1((unsigned)L.nchunks), b1(256);
 #define PREP_CASE(KK)                                                        \
     case KK:                                                                 \
@@ -293,6 +337,7 @@ hipError_t launch_prep(const int32_t* ids, const float* probs, int64_t T_cap, co
         default: return hipErrorInvalidValue;
     }
 #undef PREP_CASE
+    if (L.nchunks == 1) return hipGetLastError();   // single workgroup scattered its routes
     int64_t R = T_cap * k;
     int64_t blocks = (R + 255) / 256;
     if (blocks > (int64_t)num_cu * 4) blocks = (int64_t)num_cu * 4;

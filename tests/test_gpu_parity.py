@@ -44,6 +44,11 @@ SMALL = {
     "bounded_T40_cap512": WORKLOADS["bounded_decode"].with_tokens(40, 512),
     "odd_bf16": Workload("odd_bf16", 77, 80, 96, 160, 5, 3, "bf16"),
     "odd_mxfp8": Workload("odd_mxfp8", 77, 80, 96, 160, 5, 3, "mxfp8"),
+    # experts past 128 rows (LDS-staged GEMM): ragged 256-row tiles, partial
+    # 256-column tiles, an odd number of 32-wide K steps in both GEMMs
+    "odd_bf16_big": Workload("odd_bf16_big", 700, 720, 96, 160, 5, 3, "bf16"),
+    # and an even number of K steps in both GEMMs
+    "mid_bf16_big": Workload("mid_bf16_big", 600, 600, 256, 192, 4, 2, "bf16"),
 }
 
 _cases = {}
