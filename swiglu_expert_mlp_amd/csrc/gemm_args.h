@@ -41,6 +41,8 @@ struct MxGemmArgs {
     int K;
     int topk;
     int n_tiles_n;
+    int stream_big;            // 1: the streaming kernel also takes the 256-row tiles
+                               // (as four 64-row tiles each); 0: the LDS-staged kernel does
 };
 
 }  // namespace moe

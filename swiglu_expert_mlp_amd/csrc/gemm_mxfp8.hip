@@ -18,8 +18,8 @@
 // K = 64 + 16 * (l / 16) + [0, 16).  The scale byte of lane l applies to the
 // 32-block (l / 16) of the step, i.e. 32-block q is made of the first halves
 // (q < 2) or second halves (q >= 2) of lane groups 2 (q % 2) and 2 (q % 2) + 1.
-// Work decomposition is the same as the bf16 kernels: persistent grid over
-// (M tile, N tile), 4 waves x 64 columns, up to 64 rows per M tile.
+// Work decomposition is the same as the bf16 streaming kernel: persistent
+// grid over (M tile, N tile), 4 waves x 64 columns, up to 64 rows per M tile.
 #include "gemm_args.h"
 
 namespace moe {
@@ -148,10 +148,11 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs& g, int e, int row
 template <bool FC1>
 __global__ void __launch_bounds__(256) gemm_mxfp8_kernel(MxGemmArgs g)
 {
-    // 64-row tiles: the streaming table, then each 256-row tile of the large-
-    // expert table as four 64-row tiles
+    // 64-row tiles of the streaming table (experts with few rows); the large
+    // experts' 256-row tiles run on the LDS-staged kernel, or here as four
+    // 64-row tiles each when that kernel does not apply (K not a multiple of 128)
     const int n_small = g.hdr->n_tiles;
-    const int n_mt = n_small + 4 * g.hdr->n_tiles_big;
+    const int n_mt = n_small + (g.stream_big ? 4 * g.hdr->n_tiles_big : 0);
     const int total = n_mt * g.n_tiles_n;
     const int wid = threadIdx.x >> 6;
     const int n_cb = g.N / 64 + ((g.N % 64) ? 1 : 0);

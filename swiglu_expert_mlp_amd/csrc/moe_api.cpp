@@ -33,6 +33,7 @@ namespace moe {
 hipError_t launch_gemm_bf16(bool fc1, const GemmArgs& g, int num_cu, hipStream_t s);
 hipError_t launch_gemm_bf16_big(bool fc1, const GemmArgs& g, int num_cu, hipStream_t s);
 hipError_t launch_gemm_mxfp8(bool fc1, const MxGemmArgs& g, int num_cu, hipStream_t s);
+hipError_t launch_gemm_mxfp8_big(bool fc1, const MxGemmArgs& g, int num_cu, hipStream_t s);
 }  // namespace moe
 
 using namespace moe;
@@ -305,7 +306,9 @@ moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
         g1.K = H;
         g1.topk = h->k;
         g1.n_tiles_n = ((2 * F / 64) + 3) / 4;
+        g1.stream_big = H % 128 != 0;
         e = launch_gemm_mxfp8(true, g1, h->num_cu, stream);
+        if (e == hipSuccess && !g1.stream_big) e = launch_gemm_mxfp8_big(true, g1, h->num_cu, stream);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC1 launch");
         if ((e = mark(h, 3, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
         MxGemmArgs g2 = g1;
@@ -319,7 +322,9 @@ moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
         g2.N = H;
         g2.K = F;
         g2.n_tiles_n = ((H + 63) / 64 + 3) / 4;
+        g2.stream_big = F % 128 != 0;
         e = launch_gemm_mxfp8(false, g2, h->num_cu, stream);
+        if (e == hipSuccess && !g2.stream_big) e = launch_gemm_mxfp8_big(false, g2, h->num_cu, stream);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
         if ((e = mark(h, 4, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     }

@@ -49,6 +49,9 @@ SMALL = {
     "odd_bf16_big": Workload("odd_bf16_big", 700, 720, 96, 160, 5, 3, "bf16"),
     # and an even number of K steps in both GEMMs
     "mid_bf16_big": Workload("mid_bf16_big", 600, 600, 256, 192, 4, 2, "bf16"),
+    # MXFP8 experts past 128 rows with K a multiple of 128 (LDS-staged kernel):
+    # ragged 256-row tiles, a partial 256-column tile, 2 and 3 K steps
+    "mx_big": Workload("mx_big", 600, 600, 256, 384, 4, 2, "mxfp8"),
 }
 
 _cases = {}
