@@ -9,12 +9,13 @@
 //
 // out[t][m] = fma(p_{k-1}, O[dst[t,k-1]][m], ... fma(p_0, O[dst[t,0]][m], +0.0f))
 // A route with dst < 0 (an invalid expert id) adds nothing.  Rows >= live are
-// neither read nor written.  One workgroup walks tokens; 4 columns per thread.
+// neither read nor written.  One workgroup (512 threads) walks tokens; 4
+// columns per thread.
 #include "common.h"
 
 namespace moe {
 
-__global__ void __launch_bounds__(256) finalize_kernel(
+__global__ void __launch_bounds__(512) finalize_kernel(
     const float* __restrict__ O, const int32_t* __restrict__ dst,
     const float* __restrict__ sorted_probs, int64_t T_cap, const int32_t* __restrict__ live_ptr,
     int k, int H, float* __restrict__ out)
@@ -50,7 +51,7 @@ hipError_t launch_finalize(const float* O, const int32_t* dst, const float* sort
 {
     int64_t blocks = T_cap < (int64_t)num_cu * 8 ? T_cap : (int64_t)num_cu * 8;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)blocks), dim3(256), 0, s, O, dst,
+    hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)blocks), dim3(512), 0, s, O, dst,
                        sorted_probs, T_cap, live, k, H, out);
     return hipGetLastError();
 }

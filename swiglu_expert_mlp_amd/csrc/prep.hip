@@ -16,9 +16,11 @@
 //                  the chunk is the number of set bits below its token, and
 //                  the chunk's count the bits set in all.  The workgroup that
 //                  finishes last (atomic ticket, no waiting) does the prefix
-//                  over chunks and experts, the M-tile table and the error word.
-//   prep_scatter   one thread per route: position = expert offset + chunk
-//                  base + rank; perm_src[position] = route, dst[route] = position.
+//                  over chunks (per expert, staged through LDS in coalesced
+//                  slabs) and over experts, the M-tile table and the error word.
+//   prep_scatter   one thread per route: position = expert offset + the
+//                  chunk's base inside the expert + rank; perm_src[position] =
+//                  route, dst[route] = position.
 // A launch whose capacity fits one chunk (T_cap <= 256 tokens, the decode
 // sizes) runs as a single workgroup that keeps the counts in LDS, finishes
 // without device-scope fences or a ticket, and scatters its own routes; the
@@ -60,6 +62,8 @@ __device__ int block_exclusive_scan(int v, int* total, int* lds /* >= 32 ints */
     return excl;
 }
 
+constexpr int kSlab = kMaxExperts * (kChunkTok / 32);   // ints of the LDS token bitmaps
+
 struct PrepArgs {
     const int32_t* ids;
     const float* probs;
@@ -85,31 +89,48 @@ struct PrepArgs {
 // the expert offsets go to local_off (LDS) instead of the chunk bases, and
 // local_err is the chunk's error bits.
 __device__ void prep_finish(const PrepArgs& a, int T, int nch, int k, int32_t live, int* lds,
-                            const int* local_cnt = nullptr, int* local_off = nullptr,
-                            uint32_t local_err = 0)
+                            int* slab /* kSlab ints of LDS */, const int* local_cnt = nullptr,
+                            int* local_off = nullptr, uint32_t local_err = 0)
 {
     const int E = a.E;
     constexpr int PER = kMaxExperts / 256;          // experts per thread
     int cnt[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) cnt[q] = 0;
+    if (local_cnt) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int e = threadIdx.x * PER + q;
+            if (e < E) cnt[q] = local_cnt[e];
+        }
+    } else {
+        // chunk counts [nch][E] -> each chunk's base inside its expert (exclusive
+        // prefix over chunks), a slab of whole chunk rows at a time through LDS
+        const int cs = kSlab / E > 0 ? kSlab / E : 1;
+        for (int c0 = 0; c0 < nch; c0 += cs) {
+            const int nc = nch - c0 < cs ? nch - c0 : cs;
+            int32_t* g = a.chunk_base + (int64_t)c0 * E;
+            for (int i = threadIdx.x; i < nc * E; i += blockDim.x)
+                slab[i] = __builtin_nontemporal_load(&g[i]);
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < PER; ++q) {
+                const int e = threadIdx.x * PER + q;
+                if (e < E)
+                    for (int c = 0; c < nc; ++c) {
+                        const int v = slab[c * E + e];
+                        slab[c * E + e] = cnt[q];
+                        cnt[q] += v;
+                    }
+            }
+            __syncthreads();
+            for (int i = threadIdx.x; i < nc * E; i += blockDim.x) g[i] = slab[i];
+            __syncthreads();
+        }
+    }
     int mine = 0;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        const int e = threadIdx.x * PER + q;
-        int run = 0;
-        if (e < E) {
-            if (local_cnt) {
-                run = local_cnt[e];
-            } else {
-                for (int c = 0; c < nch; ++c) {
-                    int v = __builtin_nontemporal_load(&a.chunk_base[(int64_t)c * E + e]);
-                    a.chunk_base[(int64_t)c * E + e] = run;
-                    run += v;
-                }
-            }
-        }
-        cnt[q] = run;
-        mine += run;
-    }
+    for (int q = 0; q < PER; ++q) mine += cnt[q];
     int total;
     int off = block_exclusive_scan(mine, &total, lds);
     // M tiles: an expert with at most kBigMin rows goes to the streaming GEMM
@@ -130,8 +151,6 @@ __device__ void prep_finish(const PrepArgs& a, int T, int nch, int k, int32_t li
             a.counts[e] = cnt[q];
             a.offsets[e] = off;
             if (local_off) local_off[e] = off;
-            else
-                for (int c = 0; c < nch; ++c) a.chunk_base[(int64_t)c * E + e] += off;
             if (cnt[q] > kBigMin) {
                 const int nt = (cnt[q] + kBigBMRows - 1) / kBigBMRows;
                 for (int i = 0; i < nt; ++i) a.tiles_big[bfirst + i] = make_int2(e, off + i * kBigBMRows);
@@ -178,7 +197,7 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a)
     const int E = a.E;
     const bool single = gridDim.x == 1;          // T_cap <= one chunk
     if (nch == 0 && !single) {
-        if (c == 0) prep_finish(a, T, 0, K, live, lds);
+        if (c == 0) prep_finish(a, T, 0, K, live, lds, (int*)bm);
         return;
     }
     if (c >= nch && !single) return;
@@ -250,7 +269,7 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a)
     if (single) {
         // the only chunk: finish from LDS, then each thread places its own routes
         __syncthreads();
-        prep_finish(a, T, nch, K, live, lds, loc, loc + kMaxExperts, ce);
+        prep_finish(a, T, nch, K, live, lds, (int*)bm, loc, loc + kMaxExperts, ce);
         __syncthreads();
         if (valid) {
 #pragma unroll
@@ -280,15 +299,15 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a)
     __syncthreads();
     if (!s_last) return;
     __threadfence();
-    prep_finish(a, T, nch, K, live, lds);
+    prep_finish(a, T, nch, K, live, lds, (int*)bm);
     if (threadIdx.x == 0) atomicExch(&a.hdr->ticket, 0u);
 }
 
 __global__ void __launch_bounds__(256) prep_scatter_kernel(
     int64_t T_cap, const int32_t* __restrict__ live_ptr, int E, int k,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ local_rank,
-    const int32_t* __restrict__ chunk_base, int32_t* __restrict__ perm_src,
-    int32_t* __restrict__ dst)
+    const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm_src, int32_t* __restrict__ dst)
 {
     const int T = clamp_live(*live_ptr, T_cap);
     const int64_t R = (int64_t)T * k;
@@ -298,7 +317,7 @@ __global__ void __launch_bounds__(256) prep_scatter_kernel(
         if (rk < 0) { dst[r] = -1; continue; }
         int e = sorted_ids[r];
         int c = (int)((r / k) / kChunkTok);
-        int pos = chunk_base[(int64_t)c * E + e] + rk;
+        int pos = offsets[e] + chunk_base[(int64_t)c * E + e] + rk;
         perm_src[pos] = (int32_t)r;
         dst[r] = pos;
     }
@@ -343,8 +362,8 @@ hipError_t launch_prep(const int32_t* ids, const float* probs, int64_t T_cap, co
     if (blocks > (int64_t)num_cu * 4) blocks = (int64_t)num_cu * 4;
     if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL(prep_scatter_kernel, dim3((unsigned)blocks), dim3(256), 0, s, T_cap, live, E,
-                       k, a.sorted_ids, a.local_rank, a.chunk_base, (int32_t*)(ws + L.perm_src),
-                       (int32_t*)(ws + L.dst));
+                       k, a.sorted_ids, a.local_rank, a.chunk_base, a.offsets,
+                       (int32_t*)(ws + L.perm_src), (int32_t*)(ws + L.dst));
     return hipGetLastError();
 }
 

@@ -16,16 +16,43 @@
 
 namespace moe {
 
-// Wave-wide argmax of (value, id): larger value wins, equal values go to the
-// smaller id.  Every lane returns the winner.
+// (value, id) order of the selection: larger value first, equal values go to
+// the smaller id.
+__device__ __forceinline__ bool ahead(float ov, int oid, float v, int id)
+{
+    return ov > v || (ov == v && oid < id);
+}
+
+template <int CTRL>
+__device__ __forceinline__ void dpp_amax_step(float& v, int& id)
+{
+    const float ov = __builtin_bit_cast(float,
+        __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+    const int oid = __builtin_amdgcn_mov_dpp(id, CTRL, 0xF, 0xF, false);
+    if (ahead(ov, oid, v, id)) { v = ov; id = oid; }
+}
+
+// Wave-wide argmax of (value, id).  Within each 16-lane row: DPP exchanges
+// (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror),
+// after which every lane of a row holds the row's winner; the four row
+// winners are then combined from lanes 0, 16, 32, 48.  The result is
+// wave-uniform.
 __device__ __forceinline__ void wave_argmax(float& v, int& id)
 {
+    dpp_amax_step<0xB1>(v, id);
+    dpp_amax_step<0x4E>(v, id);
+    dpp_amax_step<0x141>(v, id);
+    dpp_amax_step<0x140>(v, id);
+    float bv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    int bid = __builtin_amdgcn_readlane(id, 0);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        float ov = __shfl_xor(v, off, kWave);
-        int oid = __shfl_xor(id, off, kWave);
-        if (ov > v || (ov == v && oid < id)) { v = ov; id = oid; }
+    for (int r = 16; r < 64; r += 16) {
+        const float ov = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), r));
+        const int oid = __builtin_amdgcn_readlane(id, r);
+        if (ahead(ov, oid, bv, bid)) { bv = ov; bid = oid; }
     }
+    v = bv;
+    id = bid;
 }
 
 template <int PER_LANE>
@@ -53,39 +80,49 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ lo
             l[i] = e < E ? row[e] : -INFINITY;
             taken[i] = e >= E;
         }
-        int sel[kMaxTopk];
-        float selv[kMaxTopk];
-        for (int j = 0; j < k; ++j) {
+        // k rounds of argmax over the experts not yet taken; lane j keeps the
+        // j-th winner (descending logit)
+        int my_id = 0x7fffffff;
+        float my_v = -INFINITY, m = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kMaxTopk; ++j) {
+            if (j >= k) break;
             float bv = -INFINITY;
             int bid = 0x7fffffff;
 #pragma unroll
             for (int i = 0; i < PER_LANE; ++i) {
                 int e = lane + kWave * i;
-                if (!taken[i] && (l[i] > bv || (l[i] == bv && e < bid))) { bv = l[i]; bid = e; }
+                if (!taken[i] && ahead(l[i], e, bv, bid)) { bv = l[i]; bid = e; }
             }
             wave_argmax(bv, bid);
-            sel[j] = bid;
-            selv[j] = bv;
+            if (j == 0) m = bv;                       // the largest logit
+            if (lane == j) { my_id = bid; my_v = bv; }
 #pragma unroll
             for (int i = 0; i < PER_LANE; ++i)
                 if (lane + kWave * i == bid) taken[i] = true;
         }
-        // sel[0] holds the largest logit.  Canonical order: ascending id.
-        const float m = selv[0];
-        for (int a = 1; a < k; ++a)
-            for (int b = a; b > 0 && sel[b - 1] > sel[b]; --b) {
-                int ti = sel[b]; sel[b] = sel[b - 1]; sel[b - 1] = ti;
-                float tv = selv[b]; selv[b] = selv[b - 1]; selv[b - 1] = tv;
-            }
-        float z[kMaxTopk];
+        // canonical order: the rank of lane j's id among the k selected ids;
+        // lane j's pair moves to lane rank_j (ids are distinct)
+        int rank = 0;
+#pragma unroll
+        for (int i = 0; i < kMaxTopk; ++i) {
+            if (i >= k) break;
+            if (__builtin_amdgcn_readlane(my_id, i) < my_id) ++rank;
+        }
+        const float z = lane < k ? expf(my_v - m) : 0.0f;
+        const int dest = (lane < k ? rank : lane) * 4;
+        const int c_id = __builtin_amdgcn_ds_permute(dest, my_id);
+        const float c_z = __builtin_bit_cast(float, __builtin_amdgcn_ds_permute(dest, __builtin_bit_cast(int, z)));
+        // the selected mass, summed in ascending-id order
         float S = 0.0f;
-        for (int j = 0; j < k; ++j) { z[j] = expf(selv[j] - m); S += z[j]; }
+#pragma unroll
+        for (int i = 0; i < kMaxTopk; ++i) {
+            if (i >= k) break;
+            S += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c_z), i));
+        }
         if (lane < k) {
-            float zj = 0.0f;
-            int idj = 0;
-            for (int j = 0; j < k; ++j) if (j == lane) { zj = z[j]; idj = sel[j]; }
-            ids[t * k + lane] = idj;
-            probs[t * k + lane] = zj / S;
+            ids[t * k + lane] = c_id;
+            probs[t * k + lane] = c_z / S;
         }
     }
 }
