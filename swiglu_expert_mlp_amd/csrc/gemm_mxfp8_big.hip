@@ -29,7 +29,8 @@
 //
 // Tiles are split into 8 contiguous ranges, one per XCD (workgroups are
 // dispatched round-robin over the XCDs), so the tiles of one expert share an
-// L2.
+// L2; within an expert they go column tile by column tile, so that all of its
+// row tiles read a weight slice at the same time.
 #include <type_traits>
 
 #include "gemm_args.h"
@@ -93,10 +94,18 @@ __global__ void __launch_bounds__(512, 1) gemm_mxfp8_big_kernel(MxGemmArgs g)
     const int t_begin = xcd * chunk;
     const int t_end = min(total, t_begin + chunk);
     for (int tile = t_begin + (blockIdx.x >> 3); tile < t_end; tile += per_xcd) {
-        const int mt = tile / NT, nt = tile - mt * NT;
-        const int2 te = g.tiles_big[mt];
-        const int e = te.x, row0 = te.y;
-        int rows = g.offsets[e + 1] - row0;
+        // the tiles of one expert (its m_e row tiles x NT column tiles) keep their
+        // index range but are walked column tile by column tile: the expert's
+        // row tiles for one column tile run together and share its weight slice
+        const int2 te0 = g.tiles_big[tile / NT];
+        const int e = te0.x;
+        const int base = g.offsets[e], cnt = g.offsets[e + 1] - base;
+        const int m_e = (cnt + kMxBigBM - 1) / kMxBigBM;
+        const int b_e = tile / NT - (te0.y - base) / kMxBigBM;     // the expert's first row tile
+        const int u = tile - b_e * NT;
+        const int nt = u / m_e, mi = u - nt * m_e;
+        const int row0 = base + mi * kMxBigBM;
+        int rows = cnt - mi * kMxBigBM;
         if (rows > kMxBigBM) rows = kMxBigBM;
         const int n0 = nt * kMxBigBN;
 
