@@ -65,8 +65,9 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}))
 
 
-GEMM_SOURCES = ["swiglu_expert_mlp_amd/csrc/gemm_bf16.hip", "swiglu_expert_mlp_amd/csrc/gemm_bf16_big.hip",
-                "swiglu_expert_mlp_amd/csrc/gemm_mxfp8.hip", "swiglu_expert_mlp_amd/csrc/gemm_mxfp8_big.hip",
+GEMM_SOURCES = ["swiglu_expert_mlp_amd/csrc/gemm_bf16.hip", "swiglu_expert_mlp_amd/csrc/gemm_bf16_stream.h",
+                "swiglu_expert_mlp_amd/csrc/gemm_bf16_lds.h", "swiglu_expert_mlp_amd/csrc/gemm_mxfp8.hip",
+                "swiglu_expert_mlp_amd/csrc/gemm_mxfp8_stream.h", "swiglu_expert_mlp_amd/csrc/gemm_mxfp8_lds.h",
                 "swiglu_expert_mlp_amd/csrc/gemm_args.h", "swiglu_expert_mlp_amd/csrc/common.h"]
 
 
@@ -251,13 +252,12 @@ def main():
         roof = dict(bound="hbm", achieved=ab["fc1"] / (fc1_us * 1e-6) / 1e9,
                     peak=HBM_PEAK_GBS, unit="GB/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    # the FC1 + SwiGLU stage is two launches: the streaming kernel (experts with
-    # at most 128 rows) and the LDS-staged kernel (the others); the events
-    # bracket both, and the one that does the work here is named first
+    # the FC1 + SwiGLU stage is one launch; its tiles run on the LDS-staged loop
+    # (experts with more than 128 rows) or the streaming loop (the others)
     kind = "bf16" if w.precision == "bf16" else "mxfp8"
-    big = int(loads.max()) > 128
-    names = [f"moe::gemm_{kind}_big_kernel<true>", f"moe::gemm_{kind}_kernel<true>"]
-    roof["kernel"] = " + ".join(names if big else names[::-1])
+    roof["kernel"] = f"moe::gemm_{kind}_kernel<true>"
+    roof["tiles"] = "lds-staged" if int(loads.min()) > 128 else (
+        "streaming" if int(loads.max()) <= 128 else "lds-staged + streaming")
     roof["kernel_us"] = fc1_us
     roof["traffic"] = measured_traffic(w.name)
 

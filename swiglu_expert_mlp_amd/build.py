@@ -20,8 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["moe_api.cpp", "route.hip", "prep.hip", "gemm_bf16.hip", "gemm_bf16_big.hip",
-           "gemm_mxfp8.hip", "gemm_mxfp8_big.hip",
+SOURCES = ["moe_api.cpp", "route.hip", "prep.hip", "gemm_bf16.hip", "gemm_mxfp8.hip",
            "finalize.hip", "pack.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

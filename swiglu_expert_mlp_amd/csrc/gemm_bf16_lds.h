@@ -1,4 +1,4 @@
-// K3 / K4 for experts with many rows: LDS-staged grouped GEMM on CDNA4 MFMA,
+// K3 / K4, LDS-staged design (experts with more than 128 rows): grouped GEMM on CDNA4 MFMA,
 // bf16 operands, fp32 accumulate.
 //
 // Same arithmetic contract as gemm_bf16.hip (and therefore bitwise the same
@@ -23,6 +23,8 @@
 // share its L2.  Within an expert the tiles go column tile by column tile, so
 // that all of its row tiles read a weight slice at the same time (measured:
 // 22% less FC1 traffic than row-tile order at 16K tokens).
+#pragma once
+
 #include "gemm_args.h"
 
 namespace moe {
@@ -48,8 +50,9 @@ constexpr int kStageBytes = 32 * 1024;
 // s_waitcnt with only a vector-memory bound (expcnt and lgkmcnt left at max).
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 
+// The LDS-staged tile loop of one 8-wave workgroup (one workgroup per CU).
 template <bool FC1>
-__global__ void __launch_bounds__(512, 1) gemm_bf16_big_kernel(GemmArgs g)
+__device__ __forceinline__ void lds_tiles(const GemmArgs& g)
 {
     // [stage][A 16 blocks | B 16 blocks] of 1 KB (16 rows or columns x 32 K)
     __shared__ __attribute__((aligned(1024))) char smem[kRing][kStageBytes];
@@ -194,16 +197,6 @@ __global__ void __launch_bounds__(512, 1) gemm_bf16_big_kernel(GemmArgs g)
                 }
         }
     }
-}
-
-hipError_t launch_gemm_bf16_big(bool fc1, const GemmArgs& g, int num_cu, hipStream_t s)
-{
-    dim3 grid((unsigned)(num_cu >= 8 ? num_cu / 8 * 8 : 8)), block(512);
-    if (fc1)
-        hipLaunchKernelGGL(gemm_bf16_big_kernel<true>, grid, block, 0, s, g);
-    else
-        hipLaunchKernelGGL(gemm_bf16_big_kernel<false>, grid, block, 0, s, g);
-    return hipGetLastError();
 }
 
 }  // namespace moe

@@ -1,190 +1,26 @@
-// K3 / K4 for MXFP8: grouped expert GEMMs on the CDNA4 block-scaled MFMA
-// (E4M3 x E4M3 with one E8M0 scale per 32 elements of K, fp32 accumulate).
-//
-// Megatron-LM PR #7798, "Background": the activation and the FC2-input
-// quantization are fused into the FC1 epilogue.  cudnn-frontend PR #448:
-// MXFP8 = E4M3 data with an E8M0 scale per 32-element block.  The SwiGLU
-// output is re-quantized per 32-element block of F in the FC1 epilogue
-// (scale = power-of-two ceiling of the block's max magnitude / 448).
-//
-// Arithmetic contract: acc = 0; for k0 = 0, 128, 256, ... :
-// acc = MFMA_SCALE_16x16x128_E4M3(A[row, k0:k0+128], B[col, k0:k0+128], acc)
-// with the scales of the four 32-blocks, in that order for every row, tile
-// and launch.  A K tail shorter than 128 is padded with zero codes.
-//
-// Lane layout of one 128-wide K step (both operands; the weights are stored
-// pre-arranged in it, the activations are gathered from row-major rows): lane l holds row (l % 16);
-// its first 16 bytes are K = 16 * (l / 16) + [0, 16) and its last 16 bytes are
-// K = 64 + 16 * (l / 16) + [0, 16).  The scale byte of lane l applies to the
-// 32-block (l / 16) of the step, i.e. 32-block q is made of the first halves
-// (q < 2) or second halves (q >= 2) of lane groups 2 (q % 2) and 2 (q % 2) + 1.
-// Work decomposition is the same as the bf16 streaming kernel: persistent
-// grid over (M tile, N tile), 4 waves x 64 columns, up to 64 rows per M tile.
-#include "gemm_args.h"
+// K3 / K4, MXFP8: one launch per GEMM stage.  A workgroup is 8 waves, one per
+// CU (persistent grid): first the LDS-staged tiles (experts with more than 128
+// rows; only when K is a multiple of 128) with all 8 waves, then the streaming
+// tiles with its two 4-wave halves as independent workers.  Both designs follow
+// the same arithmetic contract (gemm_mxfp8_stream.h).
+#include "gemm_mxfp8_lds.h"
+#include "gemm_mxfp8_stream.h"
 
 namespace moe {
 
-template <bool FC1, int NG>
-__device__ __forceinline__ void mx_tile_body(const MxGemmArgs& g, int e, int row0, int rows,
-                                             int cb)
-{
-    const int lane = threadIdx.x & 63;
-    const int r16 = lane & 15, kg = lane >> 4;
-    const int K = g.K, KB = K / 32;
-    const uint8_t* ap[NG];
-    const uint8_t* as[NG];
-#pragma unroll
-    for (int rg = 0; rg < NG; ++rg) {
-        int r = 16 * rg + r16;
-        if (r >= rows) r = rows - 1;
-        int64_t arow = row0 + r;
-        if constexpr (FC1) arow = g.perm_src[arow] / g.topk;
-        ap[rg] = g.A + arow * K + 16 * kg;
-        as[rg] = g.As + arow * KB + kg;
-    }
-    // B fragments: 2 KB blocks of 16 rows x 128 K, [expert][row / 16][k / 128],
-    // each block two 1 KB halves in lane order (16 codes per lane); scales in
-    // 256-byte groups of 4 K-steps, one dword per lane (byte = step % 4).
-    const int nt16 = g.N / 16, KS = (K + 127) / 128, KQ = (KS + 3) / 4;
-    const uint8_t* bp[4];
-    const uint32_t* bs[4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-        int c16 = cb * 4 + ct;
-        if (c16 >= nt16) c16 = nt16 - 1;
-        const int64_t blk = (int64_t)e * nt16 + c16;
-        bp[ct] = g.W + blk * KS * 2048 + 16 * lane;
-        bs[ct] = (const uint32_t*)(g.Ws + blk * KQ * 256) + lane;
-    }
-    f32x4 acc[NG][4];
-#pragma unroll
-    for (int rg = 0; rg < NG; ++rg)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) acc[rg][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int k0 = 0; k0 < K; k0 += 128) {
-        // K is a multiple of 32: each 16-byte half and each 32-block is either
-        // inside K or entirely past it (then zero codes, scale 2^0)
-        const bool lo_in = k0 + 16 * kg < K, hi_in = k0 + 64 + 16 * kg < K;
-        const bool s_in = k0 + 32 * kg < K;
-        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-        i32x8 a[NG], b[4];
-        int sa[NG], sb[4];
-#pragma unroll
-        for (int rg = 0; rg < NG; ++rg) {
-            uint4 lo = lo_in ? *(const uint4*)(ap[rg] + k0) : z;
-            uint4 hi = hi_in ? *(const uint4*)(ap[rg] + k0 + 64) : z;
-            a[rg] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                          (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            sa[rg] = s_in ? (int)as[rg][k0 / 32] : 127;
-        }
-        const int step = k0 / 128;
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            // padded blocks hold zero codes and scale 2^0, so no K check here
-            uint4 lo = *(const uint4*)(bp[ct] + step * 2048);
-            uint4 hi = *(const uint4*)(bp[ct] + step * 2048 + 1024);
-            b[ct] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                          (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            sb[ct] = (int)((bs[ct][(step >> 2) * 64] >> (8 * (step & 3))) & 0xffu);
-        }
-#pragma unroll
-        for (int rg = 0; rg < NG; ++rg)
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
-                acc[rg][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    a[rg], b[ct], acc[rg][ct], 0, 0, 0, sa[rg], 0, sb[ct]);
-    }
-
-    if constexpr (FC1) {
-        // SwiGLU, then the per-32 requantization of this interleave block's 32
-        // outputs of each row: 16 lanes (same kg) x 2 tiles hold one row's block.
-        const int F = g.N / 2, FB = F / 32;
-        uint8_t* hq = (uint8_t*)g.out;
-#pragma unroll
-        for (int rg = 0; rg < NG; ++rg)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float h0, h1;
-                {
-                    float gt = acc[rg][0][i], up = acc[rg][2][i];
-                    h0 = gt / (1.0f + __expf(-gt)) * up;
-                    gt = acc[rg][1][i]; up = acc[rg][3][i];
-                    h1 = gt / (1.0f + __expf(-gt)) * up;
-                }
-                float amax = fmaxf(fabsf(h0), fabsf(h1));
-#pragma unroll
-                for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
-                int e8 = e8m0_exponent(amax);
-                float inv = e8 == 127 ? __uint_as_float(1u << 22)
-                                      : __uint_as_float((uint32_t)(127 - e8) << 23);
-                int r = 16 * rg + 4 * kg + i;
-                if (r < rows) {
-                    int64_t row = row0 + r;
-                    hq[row * F + cb * 32 + r16] = (uint8_t)f32_to_e4m3(h0 * inv);
-                    hq[row * F + cb * 32 + 16 + r16] = (uint8_t)f32_to_e4m3(h1 * inv);
-                    if (r16 == 0) g.out_scale[row * FB + cb] = (uint8_t)(e8 + 127);
-                }
-            }
-    } else {
-        float* ob = (float*)g.out;
-#pragma unroll
-        for (int rg = 0; rg < NG; ++rg)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                int r = 16 * rg + 4 * kg + i;
-                if (r < rows) {
-                    int64_t row = row0 + r;
-#pragma unroll
-                    for (int ct = 0; ct < 4; ++ct) {
-                        int col = cb * 64 + 16 * ct + r16;
-                        if (col < g.N) ob[row * g.N + col] = acc[rg][ct][i];
-                    }
-                }
-            }
-    }
-}
-
 template <bool FC1>
-__global__ void __launch_bounds__(256) gemm_mxfp8_kernel(MxGemmArgs g)
+__global__ void __launch_bounds__(512, 1) gemm_mxfp8_kernel(MxGemmArgs g)
 {
-    // 64-row tiles of the streaming table (experts with few rows); the large
-    // experts' 256-row tiles run on the LDS-staged kernel, or here as four
-    // 64-row tiles each when that kernel does not apply (K not a multiple of 128)
-    const int n_small = g.hdr->n_tiles;
-    const int n_mt = n_small + (g.stream_big ? 4 * g.hdr->n_tiles_big : 0);
-    const int total = n_mt * g.n_tiles_n;
-    const int wid = threadIdx.x >> 6;
-    const int n_cb = g.N / 64 + ((g.N % 64) ? 1 : 0);
-    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-        const int mt = tile / g.n_tiles_n;
-        const int nt = tile - mt * g.n_tiles_n;
-        int2 te;
-        if (mt < n_small) {
-            te = g.tiles[mt];
-        } else {
-            const int b = mt - n_small;
-            te = g.tiles_big[b >> 2];
-            te.y += kBM * (b & 3);
-        }
-        const int e = te.x, row0 = te.y;
-        int rows = g.offsets[e + 1] - row0;
-        if (rows > kBM) rows = kBM;
-        const int cb = nt * 4 + wid;
-        if (cb >= n_cb || rows <= 0) continue;
-        const int ng = (rows + 15) >> 4;
-        switch (ng) {
-            case 1: mx_tile_body<FC1, 1>(g, e, row0, rows, cb); break;
-            case 2: mx_tile_body<FC1, 2>(g, e, row0, rows, cb); break;
-            case 3: mx_tile_body<FC1, 3>(g, e, row0, rows, cb); break;
-            default: mx_tile_body<FC1, 4>(g, e, row0, rows, cb); break;
-        }
-    }
+    if (!g.stream_big) mx_lds_tiles<FC1>(g);
+    // the two halves of a workgroup are workers b and b + grid: consecutive
+    // tiles (the N tiles of one M tile) go to different CUs
+    mx_stream_tiles<FC1>(g, blockIdx.x + (threadIdx.x >> 8) * gridDim.x, 2 * gridDim.x, (threadIdx.x >> 6) & 3);
 }
 
 hipError_t launch_gemm_mxfp8(bool fc1, const MxGemmArgs& g, int num_cu, hipStream_t s)
 {
-    dim3 grid((unsigned)(num_cu * 3)), block(256);
+    if (!g.stream_big && g.K % 128 != 0) return hipErrorInvalidValue;
+    dim3 grid((unsigned)(num_cu >= 8 ? num_cu / 8 * 8 : 8)), block(512);
     if (fc1)
         hipLaunchKernelGGL(gemm_mxfp8_kernel<true>, grid, block, 0, s, g);
     else

@@ -1,4 +1,4 @@
-// K3 / K4 for MXFP8 experts with many rows: LDS-staged grouped GEMM on the
+// K3 / K4 for MXFP8, LDS-staged design (experts with more than 128 rows): grouped GEMM on the
 // CDNA4 block-scaled MFMA (E4M3 x E4M3, one E8M0 scale per 32 elements of K,
 // fp32 accumulate).  Used when K is a multiple of 128 (otherwise the streaming
 // kernel takes these tiles too; the choice depends on the shape only).
@@ -31,6 +31,8 @@
 // dispatched round-robin over the XCDs), so the tiles of one expert share an
 // L2; within an expert they go column tile by column tile, so that all of its
 // row tiles read a weight slice at the same time.
+#pragma once
+
 #include <type_traits>
 
 #include "gemm_args.h"
@@ -63,8 +65,10 @@ __device__ __forceinline__ i32x8 mx_frag(uint4 lo, uint4 hi)
 
 #define MX_WAIT_VMCNT0() __builtin_amdgcn_s_waitcnt(0x0F70)
 
+// The LDS-staged tile loop of one 8-wave workgroup (one workgroup per CU).
+// Requires K % 128 == 0.
 template <bool FC1>
-__global__ void __launch_bounds__(512, 1) gemm_mxfp8_big_kernel(MxGemmArgs g)
+__device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
 {
     // the two stages are separate LDS objects, always addressed with
     // compile-time selection (the step loop is unrolled by 2): the compiler
@@ -263,18 +267,6 @@ __global__ void __launch_bounds__(512, 1) gemm_mxfp8_big_kernel(MxGemmArgs g)
                 }
         }
     }
-}
-
-// Requires K % 128 == 0 (the caller routes other shapes to the streaming kernel).
-hipError_t launch_gemm_mxfp8_big(bool fc1, const MxGemmArgs& g, int num_cu, hipStream_t s)
-{
-    if (g.K % 128 != 0) return hipErrorInvalidValue;
-    dim3 grid((unsigned)(num_cu >= 8 ? num_cu / 8 * 8 : 8)), block(512);
-    if (fc1)
-        hipLaunchKernelGGL(gemm_mxfp8_big_kernel<true>, grid, block, 0, s, g);
-    else
-        hipLaunchKernelGGL(gemm_mxfp8_big_kernel<false>, grid, block, 0, s, g);
-    return hipGetLastError();
 }
 
 }  // namespace moe

@@ -31,9 +31,7 @@ hipError_t launch_quant_x(const uint16_t* x, int64_t T_cap, const int32_t* live,
 
 namespace moe {
 hipError_t launch_gemm_bf16(bool fc1, const GemmArgs& g, int num_cu, hipStream_t s);
-hipError_t launch_gemm_bf16_big(bool fc1, const GemmArgs& g, int num_cu, hipStream_t s);
 hipError_t launch_gemm_mxfp8(bool fc1, const MxGemmArgs& g, int num_cu, hipStream_t s);
-hipError_t launch_gemm_mxfp8_big(bool fc1, const MxGemmArgs& g, int num_cu, hipStream_t s);
 }  // namespace moe
 
 using namespace moe;
@@ -264,7 +262,6 @@ moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
         g1.topk = h->k;
         g1.n_tiles_n = ((2 * F / 64) + 3) / 4;
         e = launch_gemm_bf16(true, g1, h->num_cu, stream);
-        if (e == hipSuccess) e = launch_gemm_bf16_big(true, g1, h->num_cu, stream);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC1 launch");
         if ((e = mark(h, 3, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
         GemmArgs g2 = g1;
@@ -276,7 +273,6 @@ moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
         g2.K = F;
         g2.n_tiles_n = ((H + 63) / 64 + 3) / 4;
         e = launch_gemm_bf16(false, g2, h->num_cu, stream);
-        if (e == hipSuccess) e = launch_gemm_bf16_big(false, g2, h->num_cu, stream);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
         if ((e = mark(h, 4, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     } else {
@@ -308,7 +304,6 @@ moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
         g1.n_tiles_n = ((2 * F / 64) + 3) / 4;
         g1.stream_big = H % 128 != 0;
         e = launch_gemm_mxfp8(true, g1, h->num_cu, stream);
-        if (e == hipSuccess && !g1.stream_big) e = launch_gemm_mxfp8_big(true, g1, h->num_cu, stream);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC1 launch");
         if ((e = mark(h, 3, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
         MxGemmArgs g2 = g1;
@@ -324,7 +319,6 @@ moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
         g2.n_tiles_n = ((H + 63) / 64 + 3) / 4;
         g2.stream_big = F % 128 != 0;
         e = launch_gemm_mxfp8(false, g2, h->num_cu, stream);
-        if (e == hipSuccess && !g2.stream_big) e = launch_gemm_mxfp8_big(false, g2, h->num_cu, stream);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
         if ((e = mark(h, 4, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     }
