@@ -15,30 +15,40 @@
 
 namespace moe {
 
+// K (the top-k) is a template parameter so that a token's k row loads are all
+// in flight before the chain starts (a runtime loop put a memory round trip
+// between consecutive routes).
+template <int K>
 __global__ void __launch_bounds__(512) finalize_kernel(
     const float* __restrict__ O, const int32_t* __restrict__ dst,
     const float* __restrict__ sorted_probs, int64_t T_cap, const int32_t* __restrict__ live_ptr,
-    int k, int H, float* __restrict__ out)
+    int H, float* __restrict__ out)
 {
     const int32_t live = *live_ptr;
     const int64_t T = live < 0 ? 0 : (live > T_cap ? T_cap : live);
     const int H4 = H >> 2;    // H is a multiple of 32
     for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
-        int32_t d[kMaxTopk];
-        float p[kMaxTopk];
-        for (int j = 0; j < k; ++j) {
-            d[j] = dst[t * k + j];
-            p[j] = sorted_probs[t * k + j];
+        int32_t d[K];
+        float p[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            d[j] = dst[t * K + j];
+            p[j] = sorted_probs[t * K + j];
         }
         for (int c = threadIdx.x; c < H4; c += blockDim.x) {
+            float4 o[K];
+#pragma unroll
+            for (int j = 0; j < K; ++j)
+                o[j] = d[j] >= 0 ? *((const float4*)(O + (int64_t)d[j] * H) + c)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
             float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-            for (int j = 0; j < k; ++j) {
-                if (d[j] < 0) continue;
-                float4 o = *((const float4*)(O + (int64_t)d[j] * H) + c);
-                acc.x = __builtin_fmaf(p[j], o.x, acc.x);
-                acc.y = __builtin_fmaf(p[j], o.y, acc.y);
-                acc.z = __builtin_fmaf(p[j], o.z, acc.z);
-                acc.w = __builtin_fmaf(p[j], o.w, acc.w);
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                if (d[j] < 0) continue;    // a dropped route adds nothing (not even +0)
+                acc.x = __builtin_fmaf(p[j], o[j].x, acc.x);
+                acc.y = __builtin_fmaf(p[j], o[j].y, acc.y);
+                acc.z = __builtin_fmaf(p[j], o[j].z, acc.z);
+                acc.w = __builtin_fmaf(p[j], o[j].w, acc.w);
             }
             *((float4*)(out + t * H) + c) = acc;
         }
@@ -51,8 +61,19 @@ hipError_t launch_finalize(const float* O, const int32_t* dst, const float* sort
 {
     int64_t blocks = T_cap < (int64_t)num_cu * 8 ? T_cap : (int64_t)num_cu * 8;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)blocks), dim3(512), 0, s, O, dst,
-                       sorted_probs, T_cap, live, k, H, out);
+    const dim3 g((unsigned)blocks), b(512);
+#define FIN_CASE(KK)                                                                         \
+    case KK:                                                                                 \
+        hipLaunchKernelGGL(finalize_kernel<KK>, g, b, 0, s, O, dst, sorted_probs, T_cap, live, H, \
+                           out);                                                             \
+        break;
+    switch (k) {
+        FIN_CASE(1) FIN_CASE(2) FIN_CASE(3) FIN_CASE(4) FIN_CASE(5) FIN_CASE(6) FIN_CASE(7)
+        FIN_CASE(8) FIN_CASE(9) FIN_CASE(10) FIN_CASE(11) FIN_CASE(12) FIN_CASE(13) FIN_CASE(14)
+        FIN_CASE(15) FIN_CASE(16)
+        default: return hipErrorInvalidValue;
+    }
+#undef FIN_CASE
     return hipGetLastError();
 }
 

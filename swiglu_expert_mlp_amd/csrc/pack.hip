@@ -133,7 +133,10 @@ __global__ void __launch_bounds__(256) pack_mx_kernel(const uint16_t* __restrict
     }
 }
 
-// K2: x rows < live quantized per 32-block of H.
+// K2: x rows < live quantized per 32-block of H.  A lane converts 8 elements
+// (one 16-byte load, one 8-byte store); the 4 lanes of a quad hold one
+// 32-block and exchange their partial amax with two DPP steps (quad_perm
+// [1,0,3,2] and [2,3,0,1]), so every lane derives the same E8M0 exponent.
 __global__ void __launch_bounds__(256) quant_x_mx_kernel(const uint16_t* __restrict__ x,
                                                          int64_t T_cap, const int32_t* __restrict__ live_ptr,
                                                          int H, uint8_t* __restrict__ codes,
@@ -142,19 +145,51 @@ __global__ void __launch_bounds__(256) quant_x_mx_kernel(const uint16_t* __restr
     const int32_t live = *live_ptr;
     const int64_t T = live < 0 ? 0 : (live > T_cap ? T_cap : live);
     const int nb = H / 32;
-    const int64_t n = T * nb;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        int64_t t = i / nb;
-        int b = (int)(i - t * nb);
-        quant_block32(x + t * H + b * 32, codes + t * H + b * 32, scales + t * nb + b);
+    const int64_t n = T * (H / 8);                      // 8-element groups, quads never straddle rows
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i0 = (int64_t)blockIdx.x * blockDim.x; i0 < n; i0 += stride) {
+        // whole waves stay in the loop together (the DPP steps need the quad's lanes)
+        const int64_t i = i0 + threadIdx.x;
+        const bool in = i < n;
+        uint4 v = in ? ((const uint4*)x)[i] : make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        float f[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            f[2 * q] = bf16_bits_to_f32(w[q] & 0xffffu);
+            f[2 * q + 1] = bf16_bits_to_f32(w[q] >> 16);
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(f[q]));
+        amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                               __builtin_bit_cast(int, amax), 0xB1, 0xF, 0xF, false)));
+        amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                               __builtin_bit_cast(int, amax), 0x4E, 0xF, 0xF, false)));
+        const int e8 = e8m0_exponent(amax);
+        // 2^-e8 exactly; 2^-127 is an fp32 subnormal
+        const float inv = e8 == 127 ? __uint_as_float(1u << 22) : __uint_as_float((uint32_t)(127 - e8) << 23);
+        uint32_t out[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            uint32_t c0 = f32_to_e4m3(f[4 * q] * inv), c1 = f32_to_e4m3(f[4 * q + 1] * inv);
+            uint32_t c2 = f32_to_e4m3(f[4 * q + 2] * inv), c3 = f32_to_e4m3(f[4 * q + 3] * inv);
+            out[q] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+        }
+        if (in) {
+            ((uint2*)codes)[i] = make_uint2(out[0], out[1]);
+            if ((i & 3) == 0) {
+                const int64_t t = (i / 4) / nb, b = (i / 4) - t * nb;
+                scales[t * nb + b] = (uint8_t)(e8 + 127);
+            }
+        }
     }
 }
 
 hipError_t launch_quant_x(const uint16_t* x, int64_t T_cap, const int32_t* live, int H,
                           uint8_t* codes, uint8_t* scales, int num_cu, hipStream_t s)
 {
-    hipLaunchKernelGGL(quant_x_mx_kernel, dim3(num_cu * 4), dim3(256), 0, s, x, T_cap, live, H,
+    hipLaunchKernelGGL(quant_x_mx_kernel, dim3(num_cu * 8), dim3(256), 0, s, x, T_cap, live, H,
                        codes, scales);
     return hipGetLastError();
 }
