@@ -8,6 +8,14 @@
 
 namespace moe {
 
+// 16-byte load with the non-temporal (streaming) cache policy.
+__device__ __forceinline__ uint4 load_stream16(const void* p)
+{
+    typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+    const u32x4v v = __builtin_nontemporal_load((const u32x4v*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // bf16 operands.
 struct GemmArgs {
     const uint16_t* A;         // FC1: x [T_cap][H]; FC2: hbuf [rows][F]

@@ -73,11 +73,14 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, int e, int row0, in
     constexpr int D = NG <= 2 ? 4 : (NG == 3 ? 3 : 2);
     const int nsteps = K / 32;
     uint4 ar[D][NG], br[D][4];
+    // weights are read once per tile: non-temporal loads keep them from
+    // evicting the activation rows that the other N tiles of the M tile reuse
+    // (measured: decode FC1 98.5 -> 93.2 us, FC2 64.6 -> 61.5 us)
     auto load = [&](int d, int s) {
 #pragma unroll
         for (int rg = 0; rg < NG; ++rg) ar[d][rg] = *(const uint4*)(ap[rg] + 32 * s);
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) br[d][ct] = *(const uint4*)(bp[ct] + 512 * s);
+        for (int ct = 0; ct < 4; ++ct) br[d][ct] = load_stream16(bp[ct] + 512 * s);
     };
     auto mfma = [&](int d) {
 #pragma unroll

@@ -85,8 +85,9 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs& g, int e, int row
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
             // padded blocks hold zero codes and scale 2^0, so no K check here
-            uint4 lo = *(const uint4*)(bp[ct] + step * 2048);
-            uint4 hi = *(const uint4*)(bp[ct] + step * 2048 + 1024);
+            // weights are read once per tile (non-temporal, see the bf16 kernel)
+            uint4 lo = load_stream16(bp[ct] + step * 2048);
+            uint4 hi = load_stream16(bp[ct] + step * 2048 + 1024);
             b[ct] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                           (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
             sb[ct] = (int)((bs[ct][(step >> 2) * 64] >> (8 * (step & 3))) & 0xffu);
