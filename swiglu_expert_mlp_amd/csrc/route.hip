@@ -86,7 +86,7 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ lo
         float my_v = -INFINITY, m = -INFINITY;
 #pragma unroll
         for (int j = 0; j < kMaxTopk; ++j) {
-            if (j >= k) break;
+            if (j >= k) continue;
             float bv = -INFINITY;
             int bid = 0x7fffffff;
 #pragma unroll
@@ -105,10 +105,8 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ lo
         // lane j's pair moves to lane rank_j (ids are distinct)
         int rank = 0;
 #pragma unroll
-        for (int i = 0; i < kMaxTopk; ++i) {
-            if (i >= k) break;
-            if (__builtin_amdgcn_readlane(my_id, i) < my_id) ++rank;
-        }
+        for (int i = 0; i < kMaxTopk; ++i)
+            if (i < k && __builtin_amdgcn_readlane(my_id, i) < my_id) ++rank;
         const float z = lane < k ? expf(my_v - m) : 0.0f;
         const int dest = (lane < k ? rank : lane) * 4;
         const int c_id = __builtin_amdgcn_ds_permute(dest, my_id);
@@ -116,10 +114,9 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ lo
         // the selected mass, summed in ascending-id order
         float S = 0.0f;
 #pragma unroll
-        for (int i = 0; i < kMaxTopk; ++i) {
-            if (i >= k) break;
-            S += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c_z), i));
-        }
+        for (int i = 0; i < kMaxTopk; ++i)
+            if (i < k)
+                S += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c_z), i));
         if (lane < k) {
             ids[t * k + lane] = c_id;
             probs[t * k + lane] = c_z / S;
