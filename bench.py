@@ -280,9 +280,57 @@ def main():
         "roofline": roof,
     }
 
+    if w.name == "bounded_decode":
+        res["live_tracking"] = live_tracking(w, moes, x, logits, route_fn, fwd_fn, ids, probs, out, ws,
+                                             live, sh, n_rot)
+
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_seconds)
     print(json.dumps(res))
+
+
+def live_tracking(w, moes, x, logits, route_fn, fwd_fn, ids, probs, out, ws, live, sh, n_rot,
+                  steps: int = 20) -> dict:
+    """Step time against the live count at the full capacity (live 64 .. 1024),
+    and at live = w.T with the buffers sized to the live rows instead.  Rows
+    w.T .. 2 w.T - 1 of x and the logits become copies of the first w.T rows,
+    so that every swept live count routes real data."""
+    import torch
+    T = w.T
+    x[T:2 * T] = x[:T]
+    logits[T:2 * T] = logits[:T]
+    ev = HipEvents()
+
+    def time_steps(route, fwd):
+        for i in range(3):
+            route[i % n_rot]()
+            fwd[i % n_rot]()
+        a, b = ev.new(), ev.new()
+        torch.cuda.synchronize()
+        ev.record(a, sh)
+        for i in range(steps):
+            route[i % n_rot]()
+            fwd[i % n_rot]()
+        ev.record(b, sh)
+        torch.cuda.synchronize()
+        return ev.ms(a, b) / steps * 1e3
+
+    by_live = {}
+    for n in (64, 128, 256, 512, 1024):
+        live.fill_(n)
+        by_live[str(n)] = time_steps(route_fn, fwd_fn)
+    live.fill_(T)
+    # the same live tokens with every buffer sized to them
+    xs, ls = x[:T].contiguous(), logits[:T].contiguous()
+    ids_s, probs_s, out_s = ids[:T].contiguous(), probs[:T].contiguous(), out[:T].contiguous()
+    ws_s = moes[0].new_workspace(T)
+    route_s = [m.bind_route(ls, live, ids_s, probs_s, ws_s) for m in moes]
+    fwd_s = [m.bind_forward(xs, ids_s, probs_s, live, out_s, ws_s) for m in moes]
+    small = time_steps(route_s, fwd_s)
+    ev.close()
+    return {"token_capacity": w.T_cap, "us_per_step_by_live": by_live,
+            f"us_per_step_live_{T}_capacity_{T}": small,
+            f"us_per_step_live_{T}_capacity_{w.T_cap}": by_live[str(T)]}
 
 
 def cpu_baseline(w, inp, target_s: float) -> dict:

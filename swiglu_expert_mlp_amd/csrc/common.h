@@ -56,36 +56,21 @@ __device__ __forceinline__ int e8m0_exponent(float amax)
     return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-// fp32 -> E4M3FN code, round to nearest even, for |v| <= 448 (guaranteed by
-// the block scale).  Works on the fp32 bit pattern: the value is re-expressed
-// at 3 mantissa bits (normals) or in units of 2^-9 (subnormals) with an
-// integer round-half-even on the dropped bits.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float v)
+// fp32 -> E4M3FN codes with the hardware converter (v_cvt_pk_fp8_f32): round
+// to nearest even, the OCP E4M3FN encoding.  Callers pass finite values with
+// |v| <= 448, which the MX block scale guarantees; on that range the converter
+// is exact rounding (checked exhaustively against a bit-level software
+// rounding of every such fp32 value).  x2: code of a in byte 0, b in byte 1.
+__device__ __forceinline__ uint32_t cvt_e4m3x2(float a, float b)
 {
-    uint32_t u = __float_as_uint(v);
-    uint32_t sign = (u >> 24) & 0x80u;
-    uint32_t a = u & 0x7fffffffu;
-    if (a > 0x7f800000u) return sign | 0x7fu;            // NaN
-    int ef = (int)(a >> 23);                               // biased fp32 exponent
-    int e = ef - 127;
-    if (e < -6) {
-        // subnormal E4M3: q = round(|v| * 2^9), |v| < 2^-6 => q in [0, 8]
-        if (ef == 0) return sign;                          // fp32 subnormal -> 0
-        uint32_t m = (a & 0x7fffffu) | 0x800000u;          // |v| = m * 2^(e-23)
-        int sh = 23 - 9 - e;                                // q = m >> sh, rounded
-        if (sh > 24) return sign;
-        uint32_t q = m >> sh;
-        uint32_t rem = m & ((1u << sh) - 1u);
-        uint32_t half = 1u << (sh - 1);
-        if (rem > half || (rem == half && (q & 1u))) q += 1u;
-        return sign | q;                                    // q == 8 is the smallest normal
-    }
-    uint32_t m = a & 0x7fffffu;
-    uint32_t q = m >> 20;                                   // 3 kept mantissa bits
-    uint32_t rem = m & 0xfffffu;
-    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) q += 1u;
-    uint32_t code = ((uint32_t)(e + 7) << 3) + q;           // carry moves into the exponent
-    return sign | code;
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+}
+
+// four codes, a in byte 0 .. d in byte 3
+__device__ __forceinline__ uint32_t cvt_e4m3x4(float a, float b, float c, float d)
+{
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
 // ---------------------------------------------------------------- workspace

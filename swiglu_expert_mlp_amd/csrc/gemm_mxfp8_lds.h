@@ -243,8 +243,9 @@ __device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
                         const int r = 128 * wm + 16 * i + 4 * kg + v;
                         if (r < rows) {
                             const int64_t row = row0 + r;
-                            hq[row * F + cb * 32 + r16] = (uint8_t)f32_to_e4m3(h0 * inv);
-                            hq[row * F + cb * 32 + 16 + r16] = (uint8_t)f32_to_e4m3(h1 * inv);
+                            const uint32_t c2 = cvt_e4m3x2(h0 * inv, h1 * inv);
+                            hq[row * F + cb * 32 + r16] = (uint8_t)c2;
+                            hq[row * F + cb * 32 + 16 + r16] = (uint8_t)(c2 >> 8);
                             if (r16 == 0) g.out_scale[row * FB + cb] = (uint8_t)(e8 + 127);
                         }
                     }

@@ -125,8 +125,9 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs& g, int e, int row
                 int r = 16 * rg + 4 * kg + i;
                 if (r < rows) {
                     int64_t row = row0 + r;
-                    hq[row * F + cb * 32 + r16] = (uint8_t)f32_to_e4m3(h0 * inv);
-                    hq[row * F + cb * 32 + 16 + r16] = (uint8_t)f32_to_e4m3(h1 * inv);
+                    const uint32_t c2 = cvt_e4m3x2(h0 * inv, h1 * inv);
+                    hq[row * F + cb * 32 + r16] = (uint8_t)c2;
+                    hq[row * F + cb * 32 + 16 + r16] = (uint8_t)(c2 >> 8);
                     if (r16 == 0) g.out_scale[row * FB + cb] = (uint8_t)(e8 + 127);
                 }
             }

@@ -80,9 +80,7 @@ __device__ __forceinline__ void quant_block32(const uint16_t* __restrict__ src,
     uint32_t out[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-        uint32_t c0 = f32_to_e4m3(f[4 * q] * inv), c1 = f32_to_e4m3(f[4 * q + 1] * inv);
-        uint32_t c2 = f32_to_e4m3(f[4 * q + 2] * inv), c3 = f32_to_e4m3(f[4 * q + 3] * inv);
-        out[q] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+        out[q] = cvt_e4m3x4(f[4 * q] * inv, f[4 * q + 1] * inv, f[4 * q + 2] * inv, f[4 * q + 3] * inv);
     }
     uint4* d4 = (uint4*)codes;
     d4[0] = make_uint4(out[0], out[1], out[2], out[3]);
@@ -172,9 +170,7 @@ __global__ void __launch_bounds__(256) quant_x_mx_kernel(const uint16_t* __restr
         uint32_t out[2];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            uint32_t c0 = f32_to_e4m3(f[4 * q] * inv), c1 = f32_to_e4m3(f[4 * q + 1] * inv);
-            uint32_t c2 = f32_to_e4m3(f[4 * q + 2] * inv), c3 = f32_to_e4m3(f[4 * q + 3] * inv);
-            out[q] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+            out[q] = cvt_e4m3x4(f[4 * q] * inv, f[4 * q + 1] * inv, f[4 * q + 2] * inv, f[4 * q + 3] * inv);
         }
         if (in) {
             ((uint2*)codes)[i] = make_uint2(out[0], out[1]);
