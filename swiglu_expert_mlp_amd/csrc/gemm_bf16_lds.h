@@ -151,6 +151,11 @@ __device__ __forceinline__ void lds_tiles(const GemmArgs& g)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            // issue all twelve fragment reads before the MFMAs: left alone, the
+            // scheduler reads two A fragments at a time and waits for them
+            // between groups of eight MFMAs (four LDS round trips per step)
+            __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
         }
 
         // epilogue: lane holds rows 4 (lane / 16) + v of each 16-row group, column lane % 16
