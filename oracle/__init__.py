@@ -68,6 +68,9 @@ def lib() -> ctypes.CDLL:
             "orc_prepare": (u32, [P, P, i64, i32, ctypes.c_int, ctypes.c_int,
                                   P, P, P, P, P, P, P]),
             "orc_finalize": (None, [P, P, P, i32, ctypes.c_int, ctypes.c_int, P]),
+            "orc_finalize_bf16": (None, [P, P, P, i32, ctypes.c_int, ctypes.c_int, P]),
+            "orc_finalize_rows": (None, [P, P, i32, ctypes.c_int, ctypes.c_int, P]),
+            "orc_forward_ex": (u32, [P, P, P, P, i64, i32, ctypes.c_int, P, P, P]),
             "orc_weights_create": (P, [ctypes.c_int] * 5 + [P, P]),
             "orc_weights_destroy": (None, [P]),
             "orc_forward": (u32, [P, P, P, P, i64, i32, P, P, P]),
@@ -189,6 +192,30 @@ def finalize(O: np.ndarray, dst: np.ndarray, sorted_probs: np.ndarray, H: int) -
     return out
 
 
+def finalize_bf16(O: np.ndarray, dst: np.ndarray, sorted_probs: np.ndarray, H: int) -> np.ndarray:
+    """The fp32 combine rounded to bf16: uint16 bits [T, H]."""
+    O = np.ascontiguousarray(O, dtype=np.float32)
+    dst = np.ascontiguousarray(dst, dtype=np.int32)
+    sorted_probs = np.ascontiguousarray(sorted_probs, dtype=np.float32)
+    T, k = dst.shape
+    out = np.zeros((T, H), dtype=np.uint16)
+    lib().orc_finalize_bf16(_p(O), _p(dst), _p(sorted_probs), T, k, H, _p(out))
+    return out
+
+
+def finalize_rows(O: np.ndarray, dst: np.ndarray, H: int) -> np.ndarray:
+    """Row mode: each route as a top-1 token with probability 1: fp32 [T, k, H]."""
+    O = np.ascontiguousarray(O, dtype=np.float32)
+    dst = np.ascontiguousarray(dst, dtype=np.int32)
+    T, k = dst.shape
+    out = np.zeros((T, k, H), dtype=np.float32)
+    lib().orc_finalize_rows(_p(O), _p(dst), T, k, H, _p(out))
+    return out
+
+
+COMBINES = {"fp32": 0, "bf16": 1, "rows": 2}
+
+
 # ---------------------------------------------------------------- forward
 
 class Model:
@@ -214,22 +241,32 @@ class Model:
             lib().orc_weights_destroy(h)
             self._h = None
 
-    def forward(self, x_bits, ids, probs, live, want_rows: bool = False):
-        """Whole forward.  Returns (out [T_cap, H] fp32 with rows >= T left NaN, err,
-        extras) where extras holds O rows and FC2 operand rows when asked."""
+    def forward(self, x_bits, ids, probs, live, want_rows: bool = False, combine: str = "fp32"):
+        """Whole forward.  Returns (out, err, extras); out is fp32 [T_cap, H] (combine
+        "fp32"), bf16 bits [T_cap, H] ("bf16") or fp32 [T_cap, k, H] ("rows"), with rows
+        of tokens >= T left NaN (0xFFFF for bf16); extras holds O rows and FC2 operand
+        rows when asked.  probs may be None in row mode (it does not use them)."""
         x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
         ids = np.ascontiguousarray(ids, dtype=np.int32)
+        if probs is None:
+            assert combine == "rows"
+            probs = np.ones(ids.shape, dtype=np.float32)
         probs = np.ascontiguousarray(probs, dtype=np.float32)
         T_cap = x_bits.shape[0]
-        out = np.full((T_cap, self.H), np.nan, dtype=np.float32)
+        if combine == "bf16":
+            out = np.full((T_cap, self.H), 0xFFFF, dtype=np.uint16)
+        elif combine == "rows":
+            out = np.full((T_cap, self.k, self.H), np.nan, dtype=np.float32)
+        else:
+            out = np.full((T_cap, self.H), np.nan, dtype=np.float32)
         extras = {}
         O = Hr = None
         if want_rows:
             n = max(1, T_cap * self.k)
             O = np.zeros((n, self.H), dtype=np.float32)
             Hr = np.zeros((n, self.F), dtype=np.float32)
-        err = lib().orc_forward(self._h, _p(x_bits), _p(ids), _p(probs), T_cap, int(live),
-                                _p(out), _p(O), _p(Hr))
+        err = lib().orc_forward_ex(self._h, _p(x_bits), _p(ids), _p(probs), T_cap, int(live),
+                                   COMBINES[combine], _p(out), _p(O), _p(Hr))
         if want_rows:
             extras = dict(O=O, H=Hr)
         return out, err, extras

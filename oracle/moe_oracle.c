@@ -402,6 +402,49 @@ void orc_finalize(const float* O, const int32_t* dst, const float* sorted_probs,
     }
 }
 
+/* BF16 combine ([VALUE] "What is changed", the BF16_RANK_PARTIALS unpermute,
+ * which does what FlashInfer's finalize does): on one rank, a token's routes
+ * are added as fp32 fused multiply-adds of probability and row from zero, in
+ * the listed (canonical) order, and the sum is quantized to bf16 (round to
+ * nearest even).  The fp32 sum is orc_finalize's. */
+void orc_finalize_bf16(const float* O, const int32_t* dst, const float* sorted_probs,
+                       int32_t T, int k, int H, uint16_t* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t mo = 0; mo < H; ++mo) {
+            float acc = 0.0f;
+            for (int j = 0; j < k; ++j) {
+                int32_t d = dst[t * k + j];
+                if (d < 0) continue;
+                acc = fmaf(sorted_probs[t * k + j], O[(int64_t)d * H + mo], acc);
+            }
+            out[t * H + mo] = orc_bf16_bits(acc);
+        }
+    }
+}
+
+/* Row mode ([VALUE] "What is changed", expert compute; [API]
+ * expert_value_pass): every route goes through the finalize as a top-1 token
+ * with probability 1.0, so the finalize returns the route's expert output
+ * unscaled: rows[t][j][m] = fmaf(1.0f, O[dst[t*k+j]][m], +0.0f) for the j-th
+ * route of token t in canonical order.  A dropped route (dst < 0) is a top-1
+ * token with nothing to add: a row of +0.0.  Rows of tokens >= T are not
+ * written. */
+void orc_finalize_rows(const float* O, const int32_t* dst, int32_t T, int k, int H,
+                       float* rows)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < (int64_t)T * k; ++r) {
+        int32_t d = dst[r];
+        for (int64_t mo = 0; mo < H; ++mo) {
+            float acc = 0.0f;
+            if (d >= 0) acc = fmaf(1.0f, O[(int64_t)d * H + mo], acc);
+            rows[r * H + mo] = acc;
+        }
+    }
+}
+
 /* Operand values of x for the live tokens: bf16 values, or the MXFP8
  * quantization of those bf16 values (per token, per 32-block of H). */
 static double* x_operands(const uint16_t* x, int64_t T, int H, int mx)
@@ -473,11 +516,13 @@ void orc_weights_destroy(void* p)
 
 /* The whole forward, step by step: canonical sort and permutation
  * (orc_prepare), the expert MLP of every permuted row, in permuted order,
- * into O rows, then the finalize.  Optional outputs: O_out [T*k][H] fp32
- * (permuted order) and H_out [T*k][F] fp32 (the FC2 operand values).
- * Returns error bits. */
-uint32_t orc_forward(void* wp, const uint16_t* x, const int32_t* ids, const float* probs,
-                     int64_t T_cap, int32_t live, float* out, float* O_out, float* H_out)
+ * into O rows, then the finalize.  combine 0: out fp32 [T_cap][H] (orc_finalize);
+ * 1: out bf16 bits [T_cap][H] (orc_finalize_bf16); 2: out fp32 [T_cap][k][H]
+ * (orc_finalize_rows).  Optional outputs: O_out [T*k][H] fp32 (permuted order)
+ * and H_out [T*k][F] fp32 (the FC2 operand values).  Returns error bits. */
+uint32_t orc_forward_ex(void* wp, const uint16_t* x, const int32_t* ids, const float* probs,
+                        int64_t T_cap, int32_t live, int combine, void* out, float* O_out,
+                        float* H_out)
 {
     orc_weights* w = (orc_weights*)wp;
     const orc_model* m = &w->m;
@@ -509,11 +554,23 @@ uint32_t orc_forward(void* wp, const uint16_t* x, const int32_t* ids, const floa
         }
         free(a32); free(hrow);
     }
-    orc_finalize(O, dst, sorted_probs, T, k, H, out);
+    if (combine == 1)
+        orc_finalize_bf16(O, dst, sorted_probs, T, k, H, (uint16_t*)out);
+    else if (combine == 2)
+        orc_finalize_rows(O, dst, T, k, H, (float*)out);
+    else
+        orc_finalize(O, dst, sorted_probs, T, k, H, (float*)out);
     if (O_out) memcpy(O_out, O, sizeof(float) * nrows * H);
     free(O); free(xo);
     free(sorted_ids); free(sorted_probs); free(counts); free(offsets); free(perm_src); free(dst);
     return err;
+}
+
+/* The forward with the fp32 combine (out fp32 [T_cap][H]). */
+uint32_t orc_forward(void* wp, const uint16_t* x, const int32_t* ids, const float* probs,
+                     int64_t T_cap, int32_t live, float* out, float* O_out, float* H_out)
+{
+    return orc_forward_ex(wp, x, ids, probs, T_cap, live, 0, out, O_out, H_out);
 }
 
 /* The naive per-token loop (no permutation): for each listed token, sort its

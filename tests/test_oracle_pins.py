@@ -254,6 +254,93 @@ def test_finalize_vs_exact_fma_chain():
             assert out[t, m].view(np.uint32) == np.float32(acc).view(np.uint32), (t, m)
 
 
+# ------------------------------------------------------------------ combine variants
+
+def _load_combine_cases():
+    with open(os.path.join(GOLDEN, "combine_cases.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("c", _load_combine_cases(), ids=lambda c: c["name"])
+def test_combine_golden(c):
+    """Hand cases of the bf16 combine and the row mode (tests/golden/combine_cases.json)."""
+    O = np.array(c["O"], np.float32)
+    dst = np.array(c["dst"], np.int32)
+    p = np.array(c["probs"], np.float32)
+    if c["mode"] == "bf16":
+        got = oracle.finalize_bf16(O, dst, p, c["H"])
+        assert np.array_equal(got, np.array(c["expected_bf16"], np.uint16)), got
+    else:
+        got = oracle.finalize_rows(O, dst, c["H"])
+        assert np.array_equal(got.view(np.uint32), np.array(c["expected_rows_bits"], np.uint32)), got
+
+
+def _random_combine_inputs(seed):
+    rng = np.random.default_rng(seed)
+    T, k, H = 30, 5, 12
+    R = T * k
+    O = (rng.standard_normal((R, H)) * 2.0 ** rng.integers(-20, 20, (R, 1))).astype(np.float32)
+    O[rng.random((R, H)) < 0.05] = -0.0
+    p = rng.random((T, k)).astype(np.float32)
+    dst = rng.permutation(R).astype(np.int32).reshape(T, k)
+    dst[2, 3] = -1
+    dst[7, 0] = -1
+    return O, dst, p, H
+
+
+def test_finalize_bf16_is_torch_cast_of_fp32_chain():
+    """The bf16 combine rounds the (separately pinned) fp32 chain; torch's cast is an
+    independent round-to-nearest-even."""
+    O, dst, p, H = _random_combine_inputs(21)
+    f32 = oracle.finalize(O, dst, p, H)
+    ref = torch.from_numpy(f32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.finalize_bf16(O, dst, p, H), ref)
+
+
+def test_finalize_rows_closed_form():
+    """Row mode: the routed row plus +0 (numpy's IEEE add), zeros for a dropped route,
+    probabilities ignored."""
+    O, dst, p, H = _random_combine_inputs(22)
+    ref = np.where((dst >= 0)[:, :, None], O[np.maximum(dst, 0)] + np.float32(0.0), np.float32(0.0))
+    got = oracle.finalize_rows(O, dst, H)
+    assert np.array_equal(got.view(np.uint32), ref.astype(np.float32).view(np.uint32))
+    assert not np.any(got.view(np.uint32) == 0x80000000), "a -0 survived"
+
+
+@pytest.mark.parametrize("precision", ["bf16", "mxfp8"])
+def test_forward_rows_are_top1_tokens_with_probability_one(precision):
+    """Row mode by its definition: every route of the k-model equals the forward of a
+    top-1 model on that route's token alone, with probability 1."""
+    w = WORKLOADS["tiny"]
+    inp = make_inputs(w, seed=13, outliers=(precision == "mxfp8"))
+    ids, probs, _ = oracle.route(inp["logits"], w.T, w.k)
+    m = oracle.Model(w.E, w.H, w.F, w.k, inp["w1_bits"], inp["w2_bits"], precision)
+    rows, err, _ = m.forward(inp["x_bits"], ids[:, ::-1].copy(), None, w.T, combine="rows")
+    assert err == 0 and rows.shape == (w.T_cap, w.k, w.H)
+    m1 = oracle.Model(w.E, w.H, w.F, 1, inp["w1_bits"], inp["w2_bits"], precision)
+    sid = np.sort(ids[: w.T], axis=1)                      # canonical order of the routes
+    x1 = np.repeat(inp["x_bits"][: w.T], w.k, axis=0)
+    one, err1, _ = m1.forward(x1, sid.reshape(-1, 1).copy(), np.ones((w.T * w.k, 1), np.float32),
+                              w.T * w.k)
+    assert err1 == 0
+    assert np.array_equal(rows[: w.T].reshape(-1, w.H).view(np.uint32), one.view(np.uint32))
+    assert np.all(np.isnan(rows[w.T:])), "rows of tokens past live were written"
+
+
+@pytest.mark.parametrize("precision", ["bf16", "mxfp8"])
+def test_forward_bf16_combine_is_rounded_fp32_combine(precision):
+    w = WORKLOADS["tiny"].with_tokens(40, 64)
+    inp = make_inputs(w, seed=11, outliers=(precision == "mxfp8"))
+    ids, probs, _ = oracle.route(inp["logits"], w.T, w.k)
+    m = oracle.Model(w.E, w.H, w.F, w.k, inp["w1_bits"], inp["w2_bits"], precision)
+    f32, _, _ = m.forward(inp["x_bits"], ids, probs, w.T)
+    b16, err, _ = m.forward(inp["x_bits"], ids, probs, w.T, combine="bf16")
+    assert err == 0
+    ref = torch.from_numpy(f32[: w.T]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(b16[: w.T], ref)
+    assert np.all(b16[w.T:] == 0xFFFF), "rows of tokens past live were written"
+
+
 # ------------------------------------------------------------------ hand cases
 
 def _load_hand_cases():
