@@ -44,6 +44,9 @@ def _args():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode")
     p.add_argument("--seed", type=int, default=11)
+    p.add_argument("--combine", default="fp32", choices=["fp32", "bf16", "rows"],
+                   help="how a token's routes are combined (moe_forward_ex): the fp32 chain, "
+                        "the fp32 chain rounded to bf16, or every route's row unscaled")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
@@ -90,16 +93,18 @@ def measured_traffic(workload: str):
     return entry["fetch_bytes_per_launch"] + entry["write_bytes_per_launch"]
 
 
-def alg_bytes(w, precision: str, touched: int) -> dict:
+def alg_bytes(w, precision: str, touched: int, combine: str = "fp32") -> dict:
     """Algorithmic bytes: each touched expert's weights once, each live token's
     x row once, routed rows written/read once where a stage must (FC1 writes
-    the SwiGLU row, FC2 reads it), ids/probs once, the fp32 output once."""
+    the SwiGLU row, FC2 reads it), ids/probs once, the output once (fp32 [T, H],
+    bf16 [T, H] or fp32 [T, k, H] by combine)."""
     wb = 2 if precision == "bf16" else 1
     sb = 0 if precision == "bf16" else 1.0 / 32          # E8M0 bytes per element
     H, F, T, R = w.H, w.F, w.T, w.R
     fc1 = touched * 2 * F * H * (wb + sb) + T * H * 2 + R * F * (wb + sb)
     fc2 = touched * H * F * (wb + sb) + R * F * (wb + sb) + R * H * 4
-    step = touched * 3 * F * H * (wb + sb) + T * H * 2 + T * w.k * 8 + T * H * 4
+    out_b = {"fp32": T * H * 4, "bf16": T * H * 2, "rows": R * H * 4}[combine]
+    step = touched * 3 * F * H * (wb + sb) + T * H * 2 + T * w.k * 8 + out_b
     return dict(fc1=fc1, fc2=fc2, step=step)
 
 
@@ -183,11 +188,14 @@ def main():
     ws = moe0.new_workspace(w.T_cap)
     ids = torch.empty((w.T_cap, w.k), dtype=torch.int32, device=dev)
     probs = torch.empty((w.T_cap, w.k), dtype=torch.float32, device=dev)
-    out = torch.empty((w.T_cap, w.H), dtype=torch.float32, device=dev)
+    out = {"fp32": lambda: torch.empty((w.T_cap, w.H), dtype=torch.float32, device=dev),
+           "bf16": lambda: torch.empty((w.T_cap, w.H), dtype=torch.bfloat16, device=dev),
+           "rows": lambda: torch.empty((w.T_cap, w.k, w.H), dtype=torch.float32, device=dev)}[
+        a.combine]()
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     route_fn = [m.bind_route(logits, live, ids, probs, ws) for m in moes]
-    fwd_fn = [m.bind_forward(x, ids, probs, live, out, ws) for m in moes]
+    fwd_fn = [m.bind_forward(x, ids, probs, live, out, ws, combine=a.combine) for m in moes]
 
     def step(i):
         route_fn[i % n_rot]()
@@ -240,7 +248,7 @@ def main():
     stage_us = {"route": float(np.mean([ev.ms(d[6], d[7]) for d in diag]) * 1e3), **stage_us}
     ev.close()
 
-    ab = alg_bytes(w, w.precision, touched)
+    ab = alg_bytes(w, w.precision, touched, a.combine)
     flops = w.flops()
     tokens_s = w.T / (ms_step * 1e-3)
     tflops = flops / (ms_step * 1e-3) / 1e12
@@ -268,7 +276,7 @@ def main():
         "dtype": w.precision, "data": "synthetic (seeded N(0,1) tokens, N(0,0.02^2) weights)",
         "config": {"workload": w.name, "tokens": w.T, "token_capacity": w.T_cap, "hidden": w.H,
                    "ffn": w.F, "experts": w.E, "topk": w.k, "precision": w.precision,
-                   "parallelism": "one GPU, all experts local"},
+                   "combine": a.combine, "parallelism": "one GPU, all experts local"},
         "tflops": tflops,
         "mfma_frac": tflops / MFMA_PEAK_TFLOPS[w.precision],
         "hbm_gbs_step": ab["step"] / (ms_step * 1e-3) / 1e9,
@@ -282,15 +290,15 @@ def main():
 
     if w.name == "bounded_decode":
         res["live_tracking"] = live_tracking(w, moes, x, logits, route_fn, fwd_fn, ids, probs, out, ws,
-                                             live, sh, n_rot)
+                                             live, sh, n_rot, a.combine)
 
     if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_seconds, a.combine)
     print(json.dumps(res))
 
 
 def live_tracking(w, moes, x, logits, route_fn, fwd_fn, ids, probs, out, ws, live, sh, n_rot,
-                  steps: int = 20) -> dict:
+                  combine: str, steps: int = 20) -> dict:
     """Step time against the live count at the full capacity (live 64 .. 1024),
     and at live = w.T with the buffers sized to the live rows instead.  Rows
     w.T .. 2 w.T - 1 of x and the logits become copies of the first w.T rows,
@@ -325,7 +333,7 @@ def live_tracking(w, moes, x, logits, route_fn, fwd_fn, ids, probs, out, ws, liv
     ids_s, probs_s, out_s = ids[:T].contiguous(), probs[:T].contiguous(), out[:T].contiguous()
     ws_s = moes[0].new_workspace(T)
     route_s = [m.bind_route(ls, live, ids_s, probs_s, ws_s) for m in moes]
-    fwd_s = [m.bind_forward(xs, ids_s, probs_s, live, out_s, ws_s) for m in moes]
+    fwd_s = [m.bind_forward(xs, ids_s, probs_s, live, out_s, ws_s, combine=combine) for m in moes]
     small = time_steps(route_s, fwd_s)
     ev.close()
     return {"token_capacity": w.T_cap, "us_per_step_by_live": by_live,
@@ -333,7 +341,7 @@ def live_tracking(w, moes, x, logits, route_fn, fwd_fn, ids, probs, out, ws, liv
             f"us_per_step_live_{T}_capacity_{w.T_cap}": by_live[str(T)]}
 
 
-def cpu_baseline(w, inp, target_s: float) -> dict:
+def cpu_baseline(w, inp, target_s: float, combine: str = "fp32") -> dict:
     """The CPU oracle (as it stands) on a bounded sample of the same workload:
     the first S live tokens, S sized from a short calibration run."""
     import oracle
@@ -343,7 +351,8 @@ def cpu_baseline(w, inp, target_s: float) -> dict:
 
     def run(S):
         t = time.time()
-        model.forward(inp["x_bits"][:S].copy(), ids[:S].copy(), probs[:S].copy(), S)
+        model.forward(inp["x_bits"][:S].copy(), ids[:S].copy(), probs[:S].copy(), S,
+                      combine=combine)
         return time.time() - t
 
     S0 = min(w.T, 16)

@@ -136,6 +136,36 @@ moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
                        const float* probs, int64_t T_cap, const int32_t* live_rows_dev,
                        float* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* How moe_forward_ex combines a token's routes. */
+typedef enum {
+    MOE_COMBINE_FP32 = 0,  /* moe_forward's combine: out fp32 [T_cap][H]                  */
+    MOE_COMBINE_BF16 = 1,  /* the same fp32 chain rounded to bf16: out bf16 [T_cap][H]     */
+    MOE_COMBINE_ROWS = 2,  /* each route unscaled: out fp32 [T_cap][topk][H]              */
+} moe_combine;
+
+/* moe_forward with a choice of combine; every stage before the combine is
+ * moe_forward's, so the FC2 rows are bit-identical across the three.
+ *   MOE_COMBINE_FP32: exactly moe_forward.
+ *   MOE_COMBINE_BF16 (Megatron-LM PR #7798, "What is changed": the
+ *     BF16_RANK_PARTIALS unpermute, which on one rank adds a token's routes as
+ *     fp32 fused multiply-adds of probability and row from zero, in the listed
+ *     order, and quantizes the sum to BF16 as FlashInfer's finalize does):
+ *     out[t][m] = bf16_rne(the fp32 chain of moe_forward); out is bf16 (uint16
+ *     bits) [T_cap][H].
+ *   MOE_COMBINE_ROWS (Megatron-LM PR #7798, "What is changed", expert compute;
+ *     Megatron-Core API docs, expert_value_pass): every route runs as a top-1
+ *     token with probability 1.0, so the finalize returns its expert output
+ *     unscaled: out[t][j][m] = fma(1, O_j[m], +0.0f) for the j-th route of
+ *     token t in canonical (ascending expert id) order, where O_j is that
+ *     route's fp32 FC2 row; -0 comes back as +0 and a dropped route (invalid
+ *     or repeated id) as a row of +0.  out is fp32 [T_cap][topk][H].  probs
+ *     is not read and may be NULL.
+ * Rows of tokens >= live are never written in any mode.  Errors: an unknown
+ * combine is MOE_ERR_INVALID_ARG; otherwise as moe_forward. */
+moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids,
+                          const float* probs, int64_t T_cap, const int32_t* live_rows_dev,
+                          int combine, void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Copy the permutation of the last forward to host arrays (synchronizes the
  * stream).  counts: int32 [E]; offsets: int32 [E+1]; perm_src: int32 [n_rows]
  * (= t*topk + j of the route at each grouped row, experts ascending, tokens

@@ -32,6 +32,8 @@ DEVERR_DUP_EXPERT_ID = 2
 DEVERR_LIVE_ABOVE_CAP = 4
 DEVERR_LIVE_NEGATIVE = 8
 WS_HEADER_BYTES = 256
+# moe_forward_ex combines (moe_combine in include/moe.h)
+COMBINES = {"fp32": 0, "bf16": 1, "rows": 2}
 
 # every symbol include/moe.h declares, with its ctypes signature
 _P = ctypes.c_void_p
@@ -43,6 +45,8 @@ _SIGNATURES = {
     "moe_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int64]),
     "moe_route": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_forward": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_forward_ex": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, _P, ctypes.c_int, _P, _P,
+                                      ctypes.c_size_t, _P]),
     "moe_get_indices": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P]),
     "moe_get_rows": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P, _P, _P, _P, _P]),
     "moe_check": (ctypes.c_int, [_P, _P, _P, ctypes.POINTER(ctypes.c_uint32)]),
@@ -181,21 +185,35 @@ class MoE:
                "moe_route")
         return ids, probs
 
-    def forward(self, x, ids, probs, live, out=None, ws=None, stream=None):
+    def _out_spec(self, T_cap: int, combine: str):
+        """(dtypes, shape, allocation dtype) of the output of a combine."""
+        torch = _torch()
+        if combine == "fp32":
+            return (torch.float32,), (T_cap, self.H), torch.float32
+        if combine == "bf16":
+            return (torch.bfloat16, torch.int16, torch.uint16), (T_cap, self.H), torch.bfloat16
+        if combine == "rows":
+            return (torch.float32,), (T_cap, self.topk, self.H), torch.float32
+        raise ValueError(f"combine must be one of {sorted(COMBINES)}")
+
+    def forward(self, x, ids, probs, live, out=None, ws=None, stream=None, combine="fp32"):
+        """The forward (moe_forward_ex).  combine: "fp32" (out fp32 [T_cap, H]), "bf16"
+        (out bf16 [T_cap, H]) or "rows" (out fp32 [T_cap, topk, H]; probs may be None)."""
         torch = _torch()
         T_cap = x.shape[0]
+        dts, shape, alloc = self._out_spec(T_cap, combine)
         px = _dev(x, "x", (torch.bfloat16, torch.int16, torch.uint16), (T_cap, self.H))
         pi = _dev(ids, "expert_ids", (torch.int32,), (T_cap, self.topk))
-        pp = _dev(probs, "probs", (torch.float32,), (T_cap, self.topk))
+        pp = None if probs is None else _dev(probs, "probs", (torch.float32,), (T_cap, self.topk))
         plive = _dev(live, "live", (torch.int32,))
         if out is None:
-            out = torch.empty((T_cap, self.H), dtype=torch.float32, device=x.device)
-        po = _dev(out, "out", (torch.float32,), (T_cap, self.H))
+            out = torch.empty(shape, dtype=alloc, device=x.device)
+        po = _dev(out, "out", dts, shape)
         if ws is None:
             ws = self.new_workspace(T_cap, x.device)
         pw = _dev(ws, "ws", (torch.uint8,))
-        _check(lib().moe_forward(self._h, px, pi, pp, T_cap, plive, po, pw, ws.numel(),
-                                 _stream(stream)), "moe_forward")
+        _check(lib().moe_forward_ex(self._h, px, pi, pp, T_cap, plive, COMBINES[combine], po, pw,
+                                    ws.numel(), _stream(stream)), "moe_forward")
         return out
 
     # ------------------------------------------------------------- inspection
@@ -260,19 +278,20 @@ class MoE:
         arr = (_P * 6)(*handles)
         _check(lib().moe_set_stage_events(self._h, arr, 6), "moe_set_stage_events")
 
-    def bind_forward(self, x, ids, probs, live, out, ws, stream=None):
+    def bind_forward(self, x, ids, probs, live, out, ws, stream=None, combine="fp32"):
         """Check the arguments once and return a no-argument callable that
         enqueues this forward (for launch loops where per-call checks would
         cost more host time than the GPU work)."""
         torch = _torch()
         T_cap = x.shape[0]
+        dts, shape, _ = self._out_spec(T_cap, combine)
         args = (self._h, _dev(x, "x", (torch.bfloat16, torch.int16, torch.uint16), (T_cap, self.H)),
                 _dev(ids, "expert_ids", (torch.int32,), (T_cap, self.topk)),
-                _dev(probs, "probs", (torch.float32,), (T_cap, self.topk)), T_cap,
-                _dev(live, "live", (torch.int32,)),
-                _dev(out, "out", (torch.float32,), (T_cap, self.H)),
+                None if probs is None else _dev(probs, "probs", (torch.float32,), (T_cap, self.topk)),
+                T_cap, _dev(live, "live", (torch.int32,)), COMBINES[combine],
+                _dev(out, "out", dts, shape),
                 _dev(ws, "ws", (torch.uint8,)), ws.numel(), _stream(stream))
-        fn = lib().moe_forward
+        fn = lib().moe_forward_ex
         keep = (x, ids, probs, live, out, ws)
 
         def call():

@@ -11,6 +11,16 @@
 // A route with dst < 0 (an invalid expert id) adds nothing.  Rows >= live are
 // neither read nor written.  One workgroup (512 threads) walks tokens; 4
 // columns per thread.
+//
+// Two more combines (the value pass of Megatron-LM PR #7798, "What is
+// changed"):
+//   bf16: the same fp32 chain rounded to bf16 (round to nearest even), which
+//     is one rank of its BF16_RANK_PARTIALS unpermute and what FlashInfer's
+//     finalize returns; out bf16 [T_cap][H].
+//   rows: every route through the finalize as a top-1 token with probability
+//     1.0, so each route's expert output comes back unscaled:
+//     out[t][j][m] = fma(1, O[dst[t,j]][m], +0.0f) (-0 becomes +0; a dropped
+//     route gives +0); out fp32 [T_cap][k][H].
 #include "common.h"
 
 namespace moe {
@@ -19,12 +29,16 @@ namespace moe {
 // in flight before the chain starts (a runtime loop put a memory round trip
 // between consecutive routes).  The FC2 rows are read and the output written
 // with non-temporal accesses: each byte is touched once (measured 15 % faster
-// at 16K tokens than with the default cache policy).
-template <int K>
+// at 16K tokens than with the default cache policy).  MODE: 0 fp32 combine,
+// 1 bf16 combine, 2 rows.
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef unsigned u2v __attribute__((ext_vector_type(2)));
+
+template <int K, int MODE>
 __global__ void __launch_bounds__(512) finalize_kernel(
     const float* __restrict__ O, const int32_t* __restrict__ dst,
     const float* __restrict__ sorted_probs, int64_t T_cap, const int32_t* __restrict__ live_ptr,
-    int H, float* __restrict__ out)
+    int H, void* __restrict__ out)
 {
     const int32_t live = *live_ptr;
     const int64_t T = live < 0 ? 0 : (live > T_cap ? T_cap : live);
@@ -35,48 +49,67 @@ __global__ void __launch_bounds__(512) finalize_kernel(
 #pragma unroll
         for (int j = 0; j < K; ++j) {
             d[j] = dst[t * K + j];
-            p[j] = sorted_probs[t * K + j];
+            p[j] = MODE == 2 ? 1.0f : sorted_probs[t * K + j];
         }
         for (int c = threadIdx.x; c < H4; c += blockDim.x) {
-            float4 o[K];
+            f4v o[K];
 #pragma unroll
             for (int j = 0; j < K; ++j)
-                if (d[j] >= 0) {
-                    typedef float f4v __attribute__((ext_vector_type(4)));
-                    f4v v = __builtin_nontemporal_load((const f4v*)(O + (int64_t)d[j] * H) + c);
-                    o[j] = make_float4(v.x, v.y, v.z, v.w);
-                } else {
-                    o[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-                }
-            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (d[j] >= 0)
+                    o[j] = __builtin_nontemporal_load((const f4v*)(O + (int64_t)d[j] * H) + c);
+                else
+                    o[j] = f4v{0.f, 0.f, 0.f, 0.f};
+            if constexpr (MODE == 2) {
+                // each route alone: one fma from +0 (a dropped route stays +0)
 #pragma unroll
-            for (int j = 0; j < K; ++j) {
-                if (d[j] < 0) continue;    // a dropped route adds nothing (not even +0)
-                acc.x = __builtin_fmaf(p[j], o[j].x, acc.x);
-                acc.y = __builtin_fmaf(p[j], o[j].y, acc.y);
-                acc.z = __builtin_fmaf(p[j], o[j].z, acc.z);
-                acc.w = __builtin_fmaf(p[j], o[j].w, acc.w);
-            }
-            {
-                typedef float f4v __attribute__((ext_vector_type(4)));
-                f4v v = {acc.x, acc.y, acc.z, acc.w};
-                __builtin_nontemporal_store(v, (f4v*)(out + t * H) + c);
+                for (int j = 0; j < K; ++j) {
+                    f4v r = {0.f, 0.f, 0.f, 0.f};
+                    if (d[j] >= 0) {
+                        r.x = __builtin_fmaf(p[j], o[j].x, 0.0f);
+                        r.y = __builtin_fmaf(p[j], o[j].y, 0.0f);
+                        r.z = __builtin_fmaf(p[j], o[j].z, 0.0f);
+                        r.w = __builtin_fmaf(p[j], o[j].w, 0.0f);
+                    }
+                    __builtin_nontemporal_store(r, (f4v*)((float*)out + (t * K + j) * H) + c);
+                }
+            } else {
+                f4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < K; ++j) {
+                    if (d[j] < 0) continue;    // a dropped route adds nothing (not even +0)
+                    acc.x = __builtin_fmaf(p[j], o[j].x, acc.x);
+                    acc.y = __builtin_fmaf(p[j], o[j].y, acc.y);
+                    acc.z = __builtin_fmaf(p[j], o[j].z, acc.z);
+                    acc.w = __builtin_fmaf(p[j], o[j].w, acc.w);
+                }
+                if constexpr (MODE == 0) {
+                    __builtin_nontemporal_store(acc, (f4v*)((float*)out + t * H) + c);
+                } else {
+                    const u2v v = {(unsigned)f32_to_bf16_bits(acc.x) | ((unsigned)f32_to_bf16_bits(acc.y) << 16),
+                                   (unsigned)f32_to_bf16_bits(acc.z) | ((unsigned)f32_to_bf16_bits(acc.w) << 16)};
+                    __builtin_nontemporal_store(v, (u2v*)((uint16_t*)out + t * H) + c);
+                }
             }
         }
     }
 }
 
 hipError_t launch_finalize(const float* O, const int32_t* dst, const float* sorted_probs,
-                           int64_t T_cap, const int32_t* live, int k, int H, float* out, int num_cu,
-                           hipStream_t s)
+                           int64_t T_cap, const int32_t* live, int k, int H, int mode, void* out,
+                           int num_cu, hipStream_t s)
 {
     int64_t blocks = T_cap < (int64_t)num_cu * 8 ? T_cap : (int64_t)num_cu * 8;
     if (blocks < 1) blocks = 1;
     const dim3 g((unsigned)blocks), b(512);
+    if (mode < 0 || mode > 2) return hipErrorInvalidValue;
+#define FIN_MODE(KK, MM)                                                                     \
+    hipLaunchKernelGGL((finalize_kernel<KK, MM>), g, b, 0, s, O, dst, sorted_probs, T_cap, live, \
+                       H, out)
 #define FIN_CASE(KK)                                                                         \
     case KK:                                                                                 \
-        hipLaunchKernelGGL(finalize_kernel<KK>, g, b, 0, s, O, dst, sorted_probs, T_cap, live, H, \
-                           out);                                                             \
+        if (mode == 0) FIN_MODE(KK, 0);                                                      \
+        else if (mode == 1) FIN_MODE(KK, 1);                                                 \
+        else FIN_MODE(KK, 2);                                                                \
         break;
     switch (k) {
         FIN_CASE(1) FIN_CASE(2) FIN_CASE(3) FIN_CASE(4) FIN_CASE(5) FIN_CASE(6) FIN_CASE(7)
@@ -85,6 +118,7 @@ hipError_t launch_finalize(const float* O, const int32_t* dst, const float* sort
         default: return hipErrorInvalidValue;
     }
 #undef FIN_CASE
+#undef FIN_MODE
     return hipGetLastError();
 }
 

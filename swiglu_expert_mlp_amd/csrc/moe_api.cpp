@@ -16,8 +16,8 @@ hipError_t launch_route(const float* logits, int64_t T_cap, const int32_t* live,
 hipError_t launch_prep(const int32_t* ids, const float* probs, int64_t T_cap, const int32_t* live,
                        int E, int k, int num_cu, char* ws, const WsLayout& L, hipStream_t s);
 hipError_t launch_finalize(const float* O, const int32_t* dst, const float* sorted_probs,
-                           int64_t T_cap, const int32_t* live, int k, int H, float* out, int num_cu,
-                           hipStream_t s);
+                           int64_t T_cap, const int32_t* live, int k, int H, int mode, void* out,
+                           int num_cu, hipStream_t s);
 hipError_t launch_pack_bf16(const uint16_t* w1, const uint16_t* w2, uint8_t* kbuf, int E, int H,
                             int F, int num_cu, hipStream_t s);
 hipError_t launch_pack_mxfp8(const uint16_t* w1, const uint16_t* w2, uint8_t* kbuf, int E, int H,
@@ -221,14 +221,26 @@ moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
                        const float* probs, int64_t T_cap, const int32_t* live_rows_dev,
                        float* out, void* ws, size_t ws_bytes, hipStream_t stream)
 {
+    return moe_forward_ex(h, x, expert_ids, probs, T_cap, live_rows_dev, MOE_COMBINE_FP32, out, ws,
+                          ws_bytes, stream);
+}
+
+moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids,
+                          const float* probs, int64_t T_cap, const int32_t* live_rows_dev,
+                          int combine, void* out, void* ws, size_t ws_bytes, hipStream_t stream)
+{
     if (!h) return fail(MOE_ERR_INVALID_ARG, "moe_forward: NULL handle");
     if (!h->kbuf) return fail(MOE_ERR_NOT_LOADED, "moe_forward: no weights loaded (moe_load_weights)");
     if (T_cap < 0 || T_cap > (int64_t)1 << 26)
         return fail(MOE_ERR_INVALID_ARG, "moe_forward: T_cap=%lld out of range", (long long)T_cap);
-    if (!x || !expert_ids || !probs || !live_rows_dev || !out || !ws)
+    if (combine != MOE_COMBINE_FP32 && combine != MOE_COMBINE_BF16 && combine != MOE_COMBINE_ROWS)
+        return fail(MOE_ERR_INVALID_ARG, "moe_forward: unknown combine %d", combine);
+    // row mode does not use the probabilities (every route has probability 1)
+    if (!x || !expert_ids || (!probs && combine != MOE_COMBINE_ROWS) || !live_rows_dev || !out ||
+        !ws)
         return fail(MOE_ERR_INVALID_ARG, "moe_forward: NULL pointer");
-    if (!aligned16(x) || !aligned16(expert_ids) || !aligned16(probs) || !aligned16(out) ||
-        !aligned16(ws))
+    if (!aligned16(x) || !aligned16(expert_ids) || (probs && !aligned16(probs)) ||
+        !aligned16(out) || !aligned16(ws))
         return fail(MOE_ERR_INVALID_ARG, "moe_forward: pointers must be 16-byte aligned");
     const WsLayout L = layout_of(h, T_cap);
     if (ws_bytes < L.total)
@@ -323,8 +335,8 @@ moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
         if ((e = mark(h, 4, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     }
     e = launch_finalize((const float*)(w + L.obuf), (const int32_t*)(w + L.dst),
-                        (const float*)(w + L.sorted_probs), T_cap, live_rows_dev, h->k, H, out,
-                        h->num_cu, stream);
+                        (const float*)(w + L.sorted_probs), T_cap, live_rows_dev, h->k, H, combine,
+                        out, h->num_cu, stream);
     if (e != hipSuccess) return hip_fail(e, "moe_forward: finalize launch");
     if ((e = mark(h, 5, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     return MOE_OK;

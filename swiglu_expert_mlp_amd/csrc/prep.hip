@@ -211,7 +211,8 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a)
 #pragma unroll
     for (int j = 0; j < K; ++j) {
         id[j] = valid ? a.ids[(int64_t)t * K + j] : -1;
-        p[j] = valid ? a.probs[(int64_t)t * K + j] : 0.0f;
+        // no probabilities (row mode): every route has probability 1
+        p[j] = valid ? (a.probs ? a.probs[(int64_t)t * K + j] : 1.0f) : 0.0f;
     }
 #pragma unroll
     for (int x = 1; x < K; ++x)
