@@ -64,6 +64,11 @@ def lib() -> ctypes.CDLL:
             "orc_e8m0_exponent": (ctypes.c_int, [ctypes.c_float]),
             "orc_mx_quantize": (None, [P, i64, i64, P, P]),
             "orc_mx_dequantize": (None, [P, P, i64, i64, P]),
+            "orc_e2m1_decode": (ctypes.c_double, [ctypes.c_uint8]),
+            "orc_e2m1_encode": (ctypes.c_uint8, [ctypes.c_double]),
+            "orc_e8m0_exponent_fp4": (ctypes.c_int, [ctypes.c_float]),
+            "orc_mx4_quantize": (None, [P, i64, i64, P, P]),
+            "orc_mx4_dequantize": (None, [P, P, i64, i64, P]),
             "orc_route": (u32, [P, i64, i32, ctypes.c_int, ctypes.c_int, P, P]),
             "orc_prepare": (u32, [P, P, i64, i32, ctypes.c_int, ctypes.c_int,
                                   P, P, P, P, P, P, P]),
@@ -77,6 +82,8 @@ def lib() -> ctypes.CDLL:
             "orc_forward_tokens": (None, [P, P, P, P, P, i64, P]),
             "orc_pack_bf16": (None, [ctypes.c_int] * 3 + [P, P, P]),
             "orc_pack_mxfp8": (None, [ctypes.c_int] * 3 + [P, P, P]),
+            "orc_pack_mxfp4": (None, [ctypes.c_int] * 3 + [P, P, P]),
+            "orc_pack_mx4_offsets": (None, [ctypes.c_int] * 3 + [P]),
             "orc_pack_bytes": (i64, [ctypes.c_int] * 4),
             "orc_pack_mx_offsets": (None, [ctypes.c_int] * 3 + [P]),
         }
@@ -140,6 +147,42 @@ def mx_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     out = np.empty((rows, cols), dtype=np.float64)
     lib().orc_mx_dequantize(_p(codes), _p(scales), rows, cols, _p(out))
     return out
+
+
+def e2m1_decode(code: int) -> float:
+    return lib().orc_e2m1_decode(int(code))
+
+
+def e2m1_encode(v: float) -> int:
+    return lib().orc_e2m1_encode(float(v))
+
+
+def e8m0_exponent_fp4(amax: float) -> int:
+    return lib().orc_e8m0_exponent_fp4(float(amax))
+
+
+def mx4_quantize(v: np.ndarray):
+    """[rows, cols] fp32 -> (E2M1 codes uint8 [rows, cols] one per byte,
+    scales uint8 [rows, cols/32])."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    rows, cols = v.shape
+    assert cols % 32 == 0
+    codes = np.empty((rows, cols), dtype=np.uint8)
+    scales = np.empty((rows, cols // 32), dtype=np.uint8)
+    lib().orc_mx4_quantize(_p(v), rows, cols, _p(codes), _p(scales))
+    return codes, scales
+
+
+def mx4_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows, cols = codes.shape
+    out = np.empty((rows, cols), dtype=np.float64)
+    lib().orc_mx4_dequantize(_p(codes), _p(scales), rows, cols, _p(out))
+    return out
+
+
+PRECISIONS = {"bf16": 0, "mxfp8": 1, "mxfp4": 2}
 
 
 # ---------------------------------------------------------------- router / prepare
@@ -221,18 +264,19 @@ COMBINES = {"fp32": 0, "bf16": 1, "rows": 2}
 class Model:
     """Oracle weights: bf16 W1 [E, 2F, H] (gate rows first) and W2 [E, H, F].
 
-    precision: "bf16" or "mxfp8" (weights quantized per 32-block along K).
+    precision: "bf16", "mxfp8" (weights quantized to E4M3 per 32-block along K) or
+    "mxfp4" (weights quantized to E2M1 per 32-block along K; activations MXFP8).
     """
 
     def __init__(self, E, H, F, k, w1_bits: np.ndarray, w2_bits: np.ndarray,
                  precision: str = "bf16"):
-        assert precision in ("bf16", "mxfp8")
+        assert precision in PRECISIONS
         self.E, self.H, self.F, self.k = E, H, F, k
         self.precision = precision
         self._w1 = np.ascontiguousarray(w1_bits, dtype=np.uint16)
         self._w2 = np.ascontiguousarray(w2_bits, dtype=np.uint16)
         assert self._w1.size == E * 2 * F * H and self._w2.size == E * H * F
-        self._h = lib().orc_weights_create(E, H, F, k, int(precision == "mxfp8"),
+        self._h = lib().orc_weights_create(E, H, F, k, PRECISIONS[precision],
                                            _p(self._w1), _p(self._w2))
 
     def __del__(self):
@@ -284,14 +328,15 @@ class Model:
 
 
 def pack_bytes(E, H, F, precision="bf16") -> int:
-    return int(lib().orc_pack_bytes(E, H, F, int(precision == "mxfp8")))
+    return int(lib().orc_pack_bytes(E, H, F, PRECISIONS[precision]))
 
 
-def pack_mx_offsets(E, H, F) -> list:
-    """Byte offsets of the MXFP8 buffer sections: FC1 codes, FC2 codes, FC1
-    scales, FC2 scales, end (each section's padding is part of the layout)."""
+def pack_mx_offsets(E, H, F, precision="mxfp8") -> list:
+    """Byte offsets of the MXFP8 / MXFP4 buffer sections: FC1 codes, FC2 codes,
+    FC1 scales, FC2 scales, end (each section's padding is part of the layout)."""
     off = np.zeros(5, dtype=np.int64)
-    lib().orc_pack_mx_offsets(E, H, F, _p(off))
+    fn = lib().orc_pack_mx4_offsets if precision == "mxfp4" else lib().orc_pack_mx_offsets
+    fn(E, H, F, _p(off))
     return [int(v) for v in off]
 
 
@@ -300,6 +345,7 @@ def pack(E, H, F, w1_bits, w2_bits, precision="bf16") -> np.ndarray:
     w1 = np.ascontiguousarray(w1_bits, dtype=np.uint16)
     w2 = np.ascontiguousarray(w2_bits, dtype=np.uint16)
     buf = np.zeros(pack_bytes(E, H, F, precision), dtype=np.uint8)
-    fn = lib().orc_pack_mxfp8 if precision == "mxfp8" else lib().orc_pack_bf16
+    fn = {"bf16": lib().orc_pack_bf16, "mxfp8": lib().orc_pack_mxfp8,
+          "mxfp4": lib().orc_pack_mxfp4}[precision]
     fn(E, H, F, _p(w1), _p(w2), _p(buf))
     return buf

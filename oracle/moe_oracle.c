@@ -175,6 +175,89 @@ void orc_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows
                                       (int)scales[r * nb + c / 32] - 127);
 }
 
+/* E2M1 (OCP MX 4-bit float): 1 sign bit, 2 exponent bits with bias 1, 1
+ * mantissa bit; no infinities or NaN.  Exponent field 0 is subnormal
+ * (0.m * 2^0); the magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4 and 6.  Decoding
+ * follows that definition. */
+double orc_e2m1_decode(uint8_t c)
+{
+    int sign = (c >> 3) & 1;
+    int ef = (c >> 1) & 3;
+    int m = c & 1;
+    double mag = ef == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, ef - 1);
+    return sign ? -mag : mag;
+}
+
+/* Encode a value whose magnitude is at most 6 (the caller's scale choice
+ * guarantees it) to the nearest E2M1 value, ties to the even code, keeping
+ * the sign (-0 and negatives that round to zero give code 8).  Exhaustive
+ * search over the eight magnitudes. */
+uint8_t orc_e2m1_encode(double v)
+{
+    uint8_t sign = signbit(v) ? 8 : 0;
+    double a = fabs(v);
+    int best = 0;
+    double bd = INFINITY;
+    for (int c = 0; c < 8; ++c) {
+        double d = fabs(orc_e2m1_decode((uint8_t)c) - a);
+        if (d < bd || (d == bd && (c & 1) == 0 && (best & 1))) { best = c; bd = d; }
+    }
+    return (uint8_t)(sign | best);
+}
+
+/* E8M0 block exponent for MXFP4: the smallest integer e in [-127, 127] with
+ * amax <= 6 * 2^e (the power-of-two ceiling of amax / 6, the MXFP8 rule with
+ * E2M1's largest value in place of E4M3's); amax == 0 gives -127.  Exact
+ * search, as orc_e8m0_exponent. */
+int orc_e8m0_exponent_fp4(float amax)
+{
+    if (!(amax > 0.0f)) return -127;
+    int ex;
+    frexp((double)amax, &ex);
+    int e = ex - 4;                                 /* below the answer */
+    while (!((double)amax <= ldexp(6.0, e))) e += 1;
+    while (e > -127 && (double)amax <= ldexp(6.0, e - 1)) e -= 1;
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e;
+}
+
+/* MXFP4 quantization of a [rows][cols] fp32 matrix along cols, one E8M0
+ * scale per 32 consecutive elements: scale byte = e + 127, code (one per
+ * byte here) = E2M1(v / 2^e).  cols must be a multiple of 32. */
+void orc_mx4_quantize(const float* v, int64_t rows, int64_t cols, uint8_t* codes,
+                      uint8_t* scales)
+{
+    int64_t nb = cols / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const float* blk = v + r * cols + b * 32;
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i) {
+                float a = fabsf(blk[i]);
+                if (a > amax) amax = a;
+            }
+            int e = orc_e8m0_exponent_fp4(amax);
+            scales[r * nb + b] = (uint8_t)(e + 127);
+            for (int i = 0; i < 32; ++i)
+                codes[r * cols + b * 32 + i] = orc_e2m1_encode(ldexp((double)blk[i], -e));
+        }
+    }
+}
+
+/* Value of an MXFP4 element: E2M1 value times 2^(scale - 127). */
+void orc_mx4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                        int64_t cols, double* out)
+{
+    int64_t nb = cols / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            out[r * cols + c] = ldexp(orc_e2m1_decode(codes[r * cols + c]),
+                                      (int)scales[r * nb + c / 32] - 127);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Router ([API] `_route`; softmax, top-k, renormalize)                      */
 /* ------------------------------------------------------------------------ */
@@ -302,7 +385,7 @@ uint32_t orc_prepare(const int32_t* ids, const float* probs, int64_t T_cap, int3
 
 /* Exact dot products of an operand row (fp64 values) with a weight row,
  * accumulated in fp64 and rounded once to fp32.  bf16 x bf16 and
- * MXFP8 x MXFP8 products are exact in fp64.  Weight rows are read either as
+ * MXFP8 x MXFP8 and MXFP8 x MXFP4 products are exact in fp64.  Weight rows are read either as
  * bf16 bit patterns or as fp32 values (the MXFP8 operand values, which fp32
  * holds exactly). */
 static float dot_bf16(const double* a, const uint16_t* b, int64_t n)
@@ -332,10 +415,10 @@ static float swiglu_f32(float g, float u)
  * copied) or fp32 operand values (MXFP8 path: the dequantized quantization). */
 typedef struct {
     int E, H, F, k;
-    int mx;                 /* 0: bf16 path, 1: MXFP8 path */
+    int mx;                 /* 0: bf16 path, 1: MXFP8 path, 2: MXFP4 weights + MXFP8 activations */
     const uint16_t* w1b;    /* bf16 [E][2F][H] (gate rows 0..F-1, up rows F..2F-1) */
     const uint16_t* w2b;    /* bf16 [E][H][F] */
-    const float* w1f;       /* MXFP8 operand values, same shapes */
+    const float* w1f;       /* MXFP8 / MXFP4 weight operand values, same shapes */
     const float* w2f;
 } orc_model;
 
@@ -484,6 +567,26 @@ static float* w_mx_operands(const uint16_t* w, int64_t rows, int64_t cols)
     return wf;
 }
 
+/* MXFP4 weight operand values: the E2M1 quantization of the bf16 values
+ * along K, dequantized to fp32 (exact). */
+static float* w_mx4_operands(const uint16_t* w, int64_t rows, int64_t cols)
+{
+    float* wf = (float*)malloc(sizeof(float) * rows * cols);
+    uint8_t* c = (uint8_t*)malloc(rows * cols);
+    uint8_t* s = (uint8_t*)malloc(rows * (cols / 32));
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows * cols; ++i) wf[i] = orc_bf16_value(w[i]);
+    orc_mx4_quantize(wf, rows, cols, c, s);
+    int64_t nb = cols / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t q = 0; q < cols; ++q)
+            wf[r * cols + q] = (float)ldexp(orc_e2m1_decode(c[r * cols + q]),
+                                            (int)s[r * nb + q / 32] - 127);
+    free(c); free(s);
+    return wf;
+}
+
 /* Opaque prepared weights, so that repeated oracle calls on the same model
  * (sampled tokens, timing) do not rebuild the operand values.  In the bf16
  * path the caller's arrays are read in place and must outlive the handle. */
@@ -498,9 +601,12 @@ void* orc_weights_create(int E, int H, int F, int k, int mx, const uint16_t* w1,
 {
     orc_weights* w = (orc_weights*)calloc(1, sizeof(orc_weights));
     w->m.E = E; w->m.H = H; w->m.F = F; w->m.k = k; w->m.mx = mx;
-    if (mx) {
+    if (mx == 1) {
         w->w1f = w_mx_operands(w1, (int64_t)E * 2 * F, H);
         w->w2f = w_mx_operands(w2, (int64_t)E * H, F);
+    } else if (mx == 2) {
+        w->w1f = w_mx4_operands(w1, (int64_t)E * 2 * F, H);
+        w->w2f = w_mx4_operands(w2, (int64_t)E * H, F);
     }
     w->m.w1b = w1; w->m.w2b = w2;
     w->m.w1f = w->w1f; w->m.w2f = w->w2f;
@@ -711,16 +817,71 @@ void orc_pack_mxfp8(int E, int H, int F, const uint16_t* w1, const uint16_t* w2,
     pack_mx_section(E, H, F, F, 0, w2, kbuf + c1, kbuf + c1 + c2 + s1);
 }
 
+/* MXFP4 codes of a weight with N rows of K elements: one 1 KB block per 16
+ * rows x 128 K, lane (k%128)/32*16 + n%16 holding K (k%128)/32*32 + [0, 32)
+ * of row n as 16 bytes, two codes per byte, the lower K in the low nibble:
+ *   ((e*(N/16) + n/16)*KS + k/128)*1024 + ((k%128)/32*16 + n%16)*16 + (k%32)/2,
+ *   nibble (k%2).
+ * Scales as MXFP8.  Codes for k >= K are 0, scales 127 (2^0). */
+static int64_t code4_bytes(int E, int64_t N, int64_t K) { return (int64_t)E * (N / 16) * ksteps(K) * 1024; }
+
+static void pack_mx4_section(int E, int64_t N, int64_t K, int64_t F, int fc1, const uint16_t* w,
+                             uint8_t* codes, uint8_t* scales)
+{
+    int64_t KS = ksteps(K), KQ = (KS + 3) / 4;
+    memset(codes, 0, code4_bytes(E, N, K));
+    memset(scales, 127, scale_bytes(E, N, K));
+    float* row = (float*)malloc(sizeof(float) * K);
+    uint8_t* c = (uint8_t*)malloc(K);
+    uint8_t* sc = (uint8_t*)malloc(K / 32);
+    for (int64_t e = 0; e < E; ++e)
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t src = fc1 ? fc1_logical_row(n, F) : n;
+            for (int64_t k = 0; k < K; ++k) row[k] = orc_bf16_value(w[(e * N + src) * K + k]);
+            orc_mx4_quantize(row, 1, K, c, sc);
+            int64_t blk = e * (N / 16) + n / 16;
+            for (int64_t k = 0; k < K; ++k)
+                codes[(blk * KS + k / 128) * 1024 + ((k % 128) / 32 * 16 + n % 16) * 16 + (k % 32) / 2] |=
+                    (uint8_t)(c[k] << (4 * (k % 2)));
+            for (int64_t b = 0; b < K / 32; ++b)
+                scales[(blk * KQ + (b / 4) / 4) * 256 + ((b % 4) * 16 + n % 16) * 4 + (b / 4) % 4] =
+                    sc[b];
+        }
+    free(row); free(c); free(sc);
+}
+
+/* MXFP4 buffer: FC1 codes, FC2 codes, FC1 scales, FC2 scales, each section
+ * starting at a multiple of 256 bytes. */
+void orc_pack_mxfp4(int E, int H, int F, const uint16_t* w1, const uint16_t* w2, uint8_t* kbuf)
+{
+    int64_t c1 = up256(code4_bytes(E, 2 * (int64_t)F, H)), c2 = up256(code4_bytes(E, H, F));
+    int64_t s1 = up256(scale_bytes(E, 2 * (int64_t)F, H));
+    pack_mx4_section(E, 2 * (int64_t)F, H, F, 1, w1, kbuf, kbuf + c1 + c2);
+    pack_mx4_section(E, H, F, F, 0, w2, kbuf + c1, kbuf + c1 + c2 + s1);
+}
+
 int64_t orc_pack_bytes(int E, int H, int F, int mx)
 {
     int64_t n1 = (int64_t)E * 2 * F * H, n2 = (int64_t)E * H * F;
     if (!mx) return 2 * (n1 + n2);
+    if (mx == 2)
+        return up256(code4_bytes(E, 2 * (int64_t)F, H)) + up256(code4_bytes(E, H, F)) +
+               up256(scale_bytes(E, 2 * (int64_t)F, H)) + up256(scale_bytes(E, H, F));
     return up256(code_bytes(E, 2 * (int64_t)F, H)) + up256(code_bytes(E, H, F)) +
            up256(scale_bytes(E, 2 * (int64_t)F, H)) + up256(scale_bytes(E, H, F));
 }
 
 /* Section offsets of the MXFP8 buffer: FC1 codes, FC2 codes, FC1 scales,
  * FC2 scales, and the end. */
+void orc_pack_mx4_offsets(int E, int H, int F, int64_t* off)
+{
+    off[0] = 0;
+    off[1] = up256(code4_bytes(E, 2 * (int64_t)F, H));
+    off[2] = off[1] + up256(code4_bytes(E, H, F));
+    off[3] = off[2] + up256(scale_bytes(E, 2 * (int64_t)F, H));
+    off[4] = off[3] + up256(scale_bytes(E, H, F));
+}
+
 void orc_pack_mx_offsets(int E, int H, int F, int64_t* off)
 {
     off[0] = 0;

@@ -138,6 +138,91 @@ def test_mx_quantize_vs_torch():
             assert np.array_equal(codes[r, b * 32:(b + 1) * 32], ref)
 
 
+# ------------------------------------------------------------------ MXFP4 primitives
+
+E2M1_MAGNITUDES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]   # codes 0..7 (OCP MX FP4)
+
+
+def _e2m1_by_intervals(v):
+    """Nearest E2M1 code with ties to the even code, written as the intervals
+    between neighbouring magnitudes (an independent formulation of the rule)."""
+    a = abs(v)
+    if a <= 0.25: c = 0
+    elif a < 0.75: c = 1
+    elif a <= 1.25: c = 2
+    elif a < 1.75: c = 3
+    elif a <= 2.5: c = 4
+    elif a < 3.5: c = 5
+    elif a <= 5.0: c = 6
+    else: c = 7
+    return c | (8 if np.signbit(v) else 0)
+
+
+def test_e2m1_decode_table():
+    for c in range(16):
+        mag = E2M1_MAGNITUDES[c & 7]
+        want = -mag if c & 8 else mag
+        got = oracle.e2m1_decode(c)
+        assert got == want and np.signbit(got) == bool(c & 8), c
+
+
+def test_e2m1_encode_vs_intervals():
+    rng = np.random.default_rng(23)
+    vals = [i / 64 for i in range(-384, 385)] + [-0.0, 0.0]
+    vals += list(rng.uniform(-6, 6, 4000))
+    vals += [m + d for m in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0) for d in (-1e-9, 1e-9)]
+    for v in vals:
+        assert oracle.e2m1_encode(v) == _e2m1_by_intervals(v), v
+
+
+def _e8m0_fp4_linear(amax):
+    if amax == 0:
+        return -127
+    for e in range(-127, 128):
+        if Fraction(amax) <= 6 * Fraction(2) ** e:
+            return e
+    return 127
+
+
+def test_e8m0_fp4_vs_linear_search():
+    rng = np.random.default_rng(24)
+    vals = [0.0, 6.0, 6.000001, 3.0, 2.9999998, 1.5, 1.0, 1e-45, 1e-38, 3.4e38]
+    vals += [float(np.float32(6.0 * 2.0 ** e)) for e in range(-126, 126)]
+    vals += [float(np.nextafter(np.float32(6.0 * 2.0 ** e), np.float32(np.inf)))
+             for e in range(-120, 125)]
+    vals += list((2.0 ** rng.uniform(-140, 127, 2000)).astype(np.float32).astype(float))
+    for a in vals:
+        a32 = float(np.float32(a))
+        assert oracle.e8m0_exponent_fp4(a32) == _e8m0_fp4_linear(a32), a32
+
+
+def test_mx4_blocks_golden():
+    """Hand cases of the MXFP4 block quantizer (tests/golden/mx4_blocks.json)."""
+    with open(os.path.join(GOLDEN, "mx4_blocks.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        blk = np.array(c["block"], dtype=np.float32)[None, :]
+        codes, scales = oracle.mx4_quantize(blk)
+        assert int(scales[0, 0]) == c["scale_exp"] + 127, c["name"]
+        deq = oracle.mx4_dequantize(codes, scales)[0]
+        assert np.array_equal(deq, np.array(c["values"])), c["name"]
+
+
+def test_mx4_quantize_vs_rules():
+    """Scales from the linear search, codes from the interval rule."""
+    rng = np.random.default_rng(25)
+    v = (rng.standard_normal((32, 128)) * 2.0 ** rng.integers(-20, 20, (32, 1))).astype(np.float32)
+    v[5, 32:64] = 0
+    codes, scales = oracle.mx4_quantize(v)
+    for r in range(v.shape[0]):
+        for b in range(v.shape[1] // 32):
+            blk = v[r, b * 32:(b + 1) * 32]
+            e = _e8m0_fp4_linear(float(np.max(np.abs(blk))))
+            assert scales[r, b] == e + 127
+            want = [_e2m1_by_intervals(float(x) * 2.0 ** -e) for x in blk]
+            assert list(codes[r, b * 32:(b + 1) * 32]) == want
+
+
 # ------------------------------------------------------------------ router
 
 def test_route_vs_sort_and_numpy_softmax():
@@ -399,6 +484,21 @@ def test_hand_case_hc3_bitwise_hc2():
 
 # ------------------------------------------------------------------ expert MLP
 
+def _operand_values(precision, xv, w1v, w2v, w):
+    """Operand values of x and the weights for a precision: bf16 values as they
+    are; MXFP8 activations for "mxfp8" and "mxfp4"; weights MXFP8 ("mxfp8") or
+    MXFP4 ("mxfp4"), each quantized per 32-block along K (the quantizers are
+    pinned on their own above)."""
+    if precision == "bf16":
+        return xv, w1v, w2v
+    xv = oracle.mx_dequantize(*oracle.mx_quantize(xv.astype(np.float32)))
+    q, dq = ((oracle.mx_quantize, oracle.mx_dequantize) if precision == "mxfp8"
+             else (oracle.mx4_quantize, oracle.mx4_dequantize))
+    w1v = dq(*q(w1v.reshape(-1, w.H).astype(np.float32))).reshape(w1v.shape)
+    w2v = dq(*q(w2v.reshape(-1, w.F).astype(np.float32))).reshape(w2v.shape)
+    return xv, w1v, w2v
+
+
 def _dense_mlp_fp64(x_vals, w1_vals, w2_vals, F, mx_h=False):
     """torch fp64 reference of one expert: g, u rounded to fp32, SwiGLU in fp64
     rounded to fp32, FC2 operand rounded to bf16 (torch cast) or MXFP8, FC2 in
@@ -417,7 +517,7 @@ def _dense_mlp_fp64(x_vals, w1_vals, w2_vals, F, mx_h=False):
     return (h @ w2.T).float()
 
 
-@pytest.mark.parametrize("precision", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("precision", ["bf16", "mxfp8", "mxfp4"])
 def test_expert_mlp_top1_vs_dense_torch(precision):
     """Top-1 routing with p = 1 reduces the layer to dense per-expert MLPs."""
     w = WORKLOADS["tiny"]
@@ -431,17 +531,12 @@ def test_expert_mlp_top1_vs_dense_torch(precision):
     xv = oracle.bf16_value(inp["x_bits"]).astype(np.float64)
     w1v = oracle.bf16_value(inp["w1_bits"]).astype(np.float64)
     w2v = oracle.bf16_value(inp["w2_bits"]).astype(np.float64)
-    if precision == "mxfp8":
-        xv = oracle.mx_dequantize(*oracle.mx_quantize(xv.astype(np.float32)))
-        w1v = oracle.mx_dequantize(*oracle.mx_quantize(
-            w1v.reshape(-1, w.H).astype(np.float32))).reshape(w1v.shape)
-        w2v = oracle.mx_dequantize(*oracle.mx_quantize(
-            w2v.reshape(-1, w.F).astype(np.float32))).reshape(w2v.shape)
+    xv, w1v, w2v = _operand_values(precision, xv, w1v, w2v, w)
     for e in range(w.E):
         rows = np.nonzero(ids[:, 0] == e)[0]
         if len(rows) == 0:
             continue
-        ref = _dense_mlp_fp64(xv[rows], w1v[e], w2v[e], w.F, precision == "mxfp8").numpy()
+        ref = _dense_mlp_fp64(xv[rows], w1v[e], w2v[e], w.F, precision != "bf16").numpy()
         got = out[rows]
         # independent fp64 summation orders: agree to fp32 rounding, except where a
         # rounding decision on the FC2 operand flips (rare, one operand step)
@@ -467,7 +562,7 @@ def test_gate_up_roles_and_expert_index_matter():
     assert np.linalg.norm(out_sh - out) > 0.1 * scale
 
 
-@pytest.mark.parametrize("precision", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("precision", ["bf16", "mxfp8", "mxfp4"])
 def test_forward_vs_numpy_fp64_formulation(precision):
     """Whole layer vs an independent dense fp64 formulation (k = 2, real probs)."""
     w = WORKLOADS["tiny"]
@@ -479,23 +574,18 @@ def test_forward_vs_numpy_fp64_formulation(precision):
     xv = oracle.bf16_value(inp["x_bits"]).astype(np.float64)
     w1v = oracle.bf16_value(inp["w1_bits"]).astype(np.float64)
     w2v = oracle.bf16_value(inp["w2_bits"]).astype(np.float64)
-    if precision == "mxfp8":
-        xv = oracle.mx_dequantize(*oracle.mx_quantize(xv.astype(np.float32)))
-        w1v = oracle.mx_dequantize(*oracle.mx_quantize(
-            w1v.reshape(-1, w.H).astype(np.float32))).reshape(w1v.shape)
-        w2v = oracle.mx_dequantize(*oracle.mx_quantize(
-            w2v.reshape(-1, w.F).astype(np.float32))).reshape(w2v.shape)
+    xv, w1v, w2v = _operand_values(precision, xv, w1v, w2v, w)
     ref = np.zeros((w.T, w.H))
     for t in range(w.T):
         for j in range(w.k):
             e = ids[t, j]
-            o = _dense_mlp_fp64(xv[t:t + 1], w1v[e], w2v[e], w.F, precision == "mxfp8")
+            o = _dense_mlp_fp64(xv[t:t + 1], w1v[e], w2v[e], w.F, precision != "bf16")
             ref[t] += float(probs[t, j]) * o.numpy()[0].astype(np.float64)
     rel = np.linalg.norm(out - ref) / np.linalg.norm(ref)
     assert rel < 1e-5, rel
 
 
-@pytest.mark.parametrize("name,precision", [("tiny", "bf16"), ("tiny", "mxfp8")])
+@pytest.mark.parametrize("name,precision", [("tiny", "bf16"), ("tiny", "mxfp8"), ("tiny", "mxfp4")])
 def test_forward_bitwise_equals_naive_per_token_loop(name, precision):
     """Permutation bookkeeping: permuted forward == per-token loop, bitwise."""
     w = WORKLOADS[name]
@@ -548,6 +638,19 @@ def _unswizzle_mx(codes, scales, E, N, K):
     return c, sc
 
 
+def _unswizzle_mx4(codes, scales, E, N, K):
+    """Inverse of the MXFP4 layout by reshapes: blocks [E][N/16][KS] of
+    [4 (k%128 / 32)][16 (n%16)][16 bytes], two codes per byte, low nibble first."""
+    KS = (K + 127) // 128
+    KQ = (KS + 3) // 4
+    b = codes.reshape(E, N // 16, KS, 4, 16, 16)               # e n16 step g r16 byte
+    nib = np.stack([b & 15, b >> 4], axis=-1)                   # ... byte nibble
+    c = nib.transpose(0, 1, 4, 2, 3, 5, 6).reshape(E, N, KS * 128)
+    sc = scales.reshape(E, N // 16, KQ, 4, 16, 4)
+    sc = sc.transpose(0, 1, 4, 2, 5, 3).reshape(E, N, KQ * 16)
+    return c, sc
+
+
 def test_pack_bf16_layout_definition():
     """Unswizzled by reshapes, the packed buffer is the interleaved weight."""
     E, H, F = 2, 64, 96
@@ -585,6 +688,32 @@ def test_pack_mxfp8_layout_definition(H, F):
                               buf[off[scales_at]:off[scales_at] + ns], E, N, K)
         logical = _interleave(w, F) if fc1 else w
         qc, qs = oracle.mx_quantize(oracle.bf16_value(logical).reshape(-1, K))
+        assert np.array_equal(c[:, :, :K].reshape(-1, K), qc)
+        assert np.array_equal(sc[:, :, :K // 32].reshape(-1, K // 32), qs)
+        assert np.all(c[:, :, K:] == 0) and np.all(sc[:, :, K // 32:] == 127)
+
+
+@pytest.mark.parametrize("H,F", [(256, 128), (96, 160)])
+def test_pack_mxfp4_layout_definition(H, F):
+    """MXFP4 codes and scales, unswizzled, are the per-row E2M1 quantization of
+    the interleaved bf16 weight; padding past K is code 0 and scale 127."""
+    E = 2
+    rng = np.random.default_rng(5)
+    w1 = oracle.bf16_bits(rng.standard_normal((E, 2 * F, H)).astype(np.float32))
+    w2 = oracle.bf16_bits(rng.standard_normal((E, H, F)).astype(np.float32))
+    buf = oracle.pack(E, H, F, w1, w2, "mxfp4")
+    off = oracle.pack_mx_offsets(E, H, F, "mxfp4")
+    assert len(buf) == off[4] == oracle.pack_bytes(E, H, F, "mxfp4")
+    for (codes_at, scales_at, w, N, K, fc1) in ((0, 2, w1, 2 * F, H, True),
+                                                (1, 3, w2, H, F, False)):
+        KS = (K + 127) // 128
+        KQ = (KS + 3) // 4
+        nc = E * (N // 16) * KS * 1024
+        ns = E * (N // 16) * KQ * 256
+        c, sc = _unswizzle_mx4(buf[off[codes_at]:off[codes_at] + nc],
+                               buf[off[scales_at]:off[scales_at] + ns], E, N, K)
+        logical = _interleave(w, F) if fc1 else w
+        qc, qs = oracle.mx4_quantize(oracle.bf16_value(logical).reshape(-1, K))
         assert np.array_equal(c[:, :, :K].reshape(-1, K), qc)
         assert np.array_equal(sc[:, :, :K // 32].reshape(-1, K // 32), qs)
         assert np.all(c[:, :, K:] == 0) and np.all(sc[:, :, K // 32:] == 127)

@@ -18,6 +18,9 @@ synthetic, there are no trained weights or prompts here):
   bounded_decode  buffer of 65,536 token rows, 512 live, hidden 2688,
                   FFN 1856, 128 experts, top-6, bf16; rows past the live count
                   are NaN
+  decode_mxfp4    the decode shapes with MXFP4 weights (E2M1 + E8M0 per 32)
+                  and MXFP8 activations
+  mxfp4_16k       the 16K-token shapes with MXFP4 weights and MXFP8 activations
 
 Draw order for one seed (one CPU torch.Generator): x ~ N(0,1) [T_cap, H],
 W1 ~ N(0, 0.02^2) [E, 2F, H] (gate rows first), W2 ~ N(0, 0.02^2) [E, H, F],
@@ -45,7 +48,7 @@ class Workload:
     F: int
     E: int
     k: int
-    precision: str    # "bf16" | "mxfp8"
+    precision: str    # "bf16" | "mxfp8" | "mxfp4"
     bias: bool = False
 
     @property
@@ -67,6 +70,8 @@ WORKLOADS = {
     "mxfp8_16k": Workload("mxfp8_16k", 16384, 16384, 2048, 1024, 128, 8, "mxfp8"),
     "bf16_16k": Workload("bf16_16k", 16384, 16384, 2048, 1024, 128, 8, "bf16"),
     "bounded_decode": Workload("bounded_decode", 512, 65536, 2688, 1856, 128, 6, "bf16"),
+    "decode_mxfp4": Workload("decode_mxfp4", 256, 256, 2048, 1024, 64, 6, "mxfp4"),
+    "mxfp4_16k": Workload("mxfp4_16k", 16384, 16384, 2048, 1024, 128, 8, "mxfp4"),
 }
 
 
