@@ -33,7 +33,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "routed MoE fwd tokens/s + TFLOP/s (% MFMA peak; % HBM peak at decode)"
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0}
+# dense MFMA peaks; MXFP4 weights meet MXFP8 activations, so its MFMA runs at the
+# fp8 rate (the 10.1 PF/s fp4 figure is for 4-bit operands on both sides)
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "mxfp4": 5000.0}
+MFMA_BOUND = ("bf16_16k", "mxfp8_16k", "mxfp4_16k")
 MALL_BYTES = 256 << 20
 
 
@@ -98,13 +101,14 @@ def alg_bytes(w, precision: str, touched: int, combine: str = "fp32") -> dict:
     x row once, routed rows written/read once where a stage must (FC1 writes
     the SwiGLU row, FC2 reads it), ids/probs once, the output once (fp32 [T, H],
     bf16 [T, H] or fp32 [T, k, H] by combine)."""
-    wb = 2 if precision == "bf16" else 1
-    sb = 0 if precision == "bf16" else 1.0 / 32          # E8M0 bytes per element
+    # weight and activation (SwiGLU row) bytes per element, E8M0 scales included
+    ww = {"bf16": 2.0, "mxfp8": 1 + 1.0 / 32, "mxfp4": 0.5 + 1.0 / 32}[precision]
+    wa = 2.0 if precision == "bf16" else 1 + 1.0 / 32
     H, F, T, R = w.H, w.F, w.T, w.R
-    fc1 = touched * 2 * F * H * (wb + sb) + T * H * 2 + R * F * (wb + sb)
-    fc2 = touched * H * F * (wb + sb) + R * F * (wb + sb) + R * H * 4
+    fc1 = touched * 2 * F * H * ww + T * H * 2 + R * F * wa
+    fc2 = touched * H * F * ww + R * F * wa + R * H * 4
     out_b = {"fp32": T * H * 4, "bf16": T * H * 2, "rows": R * H * 4}[combine]
-    step = touched * 3 * F * H * (wb + sb) + T * H * 2 + T * w.k * 8 + out_b
+    step = touched * 3 * F * H * ww + T * H * 2 + T * w.k * 8 + out_b
     return dict(fc1=fc1, fc2=fc2, step=step)
 
 
@@ -168,7 +172,7 @@ def main():
 
     w = WORKLOADS[a.workload]
     dev = torch.device("cuda:0")
-    inp = make_inputs(w, seed=a.seed, outliers=(w.precision == "mxfp8"))
+    inp = make_inputs(w, seed=a.seed, outliers=(w.precision != "bf16"))
     bf = lambda arr: torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(
         torch.bfloat16).to(dev)
     x = bf(inp["x_bits"])
@@ -252,7 +256,7 @@ def main():
     flops = w.flops()
     tokens_s = w.T / (ms_step * 1e-3)
     tflops = flops / (ms_step * 1e-3) / 1e12
-    if w.precision == "mxfp8" or w.name in ("bf16_16k",):
+    if w.name in MFMA_BOUND:
         fc1_flops = 4.0 * w.H * w.F * w.R
         roof = dict(bound="mfma", achieved=fc1_flops / (fc1_us * 1e-6) / 1e12,
                     peak=MFMA_PEAK_TFLOPS[w.precision], unit="TFLOP/s")
@@ -262,8 +266,9 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     # the FC1 + SwiGLU stage is one launch; its tiles run on the LDS-staged loop
     # (experts with more than 128 rows) or the streaming loop (the others)
-    kind = "bf16" if w.precision == "bf16" else "mxfp8"
-    roof["kernel"] = f"moe::gemm_{kind}_kernel<true>"
+    roof["kernel"] = {"bf16": "moe::gemm_bf16_kernel<true>",
+                      "mxfp8": "moe::gemm_mxfp8_kernel<true, false>",
+                      "mxfp4": "moe::gemm_mxfp8_kernel<true, true>"}[w.precision]
     roof["tiles"] = "lds-staged" if int(loads.min()) > 128 else (
         "streaming" if int(loads.max()) <= 128 else "lds-staged + streaming")
     roof["kernel_us"] = fc1_us

@@ -56,7 +56,7 @@ extern "C" {
 
 typedef struct moe_ctx* moe_handle;
 
-typedef enum { MOE_BF16 = 0, MOE_MXFP8 = 1 } moe_precision;
+typedef enum { MOE_BF16 = 0, MOE_MXFP8 = 1, MOE_MXFP4 = 2 } moe_precision;
 
 typedef enum {
     MOE_OK = 0,
@@ -75,9 +75,13 @@ typedef enum {
 /* Create a handle for E experts, hidden size H, expert FFN size F, top-k.
  * Checks (Megatron-LM PR #7830, construction-time validation; cudnn-frontend
  * PR #448, MXFP8 block of 32): 1 <= E <= 1024; 1 <= topk <= min(E, 16);
- * H and F positive multiples of 32 (the interleave block and the MXFP8
- * block); precision MOE_BF16 or MOE_MXFP8, else MOE_ERR_UNSUPPORTED.  Host
- * only: no device work; the device is the one current at the first launch. */
+ * H and F positive multiples of 32 (the interleave block and the MX
+ * block); precision MOE_BF16, MOE_MXFP8 or MOE_MXFP4, else
+ * MOE_ERR_UNSUPPORTED.  MOE_MXFP4: weights in E2M1 (the OCP MX 4-bit float)
+ * with one E8M0 scale per 32 elements of K, activations and the SwiGLU rows
+ * in MXFP8 as with MOE_MXFP8 (the CDNA4-native counterpart of a 4-bit-weight,
+ * 8-bit-activation expert GEMM).  Host only: no device work; the device is
+ * the one current at the first launch. */
 moe_status moe_create(int E, int H, int F, int topk, int precision, moe_handle* out);
 
 /* Free the handle (host state only).  NULL is ignored. */
@@ -106,6 +110,12 @@ size_t moe_weight_bytes(moe_handle h);
  *       ((e*(N/16) + n/16)*KQ + (b/4)/4)*256 + ((b%4)*16 + n%16)*4 + (b/4)%4;
  *     positions past K hold code 0 and scale 127.  Scale = power-of-two
  *     ceiling of the block's max magnitude / 448 (so no code saturates).
+ *   kbuf layout (mxfp4): as mxfp8, with one 1 KB code block per 16 rows x
+ *     128 K: code (e, n, k) in byte
+ *       ((e*(N/16) + n/16)*KS + k/128)*1024 + ((k%128)/32*16 + n%16)*16 + (k%32)/2,
+ *     the low nibble for even k; scales as mxfp8 with the scale =
+ *     power-of-two ceiling of the block's max magnitude / 6, codes rounded to
+ *     the nearest E2M1 value with ties to the even code.
  * The handle remembers kbuf: every later forward reads it.  Calling again
  * (same or another buffer) is the refit; forwards enqueued before it on the
  * same stream read the old contents.  w1/w2 may be freed once the work on

@@ -25,8 +25,8 @@ __all__ = ["MoE", "lib", "LIB_PATH", "MoEError", "DEVERR_BAD_EXPERT_ID", "DEVERR
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-MOE_BF16, MOE_MXFP8 = 0, 1
-_PRECISION = {"bf16": MOE_BF16, "mxfp8": MOE_MXFP8}
+MOE_BF16, MOE_MXFP8, MOE_MXFP4 = 0, 1, 2
+_PRECISION = {"bf16": MOE_BF16, "mxfp8": MOE_MXFP8, "mxfp4": MOE_MXFP4}
 DEVERR_BAD_EXPERT_ID = 1
 DEVERR_DUP_EXPERT_ID = 2
 DEVERR_LIVE_ABOVE_CAP = 4
@@ -119,7 +119,7 @@ class MoE:
 
     def __init__(self, E: int, H: int, F: int, topk: int, precision: str = "bf16"):
         if precision not in _PRECISION:
-            raise NotImplementedError(f"precision {precision!r} is not supported (bf16, mxfp8)")
+            raise NotImplementedError(f"precision {precision!r} is not supported (bf16, mxfp8, mxfp4)")
         h = _P()
         _check(lib().moe_create(E, H, F, topk, _PRECISION[precision], ctypes.byref(h)),
                "moe_create")

@@ -56,6 +56,32 @@ __device__ __forceinline__ int e8m0_exponent(float amax)
     return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
+// E8M0 exponent of an MXFP4 block: the smallest e with amax <= 6 * 2^e (the
+// power-of-two ceiling of amax / 6), clamped to [-127, 127]; amax == 0 (or an
+// fp32 subnormal, whose block then scales to below 2^-126 * 2^127 = 2) gives
+// -127.  From the fp32 bits: amax = 2^E (1 + m) needs e = E - 2 when
+// 1 + m <= 1.5 and E - 1 otherwise.
+__device__ __forceinline__ int e8m0_exponent_fp4(float amax)
+{
+    uint32_t u = __float_as_uint(amax) & 0x7fffffffu;
+    int ef = (int)(u >> 23);
+    if (ef == 0) return -127;
+    int e = ef - 127 - 2 + ((u & 0x7fffffu) > 0x400000u ? 1 : 0);
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// fp32 -> E2M1 code (OCP MX FP4: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) for
+// |v| <= 6, round to nearest with ties to the even code; the sign is kept.
+// The intervals between neighbouring magnitudes, with each midpoint going to
+// the neighbour whose mantissa bit is 0.
+__device__ __forceinline__ uint32_t f32_to_e2m1(float v)
+{
+    const float a = fabsf(v);
+    const uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                     : a <= 2.5f  ? 4u : a < 3.5f  ? 5u : a <= 5.0f  ? 6u : 7u;
+    return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
 // fp32 -> E4M3FN codes with the hardware converter (v_cvt_pk_fp8_f32): round
 // to nearest even, the OCP E4M3FN encoding.  Callers pass finite values with
 // |v| <= 448, which the MX block scale guarantees; on that range the converter

@@ -21,16 +21,24 @@
 // (q < 2) or second halves (q >= 2) of lane groups 2 (q % 2) and 2 (q % 2) + 1.
 // Work decomposition is the same as the bf16 streaming kernel: persistent
 // grid over (M tile, N tile), 4 waves x 64 columns, up to 64 rows per M tile.
+//
+// W4: MXFP4 weights (E2M1 codes with one E8M0 scale per 32 elements of K)
+// against the same MXFP8 activations: the B operand of a 128-wide K step is
+// then 16 bytes per lane, lane l holding K = 32 (l / 16) + [0, 32) of column
+// l % 16 (two codes per byte, the lower K in the low nibble; measured on the
+// MI355X), so a block of 16 columns is 1 KB; the scale of lane l covers the
+// same 32-block (l / 16).  Same contract, with the E2M1 B format.
 #pragma once
 
 #include "gemm_args.h"
 
 namespace moe {
 
-template <bool FC1, int NG>
+template <bool FC1, int NG, bool W4>
 __device__ __forceinline__ void mx_tile_body(const MxGemmArgs& g, int e, int row0, int rows,
                                              int cb)
 {
+    constexpr int kBlk = W4 ? 1024 : 2048;    // bytes of a 16-column x 128-K weight block
     const int lane = threadIdx.x & 63;
     const int r16 = lane & 15, kg = lane >> 4;
     const int K = g.K, KB = K / 32;
@@ -45,9 +53,10 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs& g, int e, int row
         ap[rg] = g.A + arow * K + 16 * kg;
         as[rg] = g.As + arow * KB + kg;
     }
-    // B fragments: 2 KB blocks of 16 rows x 128 K, [expert][row / 16][k / 128],
-    // each block two 1 KB halves in lane order (16 codes per lane); scales in
-    // 256-byte groups of 4 K-steps, one dword per lane (byte = step % 4).
+    // B fragments: 2 KB (MXFP4: 1 KB) blocks of 16 rows x 128 K,
+    // [expert][row / 16][k / 128], in lane order (MXFP8: two 1 KB halves, 16
+    // codes per lane each); scales in 256-byte groups of 4 K-steps, one dword
+    // per lane (byte = step % 4).
     const int nt16 = g.N / 16, KS = (K + 127) / 128, KQ = (KS + 3) / 4;
     const uint8_t* bp[4];
     const uint32_t* bs[4];
@@ -56,7 +65,7 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs& g, int e, int row
         int c16 = cb * 4 + ct;
         if (c16 >= nt16) c16 = nt16 - 1;
         const int64_t blk = (int64_t)e * nt16 + c16;
-        bp[ct] = g.W + blk * KS * 2048 + 16 * lane;
+        bp[ct] = g.W + blk * KS * kBlk + 16 * lane;
         bs[ct] = (const uint32_t*)(g.Ws + blk * KQ * 256) + lane;
     }
     f32x4 acc[NG][4];
@@ -84,20 +93,27 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs& g, int e, int row
         const int step = k0 / 128;
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
-            // padded blocks hold zero codes and scale 2^0, so no K check here
+            // padded blocks hold zero codes and scale 2^0, so no K check here;
             // weights are read once per tile (non-temporal, see the bf16 kernel)
-            uint4 lo = load_stream16(bp[ct] + step * 2048);
-            uint4 hi = load_stream16(bp[ct] + step * 2048 + 1024);
-            b[ct] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                          (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            if constexpr (W4) {
+                // the upper half of an E2M1 operand is not read by the MFMA
+                const uint4 lo = load_stream16(bp[ct] + step * 1024);
+                b[ct] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
+            } else {
+                const uint4 lo = load_stream16(bp[ct] + step * 2048);
+                const uint4 hi = load_stream16(bp[ct] + step * 2048 + 1024);
+                b[ct] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                              (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            }
             sb[ct] = (int)((bs[ct][(step >> 2) * 64] >> (8 * (step & 3))) & 0xffu);
         }
 #pragma unroll
         for (int rg = 0; rg < NG; ++rg)
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct)
+                // A format 0 (E4M3); B format 0 (E4M3) or 4 (E2M1)
                 acc[rg][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    a[rg], b[ct], acc[rg][ct], 0, 0, 0, sa[rg], 0, sb[ct]);
+                    a[rg], b[ct], acc[rg][ct], 0, W4 ? 4 : 0, 0, sa[rg], 0, sb[ct]);
     }
 
     if constexpr (FC1) {
@@ -154,7 +170,7 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs& g, int e, int row
 // 64-row tiles of the streaming table, and the large experts' 256-row tiles as
 // four 64-row tiles each when the LDS-staged loop does not apply (K not a
 // multiple of 128).
-template <bool FC1>
+template <bool FC1, bool W4>
 __device__ __forceinline__ void mx_stream_tiles(const MxGemmArgs& g, int worker, int nworkers, int wid)
 {
     const int n_small = g.hdr->n_tiles;
@@ -179,10 +195,10 @@ __device__ __forceinline__ void mx_stream_tiles(const MxGemmArgs& g, int worker,
         if (cb >= n_cb || rows <= 0) continue;
         const int ng = (rows + 15) >> 4;
         switch (ng) {
-            case 1: mx_tile_body<FC1, 1>(g, e, row0, rows, cb); break;
-            case 2: mx_tile_body<FC1, 2>(g, e, row0, rows, cb); break;
-            case 3: mx_tile_body<FC1, 3>(g, e, row0, rows, cb); break;
-            default: mx_tile_body<FC1, 4>(g, e, row0, rows, cb); break;
+            case 1: mx_tile_body<FC1, 1, W4>(g, e, row0, rows, cb); break;
+            case 2: mx_tile_body<FC1, 2, W4>(g, e, row0, rows, cb); break;
+            case 3: mx_tile_body<FC1, 3, W4>(g, e, row0, rows, cb); break;
+            default: mx_tile_body<FC1, 4, W4>(g, e, row0, rows, cb); break;
         }
     }
 }

@@ -23,6 +23,9 @@ hipError_t launch_pack_bf16(const uint16_t* w1, const uint16_t* w2, uint8_t* kbu
 hipError_t launch_pack_mxfp8(const uint16_t* w1, const uint16_t* w2, uint8_t* kbuf, int E, int H,
                              int F, int num_cu, hipStream_t s);
 void mx_section_bytes(int E, int H, int F, size_t* c1, size_t* c2, size_t* s1, size_t* s2);
+hipError_t launch_pack_mxfp4(const uint16_t* w1, const uint16_t* w2, uint8_t* kbuf, int E, int H,
+                             int F, int num_cu, hipStream_t s);
+void mx4_section_bytes(int E, int H, int F, size_t* c1, size_t* c2, size_t* s1, size_t* s2);
 hipError_t launch_quant_x(const uint16_t* x, int64_t T_cap, const int32_t* live, int H,
                           uint8_t* codes, uint8_t* scales, int num_cu, hipStream_t s);
 }  // namespace moe
@@ -31,7 +34,7 @@ hipError_t launch_quant_x(const uint16_t* x, int64_t T_cap, const int32_t* live,
 
 namespace moe {
 hipError_t launch_gemm_bf16(bool fc1, const GemmArgs& g, int num_cu, hipStream_t s);
-hipError_t launch_gemm_mxfp8(bool fc1, const MxGemmArgs& g, int num_cu, hipStream_t s);
+hipError_t launch_gemm_mxfp8(bool fc1, bool w4, const MxGemmArgs& g, int num_cu, hipStream_t s);
 }  // namespace moe
 
 using namespace moe;
@@ -137,9 +140,9 @@ moe_status moe_create(int E, int H, int F, int topk, int precision, moe_handle* 
 {
     if (!out) return fail(MOE_ERR_INVALID_ARG, "moe_create: out is NULL");
     *out = nullptr;
-    if (precision != MOE_BF16 && precision != MOE_MXFP8)
-        return fail(MOE_ERR_UNSUPPORTED, "moe_create: precision %d is not supported (bf16=0, mxfp8=1)",
-                    precision);
+    if (precision != MOE_BF16 && precision != MOE_MXFP8 && precision != MOE_MXFP4)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "moe_create: precision %d is not supported (bf16=0, mxfp8=1, mxfp4=2)", precision);
     if (E < 1 || E > kMaxExperts)
         return fail(MOE_ERR_INVALID_ARG, "moe_create: E=%d outside [1, %d]", E, kMaxExperts);
     if (topk < 1 || topk > kMaxTopk || topk > E)
@@ -163,7 +166,10 @@ size_t moe_weight_bytes(moe_handle h)
     size_t n1 = (size_t)h->E * 2 * h->F * h->H, n2 = (size_t)h->E * h->H * h->F;
     if (h->precision == MOE_BF16) return 2 * (n1 + n2);
     size_t c1, c2, s1, s2;
-    mx_section_bytes(h->E, h->H, h->F, &c1, &c2, &s1, &s2);
+    if (h->precision == MOE_MXFP4)
+        mx4_section_bytes(h->E, h->H, h->F, &c1, &c2, &s1, &s2);
+    else
+        mx_section_bytes(h->E, h->H, h->F, &c1, &c2, &s1, &s2);
     return c1 + c2 + s1 + s2;
 }
 
@@ -185,11 +191,13 @@ moe_status moe_load_weights(moe_handle h, const void* w1, const void* w2, void* 
                     moe_weight_bytes(h));
     moe_status st = ensure_device(h);
     if (st != MOE_OK) return st;
-    hipError_t e = h->precision == MOE_BF16
-                       ? launch_pack_bf16((const uint16_t*)w1, (const uint16_t*)w2, (uint8_t*)kbuf,
-                                          h->E, h->H, h->F, h->num_cu, stream)
-                       : launch_pack_mxfp8((const uint16_t*)w1, (const uint16_t*)w2, (uint8_t*)kbuf,
-                                           h->E, h->H, h->F, h->num_cu, stream);
+    const uint16_t* a = (const uint16_t*)w1;
+    const uint16_t* b = (const uint16_t*)w2;
+    uint8_t* kb = (uint8_t*)kbuf;
+    hipError_t e =
+        h->precision == MOE_BF16    ? launch_pack_bf16(a, b, kb, h->E, h->H, h->F, h->num_cu, stream)
+        : h->precision == MOE_MXFP8 ? launch_pack_mxfp8(a, b, kb, h->E, h->H, h->F, h->num_cu, stream)
+                                    : launch_pack_mxfp4(a, b, kb, h->E, h->H, h->F, h->num_cu, stream);
     if (e != hipSuccess) return hip_fail(e, "moe_load_weights: launch");
     h->kbuf = (const uint8_t*)kbuf;
     return MOE_OK;
@@ -288,8 +296,13 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
         if ((e = mark(h, 4, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     } else {
+        // MXFP8, or MXFP4 weights with MXFP8 activations (streaming tiles only)
+        const bool w4 = h->precision == MOE_MXFP4;
         size_t b1, b2, b3, b4;
-        mx_section_bytes(E, H, F, &b1, &b2, &b3, &b4);
+        if (w4)
+            mx4_section_bytes(E, H, F, &b1, &b2, &b3, &b4);
+        else
+            mx_section_bytes(E, H, F, &b1, &b2, &b3, &b4);
         const uint8_t* c1 = h->kbuf;
         const uint8_t* c2 = c1 + b1;
         const uint8_t* s1 = c2 + b2;
@@ -314,8 +327,8 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         g1.K = H;
         g1.topk = h->k;
         g1.n_tiles_n = ((2 * F / 64) + 3) / 4;
-        g1.stream_big = H % 128 != 0;
-        e = launch_gemm_mxfp8(true, g1, h->num_cu, stream);
+        g1.stream_big = w4 || H % 128 != 0;
+        e = launch_gemm_mxfp8(true, w4, g1, h->num_cu, stream);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC1 launch");
         if ((e = mark(h, 3, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
         MxGemmArgs g2 = g1;
@@ -329,8 +342,8 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         g2.N = H;
         g2.K = F;
         g2.n_tiles_n = ((H + 63) / 64 + 3) / 4;
-        g2.stream_big = F % 128 != 0;
-        e = launch_gemm_mxfp8(false, g2, h->num_cu, stream);
+        g2.stream_big = w4 || F % 128 != 0;
+        e = launch_gemm_mxfp8(false, w4, g2, h->num_cu, stream);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
         if ((e = mark(h, 4, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     }

@@ -22,6 +22,10 @@
 //          [expert][n/16][k/128]; E8M0 scales 4 K-steps per lane dword:
 //          256 B groups [expert][n/16][k/512], byte (k/128)%4 of lane
 //          16 * ((k/32)%4) + n%16.
+//   MXFP4: 16 rows x 128 K per 1 KB block, lane = 16 * (k%128 / 32) + n%16,
+//          32 E2M1 codes per lane as 16 bytes (the lower K in the low nibble);
+//          blocks [expert][n/16][k/128]; scales as MXFP8.  The scale is the
+//          power-of-two ceiling of the block's max magnitude / 6.
 #include "common.h"
 
 namespace moe {
@@ -131,6 +135,64 @@ __global__ void __launch_bounds__(256) pack_mx_kernel(const uint16_t* __restrict
     }
 }
 
+// MXFP4 weights, tiled layout.  One thread quantizes one 32-element block
+// (row n, block q of K) and writes its 32 codes as the 16 bytes of lane
+// 16 (q % 4) + n % 16 of the row's 1 KB block of K step q / 4; blocks past
+// K/32 (the padding of the last step) get zero codes and scale 127.
+__global__ void __launch_bounds__(256) pack_mx4_kernel(const uint16_t* __restrict__ src,
+                                                       uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales, int E, int N,
+                                                       int K, int F, int fc1)
+{
+    const int64_t KS = (K + 127) / 128, KQ = (KS + 3) / 4, nt = N / 16;
+    const int64_t nbk = KQ * 16;                  // padded 32-blocks per row
+    const int64_t n_items = (int64_t)E * N * nbk;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_items;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t q = i % nbk;
+        const int64_t row = i / nbk;               // e * N + n
+        const int64_t e = row / N, n = row - e * N;
+        const int64_t n16 = n >> 4, r16 = n & 15;
+        const int64_t step = q >> 2, kg = q & 3;
+        uint8_t* sc = scales + ((e * nt + n16) * KQ + (step >> 2)) * 256 +
+                      ((kg * 16 + r16) * 4) + (step & 3);
+        uint4* dst = (uint4*)(codes + ((e * nt + n16) * KS + step) * 1024 + (kg * 16 + r16) * 16);
+        if (q >= K / 32) {
+            *sc = 127;
+            if (step < KS) *dst = make_uint4(0, 0, 0, 0);
+            continue;
+        }
+        const int64_t srow = fc1 ? fc1_src_row(n, F) : n;
+        const uint4* s4 = (const uint4*)(src + (e * N + srow) * K + q * 32);
+        uint4 v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = s4[j];
+        const uint32_t* w = (const uint32_t*)v;
+        float f[32];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            f[2 * j] = bf16_bits_to_f32(w[j] & 0xffffu);
+            f[2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(f[j]));
+        const int e4 = e8m0_exponent_fp4(amax);
+        // 2^-e4 exactly; 2^-127 is an fp32 subnormal
+        const float inv = e4 == 127 ? __uint_as_float(1u << 22) : __uint_as_float((uint32_t)(127 - e4) << 23);
+        uint32_t out[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) word |= f32_to_e2m1(f[8 * j + t] * inv) << (4 * t);
+            out[j] = word;
+        }
+        *dst = make_uint4(out[0], out[1], out[2], out[3]);
+        *sc = (uint8_t)(e4 + 127);
+    }
+}
+
 // K2: x rows < live quantized per 32-block of H.  A lane converts 8 elements
 // (one 16-byte load, one 8-byte store); the 4 lanes of a quad hold one
 // 32-block and exchange their partial amax with two DPP steps (quad_perm
@@ -214,6 +276,34 @@ void mx_section_bytes(int E, int H, int F, size_t* c1, size_t* c2, size_t* s1, s
     *c2 = up256(codes(H, F));
     *s1 = up256(scl(2 * F, H));
     *s2 = up256(scl(H, F));
+}
+
+// Section sizes of the MXFP4 buffer (codes and scales of FC1, then FC2).
+void mx4_section_bytes(int E, int H, int F, size_t* c1, size_t* c2, size_t* s1, size_t* s2)
+{
+    auto codes = [&](int64_t N, int64_t K) { return (size_t)E * (N / 16) * ((K + 127) / 128) * 1024; };
+    auto scl = [&](int64_t N, int64_t K) {
+        int64_t KS = (K + 127) / 128;
+        return (size_t)E * (N / 16) * ((KS + 3) / 4) * 256;
+    };
+    *c1 = up256(codes(2 * F, H));
+    *c2 = up256(codes(H, F));
+    *s1 = up256(scl(2 * F, H));
+    *s2 = up256(scl(H, F));
+}
+
+hipError_t launch_pack_mxfp4(const uint16_t* w1, const uint16_t* w2, uint8_t* kbuf, int E, int H,
+                             int F, int num_cu, hipStream_t s)
+{
+    size_t c1, c2, s1, s2;
+    mx4_section_bytes(E, H, F, &c1, &c2, &s1, &s2);
+    uint8_t* pc1 = kbuf;
+    uint8_t* pc2 = pc1 + c1;
+    uint8_t* ps1 = pc2 + c2;
+    uint8_t* ps2 = ps1 + s1;
+    hipLaunchKernelGGL(pack_mx4_kernel, dim3(num_cu * 8), dim3(256), 0, s, w1, pc1, ps1, E, 2 * F, H, F, 1);
+    hipLaunchKernelGGL(pack_mx4_kernel, dim3(num_cu * 8), dim3(256), 0, s, w2, pc2, ps2, E, H, F, F, 0);
+    return hipGetLastError();
 }
 
 hipError_t launch_pack_mxfp8(const uint16_t* w1, const uint16_t* w2, uint8_t* kbuf, int E, int H,

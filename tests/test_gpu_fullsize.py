@@ -28,13 +28,14 @@ def _sample(T, n=24, seed=3):
     return np.array(sorted(pick), dtype=np.int64)
 
 
-@pytest.mark.parametrize("name", ["decode", "logprob", "mxfp8_16k", "bf16_16k", "bounded_decode"])
+@pytest.mark.parametrize("name", ["decode", "logprob", "mxfp8_16k", "bf16_16k", "bounded_decode",
+                                  "decode_mxfp4", "mxfp4_16k"])
 def test_full_size(name):
     from swiglu_expert_mlp_amd import MoE
     w = WORKLOADS[name]
     print(f"[full-size] {name}: T={w.T} T_cap={w.T_cap} H={w.H} F={w.F} E={w.E} k={w.k} "
           f"{w.precision}", flush=True)
-    c = Case(w, seed=11, outliers=w.precision == "mxfp8")
+    c = Case(w, seed=11, outliers=w.precision != "bf16")
     m = MoE(w.E, w.H, w.F, w.k, w.precision)
     w1, w2 = c.weights_dev()
     m.load_weights(w1, w2)

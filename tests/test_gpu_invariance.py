@@ -30,13 +30,14 @@ INV = {
     "logprob_T300": WORKLOADS["logprob"].with_tokens(300),
     "mxfp8_T300": WORKLOADS["mxfp8_16k"].with_tokens(300),
     "odd_mxfp8_T300": Workload("odd_mxfp8", 300, 300, 96, 160, 5, 3, "mxfp8"),
+    "mxfp4_T300": WORKLOADS["mxfp4_16k"].with_tokens(300),
 }
 _cases = {}
 
 
 def case(name):
     if name not in _cases:
-        _cases[name] = Case(INV[name], seed=12, outliers=INV[name].precision == "mxfp8")
+        _cases[name] = Case(INV[name], seed=12, outliers=INV[name].precision != "bf16")
     return _cases[name]
 
 
@@ -102,7 +103,7 @@ def test_streaming_and_lds_staged_gemms_agree_bitwise(name):
         assert np.array_equal(bits(part), wide[t0:t0 + 128]), f"tokens {t0}.."
 
 
-@pytest.mark.parametrize("name", ["decode_T300", "mxfp8_T300"])
+@pytest.mark.parametrize("name", ["decode_T300", "mxfp8_T300", "mxfp4_T300"])
 def test_capacity_and_live_count_invariance(name):
     """Same tokens: capacity T vs 4T (rows past live are NaN), and live counts
     T, 171, 1, 0 at a fixed capacity give the same bits for the live tokens and
@@ -127,7 +128,7 @@ def test_capacity_and_live_count_invariance(name):
         assert np.all(got[live:] == SENTINEL_BITS), live
 
 
-@pytest.mark.parametrize("name", ["decode_T300", "mxfp8_T300"])
+@pytest.mark.parametrize("name", ["decode_T300", "mxfp8_T300", "mxfp4_T300"])
 def test_token_order_invariance(name):
     c, m = case(name), handle(name)
     x, ids, probs = c.dev()
@@ -212,7 +213,7 @@ def test_two_handles_are_independent():
     assert not np.array_equal(ra, rb)
 
 
-@pytest.mark.parametrize("precision", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("precision", ["bf16", "mxfp8", "mxfp4"])
 def test_contract_violations_flagged_and_match_oracle(precision):
     """An out-of-range id drops that route, a repeated id drops the repeat, and
     both set their bit; live above capacity is clamped, below zero writes

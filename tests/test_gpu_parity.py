@@ -52,6 +52,11 @@ SMALL = {
     # MXFP8 experts past 128 rows with K a multiple of 128 (LDS-staged kernel):
     # ragged 256-row tiles, a partial 256-column tile, 2 and 3 K steps
     "mx_big": Workload("mx_big", 600, 600, 256, 384, 4, 2, "mxfp8"),
+    # MXFP4 weights (streaming tiles for every expert size)
+    "decode_mx4_T64": WORKLOADS["decode_mxfp4"].with_tokens(64),
+    "mx4_T96": WORKLOADS["mxfp4_16k"].with_tokens(96),
+    "odd_mxfp4": Workload("odd_mxfp4", 77, 80, 96, 160, 5, 3, "mxfp4"),
+    "mx4_big": Workload("mx4_big", 600, 600, 256, 384, 4, 2, "mxfp4"),
 }
 
 _cases = {}
@@ -60,7 +65,7 @@ _cases = {}
 def get_case(name, seed=11):
     key = (name, seed)
     if key not in _cases:
-        _cases[key] = Case(SMALL[name], seed=seed, outliers=SMALL[name].precision == "mxfp8")
+        _cases[key] = Case(SMALL[name], seed=seed, outliers=SMALL[name].precision != "bf16")
     return _cases[key]
 
 
@@ -86,7 +91,7 @@ def _hand_cases():
         return json.load(f)["cases"]
 
 
-@pytest.mark.parametrize("precision", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("precision", ["bf16", "mxfp8", "mxfp4"])
 @pytest.mark.parametrize("c", _hand_cases(), ids=lambda c: c["name"])
 def test_hand_cases_exact(c, precision):
     from test_oracle_pins import hand_case_arrays
@@ -100,7 +105,7 @@ def test_hand_cases_exact(c, precision):
                 live_tensor(c["live"]), out=out, ws=ws)
     got = out.cpu().numpy()
     # the hand-case operands (one-hot x, small integers, powers of two, 32) are
-    # exact in E4M3 with their block scales too, so both precisions are exact
+    # exact in E4M3 and E2M1 with their block scales too, so every precision is exact
     for t, row in enumerate(c["expected"]):
         if row is None:
             assert np.all(got[t].view(np.uint32) == SENTINEL_BITS), f"row {t} past live written"
@@ -111,7 +116,7 @@ def test_hand_cases_exact(c, precision):
 
 # ------------------------------------------------------------------ packer
 
-@pytest.mark.parametrize("precision", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("precision", ["bf16", "mxfp8", "mxfp4"])
 @pytest.mark.parametrize("name", ["tiny", "odd_bf16", "bounded_T40_cap512"])
 def test_pack_bytes_bitwise(name, precision):
     c = get_case(name)
@@ -129,9 +134,10 @@ def test_pack_bytes_bitwise(name, precision):
     if precision == "bf16":
         sections = [(0, 2 * (n1 + n2))]
     else:
-        off = oracle.pack_mx_offsets(w.E, w.H, w.F)
+        off = oracle.pack_mx_offsets(w.E, w.H, w.F, precision)
         KS = lambda K: (K + 127) // 128
-        sizes = [w.E * (2 * w.F // 16) * KS(w.H) * 2048, w.E * (w.H // 16) * KS(w.F) * 2048,
+        blk = 2048 if precision == "mxfp8" else 1024
+        sizes = [w.E * (2 * w.F // 16) * KS(w.H) * blk, w.E * (w.H // 16) * KS(w.F) * blk,
                  w.E * (2 * w.F // 16) * ((KS(w.H) + 3) // 4) * 256,
                  w.E * (w.H // 16) * ((KS(w.F) + 3) // 4) * 256]
         sections = [(off[i], off[i] + sizes[i]) for i in range(4)]

@@ -454,6 +454,23 @@ def hand_case_arrays(c):
     return x, ids, pr, w1, w2
 
 
+@pytest.mark.parametrize("precision", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("c", _load_hand_cases(), ids=lambda c: c["name"])
+def test_oracle_hand_cases_block_scaled(c, precision):
+    """The hand cases' operands (one-hot x, gate 32, small integers, powers of two)
+    are exact in E4M3 and in E2M1 with their block scales, so the MXFP8 and MXFP4
+    paths must reproduce the exact outputs too."""
+    x, ids, pr, w1, w2 = hand_case_arrays(c)
+    m = oracle.Model(c["E"], c["H"], c["F"], c["k"], w1, w2, precision)
+    out, err, _ = m.forward(x, ids, pr, c["live"])
+    assert err == 0
+    for t, row in enumerate(c["expected"]):
+        if row is None:
+            assert np.all(np.isnan(out[t]))
+        else:
+            assert np.array_equal(out[t], np.array(row, np.float32)), t
+
+
 @pytest.mark.parametrize("c", _load_hand_cases(), ids=lambda c: c["name"])
 def test_oracle_hand_cases(c):
     x, ids, pr, w1, w2 = hand_case_arrays(c)
