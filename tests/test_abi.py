@@ -60,7 +60,8 @@ def _create(L, E, H, F, k, p):
     ((8, 128, 256, 9, 0), -1),
     ((64, 128, 256, 17, 0), -1),
     ((2000, 128, 256, 2, 0), -1),
-    ((8, 128, 256, 2, 2), -2),
+    ((8, 128, 256, 2, 2), 0),             # MXFP4 weights
+    ((8, 128, 256, 2, 3), -2),
     ((8, 128, 256, 2, -1), -2),
 ])
 def test_create_status(L, args, status):
