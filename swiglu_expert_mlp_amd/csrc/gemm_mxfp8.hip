@@ -2,8 +2,8 @@
 // CU (persistent grid): first the LDS-staged tiles (experts with more than 128
 // rows; only when K is a multiple of 128) with all 8 waves, then the streaming
 // tiles with its two 4-wave halves as independent workers.  Both designs follow
-// the same arithmetic contract (gemm_mxfp8_stream.h).  W4 (MXFP4 weights):
-// streaming tiles only, every expert's rows included (stream_big set).
+// the same arithmetic contract (gemm_mxfp8_stream.h).  W4: MXFP4 weights
+// (E2M1 B format) in both designs.
 #include "gemm_mxfp8_lds.h"
 #include "gemm_mxfp8_stream.h"
 
@@ -12,8 +12,7 @@ namespace moe {
 template <bool FC1, bool W4>
 __global__ void __launch_bounds__(512, 1) gemm_mxfp8_kernel(MxGemmArgs g)
 {
-    if constexpr (!W4)
-        if (!g.stream_big) mx_lds_tiles<FC1>(g);
+    if (!g.stream_big) mx_lds_tiles<FC1, W4>(g);
     // the two halves of a workgroup are workers b and b + grid: consecutive
     // tiles (the N tiles of one M tile) go to different CUs
     mx_stream_tiles<FC1, W4>(g, blockIdx.x + (threadIdx.x >> 8) * gridDim.x, 2 * gridDim.x, (threadIdx.x >> 6) & 3);
@@ -21,7 +20,7 @@ __global__ void __launch_bounds__(512, 1) gemm_mxfp8_kernel(MxGemmArgs g)
 
 hipError_t launch_gemm_mxfp8(bool fc1, bool w4, const MxGemmArgs& g, int num_cu, hipStream_t s)
 {
-    if (!g.stream_big && (g.K % 128 != 0 || w4)) return hipErrorInvalidValue;
+    if (!g.stream_big && g.K % 128 != 0) return hipErrorInvalidValue;
     dim3 grid((unsigned)(num_cu >= 8 ? num_cu / 8 * 8 : 8)), block(512);
     if (w4) {
         if (fc1)

@@ -20,6 +20,7 @@
 //    free of bank conflicts; the permutation is applied on the global side.
 //  * weight codes: the kernel-weight buffer holds 2 KB blocks (16 columns x
 //    128 K, two 1 KB halves in MFMA lane order), moved into LDS as they are.
+//    W4 (MXFP4 weights, E2M1 B format): 1 KB blocks, half of the B region.
 //  * activation scales: the step's 4 scale bytes of each of the 256 rows, one
 //    dword per lane (rows are 4-byte aligned because K is a multiple of 128),
 //    placed so that the 8 row groups of a fragment lane are 8 consecutive
@@ -67,7 +68,7 @@ __device__ __forceinline__ i32x8 mx_frag(uint4 lo, uint4 hi)
 
 // The LDS-staged tile loop of one 8-wave workgroup (one workgroup per CU).
 // Requires K % 128 == 0.
-template <bool FC1>
+template <bool FC1, bool W4>
 __device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
 {
     // the two stages are separate LDS objects, always addressed with
@@ -150,12 +151,19 @@ __device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 mx_load_block_to_lds(aptr[i] + 128 * s, st + (4 * wid + i) * 1024);
+            if constexpr (W4) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+                for (int i = 0; i < 2; ++i)
+                    mx_load_block_to_lds(g.W + (bblk[i] * KS + s) * 1024 + 16 * lane,
+                                         st + 32768 + (2 * wid + i) * 1024);
+            } else {
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    mx_load_block_to_lds(g.W + (bblk[i] * KS + s) * 2048 + h * 1024 + 16 * lane,
-                                         st + 32768 + ((2 * wid + i) * 2 + h) * 1024);
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        mx_load_block_to_lds(g.W + (bblk[i] * KS + s) * 2048 + h * 1024 + 16 * lane,
+                                             st + 32768 + ((2 * wid + i) * 2 + h) * 1024);
+            }
             if (wid < 4) mx_load_dword_to_lds(sptr + 4 * s, st + kMxAsOff + 256 * wid);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
@@ -186,8 +194,11 @@ __device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
             int sb[4];
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
-                b[ct] = mx_frag(*(const uint4*)(Bs + (4 * wn + ct) * 2048),
-                                *(const uint4*)(Bs + (4 * wn + ct) * 2048 + 1024));
+                if constexpr (W4)   // the upper half of an E2M1 operand is not read
+                    b[ct] = mx_frag(*(const uint4*)(Bs + (4 * wn + ct) * 1024), make_uint4(0, 0, 0, 0));
+                else
+                    b[ct] = mx_frag(*(const uint4*)(Bs + (4 * wn + ct) * 2048),
+                                    *(const uint4*)(Bs + (4 * wn + ct) * 2048 + 1024));
                 sb[ct] = Sb[(4 * wn + ct) * 256];
             }
             const uint4 sa_lo = *(const uint4*)Sa, sa_hi = *(const uint4*)(Sa + 16);
@@ -201,8 +212,9 @@ __device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
                 const int sa = (int)((sad[i] >> (8 * kg)) & 0xffu);
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct)
+                    // A format 0 (E4M3); B format 0 (E4M3) or 4 (E2M1)
                     acc[i][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        a, b[ct], acc[i][ct], 0, 0, 0, sa, 0, sb[ct]);
+                        a, b[ct], acc[i][ct], 0, W4 ? 4 : 0, 0, sa, 0, sb[ct]);
             }
         };
 

@@ -296,7 +296,7 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
         if ((e = mark(h, 4, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     } else {
-        // MXFP8, or MXFP4 weights with MXFP8 activations (streaming tiles only)
+        // MXFP8, or MXFP4 weights with MXFP8 activations
         const bool w4 = h->precision == MOE_MXFP4;
         size_t b1, b2, b3, b4;
         if (w4)
@@ -327,7 +327,7 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         g1.K = H;
         g1.topk = h->k;
         g1.n_tiles_n = ((2 * F / 64) + 3) / 4;
-        g1.stream_big = w4 || H % 128 != 0;
+        g1.stream_big = H % 128 != 0;
         e = launch_gemm_mxfp8(true, w4, g1, h->num_cu, stream);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC1 launch");
         if ((e = mark(h, 3, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
@@ -342,7 +342,7 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         g2.N = H;
         g2.K = F;
         g2.n_tiles_n = ((H + 63) / 64 + 3) / 4;
-        g2.stream_big = w4 || F % 128 != 0;
+        g2.stream_big = F % 128 != 0;
         e = launch_gemm_mxfp8(false, w4, g2, h->num_cu, stream);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
         if ((e = mark(h, 4, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
