@@ -10,10 +10,13 @@
 // operands staged through LDS in 32-wide K stages,
 // a ring of 4 stages with 3 in flight.  Stages are filled with direct global->LDS loads
 // (global_load_lds_dwordx4): one wave instruction moves one 16 x 32 operand
-// block (1 KB) into LDS already in MFMA lane order, so every LDS read of a
-// fragment is a conflict-free 16-byte-per-lane read.  The weight blocks are
-// stored in exactly that order in the kernel-weight buffer (1 KB contiguous
-// per block); activation blocks are gathered 16 rows x 64 bytes at a time.
+// block (1 KB) into LDS.  The weight blocks are stored in MFMA lane order in
+// the kernel-weight buffer (1 KB contiguous per block) and land as stored.
+// Activation blocks are gathered 16 rows x 64 bytes at a time with a quad of
+// lanes per row, each quad one 64-byte segment (lane-to-row by lane % 16
+// spreads every quad over four rows and moves a third less per second through
+// the L1), and land with a row's four 16-byte chunks permuted so that the
+// fragment reads stay free of bank conflicts.
 //
 // Tiles: the device-built table of 256-row M tiles (experts with more rows
 // than the streaming kernel takes) x 256-column N tiles.  The persistent grid
@@ -44,6 +47,10 @@ __device__ __forceinline__ bf16x8 lds_frag(const char* base, int lane)
     return __builtin_bit_cast(bf16x8, *(const uint4*)(base + 16 * lane));
 }
 
+// chunk permutation of an activation block row (measured free of LDS bank
+// conflicts for the fragment reads)
+__device__ __forceinline__ int a_swz(int r) { return (r >> 1) & 3; }
+
 constexpr int kRing = 4;          // LDS stages (one 32-wide K step each)
 constexpr int kStageBytes = 32 * 1024;
 
@@ -64,6 +71,8 @@ __device__ __forceinline__ void lds_tiles(const GemmArgs& g)
     const int K = g.K;
     const int nsteps = K / 32;                                    // 32-wide K steps
     const int nt16 = g.N / 16;
+    // fragment lane (row l % 16, chunk l / 16) of an activation block
+    const int a_off = 16 * (4 * (lane & 15) + ((lane >> 4) ^ a_swz(lane & 15)));
 
     // contiguous range of tiles for this XCD, strided over its workgroups
     const int xcd = blockIdx.x & 7, per_xcd = gridDim.x >> 3;
@@ -88,15 +97,18 @@ __device__ __forceinline__ void lds_tiles(const GemmArgs& g)
 
         // loads: wave w moves the A blocks of row groups 2w, 2w+1 and the B
         // blocks of column groups 2w, 2w+1 of each K step (4 instructions)
+        // activation blocks: a quad of lanes fetches one row's 64 bytes (lane i's
+        // 16 bytes land at LDS slot i), chunk c of block row r at slot 4 r + (c ^ sw(r))
         const uint16_t* arow[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            int r = 16 * (2 * wid + i) + (lane & 15);
+            const int rr = lane >> 2;
+            int r = 16 * (2 * wid + i) + rr;
             if (r >= rows) r = rows - 1;
             const int row = row0 + r;
             int64_t src_row = row;
             if constexpr (FC1) src_row = g.perm_src[row] / g.topk;
-            arow[i] = g.A + src_row * K + 8 * (lane >> 4);
+            arow[i] = g.A + src_row * K + 8 * ((lane & 3) ^ a_swz(rr));
         }
         const uint16_t* bblk[2];
 #pragma unroll
@@ -143,7 +155,7 @@ __device__ __forceinline__ void lds_tiles(const GemmArgs& g)
             const char* Bs = As + 16 * 1024;
             bf16x8 a[8], b[4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) a[i] = lds_frag(As + (8 * wm + i) * 1024, lane);
+            for (int i = 0; i < 8; ++i) a[i] = __builtin_bit_cast(bf16x8, *(const uint4*)(As + (8 * wm + i) * 1024 + a_off));
 #pragma unroll
             for (int j = 0; j < 4; ++j) b[j] = lds_frag(Bs + (4 * wn + j) * 1024, lane);
 #pragma unroll
