@@ -71,7 +71,7 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}))
 
 
-GEMM_SOURCES = ["swiglu_expert_mlp_amd/csrc/gemm_bf16.hip", "swiglu_expert_mlp_amd/csrc/gemm_bf16_stream.h",
+GEMM_SOURCES = ["swiglu_expert_mlp_amd/csrc/gemm_bf16.hip", "swiglu_expert_mlp_amd/csrc/gemm_bf16_small.h",
                 "swiglu_expert_mlp_amd/csrc/gemm_bf16_lds.h", "swiglu_expert_mlp_amd/csrc/gemm_mxfp8.hip",
                 "swiglu_expert_mlp_amd/csrc/gemm_mxfp8_stream.h", "swiglu_expert_mlp_amd/csrc/gemm_mxfp8_lds.h",
                 "swiglu_expert_mlp_amd/csrc/gemm_args.h", "swiglu_expert_mlp_amd/csrc/common.h"]
@@ -264,13 +264,13 @@ def main():
         roof = dict(bound="hbm", achieved=ab["fc1"] / (fc1_us * 1e-6) / 1e9,
                     peak=HBM_PEAK_GBS, unit="GB/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    # the FC1 + SwiGLU stage is one launch; its tiles run on the LDS-staged loop
-    # (experts with more than 128 rows) or the streaming loop (the others)
+    # the FC1 + SwiGLU stage is one launch; its tiles are 256-row tiles (experts
+    # with more than 128 rows) or 64-row tiles (the others)
     roof["kernel"] = {"bf16": "moe::gemm_bf16_kernel<true>",
                       "mxfp8": "moe::gemm_mxfp8_kernel<true, false>",
                       "mxfp4": "moe::gemm_mxfp8_kernel<true, true>"}[w.precision]
-    roof["tiles"] = "lds-staged" if int(loads.min()) > 128 else (
-        "streaming" if int(loads.max()) <= 128 else "lds-staged + streaming")
+    roof["tiles"] = "256-row" if int(loads.min()) > 128 else (
+        "64-row" if int(loads.max()) <= 128 else "256-row + 64-row")
     roof["kernel_us"] = fc1_us
     roof["traffic"] = measured_traffic(w.name)
 

@@ -99,8 +99,11 @@ size_t moe_weight_bytes(moe_handle h);
  *     tiled into MFMA operand blocks so that one wave's load is 1 KB contiguous.
  *     For a section with N rows of K elements per expert:
  *   kbuf layout (bf16): FC1 section (N = 2F, K = H) then FC2 section (N = H,
- *     K = F); element (e, n, k) at element index
- *       (((e*(N/16) + n/16)*(K/32) + k/32)*4 + (k%32)/8)*128 + (n%16)*8 + k%8.
+ *     K = F) of 1 KB blocks (16 rows x 32 K).  With c = n/16, s = k/32,
+ *     KS = K/32, g = c/32 and w = min(32, N/16 - 32g) (the width of c's
+ *     512-row group), element (e, n, k) is at element index
+ *       (e*(N/16)*KS + g*32*KS + s*w + c%32)*512 + ((k%32)/8)*128 + (n%16)*8 + k%8,
+ *     so that one K step of a 512-row group is one contiguous run of blocks.
  *   kbuf layout (mxfp8): sections FC1 codes, FC2 codes, FC1 scales, FC2
  *     scales, each starting at a multiple of 256 bytes.  With KS = ceil(K/128)
  *     and KQ = ceil(KS/4), code (e, n, k) at byte

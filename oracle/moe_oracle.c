@@ -741,13 +741,16 @@ static int64_t fc1_logical_row(int64_t packed, int64_t F)
     return i < 32 ? 32 * b + i : F + 32 * b + (i - 32);
 }
 
-/* bf16 section of a weight with N rows of K elements per expert: element
- * (e, n, k) sits at element index
- *   (((e*(N/16) + n/16)*(K/32) + k/32)*4 + (k%32)/8)*128 + (n%16)*8 + k%8 . */
+/* bf16 section of a weight with N rows of K elements per expert: 1 KB blocks
+ * of 16 rows x 32 K; with c = n/16, s = k/32, KS = K/32, g = c/32 and
+ * w = min(32, N/16 - 32g), element (e, n, k) sits at element index
+ *   (e*(N/16)*KS + g*32*KS + s*w + c%32)*512 + ((k%32)/8)*128 + (n%16)*8 + k%8 . */
 static int64_t bf16_index(int64_t e, int64_t n, int64_t k, int64_t N, int64_t K)
 {
-    return (((e * (N / 16) + n / 16) * (K / 32) + k / 32) * 4 + (k % 32) / 8) * 128 +
-           (n % 16) * 8 + k % 8;
+    const int64_t c = n / 16, s = k / 32, KS = K / 32, g = c / 32;
+    const int64_t w = N / 16 - 32 * g < 32 ? N / 16 - 32 * g : 32;
+    const int64_t block = e * (N / 16) * KS + g * 32 * KS + s * w + c % 32;
+    return block * 512 + ((k % 32) / 8) * 128 + (n % 16) * 8 + k % 8;
 }
 
 static void pack_bf16_section(int E, int64_t N, int64_t K, int64_t F, int fc1,

@@ -19,7 +19,23 @@ constexpr int kWave = 64;            // CDNA wavefront width
 constexpr int kMaxTopk = 16;
 constexpr int kMaxExperts = 1024;
 constexpr int kChunkTok = 256;       // tokens per prep workgroup
-constexpr int kBM = 64;              // rows per M tile of the streaming GEMMs
+// bf16 kernel-weight blocks (1 KB: 16 columns x 32 K in MFMA lane order) of one
+// expert's N x K section, in 512-column groups: [n16 / 32][K step][n16 % 32], so
+// one K step of a group is contiguous (the last group may be narrower).
+__host__ __device__ inline int64_t wblock_index(int64_t n16, int64_t s, int64_t nt16, int64_t ks)
+{
+    const int64_t g = n16 >> 5;
+    const int64_t w = nt16 - 32 * g < 32 ? nt16 - 32 * g : 32;
+    return g * 32 * ks + s * w + (n16 & 31);
+}
+// distance in blocks from one K step of column block n16 to the next
+__host__ __device__ inline int64_t wblock_step(int64_t n16, int64_t nt16)
+{
+    const int64_t g = n16 >> 5;
+    return nt16 - 32 * g < 32 ? nt16 - 32 * g : 32;
+}
+
+constexpr int kBM = 64;              // rows per M tile of the small-expert GEMM tiles
 constexpr int kBigBMRows = 256;      // rows per M tile of the LDS-staged GEMMs
 constexpr int kBigMin = 128;         // experts with more rows than this use the LDS-staged GEMMs
 
@@ -113,7 +129,7 @@ struct WsLayout {
     size_t sorted_probs;   // float [T_cap * k]
     size_t perm_src;       // int32 [T_cap * k]
     size_t dst;            // int32 [T_cap * k]
-    size_t tiles;          // int2 [max_tiles]: (expert, first row), streaming GEMM tiles
+    size_t tiles;          // int2 [max_tiles]: (expert, first row), 64-row GEMM tiles
     size_t tiles_big;      // int2 [max_tiles_big]: (expert, first row), LDS-staged GEMM tiles
     size_t hbuf;           // bf16 [T_cap * k][F] or E4M3 [T_cap * k][F]
     size_t hscale;         // E8M0 [T_cap * k][F / 32] (mxfp8)

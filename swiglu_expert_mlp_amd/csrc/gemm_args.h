@@ -16,6 +16,15 @@ __device__ __forceinline__ uint4 load_stream16(const void* p)
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Load of a table that an earlier launch wrote and this launch only reads, at a
+// wave-uniform address: through the constant address space it becomes a scalar
+// load, kept apart from the vector-memory count of the tile's loads and stores.
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* p)
+{
+    return *(const __attribute__((address_space(4))) T*)p;
+}
+
 // bf16 operands.
 struct GemmArgs {
     const uint16_t* A;         // FC1: x [T_cap][H]; FC2: hbuf [rows][F]

@@ -1,21 +1,20 @@
 // K3 / K4, bf16: one launch per GEMM stage.  A workgroup is 8 waves, one per
-// CU (persistent grid): first the LDS-staged tiles (experts with more than 128
-// rows) with all 8 waves, then the streaming tiles (the other experts) with
-// its two 4-wave halves as independent workers.  Both designs follow the same
-// arithmetic contract (gemm_bf16_stream.h), so which one computes a row never
-// changes its bits.
+// CU (persistent grid): first the 256-row tiles (experts with more than 128
+// rows), then the 64-row x 512-column tiles (the other experts), both staged
+// through one LDS buffer.  Both designs follow the same arithmetic contract
+// (gemm_bf16_small.h), so which one computes a row never changes its bits.
 #include "gemm_bf16_lds.h"
-#include "gemm_bf16_stream.h"
+#include "gemm_bf16_small.h"
 
 namespace moe {
 
 template <bool FC1>
 __global__ void __launch_bounds__(512, 1) gemm_bf16_kernel(GemmArgs g)
 {
-    lds_tiles<FC1>(g);
-    // the two halves of a workgroup are workers b and b + grid: consecutive
-    // tiles (the N tiles of one M tile) go to different CUs
-    stream_tiles<FC1>(g, blockIdx.x + (threadIdx.x >> 8) * gridDim.x, 2 * gridDim.x, (threadIdx.x >> 6) & 3);
+    static_assert(kSmallLds >= kRing * kStageBytes, "one LDS buffer serves both tile designs");
+    __shared__ __attribute__((aligned(1024))) char smem[kSmallLds];
+    lds_tiles<FC1>(g, smem);
+    small_tiles<FC1>(g, smem);
 }
 
 hipError_t launch_gemm_bf16(bool fc1, const GemmArgs& g, int num_cu, hipStream_t s)

@@ -1,8 +1,8 @@
 // K3 / K4, LDS-staged design (experts with more than 128 rows): grouped GEMM on CDNA4 MFMA,
 // bf16 operands, fp32 accumulate.
 //
-// Same arithmetic contract as gemm_bf16.hip (and therefore bitwise the same
-// results for a row): every output element is acc = 0; for k0 = 0, 32, ... :
+// Same arithmetic contract as the 64-row tiles of gemm_bf16_small.h (and
+// therefore bitwise the same results for a row): every output element is acc = 0; for k0 = 0, 32, ... :
 // acc = MFMA_16x16x32_bf16(A[row, k0:k0+32], B[col, k0:k0+32], acc).  Only
 // the decomposition differs: a workgroup computes a 256 x 256 tile, each of
 // its 8 waves a 128 x 64 part (8 x 4 MFMA blocks, accumulators in registers;
@@ -11,15 +11,16 @@
 // a ring of 4 stages with 3 in flight.  Stages are filled with direct global->LDS loads
 // (global_load_lds_dwordx4): one wave instruction moves one 16 x 32 operand
 // block (1 KB) into LDS.  The weight blocks are stored in MFMA lane order in
-// the kernel-weight buffer (1 KB contiguous per block) and land as stored.
+// the kernel-weight buffer (1 KB each; one K step of a tile's 16 column blocks
+// is a contiguous 16 KB run) and land as stored.
 // Activation blocks are gathered 16 rows x 64 bytes at a time with a quad of
 // lanes per row, each quad one 64-byte segment (lane-to-row by lane % 16
 // spreads every quad over four rows and moves a third less per second through
 // the L1), and land with a row's four 16-byte chunks permuted so that the
 // fragment reads stay free of bank conflicts.
 //
-// Tiles: the device-built table of 256-row M tiles (experts with more rows
-// than the streaming kernel takes) x 256-column N tiles.  The persistent grid
+// Tiles: the device-built table of 256-row M tiles (experts with more than
+// 128 rows) x 256-column N tiles.  The persistent grid
 // is one workgroup per CU; tiles are split into 8 contiguous ranges, one per
 // XCD (workgroups are dispatched round-robin over the XCDs), so the tiles of
 // one expert, which share activation and weight slices, run on one XCD and
@@ -58,11 +59,12 @@ constexpr int kStageBytes = 32 * 1024;
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 
 // The LDS-staged tile loop of one 8-wave workgroup (one workgroup per CU).
+// smem: the kernel's LDS, at least kRing * kStageBytes bytes, 1 KB aligned.
 template <bool FC1>
-__device__ __forceinline__ void lds_tiles(const GemmArgs& g)
+__device__ __forceinline__ void lds_tiles(const GemmArgs& g, char* smem_base)
 {
     // [stage][A 16 blocks | B 16 blocks] of 1 KB (16 rows or columns x 32 K)
-    __shared__ __attribute__((aligned(1024))) char smem[kRing][kStageBytes];
+    char (*smem)[kStageBytes] = (char (*)[kStageBytes])smem_base;
     const int n_mt = g.hdr->n_tiles_big;
     const int NT = (g.N + kBigBN - 1) / kBigBN;
     const int total = n_mt * NT;
@@ -111,18 +113,20 @@ __device__ __forceinline__ void lds_tiles(const GemmArgs& g)
             arow[i] = g.A + src_row * K + 8 * ((lane & 3) ^ a_swz(rr));
         }
         const uint16_t* bblk[2];
+        int bstep[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             int c16 = n0 / 16 + 2 * wid + i;
             if (c16 >= nt16) c16 = nt16 - 1;
-            bblk[i] = g.W + ((int64_t)e * nt16 + c16) * (int64_t)nsteps * 512 + 8 * lane;
+            bblk[i] = g.W + ((int64_t)e * nt16 * nsteps + wblock_index(c16, 0, nt16, nsteps)) * 512 + 8 * lane;
+            bstep[i] = (int)wblock_step(c16, nt16) * 512;
         }
         auto issue = [&](int s) {
             char* st = smem[s % kRing];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 load_block_to_lds(arow[i] + 32 * s, st + (2 * wid + i) * 1024);
-                load_block_to_lds(bblk[i] + 512 * s, st + 16 * 1024 + (2 * wid + i) * 1024);
+                load_block_to_lds(bblk[i] + (int64_t)bstep[i] * s, st + 16 * 1024 + (2 * wid + i) * 1024);
             }
         };
 

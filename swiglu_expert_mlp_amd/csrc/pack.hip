@@ -54,7 +54,8 @@ __global__ void __launch_bounds__(256) pack_bf16_kernel(const uint16_t* __restri
         const int64_t n = n16 * 16 + (lane & 15);
         const int64_t k = s * 32 + (lane >> 4) * 8;
         const int64_t srow = fc1 ? fc1_src_row(n, F) : n;
-        ((uint4*)dst)[i] = *(const uint4*)(src + ((e * N + srow) * K + k));
+        const int64_t o = (e * nt * ks + wblock_index(n16, s, nt, ks)) * 64 + lane;
+        ((uint4*)dst)[o] = *(const uint4*)(src + ((e * N + srow) * K + k));
     }
 }
 

@@ -83,9 +83,9 @@ def test_wide_equals_chunks_of_8(name):
 
 
 @pytest.mark.parametrize("name", ["logprob", "mxfp8_16k", "mxfp4_16k"])
-def test_streaming_and_lds_staged_gemms_agree_bitwise(name):
-    """Experts with more than 128 rows run on the LDS-staged GEMM, the others on
-    the streaming GEMM; a token's bits must not depend on which one ran."""
+def test_64_row_and_256_row_tiles_agree_bitwise(name):
+    """Experts with more than 128 rows run on the 256-row tiles, the others on
+    the 64-row tiles; a token's bits must not depend on which one ran."""
     from swiglu_expert_mlp_amd import MoE
     w = WORKLOADS[name].with_tokens(2048)
     c = Case(w, seed=11, outliers=w.precision != "bf16")

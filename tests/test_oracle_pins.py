@@ -639,10 +639,17 @@ def _interleave(w, F):
 
 
 def _unswizzle_bf16(buf, E, N, K):
-    """Inverse of the bf16 tiled layout by array reshapes: blocks
-    [E][N/16][K/32] of [4 (k%32 / 8)][16 (n%16)][8 (k%8)]."""
-    t = buf.reshape(E, N // 16, K // 32, 4, 16, 8)
-    return t.transpose(0, 1, 4, 2, 3, 5).reshape(E, N, K)
+    """Inverse of the bf16 tiled layout by array reshapes, one 512-row group
+    at a time: per expert, groups of w = min(32, N/16 - 32 g) column blocks,
+    each group [K/32][w] blocks of [4 (k%32 / 8)][16 (n%16)][8 (k%8)]."""
+    nt, KS = N // 16, K // 32
+    per_e = buf.reshape(E, nt * KS * 512)
+    out = np.empty((E, N, K), dtype=buf.dtype)
+    for g in range((nt + 31) // 32):
+        w = min(32, nt - 32 * g)
+        t = per_e[:, g * 32 * KS * 512:(g * 32 + w) * KS * 512].reshape(E, KS, w, 4, 16, 8)
+        out[:, g * 512:g * 512 + 16 * w] = t.transpose(0, 2, 4, 1, 3, 5).reshape(E, 16 * w, K)
+    return out
 
 
 def _unswizzle_mx(codes, scales, E, N, K):
@@ -668,9 +675,11 @@ def _unswizzle_mx4(codes, scales, E, N, K):
     return c, sc
 
 
-def test_pack_bf16_layout_definition():
-    """Unswizzled by reshapes, the packed buffer is the interleaved weight."""
-    E, H, F = 2, 64, 96
+@pytest.mark.parametrize("H,F", [(64, 96), (96, 320)])
+def test_pack_bf16_layout_definition(H, F):
+    """Unswizzled by reshapes, the packed buffer is the interleaved weight
+    (F = 320: FC1 has 40 column blocks, one full 512-row group and one of 8)."""
+    E = 2
     rng = np.random.default_rng(4)
     w1 = rng.integers(0, 65535, (E, 2 * F, H)).astype(np.uint16)
     w2 = rng.integers(0, 65535, (E, H, F)).astype(np.uint16)
@@ -679,9 +688,17 @@ def test_pack_bf16_layout_definition():
     p2 = _unswizzle_bf16(buf[E * 2 * F * H:], E, H, F)
     assert np.array_equal(p1, _interleave(w1, F))
     assert np.array_equal(p2, w2)
-    # one spot check of the lane order: element (e=1, n=17, k=45)
-    idx = (((1 * (2 * F // 16) + 1) * (H // 32) + 1) * 4 + 13 // 8) * 128 + 1 * 8 + 45 % 8
+    # spot checks of the block order and the lane order, written out by hand
+    KS, nt = H // 32, 2 * F // 16
+    # element (e=1, n=17, k=45): column block 1 of group 0, K step 1
+    w0 = min(32, nt)
+    idx = (1 * nt * KS + 1 * w0 + 1) * 512 + (13 // 8) * 128 + 1 * 8 + 45 % 8
     assert buf[idx] == _interleave(w1, F)[1, 17, 45]
+    if nt > 32:
+        # element (e=0, n=16*33+5, k=33): column block 33 = block 1 of group 1
+        # (width nt - 32), K step 1, one block past the group's first
+        idx = (32 * KS + 1 * (nt - 32) + 1) * 512 + (1 // 8) * 128 + 5 * 8 + 33 % 8
+        assert buf[idx] == _interleave(w1, F)[0, 16 * 33 + 5, 33]
 
 
 @pytest.mark.parametrize("H,F", [(64, 96), (160, 96)])
