@@ -30,6 +30,9 @@ INV = {
     "logprob_T300": WORKLOADS["logprob"].with_tokens(300),
     "mxfp8_T300": WORKLOADS["mxfp8_16k"].with_tokens(300),
     "odd_mxfp8_T300": Workload("odd_mxfp8", 300, 300, 96, 160, 5, 3, "mxfp8"),
+    # odd bf16 shapes: 256-row tiles in the wide launch, 64-row tiles with partial
+    # 512-column tiles and a half-full last 64-column block in the 8-token chunks
+    "odd_bf16_T300": Workload("odd_bf16", 300, 300, 96, 160, 5, 3, "bf16"),
     "mxfp4_T300": WORKLOADS["mxfp4_16k"].with_tokens(300),
 }
 _cases = {}

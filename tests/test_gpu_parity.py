@@ -49,6 +49,13 @@ SMALL = {
     "odd_bf16_big": Workload("odd_bf16_big", 700, 720, 96, 160, 5, 3, "bf16"),
     # and an even number of K steps in both GEMMs
     "mid_bf16_big": Workload("mid_bf16_big", 600, 600, 256, 192, 4, 2, "bf16"),
+    # bf16 experts of 95..121 rows: two 64-row tiles each, the first with four
+    # 16-row groups, the second ragged (2..4 groups); FC1 N = 320 and FC2 N = 96
+    # leave the 512-column tiles partial and FC2's last 64-column block half full
+    "rows128_bf16": Workload("rows128_bf16", 220, 224, 96, 160, 4, 2, "bf16"),
+    # one expert of 129 rows (a ragged 256-row tile) beside 64-row tiles in the
+    # same launches
+    "mixed129_bf16": Workload("mixed129_bf16", 180, 192, 96, 160, 3, 2, "bf16"),
     # MXFP8 experts past 128 rows with K a multiple of 128 (LDS-staged kernel):
     # ragged 256-row tiles, a partial 256-column tile, 2 and 3 K steps
     "mx_big": Workload("mx_big", 600, 600, 256, 384, 4, 2, "mxfp8"),
