@@ -39,6 +39,7 @@ struct GemmArgs {
     int K;                     // FC1: H;  FC2: F
     int topk;
     int n_tiles_n;             // N tiles per M tile (4 waves x 64 columns each)
+    int max_tiles;             // capacity of `tiles` (entries)
 };
 
 // MXFP8 operands: E4M3 codes with one E8M0 scale byte per 32 elements of K.

@@ -13,8 +13,16 @@ __global__ void __launch_bounds__(512, 1) gemm_bf16_kernel(GemmArgs g)
 {
     static_assert(kSmallLds >= kRing * kStageBytes, "one LDS buffer serves both tile designs");
     __shared__ __attribute__((aligned(1024))) char smem[kSmallLds];
-    lds_tiles<FC1>(g, smem);
-    small_tiles<FC1>(g, smem);
+    // both tile counts in one scalar load, and the first 64-row tile's table
+    // entry fetched beside them (its index clamped into the table; unused when
+    // the tile does not exist), so the first weight loads wait for one round trip
+    const int n_big = ld_const(&g.hdr->n_tiles_big);
+    const int n_small = ld_const(&g.hdr->n_tiles);
+    const int* te0 = (const int*)(g.tiles + min((int)blockIdx.x / small_col_tiles(g), g.max_tiles - 1));
+    const int e0 = ld_const(te0), row00 = ld_const(te0 + 1);
+    asm volatile("" : : "s"(n_big), "s"(n_small), "s"(e0), "s"(row00));   // one round trip for all four
+    lds_tiles<FC1>(g, smem, n_big);
+    small_tiles<FC1>(g, smem, n_small, e0, row00);
 }
 
 hipError_t launch_gemm_bf16(bool fc1, const GemmArgs& g, int num_cu, hipStream_t s)

@@ -59,13 +59,13 @@ constexpr int kStageBytes = 32 * 1024;
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 
 // The LDS-staged tile loop of one 8-wave workgroup (one workgroup per CU).
-// smem: the kernel's LDS, at least kRing * kStageBytes bytes, 1 KB aligned.
+// smem: the kernel's LDS, at least kRing * kStageBytes bytes, 1 KB aligned;
+// n_mt: the number of 256-row M tiles.
 template <bool FC1>
-__device__ __forceinline__ void lds_tiles(const GemmArgs& g, char* smem_base)
+__device__ __forceinline__ void lds_tiles(const GemmArgs& g, char* smem_base, int n_mt)
 {
     // [stage][A 16 blocks | B 16 blocks] of 1 KB (16 rows or columns x 32 K)
     char (*smem)[kStageBytes] = (char (*)[kStageBytes])smem_base;
-    const int n_mt = g.hdr->n_tiles_big;
     const int NT = (g.N + kBigBN - 1) / kBigBN;
     const int total = n_mt * NT;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;   // 8 waves

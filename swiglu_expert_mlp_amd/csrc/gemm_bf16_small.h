@@ -60,11 +60,14 @@ __device__ __forceinline__ void wait_vmcnt_upto15(int n)
     }
 }
 
+__device__ __forceinline__ int small_col_tiles(const GemmArgs& g) { return (g.N + kSmallCols - 1) / kSmallCols; }
+
+// n_mt: the number of 64-row M tiles; (e0, row00): the table entry of this
+// workgroup's first tile (blockIdx.x), read by the caller before n_mt was known.
 template <bool FC1>
-__device__ __forceinline__ void small_tiles(const GemmArgs& g, char* smem)
+__device__ __forceinline__ void small_tiles(const GemmArgs& g, char* smem, int n_mt, int e0, int row00)
 {
-    const int n_mt = ld_const(&g.hdr->n_tiles);
-    const int NTs = (g.N + kSmallCols - 1) / kSmallCols;
+    const int NTs = small_col_tiles(g);
     const int total = n_mt * NTs;
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -77,12 +80,38 @@ __device__ __forceinline__ void small_tiles(const GemmArgs& g, char* smem)
 
     for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
         const int mt = tile / NTs, ct = tile - mt * NTs;
-        const int* te = (const int*)(g.tiles + mt);
-        const int e = ld_const(te), row0 = ld_const(te + 1);
-        const int rows = min(kBM, ld_const(g.offsets + e + 1) - row0);
-        const int ng = (rows + 15) >> 4;
+        int e = e0, row0 = row00;
+        if (tile != (int)blockIdx.x) {
+            const int* te = (const int*)(g.tiles + mt);
+            e = ld_const(te);
+            row0 = ld_const(te + 1);
+        }
         const int cb = ct * 8 + wid;                 // this wave's 64-column block
         const bool has_cols = cb < n_cb;
+        const uint16_t* bblk[4];
+        int bstep[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c16 = min(cb * 4 + j, nt16 - 1);
+            bblk[j] = g.W + ((int64_t)e * nt16 * nsteps + wblock_index(c16, 0, nt16, nsteps)) * 512 + 8 * lane;
+            bstep[j] = (int)wblock_step(c16, nt16) * 512;
+        }
+        auto issue_b = [&](int s) {
+            char* st = smem + (s % kSmallRing) * kSmallStage;
+            if (has_cols) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    load_block_to_lds(bblk[j] + (int64_t)bstep[j] * s, st + (4 + 4 * wid + j) * 1024);
+            }
+        };
+        // every wave finished the previous tile's LDS reads before the ring is
+        // refilled; step 0's weights go out before the row count and the
+        // gathered rows (a further round trip) are known
+        __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        issue_b(0);
+        const int rows = min(kBM, ld_const(g.offsets + e + 1) - row0);
+        const int ng = (rows + 15) >> 4;
         const bool has_a = wid < ng;                 // this wave loads activation block wid
         const int nl = (has_a ? 1 : 0) + (has_cols ? 4 : 0);
 
@@ -93,23 +122,10 @@ __device__ __forceinline__ void small_tiles(const GemmArgs& g, char* smem)
             if constexpr (FC1) src = g.perm_src[src] / g.topk;
             arow = g.A + src * K + 8 * ((lane & 3) ^ a_swz(lane >> 2));
         }
-        const uint16_t* bblk[4];
-        int bstep[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c16 = min(cb * 4 + j, nt16 - 1);
-            bblk[j] = g.W + ((int64_t)e * nt16 * nsteps + wblock_index(c16, 0, nt16, nsteps)) * 512 + 8 * lane;
-            bstep[j] = (int)wblock_step(c16, nt16) * 512;
-        }
-        auto issue = [&](int s) {
-            char* st = smem + (s % kSmallRing) * kSmallStage;
-            if (has_a) load_block_to_lds(arow + 32 * s, st + wid * 1024);
-            if (has_cols) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    load_block_to_lds(bblk[j] + (int64_t)bstep[j] * s, st + (4 + 4 * wid + j) * 1024);
-            }
+        auto issue_a = [&](int s) {
+            if (has_a) load_block_to_lds(arow + 32 * s, smem + (s % kSmallRing) * kSmallStage + wid * 1024);
         };
+        auto issue = [&](int s) { issue_a(s); issue_b(s); };
 
         f32x4 acc[4][4];
 #pragma unroll
@@ -117,11 +133,10 @@ __device__ __forceinline__ void small_tiles(const GemmArgs& g, char* smem)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        // every wave finished the previous tile's LDS reads before the ring is refilled
-        __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0)
-        __builtin_amdgcn_s_barrier();
+        // a step's loads stay contiguous in issue order (step 0: weights, then rows)
+        issue_a(0);
 #pragma unroll
-        for (int s = 0; s < kSmallRing - 1; ++s)
+        for (int s = 1; s < kSmallRing - 1; ++s)
             if (s < nsteps) issue(s);
         for (int s = 0; s < nsteps; ++s) {
             // step s landed when at most the later in-flight steps remain

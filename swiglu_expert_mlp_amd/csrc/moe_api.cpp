@@ -281,6 +281,7 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         g1.K = H;
         g1.topk = h->k;
         g1.n_tiles_n = ((2 * F / 64) + 3) / 4;
+        g1.max_tiles = (int)L.max_tiles;
         e = launch_gemm_bf16(true, g1, h->num_cu, stream);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC1 launch");
         if ((e = mark(h, 3, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
