@@ -205,16 +205,53 @@ __device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
             if (s + 1 < KS) issue(std::integral_constant<int, P ^ 1>{}, s + 1);
             const uint32_t sad[8] = {sa_lo.x, sa_lo.y, sa_lo.z, sa_lo.w,
                                      sa_hi.x, sa_hi.y, sa_hi.z, sa_hi.w};
+            // FC1: activation fragments in four groups of two, each group's reads
+            // issued while the previous group's MFMAs run; the explicit
+            // lgkmcnt(0) before a group's reads is what tells the compiler that
+            // the previous group has landed (after the direct loads above it
+            // would otherwise wait for every LDS read before each MFMA)
+            i32x8 af[2][2];
+            auto read_group = [&](int gr, i32x8 (&dst)[2]) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const char* ag = As + (8 * wm + i) * 2048;
-                const i32x8 a = mx_frag(*(const uint4*)(ag + a_lo), *(const uint4*)(ag + a_hi));
-                const int sa = (int)((sad[i] >> (8 * kg)) & 0xffu);
+                for (int q = 0; q < 2; ++q) {
+                    const char* ag = As + (8 * wm + 2 * gr + q) * 2048;
+                    dst[q] = mx_frag(*(const uint4*)(ag + a_lo), *(const uint4*)(ag + a_hi));
+                }
+            };
+            auto mfma_group = [&](int gr, const i32x8 (&src)[2]) {
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct)
-                    // A format 0 (E4M3); B format 0 (E4M3) or 4 (E2M1)
-                    acc[i][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        a, b[ct], acc[i][ct], 0, W4 ? 4 : 0, 0, sa, 0, sb[ct]);
+                for (int q = 0; q < 2; ++q) {
+                    const int i = 2 * gr + q;
+                    const int sa = (int)((sad[i] >> (8 * kg)) & 0xffu);
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct)
+                        // A format 0 (E4M3); B format 0 (E4M3) or 4 (E2M1)
+                        acc[i][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            src[q], b[ct], acc[i][ct], 0, W4 ? 4 : 0, 0, sa, 0, sb[ct]);
+                }
+            };
+            if constexpr (FC1) {
+                read_group(0, af[0]);
+#pragma unroll
+                for (int gr = 0; gr < 4; ++gr) {
+                    __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): group gr is in
+                    if (gr + 1 < 4) read_group(gr + 1, af[(gr + 1) & 1]);
+                    mfma_group(gr, af[gr & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+                // FC2 is bound by its loads and output stores; the grouped reads
+                // only added register spills there
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const char* ag = As + (8 * wm + i) * 2048;
+                    const i32x8 a = mx_frag(*(const uint4*)(ag + a_lo), *(const uint4*)(ag + a_hi));
+                    const int sa = (int)((sad[i] >> (8 * kg)) & 0xffu);
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct)
+                        acc[i][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            a, b[ct], acc[i][ct], 0, W4 ? 4 : 0, 0, sa, 0, sb[ct]);
+                }
             }
         };
 
