@@ -215,8 +215,9 @@ def main():
     touched = int(np.count_nonzero(idx["counts"]))
     loads = idx["counts"].astype(np.int64)
 
-    # timed region: K steps; the library records two events around the dominant
-    # kernel (FC1 + SwiGLU) of every step
+    # timed region: K steps; the dominant launch (FC1 + SwiGLU) of every step
+    # records its own start and end into two events (hipExtLaunchKernel: the
+    # dispatch carries them, so no marker packet idles the GPU between kernels)
     ev = HipEvents()
     fc1_ev = [(ev.new(), ev.new()) for _ in range(a.steps)]
     t0, t1 = ev.new(), ev.new()

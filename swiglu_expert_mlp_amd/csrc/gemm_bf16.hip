@@ -3,6 +3,8 @@
 // rows), then the 64-row x 512-column tiles (the other experts), both staged
 // through one LDS buffer.  Both designs follow the same arithmetic contract
 // (gemm_bf16_small.h), so which one computes a row never changes its bits.
+#include <hip/hip_ext.h>
+
 #include "gemm_bf16_lds.h"
 #include "gemm_bf16_small.h"
 
@@ -25,14 +27,21 @@ __global__ void __launch_bounds__(512, 1) gemm_bf16_kernel(GemmArgs g)
     small_tiles<FC1>(g, smem, n_small, e0, row00);
 }
 
-hipError_t launch_gemm_bf16(bool fc1, const GemmArgs& g, int num_cu, hipStream_t s)
+// t0 / t1 (optional): events that receive the launch's own start and end
+// (recorded by the dispatch itself, no separate marker in the stream)
+hipError_t launch_gemm_bf16(bool fc1, const GemmArgs& g, int num_cu, hipStream_t s, hipEvent_t t0,
+                            hipEvent_t t1)
 {
     // a multiple of 8 workgroups: the LDS-staged loop splits its tiles over the 8 XCDs
     dim3 grid((unsigned)(num_cu >= 8 ? num_cu / 8 * 8 : 8)), block(512);
-    if (fc1)
-        hipLaunchKernelGGL(gemm_bf16_kernel<true>, grid, block, 0, s, g);
-    else
-        hipLaunchKernelGGL(gemm_bf16_kernel<false>, grid, block, 0, s, g);
+    auto go = [&](auto kernel) {
+        if (t0 || t1)
+            hipExtLaunchKernelGGL(kernel, grid, block, 0, s, t0, t1, 0, g);
+        else
+            hipLaunchKernelGGL(kernel, grid, block, 0, s, g);
+    };
+    if (fc1) go(gemm_bf16_kernel<true>);
+    else go(gemm_bf16_kernel<false>);
     return hipGetLastError();
 }
 

@@ -4,6 +4,8 @@
 // tiles with its two 4-wave halves as independent workers.  Both designs follow
 // the same arithmetic contract (gemm_mxfp8_stream.h).  W4: MXFP4 weights
 // (E2M1 B format) in both designs.
+#include <hip/hip_ext.h>
+
 #include "gemm_mxfp8_lds.h"
 #include "gemm_mxfp8_stream.h"
 
@@ -18,20 +20,25 @@ __global__ void __launch_bounds__(512, 1) gemm_mxfp8_kernel(MxGemmArgs g)
     mx_stream_tiles<FC1, W4>(g, blockIdx.x + (threadIdx.x >> 8) * gridDim.x, 2 * gridDim.x, (threadIdx.x >> 6) & 3);
 }
 
-hipError_t launch_gemm_mxfp8(bool fc1, bool w4, const MxGemmArgs& g, int num_cu, hipStream_t s)
+// t0 / t1 (optional): events that receive the launch's own start and end
+// (recorded by the dispatch itself, no separate marker in the stream)
+hipError_t launch_gemm_mxfp8(bool fc1, bool w4, const MxGemmArgs& g, int num_cu, hipStream_t s,
+                             hipEvent_t t0, hipEvent_t t1)
 {
     if (!g.stream_big && g.K % 128 != 0) return hipErrorInvalidValue;
     dim3 grid((unsigned)(num_cu >= 8 ? num_cu / 8 * 8 : 8)), block(512);
+    auto go = [&](auto kernel) {
+        if (t0 || t1)
+            hipExtLaunchKernelGGL(kernel, grid, block, 0, s, t0, t1, 0, g);
+        else
+            hipLaunchKernelGGL(kernel, grid, block, 0, s, g);
+    };
     if (w4) {
-        if (fc1)
-            hipLaunchKernelGGL((gemm_mxfp8_kernel<true, true>), grid, block, 0, s, g);
-        else
-            hipLaunchKernelGGL((gemm_mxfp8_kernel<false, true>), grid, block, 0, s, g);
+        if (fc1) go(gemm_mxfp8_kernel<true, true>);
+        else go(gemm_mxfp8_kernel<false, true>);
     } else {
-        if (fc1)
-            hipLaunchKernelGGL((gemm_mxfp8_kernel<true, false>), grid, block, 0, s, g);
-        else
-            hipLaunchKernelGGL((gemm_mxfp8_kernel<false, false>), grid, block, 0, s, g);
+        if (fc1) go(gemm_mxfp8_kernel<true, false>);
+        else go(gemm_mxfp8_kernel<false, false>);
     }
     return hipGetLastError();
 }

@@ -33,8 +33,10 @@ hipError_t launch_quant_x(const uint16_t* x, int64_t T_cap, const int32_t* live,
 #include "gemm_args.h"
 
 namespace moe {
-hipError_t launch_gemm_bf16(bool fc1, const GemmArgs& g, int num_cu, hipStream_t s);
-hipError_t launch_gemm_mxfp8(bool fc1, bool w4, const MxGemmArgs& g, int num_cu, hipStream_t s);
+hipError_t launch_gemm_bf16(bool fc1, const GemmArgs& g, int num_cu, hipStream_t s, hipEvent_t t0,
+                            hipEvent_t t1);
+hipError_t launch_gemm_mxfp8(bool fc1, bool w4, const MxGemmArgs& g, int num_cu, hipStream_t s,
+                             hipEvent_t t0, hipEvent_t t1);
 }  // namespace moe
 
 using namespace moe;
@@ -52,6 +54,15 @@ static hipError_t mark(moe_ctx* h, int i, hipStream_t s)
 {
     return (h->record_stages && h->stage_events[i]) ? hipEventRecord(h->stage_events[i], s)
                                                      : hipSuccess;
+}
+
+// Stage event i if stage events are on (else null).  Events 2 and 3 bracket
+// the FC1 + SwiGLU launch: they are handed to the launch itself, which records
+// its own start and end (a separate event record before and after it would
+// put marker packets in the stream, each costing ~5 us of idle GPU).
+static hipEvent_t stage_event(const moe_ctx* h, int i)
+{
+    return h->record_stages ? h->stage_events[i] : nullptr;
 }
 
 static thread_local std::string g_err;
@@ -267,7 +278,6 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
     if ((e = mark(h, 1, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     const int E = h->E, H = h->H, F = h->F;
     if (h->precision == MOE_BF16) {
-        if ((e = mark(h, 2, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
         GemmArgs g1;
         g1.A = (const uint16_t*)x;
         g1.W = (const uint16_t*)h->kbuf;
@@ -282,9 +292,8 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         g1.topk = h->k;
         g1.n_tiles_n = ((2 * F / 64) + 3) / 4;
         g1.max_tiles = (int)L.max_tiles;
-        e = launch_gemm_bf16(true, g1, h->num_cu, stream);
+        e = launch_gemm_bf16(true, g1, h->num_cu, stream, stage_event(h, 2), stage_event(h, 3));
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC1 launch");
-        if ((e = mark(h, 3, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
         GemmArgs g2 = g1;
         g2.A = (const uint16_t*)(w + L.hbuf);
         g2.W = (const uint16_t*)h->kbuf + (size_t)E * 2 * F * H;
@@ -293,7 +302,7 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         g2.N = H;
         g2.K = F;
         g2.n_tiles_n = ((H + 63) / 64 + 3) / 4;
-        e = launch_gemm_bf16(false, g2, h->num_cu, stream);
+        e = launch_gemm_bf16(false, g2, h->num_cu, stream, nullptr, nullptr);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
         if ((e = mark(h, 4, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     } else {
@@ -311,7 +320,6 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         e = launch_quant_x((const uint16_t*)x, T_cap, live_rows_dev, H, (uint8_t*)(w + L.xq),
                            (uint8_t*)(w + L.xs), h->num_cu, stream);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: quant-x launch");
-        if ((e = mark(h, 2, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
         MxGemmArgs g1;
         g1.A = (const uint8_t*)(w + L.xq);
         g1.As = (const uint8_t*)(w + L.xs);
@@ -329,9 +337,8 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         g1.topk = h->k;
         g1.n_tiles_n = ((2 * F / 64) + 3) / 4;
         g1.stream_big = H % 128 != 0;
-        e = launch_gemm_mxfp8(true, w4, g1, h->num_cu, stream);
+        e = launch_gemm_mxfp8(true, w4, g1, h->num_cu, stream, stage_event(h, 2), stage_event(h, 3));
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC1 launch");
-        if ((e = mark(h, 3, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
         MxGemmArgs g2 = g1;
         g2.A = (const uint8_t*)(w + L.hbuf);
         g2.As = (const uint8_t*)(w + L.hscale);
@@ -344,7 +351,7 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         g2.K = F;
         g2.n_tiles_n = ((H + 63) / 64 + 3) / 4;
         g2.stream_big = F % 128 != 0;
-        e = launch_gemm_mxfp8(false, w4, g2, h->num_cu, stream);
+        e = launch_gemm_mxfp8(false, w4, g2, h->num_cu, stream, nullptr, nullptr);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
         if ((e = mark(h, 4, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     }
