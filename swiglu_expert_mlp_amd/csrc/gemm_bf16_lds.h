@@ -29,6 +29,8 @@
 // 22% less FC1 traffic than row-tile order at 16K tokens).
 #pragma once
 
+#include <type_traits>
+
 #include "gemm_args.h"
 
 namespace moe {
@@ -68,7 +70,8 @@ __device__ __forceinline__ void lds_tiles(const GemmArgs& g, char* smem_base, in
     char (*smem)[kStageBytes] = (char (*)[kStageBytes])smem_base;
     const int NT = (g.N + kBigBN - 1) / kBigBN;
     const int total = n_mt * NT;
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;   // 8 waves
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // 8 waves, wave-uniform
     const int wm = wid >> 2, wn = wid & 3;                        // 2 x 4 waves
     const int K = g.K;
     const int nsteps = K / 32;                                    // 32-wide K steps
@@ -144,34 +147,56 @@ __device__ __forceinline__ void lds_tiles(const GemmArgs& g, char* smem_base, in
 #pragma unroll
         for (int s = 0; s < kRing - 1; ++s)
             if (s < nsteps) issue(s);
-        for (int s = 0; s < nsteps; ++s) {
-            // step s landed when at most the later in-flight steps remain
-            const int later = min(kRing - 2, nsteps - 1 - s);
-            if (later >= 2) WAIT_VMCNT(8);
-            else if (later == 1) WAIT_VMCNT(4);
-            else WAIT_VMCNT(0);
-            // a bare barrier: each wave has waited for its own loads of step s,
-            // and __syncthreads() would also wait for the steps still in flight
-            __builtin_amdgcn_s_barrier();
-            // refill the slot every wave finished reading in the previous step
-            if (s + kRing - 1 < nsteps) issue(s + kRing - 1);
-            const char* As = smem[s % kRing];
-            const char* Bs = As + 16 * 1024;
-            bf16x8 a[8], b[4];
+        // the K loop for a wave whose half of the tile holds NG valid 16-row
+        // groups: groups wholly past the tile's rows (the last tile of an
+        // expert) read no fragments and issue no MFMAs, which frees the SIMD's
+        // matrix pipe for the other wave on it; no valid row changes
+        auto kloop = [&](auto NGC) {
+            constexpr int NG = decltype(NGC)::value;
+            for (int s = 0; s < nsteps; ++s) {
+                // step s landed when at most the later in-flight steps remain
+                const int later = min(kRing - 2, nsteps - 1 - s);
+                if (later >= 2) WAIT_VMCNT(8);
+                else if (later == 1) WAIT_VMCNT(4);
+                else WAIT_VMCNT(0);
+                // a bare barrier: each wave has waited for its own loads of step s,
+                // and __syncthreads() would also wait for the steps still in flight
+                __builtin_amdgcn_s_barrier();
+                // refill the slot every wave finished reading in the previous step
+                if (s + kRing - 1 < nsteps) issue(s + kRing - 1);
+                if constexpr (NG > 0) {
+                    const char* As = smem[s % kRing];
+                    const char* Bs = As + 16 * 1024;
+                    bf16x8 a[NG], b[4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) a[i] = __builtin_bit_cast(bf16x8, *(const uint4*)(As + (8 * wm + i) * 1024 + a_off));
+                    for (int i = 0; i < NG; ++i)
+                        a[i] = __builtin_bit_cast(bf16x8, *(const uint4*)(As + (8 * wm + i) * 1024 + a_off));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = lds_frag(Bs + (4 * wn + j) * 1024, lane);
+                    for (int j = 0; j < 4; ++j) b[j] = lds_frag(Bs + (4 * wn + j) * 1024, lane);
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+                    for (int i = 0; i < NG; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-            // issue all twelve fragment reads before the MFMAs: left alone, the
-            // scheduler reads two A fragments at a time and waits for them
-            // between groups of eight MFMAs (four LDS round trips per step)
-            __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
+                        for (int j = 0; j < 4; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+                    // issue all fragment reads before the MFMAs: left alone, the
+                    // scheduler reads two A fragments at a time and waits for them
+                    // between groups of eight MFMAs (four LDS round trips per step)
+                    __builtin_amdgcn_sched_group_barrier(0x100, NG + 4, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NG, 0);
+                }
+            }
+        };
+        const int ngw = min(8, max(0, (rows - 128 * wm + 15) >> 4));
+        switch (ngw) {
+            case 8: kloop(std::integral_constant<int, 8>{}); break;
+            case 7: kloop(std::integral_constant<int, 7>{}); break;
+            case 6: kloop(std::integral_constant<int, 6>{}); break;
+            case 5: kloop(std::integral_constant<int, 5>{}); break;
+            case 4: kloop(std::integral_constant<int, 4>{}); break;
+            case 3: kloop(std::integral_constant<int, 3>{}); break;
+            case 2: kloop(std::integral_constant<int, 2>{}); break;
+            case 1: kloop(std::integral_constant<int, 1>{}); break;
+            default: kloop(std::integral_constant<int, 0>{}); break;
         }
 
         // epilogue: lane holds rows 4 (lane / 16) + v of each 16-row group, column lane % 16
