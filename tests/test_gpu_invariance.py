@@ -252,3 +252,25 @@ def test_contract_violations_flagged_and_match_oracle(precision):
     ws = m.new_workspace(w.T_cap)
     m.route(logits, live_tensor(w.T + 1), ws=ws)
     assert m.check(ws) == 4
+
+
+@pytest.mark.parametrize("name", ["decode_T300", "mxfp8_T300"])
+def test_stage_events_leave_outputs_unchanged(name):
+    """The stage-timing hook (events 2 and 3 are recorded by the FC1 launch's
+    own dispatch) changes no output bit, times a positive FC1 stage and keeps
+    the stage boundaries in order."""
+    c, m = case(name), handle(name)
+    x, ids, probs = c.dev()
+    T = c.w.T
+    ref = bits(forward(m, x, ids, probs, T)[0])
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    m.set_stage_events(evs)
+    try:
+        got = bits(forward(m, x, ids, probs, T)[0])
+    finally:
+        m.set_stage_events(None)
+    torch.cuda.synchronize()
+    assert np.array_equal(got, ref)
+    t = [evs[0].elapsed_time(e) for e in evs]
+    assert t[3] - t[2] > 0, t
+    assert all(b >= a - 1e-3 for a, b in zip(t, t[1:])), t
