@@ -30,7 +30,7 @@ struct GemmArgs {
     const uint16_t* A;         // FC1: x [T_cap][H]; FC2: hbuf [rows][F]
     const uint16_t* W;         // FC1: packed W1 [E][2F][H]; FC2: W2 [E][H][F]
     const int32_t* perm_src;   // FC1: grouped row -> route (t * k + j)
-    const int2* tiles;         // (expert, first row) per M tile (streaming kernel)
+    const int2* tiles;         // (expert, first row) per 64-row M tile
     const int2* tiles_big;     // (expert, first row) per 256-row M tile (LDS-staged kernel)
     const int32_t* offsets;    // [E + 1]
     const WsHeader* hdr;       // n_tiles, n_tiles_big

@@ -133,8 +133,8 @@ __device__ void prep_finish(const PrepArgs& a, int T, int nch, int k, int32_t li
     for (int q = 0; q < PER; ++q) mine += cnt[q];
     int total;
     int off = block_exclusive_scan(mine, &total, lds);
-    // M tiles: an expert with at most kBigMin rows goes to the streaming GEMM
-    // (64-row tiles), a larger one to the LDS-staged GEMM (256-row tiles)
+    // M tiles: an expert with at most kBigMin rows goes to the 64-row tiles,
+    // a larger one to the 256-row tiles
     int ntile_mine = 0, nbig_mine = 0;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {

@@ -59,7 +59,7 @@ SMALL = {
     # MXFP8 experts past 128 rows with K a multiple of 128 (LDS-staged kernel):
     # ragged 256-row tiles, a partial 256-column tile, 2 and 3 K steps
     "mx_big": Workload("mx_big", 600, 600, 256, 384, 4, 2, "mxfp8"),
-    # MXFP4 weights (streaming tiles for every expert size)
+    # MXFP4 weights: 64-row streaming tiles, and 256-row LDS-staged tiles in mx4_big
     "decode_mx4_T64": WORKLOADS["decode_mxfp4"].with_tokens(64),
     "mx4_T96": WORKLOADS["mxfp4_16k"].with_tokens(96),
     "odd_mxfp4": Workload("odd_mxfp4", 77, 80, 96, 160, 5, 3, "mxfp4"),
