@@ -36,30 +36,39 @@ __device__ __forceinline__ int32_t clamp_live(int32_t live, int64_t T_cap)
     return live < 0 ? 0 : (live > T_cap ? (int32_t)T_cap : live);
 }
 
-// Block-wide exclusive scan of one int per thread (blockDim.x <= 1024).
-// Returns the exclusive prefix; *total gets the sum.
-__device__ int block_exclusive_scan(int v, int* total, int* lds /* >= 32 ints */)
+// Block-wide exclusive scans of three ints per thread at once (blockDim.x <=
+// 1024): the shuffles of the three run side by side.  v[i] becomes its
+// exclusive prefix, total[i] the sum.
+__device__ void block_exclusive_scan3(int (&v)[3], int (&total)[3], int* lds /* >= 96 ints */)
 {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int nw = (blockDim.x + 63) >> 6;
-    int inc = v;
+    int inc[3] = {v[0], v[1], v[2]};
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        int o = __shfl_up(inc, off, kWave);
-        if (lane >= off) inc += o;
+        int o[3];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) o[i] = __shfl_up(inc[i], off, kWave);
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+            if (lane >= off) inc[i] += o[i];
     }
-    if (lane == 63) lds[wid] = inc;
+    if (lane == 63)
+#pragma unroll
+        for (int i = 0; i < 3; ++i) lds[32 * i + wid] = inc[i];
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (threadIdx.x < 3) {
         int run = 0;
-        for (int w = 0; w < nw; ++w) { int c = lds[w]; lds[w] = run; run += c; }
-        lds[31] = run;
+        for (int w = 0; w < nw; ++w) { int c = lds[32 * threadIdx.x + w]; lds[32 * threadIdx.x + w] = run; run += c; }
+        lds[32 * threadIdx.x + 31] = run;
     }
     __syncthreads();
-    int excl = lds[wid] + inc - v;
-    *total = lds[31];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        v[i] = lds[32 * i + wid] + inc[i] - v[i];
+        total[i] = lds[32 * i + 31];
+    }
     __syncthreads();
-    return excl;
 }
 
 constexpr int kSlab = kMaxExperts * (kChunkTok / 32);   // ints of the LDS token bitmaps
@@ -131,8 +140,6 @@ __device__ void prep_finish(const PrepArgs& a, int T, int nch, int k, int32_t li
     int mine = 0;
 #pragma unroll
     for (int q = 0; q < PER; ++q) mine += cnt[q];
-    int total;
-    int off = block_exclusive_scan(mine, &total, lds);
     // M tiles: an expert with at most kBigMin rows goes to the 64-row tiles,
     // a larger one to the 256-row tiles
     int ntile_mine = 0, nbig_mine = 0;
@@ -141,9 +148,10 @@ __device__ void prep_finish(const PrepArgs& a, int T, int nch, int k, int32_t li
         if (cnt[q] > kBigMin) nbig_mine += (cnt[q] + kBigBMRows - 1) / kBigBMRows;
         else ntile_mine += (cnt[q] + kBM - 1) / kBM;
     }
-    int ntotal, nbig;
-    int tfirst = block_exclusive_scan(ntile_mine, &ntotal, lds);
-    int bfirst = block_exclusive_scan(nbig_mine, &nbig, lds);
+    int sc[3] = {mine, ntile_mine, nbig_mine}, tot[3];
+    block_exclusive_scan3(sc, tot, lds);
+    int off = sc[0], tfirst = sc[1], bfirst = sc[2];
+    const int total = tot[0], ntotal = tot[1], nbig = tot[2];
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
         const int e = threadIdx.x * PER + q;
@@ -187,7 +195,7 @@ template <int K>
 __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a)
 {
     __shared__ uint32_t bm[kMaxExperts * (kChunkTok / 32)];
-    __shared__ int lds[32];
+    __shared__ int lds[96];
     __shared__ int s_last;
     __shared__ int loc[2 * kMaxExperts];         // single-chunk launch: counts, offsets
     const int32_t live = *a.live;
@@ -242,22 +250,32 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a)
     for (int j = 0; j < K; ++j)
         if (keep[j]) atomicOr(&bm[id[j] * 8 + word], 1u << bit);
     __syncthreads();
-    // stable rank = tokens of this chunk below t that route to the same expert
+    // stable rank = tokens of this chunk below t that route to the same expert:
+    // the expert's 8 bitmap words in two 16-byte reads, the words below this
+    // token's counted whole, its own word below its bit (no dependent reads)
     int rank[K];
 #pragma unroll
     for (int j = 0; j < K; ++j) {
         rank[j] = -1;
         if (keep[j]) {
-            const uint32_t* m = &bm[id[j] * 8];
-            rank[j] = __popc(m[word] & ((1u << bit) - 1u));
-            for (int w = 0; w < word; ++w) rank[j] += __popc(m[w]);
+            const uint4 m0 = *(const uint4*)&bm[id[j] * 8];
+            const uint4 m1 = *(const uint4*)&bm[id[j] * 8 + 4];
+            const uint32_t m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+            int r = 0;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                const uint32_t mask = w < word ? ~0u : (w == word ? (1u << bit) - 1u : 0u);
+                r += __popc(m[w] & mask);
+            }
+            rank[j] = r;
         }
         if (valid && !single) a.local_rank[(int64_t)t * K + j] = rank[j];
     }
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        int n = 0;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) n += __popc(bm[e * 8 + w]);
+        const uint4 m0 = *(const uint4*)&bm[e * 8];
+        const uint4 m1 = *(const uint4*)&bm[e * 8 + 4];
+        const int n = __popc(m0.x) + __popc(m0.y) + __popc(m0.z) + __popc(m0.w) +
+                      __popc(m1.x) + __popc(m1.y) + __popc(m1.z) + __popc(m1.w);
         if (single) loc[e] = n;
         else a.chunk_base[(int64_t)c * E + e] = n;
     }
