@@ -74,6 +74,7 @@ def copy_calibration():
 GEMM_SOURCES = ["swiglu_expert_mlp_amd/csrc/gemm_bf16.hip", "swiglu_expert_mlp_amd/csrc/gemm_bf16_small.h",
                 "swiglu_expert_mlp_amd/csrc/gemm_bf16_lds.h", "swiglu_expert_mlp_amd/csrc/gemm_mxfp8.hip",
                 "swiglu_expert_mlp_amd/csrc/gemm_mxfp8_stream.h", "swiglu_expert_mlp_amd/csrc/gemm_mxfp8_lds.h",
+                "swiglu_expert_mlp_amd/csrc/gemm_mx4_small.h",
                 "swiglu_expert_mlp_amd/csrc/gemm_args.h", "swiglu_expert_mlp_amd/csrc/common.h"]
 
 
@@ -265,11 +266,14 @@ def main():
         roof = dict(bound="hbm", achieved=ab["fc1"] / (fc1_us * 1e-6) / 1e9,
                     peak=HBM_PEAK_GBS, unit="GB/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    # the FC1 + SwiGLU stage is one launch; its tiles are 256-row tiles (experts
-    # with more than 128 rows) or 64-row tiles (the others)
+    # the FC1 + SwiGLU stage: its tiles are 256-row tiles (experts with more than
+    # 128 rows) or 64-row tiles (the others); one launch, except MXFP4 above a
+    # 1024-token capacity (the 256-row launch, then the 64-row launch)
     roof["kernel"] = {"bf16": "moe::gemm_bf16_kernel<true>",
                       "mxfp8": "moe::gemm_mxfp8_kernel<true, false>",
-                      "mxfp4": "moe::gemm_mxfp8_kernel<true, true>"}[w.precision]
+                      "mxfp4": "moe::gemm_mx4_small_kernel<true>" if w.T_cap <= 1024 else
+                               "moe::gemm_mxfp8_kernel<true, true> + moe::gemm_mx4_small_kernel<true>"
+                      }[w.precision]
     roof["tiles"] = "256-row" if int(loads.min()) > 128 else (
         "64-row" if int(loads.max()) <= 128 else "256-row + 64-row")
     roof["kernel_us"] = fc1_us

@@ -113,12 +113,17 @@ size_t moe_weight_bytes(moe_handle h);
  *       ((e*(N/16) + n/16)*KQ + (b/4)/4)*256 + ((b%4)*16 + n%16)*4 + (b/4)%4;
  *     positions past K hold code 0 and scale 127.  Scale = power-of-two
  *     ceiling of the block's max magnitude / 448 (so no code saturates).
- *   kbuf layout (mxfp4): as mxfp8, with one 1 KB code block per 16 rows x
- *     128 K: code (e, n, k) in byte
- *       ((e*(N/16) + n/16)*KS + k/128)*1024 + ((k%128)/32*16 + n%16)*16 + (k%32)/2,
- *     the low nibble for even k; scales as mxfp8 with the scale =
- *     power-of-two ceiling of the block's max magnitude / 6, codes rounded to
- *     the nearest E2M1 value with ties to the even code.
+ *   kbuf layout (mxfp4): sections as mxfp8, with one 1 KB code block per 16
+ *     rows x 128 K and the blocks of an expert in 512-row groups (one K step
+ *     of a group is one contiguous run): with c = n/16, t = k/128,
+ *     g = c/32 and w = min(32, N/16 - 32g), code (e, n, k) in byte
+ *       (e*(N/16)*KS + g*32*KS + t*w + c%32)*1024 + ((k%128)/32*16 + n%16)*16
+ *         + (k%32)/2,
+ *     the low nibble for even k; the scale of 32-block b = k/32 at byte
+ *       (e*(N/16)*KQ + g*32*KQ + (b/16)*w + c%32)*256 + ((b%4)*16 + n%16)*4
+ *         + (b/4)%4,
+ *     the scale = power-of-two ceiling of the block's max magnitude / 6,
+ *     codes rounded to the nearest E2M1 value with ties to the even code.
  * The handle remembers kbuf: every later forward reads it.  Calling again
  * (same or another buffer) is the refit; forwards enqueued before it on the
  * same stream read the old contents.  w1/w2 may be freed once the work on

@@ -822,11 +822,25 @@ void orc_pack_mxfp8(int E, int H, int F, const uint16_t* w1, const uint16_t* w2,
 
 /* MXFP4 codes of a weight with N rows of K elements: one 1 KB block per 16
  * rows x 128 K, lane (k%128)/32*16 + n%16 holding K (k%128)/32*32 + [0, 32)
- * of row n as 16 bytes, two codes per byte, the lower K in the low nibble:
- *   ((e*(N/16) + n/16)*KS + k/128)*1024 + ((k%128)/32*16 + n%16)*16 + (k%32)/2,
- *   nibble (k%2).
- * Scales as MXFP8.  Codes for k >= K are 0, scales 127 (2^0). */
+ * of row n as 16 bytes, two codes per byte, the lower K in the low nibble.
+ * The blocks of an expert are in 512-row groups: with c = n/16, g = c/32 and
+ * w = min(32, N/16 - 32g) (the width of c's group), block (c, t = k/128) is
+ * block number e*(N/16)*KS + g*32*KS + t*w + c%32, so code (e, n, k) is in
+ *   byte (that block)*1024 + ((k%128)/32*16 + n%16)*16 + (k%32)/2, nibble k%2.
+ * The 256-byte scale groups (4 K steps each, the MXFP8 arrangement inside)
+ * follow the same grouping with KQ for KS and the group number Q = b/16 of
+ * 32-block b for t: byte (e*(N/16)*KQ + g*32*KQ + Q*w + c%32)*256
+ * + ((b%4)*16 + n%16)*4 + (b/4)%4.  Codes for k >= K are 0, scales 127. */
 static int64_t code4_bytes(int E, int64_t N, int64_t K) { return (int64_t)E * (N / 16) * ksteps(K) * 1024; }
+
+/* block number of column block c, step (or scale group) t in an expert's
+ * section of nt column blocks and nsteps steps, 512-row grouping */
+static int64_t mx4_block(int64_t e, int64_t c, int64_t t, int64_t nt, int64_t nsteps)
+{
+    const int64_t g = c / 32;
+    const int64_t w = nt - 32 * g < 32 ? nt - 32 * g : 32;
+    return e * nt * nsteps + g * 32 * nsteps + t * w + c % 32;
+}
 
 static void pack_mx4_section(int E, int64_t N, int64_t K, int64_t F, int fc1, const uint16_t* w,
                              uint8_t* codes, uint8_t* scales)
@@ -842,12 +856,12 @@ static void pack_mx4_section(int E, int64_t N, int64_t K, int64_t F, int fc1, co
             int64_t src = fc1 ? fc1_logical_row(n, F) : n;
             for (int64_t k = 0; k < K; ++k) row[k] = orc_bf16_value(w[(e * N + src) * K + k]);
             orc_mx4_quantize(row, 1, K, c, sc);
-            int64_t blk = e * (N / 16) + n / 16;
+            const int64_t nt = N / 16;
             for (int64_t k = 0; k < K; ++k)
-                codes[(blk * KS + k / 128) * 1024 + ((k % 128) / 32 * 16 + n % 16) * 16 + (k % 32) / 2] |=
-                    (uint8_t)(c[k] << (4 * (k % 2)));
+                codes[mx4_block(e, n / 16, k / 128, nt, KS) * 1024 + ((k % 128) / 32 * 16 + n % 16) * 16 +
+                      (k % 32) / 2] |= (uint8_t)(c[k] << (4 * (k % 2)));
             for (int64_t b = 0; b < K / 32; ++b)
-                scales[(blk * KQ + (b / 4) / 4) * 256 + ((b % 4) * 16 + n % 16) * 4 + (b / 4) % 4] =
+                scales[mx4_block(e, n / 16, b / 16, nt, KQ) * 256 + ((b % 4) * 16 + n % 16) * 4 + (b / 4) % 4] =
                     sc[b];
         }
     free(row); free(c); free(sc);

@@ -61,6 +61,11 @@ struct MxGemmArgs {
     int n_tiles_n;
     int stream_big;            // 1: the streaming kernel also takes the 256-row tiles
                                // (as four 64-row tiles each); 0: the LDS-staged kernel does
+    int lds_small;             // MXFP4: 0: the streaming loop takes the 64-row tiles; 1: the
+                               // LDS-staged 64-row kernel does; 2: that kernel also takes the
+                               // 256-row tiles (four 64-row tiles each, no 256-row launch)
+    int small_batch;           // 1: decode-sized batch (the caller's token capacity <= 1024)
+    int64_t a_bytes;           // bytes of A (rows x K)
 };
 
 }  // namespace moe

@@ -8,6 +8,7 @@
 
 #include "gemm_mxfp8_lds.h"
 #include "gemm_mxfp8_stream.h"
+#include "gemm_mx4_small.h"
 
 namespace moe {
 
@@ -15,9 +16,23 @@ template <bool FC1, bool W4>
 __global__ void __launch_bounds__(512, 1) gemm_mxfp8_kernel(MxGemmArgs g)
 {
     if (!g.stream_big) mx_lds_tiles<FC1, W4>(g);
+    if (g.lds_small) return;          // the 64-row tiles have a launch of their own
     // the two halves of a workgroup are workers b and b + grid: consecutive
     // tiles (the N tiles of one M tile) go to different CUs
     mx_stream_tiles<FC1, W4>(g, blockIdx.x + (threadIdx.x >> 8) * gridDim.x, 2 * gridDim.x, (threadIdx.x >> 6) & 3);
+}
+
+// MXFP4, the LDS-staged 64-row tiles (gemm_mx4_small.h)
+template <bool FC1>
+__global__ void __launch_bounds__(512, 1) gemm_mx4_small_kernel(MxGemmArgs g)
+{
+    __shared__ __attribute__((aligned(1024))) char w0[kM6SlotAll];
+    __shared__ __attribute__((aligned(1024))) char w1[kM6SlotAll];
+    __shared__ __attribute__((aligned(1024))) char w2[kM6SlotAll];
+    __shared__ __attribute__((aligned(1024))) char q0[kM6ASlot];
+    __shared__ __attribute__((aligned(1024))) char q1[kM6ASlot];
+    __shared__ __attribute__((aligned(1024))) char q2[kM6ASlot];
+    mx4_small_tiles<FC1>(g, M6Ring{w0, w1, w2, q0, q1, q2});
 }
 
 // t0 / t1 (optional): events that receive the launch's own start and end
@@ -27,18 +42,36 @@ hipError_t launch_gemm_mxfp8(bool fc1, bool w4, const MxGemmArgs& g, int num_cu,
 {
     if (!g.stream_big && g.K % 128 != 0) return hipErrorInvalidValue;
     dim3 grid((unsigned)(num_cu >= 8 ? num_cu / 8 * 8 : 8)), block(512);
-    auto go = [&](auto kernel) {
-        if (t0 || t1)
-            hipExtLaunchKernelGGL(kernel, grid, block, 0, s, t0, t1, 0, g);
+    auto go = [&](auto kernel, hipEvent_t e0, hipEvent_t e1, const MxGemmArgs& a) {
+        if (e0 || e1)
+            hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, a);
         else
-            hipLaunchKernelGGL(kernel, grid, block, 0, s, g);
+            hipLaunchKernelGGL(kernel, grid, block, 0, s, a);
     };
+    MxGemmArgs a = g;
+    a.lds_small = 0;
+    // MXFP4 with K a multiple of 128 and 32-bit buffer offsets: the 64-row
+    // tiles go to the LDS-staged kernel, after the 256-row tiles' launch, or
+    // alone (taking the 256-row tiles too) at decode-sized batches
+    const bool mx4_lds = w4 && !g.stream_big && g.a_bytes < ((int64_t)1 << 31) &&
+                         (int64_t)g.N * g.K / 2 < ((int64_t)1 << 31);
+    if (mx4_lds) {
+        a.lds_small = g.small_batch ? 2 : 1;
+        if (a.lds_small == 1) {
+            if (fc1) go(gemm_mxfp8_kernel<true, true>, t0, nullptr, a);
+            else go(gemm_mxfp8_kernel<false, true>, t0, nullptr, a);
+        }
+        hipEvent_t e0 = a.lds_small == 2 ? t0 : nullptr;
+        if (fc1) go(gemm_mx4_small_kernel<true>, e0, t1, a);
+        else go(gemm_mx4_small_kernel<false>, e0, t1, a);
+        return hipGetLastError();
+    }
     if (w4) {
-        if (fc1) go(gemm_mxfp8_kernel<true, true>);
-        else go(gemm_mxfp8_kernel<false, true>);
+        if (fc1) go(gemm_mxfp8_kernel<true, true>, t0, t1, a);
+        else go(gemm_mxfp8_kernel<false, true>, t0, t1, a);
     } else {
-        if (fc1) go(gemm_mxfp8_kernel<true, false>);
-        else go(gemm_mxfp8_kernel<false, false>);
+        if (fc1) go(gemm_mxfp8_kernel<true, false>, t0, t1, a);
+        else go(gemm_mxfp8_kernel<false, false>, t0, t1, a);
     }
     return hipGetLastError();
 }

@@ -137,12 +137,17 @@ __device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
             sptr = g.As + src * KB;
         }
         // weight code and scale loads: column blocks 2 wid + i
-        int64_t bblk[2];
+        // weight blocks of K step s: MXFP8 [expert][c16][s] (2 KB); MXFP4 in
+        // 512-column groups (wblock_index, 1 KB codes / 256-byte scale groups)
+        int64_t bblk[2], b4[2], q4[2], w4s[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             int c16 = n0 / 16 + 2 * wid + i;
             if (c16 >= nt16) c16 = nt16 - 1;
             bblk[i] = (int64_t)e * nt16 + c16;
+            b4[i] = (int64_t)e * nt16 * KS + wblock_index(c16, 0, nt16, KS);
+            q4[i] = (int64_t)e * nt16 * KQ + wblock_index(c16, 0, nt16, KQ);
+            w4s[i] = wblock_step(c16, nt16);
         }
         // loads of step s into stage Q
         auto issue = [&](auto QC, int s) {
@@ -154,7 +159,7 @@ __device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
             if constexpr (W4) {
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
-                    mx_load_block_to_lds(g.W + (bblk[i] * KS + s) * 1024 + 16 * lane,
+                    mx_load_block_to_lds(g.W + (b4[i] + s * w4s[i]) * 1024 + 16 * lane,
                                          st + 32768 + (2 * wid + i) * 1024);
             } else {
 #pragma unroll
@@ -167,7 +172,8 @@ __device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
             if (wid < 4) mx_load_dword_to_lds(sptr + 4 * s, st + kMxAsOff + 256 * wid);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                mx_load_dword_to_lds(g.Ws + (bblk[i] * KQ + (s >> 2)) * 256 + 4 * lane,
+                mx_load_dword_to_lds(g.Ws + (W4 ? q4[i] + (s >> 2) * w4s[i] : bblk[i] * KQ + (s >> 2)) * 256 +
+                                         4 * lane,
                                      st + kMxBsOff + (2 * wid + i) * 256);
         };
 

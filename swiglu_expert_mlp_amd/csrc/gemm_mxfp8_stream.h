@@ -57,16 +57,27 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs& g, int e, int row
     // [expert][row / 16][k / 128], in lane order (MXFP8: two 1 KB halves, 16
     // codes per lane each); scales in 256-byte groups of 4 K-steps, one dword
     // per lane (byte = step % 4).
+    // MXFP4: blocks in 512-column groups (wblock_index): K step s of column
+    // block c16 at wblock_index(c16, 0) + s * wblock_step(c16), the scale
+    // group of steps 4q .. 4q + 3 likewise with q for s
     const int nt16 = g.N / 16, KS = (K + 127) / 128, KQ = (KS + 3) / 4;
     const uint8_t* bp[4];
     const uint32_t* bs[4];
+    int bstep[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
         int c16 = cb * 4 + ct;
         if (c16 >= nt16) c16 = nt16 - 1;
         const int64_t blk = (int64_t)e * nt16 + c16;
-        bp[ct] = g.W + blk * KS * kBlk + 16 * lane;
-        bs[ct] = (const uint32_t*)(g.Ws + blk * KQ * 256) + lane;
+        if constexpr (W4) {
+            bstep[ct] = (int)wblock_step(c16, nt16);
+            bp[ct] = g.W + ((int64_t)e * nt16 * KS + wblock_index(c16, 0, nt16, KS)) * 1024 + 16 * lane;
+            bs[ct] = (const uint32_t*)(g.Ws + ((int64_t)e * nt16 * KQ + wblock_index(c16, 0, nt16, KQ)) * 256) + lane;
+        } else {
+            bstep[ct] = 1;
+            bp[ct] = g.W + blk * KS * kBlk + 16 * lane;
+            bs[ct] = (const uint32_t*)(g.Ws + blk * KQ * 256) + lane;
+        }
     }
     f32x4 acc[NG][4];
 #pragma unroll
@@ -97,7 +108,7 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs& g, int e, int row
             // weights are read once per tile (non-temporal, see the bf16 kernel)
             if constexpr (W4) {
                 // the upper half of an E2M1 operand is not read by the MFMA
-                const uint4 lo = load_stream16(bp[ct] + step * 1024);
+                const uint4 lo = load_stream16(bp[ct] + step * bstep[ct] * 1024);
                 b[ct] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
             } else {
                 const uint4 lo = load_stream16(bp[ct] + step * 2048);
@@ -105,7 +116,7 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs& g, int e, int row
                 b[ct] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                               (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
             }
-            sb[ct] = (int)((bs[ct][(step >> 2) * 64] >> (8 * (step & 3))) & 0xffu);
+            sb[ct] = (int)((bs[ct][(step >> 2) * bstep[ct] * 64] >> (8 * (step & 3))) & 0xffu);
         }
 #pragma unroll
         for (int rg = 0; rg < NG; ++rg)

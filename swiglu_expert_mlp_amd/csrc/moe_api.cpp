@@ -320,7 +320,7 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         e = launch_quant_x((const uint16_t*)x, T_cap, live_rows_dev, H, (uint8_t*)(w + L.xq),
                            (uint8_t*)(w + L.xs), h->num_cu, stream);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: quant-x launch");
-        MxGemmArgs g1;
+        MxGemmArgs g1{};
         g1.A = (const uint8_t*)(w + L.xq);
         g1.As = (const uint8_t*)(w + L.xs);
         g1.W = c1;
@@ -337,6 +337,8 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         g1.topk = h->k;
         g1.n_tiles_n = ((2 * F / 64) + 3) / 4;
         g1.stream_big = H % 128 != 0;
+        g1.small_batch = T_cap <= 1024;
+        g1.a_bytes = T_cap * H;
         e = launch_gemm_mxfp8(true, w4, g1, h->num_cu, stream, stage_event(h, 2), stage_event(h, 3));
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC1 launch");
         MxGemmArgs g2 = g1;
@@ -351,6 +353,7 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         g2.K = F;
         g2.n_tiles_n = ((H + 63) / 64 + 3) / 4;
         g2.stream_big = F % 128 != 0;
+        g2.a_bytes = T_cap * h->k * F;
         e = launch_gemm_mxfp8(false, w4, g2, h->num_cu, stream, nullptr, nullptr);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
         if ((e = mark(h, 4, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");

@@ -139,7 +139,9 @@ __global__ void __launch_bounds__(256) pack_mx_kernel(const uint16_t* __restrict
 // MXFP4 weights, tiled layout.  One thread quantizes one 32-element block
 // (row n, block q of K) and writes its 32 codes as the 16 bytes of lane
 // 16 (q % 4) + n % 16 of the row's 1 KB block of K step q / 4; blocks past
-// K/32 (the padding of the last step) get zero codes and scale 127.
+// K/32 (the padding of the last step) get zero codes and scale 127.  The code
+// blocks and the 256-byte scale groups of an expert are in 512-column groups
+// (wblock_index), so one K step of a group is one contiguous run.
 __global__ void __launch_bounds__(256) pack_mx4_kernel(const uint16_t* __restrict__ src,
                                                        uint8_t* __restrict__ codes,
                                                        uint8_t* __restrict__ scales, int E, int N,
@@ -155,9 +157,10 @@ __global__ void __launch_bounds__(256) pack_mx4_kernel(const uint16_t* __restric
         const int64_t e = row / N, n = row - e * N;
         const int64_t n16 = n >> 4, r16 = n & 15;
         const int64_t step = q >> 2, kg = q & 3;
-        uint8_t* sc = scales + ((e * nt + n16) * KQ + (step >> 2)) * 256 +
+        uint8_t* sc = scales + (e * nt * KQ + wblock_index(n16, step >> 2, nt, KQ)) * 256 +
                       ((kg * 16 + r16) * 4) + (step & 3);
-        uint4* dst = (uint4*)(codes + ((e * nt + n16) * KS + step) * 1024 + (kg * 16 + r16) * 16);
+        uint4* dst = (uint4*)(codes + (e * nt * KS + wblock_index(n16, step, nt, KS)) * 1024 +
+                              (kg * 16 + r16) * 16);
         if (q >= K / 32) {
             *sc = 127;
             if (step < KS) *dst = make_uint4(0, 0, 0, 0);

@@ -663,15 +663,25 @@ def _unswizzle_mx(codes, scales, E, N, K):
 
 
 def _unswizzle_mx4(codes, scales, E, N, K):
-    """Inverse of the MXFP4 layout by reshapes: blocks [E][N/16][KS] of
-    [4 (k%128 / 32)][16 (n%16)][16 bytes], two codes per byte, low nibble first."""
+    """Inverse of the MXFP4 layout by reshapes, one 512-row group at a time:
+    per expert, groups of w = min(32, N/16 - 32 g) column blocks, each group
+    [KS][w] code blocks of [4 (k%128 / 32)][16 (n%16)][16 bytes] (two codes per
+    byte, low nibble first) and [KQ][w] scale groups of [4 (b%4)][16 (n%16)][4
+    (step%4)]."""
     KS = (K + 127) // 128
     KQ = (KS + 3) // 4
-    b = codes.reshape(E, N // 16, KS, 4, 16, 16)               # e n16 step g r16 byte
-    nib = np.stack([b & 15, b >> 4], axis=-1)                   # ... byte nibble
-    c = nib.transpose(0, 1, 4, 2, 3, 5, 6).reshape(E, N, KS * 128)
-    sc = scales.reshape(E, N // 16, KQ, 4, 16, 4)
-    sc = sc.transpose(0, 1, 4, 2, 5, 3).reshape(E, N, KQ * 16)
+    nt = N // 16
+    cb = codes.reshape(E, nt * KS * 1024)
+    sb = scales.reshape(E, nt * KQ * 256)
+    c = np.empty((E, N, KS * 128), dtype=np.uint8)
+    sc = np.empty((E, N, KQ * 16), dtype=np.uint8)
+    for g in range((nt + 31) // 32):
+        w = min(32, nt - 32 * g)
+        b = cb[:, g * 32 * KS * 1024:(g * 32 + w) * KS * 1024].reshape(E, KS, w, 4, 16, 16)
+        nib = np.stack([b & 15, b >> 4], axis=-1)               # e step c16 kg r16 byte nibble
+        c[:, g * 512:g * 512 + 16 * w] = nib.transpose(0, 2, 4, 1, 3, 5, 6).reshape(E, 16 * w, KS * 128)
+        q = sb[:, g * 32 * KQ * 256:(g * 32 + w) * KQ * 256].reshape(E, KQ, w, 4, 16, 4)
+        sc[:, g * 512:g * 512 + 16 * w] = q.transpose(0, 2, 4, 1, 5, 3).reshape(E, 16 * w, KQ * 16)
     return c, sc
 
 
@@ -727,10 +737,12 @@ def test_pack_mxfp8_layout_definition(H, F):
         assert np.all(c[:, :, K:] == 0) and np.all(sc[:, :, K // 32:] == 127)
 
 
-@pytest.mark.parametrize("H,F", [(256, 128), (96, 160)])
+@pytest.mark.parametrize("H,F", [(256, 128), (96, 160), (640, 320)])
 def test_pack_mxfp4_layout_definition(H, F):
     """MXFP4 codes and scales, unswizzled, are the per-row E2M1 quantization of
-    the interleaved bf16 weight; padding past K is code 0 and scale 127."""
+    the interleaved bf16 weight; padding past K is code 0 and scale 127
+    (H = 640, F = 320: both sections have 40 column blocks, one full 512-row
+    group and one of 8, and FC1 five K steps, so two scale groups)."""
     E = 2
     rng = np.random.default_rng(5)
     w1 = oracle.bf16_bits(rng.standard_normal((E, 2 * F, H)).astype(np.float32))
@@ -751,3 +763,18 @@ def test_pack_mxfp4_layout_definition(H, F):
         assert np.array_equal(c[:, :, :K].reshape(-1, K), qc)
         assert np.array_equal(sc[:, :, :K // 32].reshape(-1, K // 32), qs)
         assert np.all(c[:, :, K:] == 0) and np.all(sc[:, :, K // 32:] == 127)
+        # spot checks of the group order, written out by hand: row n = 16 c + 5
+        # of the last column block, K step t = KS - 1, lane group kg = 1
+        nt = N // 16
+        cl = nt - 1
+        g, w = cl // 32, min(32, nt - 32 * (cl // 32))
+        t, kg, n = KS - 1, 1, 16 * cl + 5
+        k = 128 * t + 32 * kg + 6                               # byte 3, low nibble
+        if k < K:
+            blk = 1 * nt * KS + g * 32 * KS + t * w + cl % 32   # expert 1
+            byte = buf[off[codes_at] + blk * 1024 + (kg * 16 + 5) * 16 + 3]
+            assert (byte & 15) == qc.reshape(E, N, K)[1, n, k]
+            b = k // 32                                         # its scale
+            grp = 1 * nt * KQ + g * 32 * KQ + (b // 16) * w + cl % 32
+            assert buf[off[scales_at] + grp * 256 + ((b % 4) * 16 + 5) * 4 + (b // 4) % 4] == \
+                qs.reshape(E, N, K // 32)[1, n, b]
