@@ -106,6 +106,32 @@ def test_64_row_and_256_row_tiles_agree_bitwise(name):
         assert np.array_equal(bits(part), wide[t0:t0 + 128]), f"tokens {t0}.."
 
 
+def test_mxfp4_small_capacity_runs_large_experts_as_64_row_tiles_bitwise():
+    """MXFP4 at a token capacity <= 1024 runs experts with more than 128 rows as
+    four 64-row tiles each (one launch); at a larger capacity they take the
+    256-row tiles.  Same tokens, capacity 600 vs 2400: the same bits."""
+    from swiglu_expert_mlp_amd import MoE
+    w = Workload("mx4_cap", 600, 600, 256, 384, 4, 2, "mxfp4")
+    c = Case(w, seed=13, outliers=True)
+    m = MoE(w.E, w.H, w.F, w.k, w.precision)
+    w1, w2 = c.weights_dev()
+    m.load_weights(w1, w2)
+    x, ids, probs = c.dev()
+    small, ws = forward(m, x, ids, probs, w.T)
+    counts = m.get_indices(ws, w.T)["counts"]
+    assert (counts > 128).sum() >= 2, counts
+    cap = 4 * w.T
+    xb = torch.full((cap, w.H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    xb[:w.T] = x
+    ib = torch.full((cap, w.k), 0x7FC00000, dtype=torch.int32, device="cuda")
+    ib[:w.T] = ids
+    pb = torch.full((cap, w.k), float("nan"), dtype=torch.float32, device="cuda")
+    pb[:w.T] = probs
+    large = bits(forward(m, xb, ib, pb, w.T)[0])
+    assert np.array_equal(large[:w.T], bits(small))
+    assert np.all(large[w.T:] == SENTINEL_BITS)
+
+
 @pytest.mark.parametrize("name", ["decode_T300", "mxfp8_T300", "mxfp4_T300"])
 def test_capacity_and_live_count_invariance(name):
     """Same tokens: capacity T vs 4T (rows past live are NaN), and live counts
