@@ -34,29 +34,29 @@
 
 namespace moe {
 
-constexpr int kM6Cols = 512;                    // columns per tile (8 waves x 64)
-constexpr int kM6Slot = 4096 + 1024 + 256;      // one wave's weight slot: codes, scale groups, activation scales
-constexpr int kM6SlotAll = 8 * kM6Slot;         // one weight slot of all 8 waves
-constexpr int kM6ASlot = 64 * 128;              // one activation-code slot: 64 rows x 128 bytes
-constexpr int kM6Loads = 10;                    // direct loads per wave and step
+constexpr int kMx4Cols = 512;                    // columns per tile (8 waves x 64)
+constexpr int kMx4Slot = 4096 + 1024 + 256;      // one wave's weight slot: codes, scale groups, activation scales
+constexpr int kMx4SlotAll = 8 * kMx4Slot;         // one weight slot of all 8 waves
+constexpr int kMx4ASlot = 64 * 128;              // one activation-code slot: 64 rows x 128 bytes
+constexpr int kMx4Loads = 10;                    // direct loads per wave and step
 
-typedef __attribute__((address_space(3))) void m6_lds_void;
+typedef __attribute__((address_space(3))) void mx4_lds_void;
 
 // third dword of a raw buffer descriptor on CDNA (32-bit data format, no
 // swizzle, no stride): byte-addressed loads with a range check
-constexpr int kM6RsrcWord3 = 0x00020000;
+constexpr int kMx4RsrcWord3 = 0x00020000;
 
-#define M6_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+#define MX4_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 
 // Ring slots: three weight-slot objects (w*: this wave's part) and three
 // activation-slot objects (q*), each addressed with a static slot number so
 // the compiler can tell a read of one slot from a direct load into another.
-struct M6Ring {
+struct Mx4Ring {
     char *w0, *w1, *w2, *q0, *q1, *q2;
 };
 
 template <bool FC1, int NG>
-__device__ __forceinline__ void mx4_tile(const MxGemmArgs& g, const M6Ring& rg, int wid, int e, int row0,
+__device__ __forceinline__ void mx4_tile(const MxGemmArgs& g, const Mx4Ring& rg, int wid, int e, int row0,
                                          int rows, int cb, bool has_cols)
 {
     const int lane = threadIdx.x & 63;
@@ -84,15 +84,15 @@ __device__ __forceinline__ void mx4_tile(const MxGemmArgs& g, const M6Ring& rg, 
         if constexpr (FC1) src = g.perm_src[src] / g.topk;
         soff = (int)(src * KB);
     }
-    const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, 0x7fffffff, kM6RsrcWord3);
-    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc((void*)g.As, (short)0, 0x7fffffff, kM6RsrcWord3);
+    const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, 0x7fffffff, kMx4RsrcWord3);
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc((void*)g.As, (short)0, 0x7fffffff, kMx4RsrcWord3);
     //  weights: the expert's section, block (c16, t) at wblock_index(c16, t); a
     //  wave without columns re-reads the last column block (loads stay
     //  uniform, the multiply is skipped)
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(g.W + (int64_t)e * nt16 * KS * 1024), (short)0, nt16 * KS * 1024, kM6RsrcWord3);
+        (void*)(g.W + (int64_t)e * nt16 * KS * 1024), (short)0, nt16 * KS * 1024, kMx4RsrcWord3);
     const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(g.Ws + (int64_t)e * nt16 * KQ * 256), (short)0, nt16 * KQ * 256, kM6RsrcWord3);
+        (void*)(g.Ws + (int64_t)e * nt16 * KQ * 256), (short)0, nt16 * KQ * 256, kMx4RsrcWord3);
     int b0[4], bw[4], q0[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -106,7 +106,7 @@ __device__ __forceinline__ void mx4_tile(const MxGemmArgs& g, const M6Ring& rg, 
     // activation codes of step s into shared slot q: 1 load
     auto issue_a = [&](int s, char* q) {
         const int t = min(s, KS - 1);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (m6_lds_void*)(q + wid * 1024), 16, aoff, 128 * t, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (mx4_lds_void*)(q + wid * 1024), 16, aoff, 128 * t, 0, 0);
         __builtin_amdgcn_sched_barrier(0);      // the vmcnt count below assumes source order
     };
     // weights of step s (+ activation scales) into this wave's slot w: 9 loads
@@ -114,13 +114,13 @@ __device__ __forceinline__ void mx4_tile(const MxGemmArgs& g, const M6Ring& rg, 
         const int t = min(s, KS - 1);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (m6_lds_void*)(w + j * 1024), 16, boff,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (mx4_lds_void*)(w + j * 1024), 16, boff,
                                                      (b0[j] + t * bw[j]) * 1024, 0, 0);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (m6_lds_void*)(w + 4096 + j * 256), 4, qoff,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (mx4_lds_void*)(w + 4096 + j * 256), 4, qoff,
                                                      (q0[j] + (t >> 2) * bw[j]) * 256, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (m6_lds_void*)(w + 5120), 4, soff, 4 * t, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (mx4_lds_void*)(w + 5120), 4, soff, 4 * t, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -140,7 +140,7 @@ __device__ __forceinline__ void mx4_tile(const MxGemmArgs& g, const M6Ring& rg, 
     // of s + 1, weights of s + 2) and after the weights of step s 20, so
     // vmcnt(19) covers both.
     auto step = [&](int s, const char* w, const char* q, char* qn) {
-        M6_WAIT_VMCNT(2 * kM6Loads - 1);
+        MX4_WAIT_VMCNT(2 * kMx4Loads - 1);
         __builtin_amdgcn_s_barrier();
         i32x8 a[NG];
 #pragma unroll
@@ -195,7 +195,7 @@ __device__ __forceinline__ void mx4_tile(const MxGemmArgs& g, const M6Ring& rg, 
     if (s < KS) step(s, rg.w0, rg.q0, rg.q2);
     if (s + 1 < KS) step(s + 1, rg.w1, rg.q1, rg.q0);
     // the loads past the last step land before the slots are reused
-    M6_WAIT_VMCNT(0);
+    MX4_WAIT_VMCNT(0);
     if (!has_cols) return;
 
     // epilogue: lane holds rows 4 kg + v of each 16-row group, column r16 of each block
@@ -250,18 +250,18 @@ __device__ __forceinline__ void mx4_tile(const MxGemmArgs& g, const M6Ring& rg, 
 // takes part in every tile (the barriers), a wave past N without columns.
 // With lds_small == 2 the 256-row table follows, four 64-row tiles per entry.
 template <bool FC1>
-__device__ __forceinline__ void mx4_small_tiles(const MxGemmArgs& g, const M6Ring& ring)
+__device__ __forceinline__ void mx4_small_tiles(const MxGemmArgs& g, const Mx4Ring& ring)
 {
     const int n_small = ld_const(&g.hdr->n_tiles);
     const int n_mt = n_small + (g.lds_small == 2 ? 4 * ld_const(&g.hdr->n_tiles_big) : 0);
-    const int NTs = (g.N + kM6Cols - 1) / kM6Cols;
+    const int NTs = (g.N + kMx4Cols - 1) / kMx4Cols;
     const int total = n_mt * NTs;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int n_cb = g.N / 64 + ((g.N % 64) ? 1 : 0);
-    M6Ring rg = ring;
-    rg.w0 += wid * kM6Slot;
-    rg.w1 += wid * kM6Slot;
-    rg.w2 += wid * kM6Slot;
+    Mx4Ring rg = ring;
+    rg.w0 += wid * kMx4Slot;
+    rg.w1 += wid * kMx4Slot;
+    rg.w2 += wid * kMx4Slot;
     for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
         const int mt = tile / NTs, ct = tile - mt * NTs;
         const int* te = mt < n_small ? (const int*)(g.tiles + mt) : (const int*)(g.tiles_big + ((mt - n_small) >> 2));

@@ -26,13 +26,13 @@ __global__ void __launch_bounds__(512, 1) gemm_mxfp8_kernel(MxGemmArgs g)
 template <bool FC1>
 __global__ void __launch_bounds__(512, 1) gemm_mx4_small_kernel(MxGemmArgs g)
 {
-    __shared__ __attribute__((aligned(1024))) char w0[kM6SlotAll];
-    __shared__ __attribute__((aligned(1024))) char w1[kM6SlotAll];
-    __shared__ __attribute__((aligned(1024))) char w2[kM6SlotAll];
-    __shared__ __attribute__((aligned(1024))) char q0[kM6ASlot];
-    __shared__ __attribute__((aligned(1024))) char q1[kM6ASlot];
-    __shared__ __attribute__((aligned(1024))) char q2[kM6ASlot];
-    mx4_small_tiles<FC1>(g, M6Ring{w0, w1, w2, q0, q1, q2});
+    __shared__ __attribute__((aligned(1024))) char w0[kMx4SlotAll];
+    __shared__ __attribute__((aligned(1024))) char w1[kMx4SlotAll];
+    __shared__ __attribute__((aligned(1024))) char w2[kMx4SlotAll];
+    __shared__ __attribute__((aligned(1024))) char q0[kMx4ASlot];
+    __shared__ __attribute__((aligned(1024))) char q1[kMx4ASlot];
+    __shared__ __attribute__((aligned(1024))) char q2[kMx4ASlot];
+    mx4_small_tiles<FC1>(g, Mx4Ring{w0, w1, w2, q0, q1, q2});
 }
 
 // t0 / t1 (optional): events that receive the launch's own start and end
