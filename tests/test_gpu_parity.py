@@ -59,11 +59,16 @@ SMALL = {
     # MXFP8 experts past 128 rows with K a multiple of 128 (LDS-staged kernel):
     # ragged 256-row tiles, a partial 256-column tile, 2 and 3 K steps
     "mx_big": Workload("mx_big", 600, 600, 256, 384, 4, 2, "mxfp8"),
-    # MXFP4 weights: 64-row streaming tiles, and 256-row LDS-staged tiles in mx4_big
+    # MXFP4 weights: the 64-row LDS-staged kernel (K a multiple of 128; in mx4_big
+    # it also takes the larger experts as 64-row tiles, with partial 512-column
+    # tiles, 2 and 3 K steps), and the streaming tiles in odd_mxfp4 (K = 96)
     "decode_mx4_T64": WORKLOADS["decode_mxfp4"].with_tokens(64),
     "mx4_T96": WORKLOADS["mxfp4_16k"].with_tokens(96),
     "odd_mxfp4": Workload("odd_mxfp4", 77, 80, 96, 160, 5, 3, "mxfp4"),
     "mx4_big": Workload("mx4_big", 600, 600, 256, 384, 4, 2, "mxfp4"),
+    # MXFP4 with one K step in both GEMMs (K = 128): only the prologue's and
+    # the tail's steps of the 64-row kernel, 256-column tiles
+    "mx4_k128": Workload("mx4_k128", 70, 72, 128, 128, 6, 2, "mxfp4"),
 }
 
 _cases = {}
