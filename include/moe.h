@@ -216,7 +216,9 @@ moe_status moe_check(moe_handle h, void* ws, hipStream_t stream, uint32_t* err_b
  * scan, scatter), 2 MXFP8 activation quantization (nothing in bf16), 3 FC1 +
  * SwiGLU, 4 FC2, 5 finalize.  events[2] and events[3] are the start and end
  * of the FC1 + SwiGLU launch itself, recorded by its dispatch (no marker
- * packets around it), so events[3] - events[2] is that launch's duration.
+ * packets around it), so events[3] - events[2] is that launch's duration
+ * (MXFP4 above a 1024-token capacity, where the stage is two launches: the
+ * first one's start and the second one's end).
  * n_events must be 6; NULL entries are not recorded.  The events are the
  * caller's; pass events = NULL to stop. */
 moe_status moe_set_stage_events(moe_handle h, hipEvent_t* events, int n_events);
