@@ -1,9 +1,12 @@
-// K3 / K4, MXFP8: one launch per GEMM stage.  A workgroup is 8 waves, one per
-// CU (persistent grid): first the LDS-staged tiles (experts with more than 128
-// rows; only when K is a multiple of 128) with all 8 waves, then the streaming
-// tiles with its two 4-wave halves as independent workers.  Both designs follow
-// the same arithmetic contract (gemm_mxfp8_stream.h).  W4: MXFP4 weights
-// (E2M1 B format) in both designs.
+// K3 / K4, MXFP8 / MXFP4.  A workgroup is 8 waves, one per CU (persistent
+// grid).  MXFP8: one launch per GEMM stage, first the LDS-staged 256-row tiles
+// (experts with more than 128 rows; only when K is a multiple of 128) with all
+// 8 waves, then the streaming 64-row tiles with its two 4-wave halves as
+// independent workers.  MXFP4 (W4, E2M1 B format): the same, except that with
+// K a multiple of 128 the 64-row tiles run in a launch of their own
+// (gemm_mx4_small.h), which at token capacities up to 1024 also takes the
+// 256-row tiles (then the stage is that one launch).  All designs follow the
+// same arithmetic contract (gemm_mxfp8_stream.h).
 #include <hip/hip_ext.h>
 
 #include "gemm_mxfp8_lds.h"
