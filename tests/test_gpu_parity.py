@@ -69,6 +69,9 @@ SMALL = {
     # MXFP4 with one K step in both GEMMs (K = 128): only the prologue's and
     # the tail's steps of the 64-row kernel, 256-column tiles
     "mx4_k128": Workload("mx4_k128", 70, 72, 128, 128, 6, 2, "mxfp4"),
+    # MXFP4 with H = 160: FC1 (K = 160) on the streaming tiles, FC2 (K = 256) on
+    # the 64-row LDS kernel with N = 160, its last 64-column block half full
+    "mx4_h160": Workload("mx4_h160", 60, 64, 160, 256, 4, 2, "mxfp4"),
 }
 
 _cases = {}
