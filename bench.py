@@ -1,6 +1,6 @@
 """Benchmark of the routed SwiGLU MoE forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload all|<name>]
 
 One step = the whole hot path over one batch of synthetic inputs already
 resident in HBM: the router (moe_route: softmax, top-k, canonical ids) and the
@@ -8,10 +8,14 @@ forward (moe_forward: permutation, FC1 + SwiGLU, FC2, fp32 finalize).  W
 untimed warm-up steps, then exactly K timed steps between two
 torch.cuda.synchronize() calls.  Prints ONE JSON line.
 
-The default workload is the decode-sized launch (256 tokens, hidden 2048, FFN
-1024, 64 experts, top-6, bf16).  Kernel-weight buffers are rotated between
-steps so that the ~805 MB of expert weights cannot be served from the 256 MB
-Infinity Cache.  `roofline` reports the dominant kernel's algorithmic bytes
+By default every workload is measured in the same run (tiny, decode, logprob,
+bf16_16k, mxfp8_16k, bounded_decode, decode_mxfp4, mxfp4_16k); the line's
+headline fields are the decode-sized launch (256 tokens, hidden 2048, FFN
+1024, 64 experts, top-6, bf16) and `configs` holds every workload's own
+record (step time, tokens/s, TFLOP/s, % of MFMA and HBM peak, roofline of its
+FC1 stage, CPU oracle baseline).  Kernel-weight buffers are rotated between
+steps so that the expert weights cannot be served from the 256 MB Infinity
+Cache.  `roofline` reports the dominant kernel's algorithmic bytes
 (or flops) per launch over its average duration, measured with HIP events
 recorded by the library on the forward's stream during the timed steps.
 `cpu_baseline` times the CPU oracle (test infrastructure, never tuned) on a
@@ -45,14 +49,18 @@ def _args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="decode")
+    p.add_argument("--workload", default="all",
+                   help="one workload, or 'all': every configuration in one run, with the "
+                        "decode workload as the headline line and the others under 'configs'")
     p.add_argument("--seed", type=int, default=11)
     p.add_argument("--combine", default="fp32", choices=["fp32", "bf16", "rows"],
                    help="how a token's routes are combined (moe_forward_ex): the fp32 chain, "
                         "the fp32 chain rounded to bf16, or every route's row unscaled")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
-                   help="target CPU time of the oracle sample")
+                   help="target CPU time of the oracle sample of the headline workload")
+    p.add_argument("--cpu-seconds-other", type=float, default=3.0,
+                   help="target CPU time of the oracle sample of every other workload")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy 5 times (to scale HBM counters)")
     return p.parse_args()
@@ -157,23 +165,61 @@ class HipEvents:
         self.made = []
 
 
-def main():
-    a = _args()
-    if a.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
-              f"(--gpus {a.gpus} requested)", file=sys.stderr)
-        sys.exit(2)
-    if a.copy_calibration:
-        copy_calibration()
-        return
+# every configuration the default run measures, the headline first
+ALL_WORKLOADS = ("decode", "tiny", "logprob", "bf16_16k", "mxfp8_16k", "bounded_decode",
+                 "decode_mxfp4", "mxfp4_16k")
+HEADLINE = "decode"
 
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+_INPUT_CACHE = {}
+
+
+def inputs_for(w, seed: int):
+    """Seeded inputs of workload w (workloads of equal shapes, seed and outlier
+    choice share one draw)."""
+    key = (w.T, w.T_cap, w.H, w.F, w.E, w.k, w.bias, seed, w.precision != "bf16")
+    if key not in _INPUT_CACHE:
+        from workloads import make_inputs
+        _INPUT_CACHE.clear()
+        _INPUT_CACHE[key] = make_inputs(w, seed=seed, outliers=(w.precision != "bf16"))
+    return _INPUT_CACHE[key]
+
+
+def roofline_of(w, ab: dict, fc1_us: float) -> dict:
+    """The FC1 + SwiGLU stage against the roofline whose floor is higher for it:
+    HBM (its algorithmic bytes) or MFMA (its flops at the precision's peak)."""
+    fc1_flops = 4.0 * w.H * w.F * w.R
+    t_hbm = ab["fc1"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = fc1_flops / (MFMA_PEAK_TFLOPS[w.precision] * 1e12)
+    hbm = dict(bound="hbm", achieved=ab["fc1"] / (fc1_us * 1e-6) / 1e9, peak=HBM_PEAK_GBS,
+               unit="GB/s")
+    mfma = dict(bound="mfma", achieved=fc1_flops / (fc1_us * 1e-6) / 1e12,
+                peak=MFMA_PEAK_TFLOPS[w.precision], unit="TFLOP/s")
+    roof, other = (mfma, hbm) if (w.name in MFMA_BOUND or t_mfma > t_hbm) else (hbm, mfma)
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["other_bound"] = {"bound": other["bound"], "frac": other["achieved"] / other["peak"]}
+    return roof
+
+
+def run_workload(name: str, a, cpu_seconds: float, threads1: bool) -> dict:
     import torch
-    from workloads import WORKLOADS, make_inputs
+    from workloads import WORKLOADS
     from swiglu_expert_mlp_amd import MoE
 
-    w = WORKLOADS[a.workload]
+    w = WORKLOADS[name]
     dev = torch.device("cuda:0")
-    inp = make_inputs(w, seed=a.seed, outliers=(w.precision != "bf16"))
+    inp = inputs_for(w, a.seed)
     bf = lambda arr: torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(
         torch.bfloat16).to(dev)
     x = bf(inp["x_bits"])
@@ -211,7 +257,7 @@ def main():
     torch.cuda.synchronize()
     bits = moe0.check(ws)
     if bits:
-        raise RuntimeError(f"device contract violation bits {bits}")
+        raise RuntimeError(f"{name}: device contract violation bits {bits}")
     idx = moe0.get_indices(ws, w.T_cap)
     touched = int(np.count_nonzero(idx["counts"]))
     loads = idx["counts"].astype(np.int64)
@@ -258,14 +304,7 @@ def main():
     flops = w.flops()
     tokens_s = w.T / (ms_step * 1e-3)
     tflops = flops / (ms_step * 1e-3) / 1e12
-    if w.name in MFMA_BOUND:
-        fc1_flops = 4.0 * w.H * w.F * w.R
-        roof = dict(bound="mfma", achieved=fc1_flops / (fc1_us * 1e-6) / 1e12,
-                    peak=MFMA_PEAK_TFLOPS[w.precision], unit="TFLOP/s")
-    else:
-        roof = dict(bound="hbm", achieved=ab["fc1"] / (fc1_us * 1e-6) / 1e9,
-                    peak=HBM_PEAK_GBS, unit="GB/s")
-    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof = roofline_of(w, ab, fc1_us)
     # the FC1 + SwiGLU stage: its tiles are 256-row tiles (experts with more than
     # 128 rows) or 64-row tiles (the others); one launch, except MXFP4 above a
     # 1024-token capacity (the 256-row launch, then the 64-row launch)
@@ -277,17 +316,14 @@ def main():
     roof["tiles"] = "256-row" if int(loads.min()) > 128 else (
         "64-row" if int(loads.max()) <= 128 else "256-row + 64-row")
     roof["kernel_us"] = fc1_us
+    roof["algorithmic_bytes"] = ab["fc1"]
+    roof["algorithmic_flops"] = 4.0 * w.H * w.F * w.R
     roof["traffic"] = measured_traffic(w.name)
 
     res = {
-        "metric": METRIC, "value": tokens_s, "unit": "tokens/s", "n_gpus": 1,
-        "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": w.precision, "data": "synthetic (seeded N(0,1) tokens, N(0,0.02^2) weights)",
-        "config": {"workload": w.name, "tokens": w.T, "token_capacity": w.T_cap, "hidden": w.H,
-                   "ffn": w.F, "experts": w.E, "topk": w.k, "precision": w.precision,
-                   "combine": a.combine, "parallelism": "one GPU, all experts local"},
-        "tflops": tflops,
+        "workload": w.name, "tokens": w.T, "token_capacity": w.T_cap, "hidden": w.H,
+        "ffn": w.F, "experts": w.E, "topk": w.k, "precision": w.precision,
+        "ms_per_step": ms_step, "tokens_per_s": tokens_s, "tflops": tflops,
         "mfma_frac": tflops / MFMA_PEAK_TFLOPS[w.precision],
         "hbm_gbs_step": ab["step"] / (ms_step * 1e-3) / 1e9,
         "hbm_frac_step": ab["step"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -297,13 +333,60 @@ def main():
         "weight_buffers_rotated": n_rot,
         "roofline": roof,
     }
-
     if w.name == "bounded_decode":
-        res["live_tracking"] = live_tracking(w, moes, x, logits, route_fn, fwd_fn, ids, probs, out, ws,
-                                             live, sh, n_rot, a.combine)
-
+        res["live_tracking"] = live_tracking(w, moes, x, logits, route_fn, fwd_fn, ids, probs, out,
+                                             ws, live, sh, n_rot, a.combine)
+    del moes, route_fn, fwd_fn, x, logits, ws, out, ids, probs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_seconds, a.combine)
+        res["cpu_baseline"] = cpu_baseline(w, inp, cpu_seconds, a.combine, threads1=threads1)
+    return res
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(--gpus {a.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+    if a.copy_calibration:
+        copy_calibration()
+        return
+
+    every = a.workload == "all"
+    names = ALL_WORKLOADS if every else (a.workload,)
+    headline = HEADLINE if every else a.workload
+    results = {}
+    t_start = time.time()
+    for name in names:
+        print(f"[bench] {name} ...", file=sys.stderr, flush=True)
+        results[name] = run_workload(name, a, a.cpu_seconds if name == headline else a.cpu_seconds_other,
+                                     threads1=name in ("tiny", "decode"))
+        r = results[name]
+        print(f"[bench] {name}: {r['ms_per_step'] * 1e3:.1f} us/step, "
+              f"FC1 {r['roofline']['kernel_us']:.1f} us ({r['roofline']['bound']} "
+              f"{100 * r['roofline']['frac']:.1f}%), {time.time() - t_start:.0f} s elapsed",
+              file=sys.stderr, flush=True)
+
+    h = results[headline]
+    res = {
+        "metric": METRIC, "value": h["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": h["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": h["precision"], "data": "synthetic (seeded N(0,1) tokens, N(0,0.02^2) weights)",
+        "config": {"workload": h["workload"], "tokens": h["tokens"],
+                   "token_capacity": h["token_capacity"], "hidden": h["hidden"], "ffn": h["ffn"],
+                   "experts": h["experts"], "topk": h["topk"], "precision": h["precision"],
+                   "combine": a.combine, "parallelism": "one GPU, all experts local"},
+    }
+    for key in ("tflops", "mfma_frac", "hbm_gbs_step", "hbm_frac_step", "stages_us", "expert_load",
+                "weight_buffers_rotated", "roofline", "live_tracking", "cpu_baseline"):
+        if key in h:
+            res[key] = h[key]
+    if every:
+        res["configs"] = {n: {k: v for k, v in r.items() if k != "stages_us"}
+                          for n, r in results.items()}
     print(json.dumps(res))
 
 
@@ -351,11 +434,12 @@ def live_tracking(w, moes, x, logits, route_fn, fwd_fn, ids, probs, out, ws, liv
             f"us_per_step_live_{T}_capacity_{w.T_cap}": by_live[str(T)]}
 
 
-def cpu_baseline(w, inp, target_s: float, combine: str = "fp32") -> dict:
+def cpu_baseline(w, inp, target_s: float, combine: str = "fp32", threads1: bool = False) -> dict:
     """The CPU oracle (as it stands) on a bounded sample of the same workload:
-    the first S live tokens, S sized from a short calibration run."""
+    the first S live tokens, S sized from a short calibration run; with
+    threads1 also its time on one host thread."""
     import oracle
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    cores = oracle.set_threads(0)
     model = oracle.Model(w.E, w.H, w.F, w.k, inp["w1_bits"], inp["w2_bits"], w.precision)
     ids, probs, _ = oracle.route(inp["logits"], w.T, w.k)
 
@@ -365,18 +449,32 @@ def cpu_baseline(w, inp, target_s: float, combine: str = "fp32") -> dict:
                       combine=combine)
         return time.time() - t
 
-    S0 = min(w.T, 16)
-    t0 = run(S0)
-    S = int(min(w.T, max(S0, S0 * target_s / max(t0, 1e-3))))
-    reps = 1
-    t = run(S)
-    while t * (reps + 1) / reps < target_s and S == w.T and reps < 8:
-        t += run(S)
-        reps += 1
-    tokens = S * reps
-    return {"value": tokens / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {S} of {w.T} tokens, {reps} run(s), {t:.1f} s "
-                      f"(weights prepared outside the timing)"}
+    def measure(target):
+        S0 = min(w.T, 8)
+        t0 = run(S0)
+        S = int(min(w.T, max(S0, S0 * target / max(t0, 1e-3))))
+        reps = 1
+        t = run(S)
+        while t * (reps + 1) / reps < target and S == w.T and reps < 8:
+            t += run(S)
+            reps += 1
+        return S, reps, t
+
+    S, reps, t = measure(target_s)
+    res = {"value": S * reps / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "gflops": 6.0 * w.H * w.F * w.k * S * reps / t / 1e9,
+           "sample": f"first {S} of {w.T} tokens, {reps} run(s), {t:.1f} s "
+                     f"(weights prepared outside the timing)"}
+    if threads1:
+        oracle.set_threads(1)
+        try:
+            S1, r1, t1 = measure(min(target_s, 3.0))
+        finally:
+            oracle.set_threads(cores)
+        res["one_thread"] = {"value": S1 * r1 / t1, "unit": "tokens/s", "cores": 1,
+                             "sample": f"first {S1} of {w.T} tokens, {r1} run(s), {t1:.1f} s"}
+    return res
 
 
 if __name__ == "__main__":

@@ -64,6 +64,7 @@ typedef enum {
     MOE_ERR_UNSUPPORTED = -2,      /* configuration the kernels cannot run     */
     MOE_ERR_NOT_LOADED = -3,       /* forward before any moe_load_weights      */
     MOE_ERR_HIP = -4,              /* a HIP runtime call failed                */
+    MOE_ERR_DEVICE_CONTRACT = -5,  /* moe_check found contract-violation bits  */
 } moe_status;
 
 /* Device-side contract-violation bits reported by moe_check. */
@@ -131,8 +132,13 @@ size_t moe_weight_bytes(moe_handle h);
 moe_status moe_load_weights(moe_handle h, const void* w1, const void* w2, void* kbuf,
                             size_t kbuf_bytes, hipStream_t stream);
 
-/* Workspace bytes for a token capacity T_cap.  The first 256 bytes are a
- * header that must be zero before the first use of a new workspace. */
+/* Workspace bytes for a token capacity T_cap (0 for a NULL handle or a
+ * negative T_cap).  The workspace is caller-owned device memory with no
+ * required initial contents: every launch writes what a later launch of the
+ * same call reads, so a fresh allocation (or one left by another handle) can
+ * be passed as is.  Its bytes are the library's until the work enqueued on it
+ * has finished; moe_get_indices, moe_get_rows and moe_check read the state of
+ * the last moe_route / moe_forward that used it. */
 size_t moe_workspace_bytes(moe_handle h, int64_t T_cap);
 
 /* Router (Megatron-Core `_route`): for each live token, softmax over the E
@@ -144,12 +150,22 @@ moe_status moe_route(moe_handle h, const float* logits, int64_t T_cap,
                      const int32_t* live_rows_dev, int32_t* ids, float* probs, void* ws,
                      size_t ws_bytes, hipStream_t stream);
 
-/* The routed SwiGLU MoE forward.
+/* The routed SwiGLU MoE forward (Megatron-LM PR #8367, "Problem": a device-
+ * side active-token count bounds the expert work and the finalize returns
+ * fp32; cudnn-frontend PR #448, MoeEp forward(activation, fc1_weight,
+ * fc2_weight, topk_idx, topk_weights), with the weights bound by
+ * moe_load_weights instead of passed per call).
  *   x: bf16 [T_cap][H]; expert_ids: int32 [T_cap][topk], any order per token
  *   (sorted ascending here); probs: fp32 [T_cap][topk]; out: fp32 [T_cap][H].
  *   ws: ws_bytes >= moe_workspace_bytes(h, T_cap).
+ *   out[t] for live t is the fp32 chain of the file header; rows >= live are
+ *   not written.
  * Every token's output bits are independent of the other tokens, of T_cap
- * and of the live count. */
+ * and of the live count.  Errors: MOE_ERR_INVALID_ARG (NULL or misaligned
+ * pointer, T_cap outside [0, 2^26], ws_bytes too small), MOE_ERR_NOT_LOADED
+ * (no moe_load_weights yet), MOE_ERR_HIP (a launch failed); nothing is
+ * enqueued on an error.  Contract violations inside the data (ids, live
+ * count) are reported by moe_check. */
 moe_status moe_forward(moe_handle h, const void* x, const int32_t* expert_ids,
                        const float* probs, int64_t T_cap, const int32_t* live_rows_dev,
                        float* out, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -185,7 +201,10 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
                           int combine, void* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Copy the permutation of the last forward to host arrays (synchronizes the
- * stream).  counts: int32 [E]; offsets: int32 [E+1]; perm_src: int32 [n_rows]
+ * stream).  The grouping is cudnn-frontend PR #448's route index (MoeEp class
+ * docstring): rows grouped by local expert in ascending order, token-major
+ * inside an expert; on one GPU the source rank is always 0 and is dropped.
+ * counts: int32 [E]; offsets: int32 [E+1]; perm_src: int32 [n_rows]
  * (= t*topk + j of the route at each grouped row, experts ascending, tokens
  * ascending within an expert); dst: int32 [T*topk] (grouped row of each
  * route, -1 if dropped); n_rows_out / T_out: the row and live-token counts.
@@ -198,16 +217,29 @@ moe_status moe_get_indices(moe_handle h, const void* ws, int64_t T_cap, int32_t*
  * the stream), in grouped-row order.  fc2_rows: fp32 [n_rows][H], the
  * unweighted FC2 output rows.  fc1_out_rows: the FC2 operand rows, bf16
  * [n_rows][F] (bf16 precision) or E4M3 codes [n_rows][F] followed by E8M0
- * scales [n_rows][F/32] (mxfp8).  sorted_ids / sorted_probs: int32 / fp32
- * [T][topk], each token's routes in canonical order.  Any output may be
- * NULL.  For tests and debugging. */
+ * scales [n_rows][F/32] (mxfp8, mxfp4).  sorted_ids / sorted_probs: int32 /
+ * fp32 [T][topk], each token's routes in canonical order.  x_codes /
+ * x_scales (mxfp8, mxfp4; must be NULL for bf16): the quantized activations,
+ * E4M3 codes uint8 [T][H] and E8M0 scale bytes uint8 [T][H/32] (T = the live
+ * tokens of the last forward).  Any output may be NULL.  For tests and
+ * debugging.  Errors: MOE_ERR_INVALID_ARG for a NULL handle or workspace, or
+ * x_codes / x_scales with bf16; MOE_ERR_HIP if a copy fails. */
 moe_status moe_get_rows(moe_handle h, const void* ws, int64_t T_cap, float* fc2_rows,
                         void* fc1_out_rows, int32_t* sorted_ids, float* sorted_probs,
-                        hipStream_t stream);
+                        void* x_codes, void* x_scales, hipStream_t stream);
 
-/* Synchronize the stream, return the OR of the contract-violation bits of the
- * last moe_route and the last moe_forward on this workspace (MOE_DEVERR_*)
- * in *err_bits, and clear them. */
+/* Synchronize the stream, return the contract-violation bits (MOE_DEVERR_*)
+ * of the last moe_route or moe_forward that ran on this workspace in
+ * *err_bits, and clear them.  Each of those calls overwrites the bits, so
+ * after a route and a forward they are the forward's (which checks the same
+ * live count as well as the ids); a workspace no call has run on yet holds no
+ * meaningful bits.  Returns MOE_OK when no bit is set and
+ * MOE_ERR_DEVICE_CONTRACT (with *err_bits filled in and moe_last_error naming
+ * the bits) when any is: the device-side half of the error contract, whose
+ * violations cannot be returned by the enqueueing call itself
+ * (Megatron-LM PR #7798, review discussion of the MXFP8 tile floor: a
+ * broken assumption should fail loudly rather than change numbers).  MOE_ERR_INVALID_ARG for NULL
+ * arguments, MOE_ERR_HIP if the copy fails. */
 moe_status moe_check(moe_handle h, void* ws, hipStream_t stream, uint32_t* err_bits);
 
 /* Stage timing hook (for profiling).  With events != NULL, every later

@@ -86,6 +86,7 @@ def lib() -> ctypes.CDLL:
             "orc_pack_mx4_offsets": (None, [ctypes.c_int] * 3 + [P]),
             "orc_pack_bytes": (i64, [ctypes.c_int] * 4),
             "orc_pack_mx_offsets": (None, [ctypes.c_int] * 3 + [P]),
+            "orc_set_threads": (ctypes.c_int, [ctypes.c_int]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -325,6 +326,11 @@ class Model:
         lib().orc_forward_tokens(self._h, _p(x_bits), _p(ids), _p(probs), _p(tokens),
                                  len(tokens), _p(out))
         return out
+
+
+def set_threads(n: int = 0) -> int:
+    """Set the oracle's OpenMP thread count (n > 0); returns the count in effect."""
+    return int(lib().orc_set_threads(int(n)))
 
 
 def pack_bytes(E, H, F, precision="bf16") -> int:

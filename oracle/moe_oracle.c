@@ -41,6 +41,7 @@
  * function.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -906,4 +907,12 @@ void orc_pack_mx_offsets(int E, int H, int F, int64_t* off)
     off[2] = off[1] + up256(code_bytes(E, H, F));
     off[3] = off[2] + up256(scale_bytes(E, 2 * (int64_t)F, H));
     off[4] = off[3] + up256(scale_bytes(E, H, F));
+}
+
+/* Host threads of the OpenMP loops (timing aid for the CPU baseline, no part
+ * of the method): n > 0 sets the count; returns the count in effect. */
+int orc_set_threads(int n)
+{
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
 }

@@ -31,7 +31,7 @@ DEVERR_BAD_EXPERT_ID = 1
 DEVERR_DUP_EXPERT_ID = 2
 DEVERR_LIVE_ABOVE_CAP = 4
 DEVERR_LIVE_NEGATIVE = 8
-WS_HEADER_BYTES = 256
+MOE_ERR_DEVICE_CONTRACT = -5
 # moe_forward_ex combines (moe_combine in include/moe.h)
 COMBINES = {"fp32": 0, "bf16": 1, "rows": 2}
 
@@ -48,7 +48,7 @@ _SIGNATURES = {
     "moe_forward_ex": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, _P, ctypes.c_int, _P, _P,
                                       ctypes.c_size_t, _P]),
     "moe_get_indices": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P]),
-    "moe_get_rows": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P, _P, _P, _P, _P]),
+    "moe_get_rows": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P]),
     "moe_check": (ctypes.c_int, [_P, _P, _P, ctypes.POINTER(ctypes.c_uint32)]),
     "moe_set_stage_events": (ctypes.c_int, [_P, _P, ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
@@ -143,12 +143,10 @@ class MoE:
         return int(lib().moe_workspace_bytes(self._h, int(T_cap)))
 
     def new_workspace(self, T_cap: int, device=None):
-        """A workspace for capacity T_cap with its header zeroed."""
+        """A workspace for capacity T_cap (no initial contents are required)."""
         torch = _torch()
-        ws = torch.empty(self.workspace_bytes(T_cap), dtype=torch.uint8,
-                         device=device or "cuda")
-        ws[:WS_HEADER_BYTES].zero_()
-        return ws
+        return torch.empty(self.workspace_bytes(T_cap), dtype=torch.uint8,
+                           device=device or "cuda")
 
     # ------------------------------------------------------------- calls
 
@@ -236,6 +234,8 @@ class MoE:
                     dst=dst[: T * self.topk].reshape(T, self.topk), T=T, n_rows=n_rows.value)
 
     def get_rows(self, ws, T_cap: int, n_rows: int, T: int, stream=None) -> dict:
+        """Intermediate rows of the last forward (moe_get_rows); for MXFP8 / MXFP4
+        also the quantized activations x_codes [T, H] and x_scales [T, H/32]."""
         import numpy as np
         O = np.zeros((max(1, n_rows), self.H), np.float32)
         if self.precision == "bf16":
@@ -244,9 +244,12 @@ class MoE:
             hr = np.zeros(max(1, n_rows) * (self.F + self.F // 32), np.uint8)
         sid = np.zeros((max(1, T), self.topk), np.int32)
         sp = np.zeros((max(1, T), self.topk), np.float32)
-        c = lambda a: a.ctypes.data_as(_P)
+        mx = self.precision != "bf16"
+        xc = np.zeros((max(1, T), self.H), np.uint8) if mx else None
+        xs = np.zeros((max(1, T), self.H // 32), np.uint8) if mx else None
+        c = lambda a: None if a is None else a.ctypes.data_as(_P)
         _check(lib().moe_get_rows(self._h, _dev(ws, "ws", (_torch().uint8,)), T_cap, c(O), c(hr),
-                                  c(sid), c(sp), _stream(stream)), "moe_get_rows")
+                                  c(sid), c(sp), c(xc), c(xs), _stream(stream)), "moe_get_rows")
         res = dict(fc2_rows=O[:n_rows], sorted_ids=sid[:T], sorted_probs=sp[:T])
         if self.precision == "bf16":
             res["fc1_out"] = hr[:n_rows]
@@ -254,6 +257,8 @@ class MoE:
             res["fc1_codes"] = hr[: n_rows * self.F].reshape(n_rows, self.F)
             res["fc1_scales"] = hr[n_rows * self.F: n_rows * (self.F + self.F // 32)].reshape(
                 n_rows, self.F // 32)
+            res["x_codes"] = xc[:T]
+            res["x_scales"] = xs[:T]
         return res
 
     STAGES = ("permute", "quant_x", "fc1_swiglu", "fc2", "finalize")
@@ -317,7 +322,12 @@ class MoE:
         return call
 
     def check(self, ws, stream=None) -> int:
+        """moe_check: the contract-violation bits (DEVERR_*) of the last route and
+        forward on ws, cleared afterwards; 0 when there were none."""
         bits = ctypes.c_uint32(0)
-        _check(lib().moe_check(self._h, _dev(ws, "ws", (_torch().uint8,)), _stream(stream),
-                               ctypes.byref(bits)), "moe_check")
+        st = lib().moe_check(self._h, _dev(ws, "ws", (_torch().uint8,)), _stream(stream),
+                             ctypes.byref(bits))
+        if st == MOE_ERR_DEVICE_CONTRACT:
+            return int(bits.value)
+        _check(st, "moe_check")
         return int(bits.value)

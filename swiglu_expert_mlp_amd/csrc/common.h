@@ -142,15 +142,16 @@ struct WsLayout {
     int64_t max_tiles_big;
 };
 
+// Every field is written by the launch that produces it before any later
+// launch reads it, so the header needs no initialisation.
 struct WsHeader {
-    uint32_t fwd_err;      // contract-violation bits of the last forward
-    uint32_t route_err;    // contract-violation bits of the last route
+    uint32_t err;          // contract-violation bits of the last route or forward
+    uint32_t unused;
     int32_t T;             // live tokens of the last forward (clamped)
     int32_t n_tiles;       // M tiles in the tile table
     int32_t n_rows;        // routed rows with a valid expert
-    uint32_t ticket;       // prep workgroups finished (the last one resets it to 0)
     int32_t n_tiles_big;   // M tiles in the LDS-staged table
-    int32_t pad[57];
+    int32_t pad[58];
 };
 
 static_assert(sizeof(WsHeader) == 256, "header is one 256-byte block");

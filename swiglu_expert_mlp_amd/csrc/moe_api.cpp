@@ -393,9 +393,11 @@ moe_status moe_get_indices(moe_handle h, const void* ws, int64_t T_cap, int32_t*
 
 moe_status moe_get_rows(moe_handle h, const void* ws, int64_t T_cap, float* fc2_rows,
                         void* fc1_out_rows, int32_t* sorted_ids, float* sorted_probs,
-                        hipStream_t stream)
+                        void* x_codes, void* x_scales, hipStream_t stream)
 {
     if (!h || !ws) return fail(MOE_ERR_INVALID_ARG, "moe_get_rows: NULL handle or workspace");
+    if ((x_codes || x_scales) && h->precision == MOE_BF16)
+        return fail(MOE_ERR_INVALID_ARG, "moe_get_rows: bf16 has no quantized activations");
     const WsLayout L = layout_of(h, T_cap);
     const char* w = (const char*)ws;
     WsHeader hdr;
@@ -403,7 +405,8 @@ moe_status moe_get_rows(moe_handle h, const void* ws, int64_t T_cap, float* fc2_
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return hip_fail(e, "moe_get_rows: header copy");
     const size_t n = (size_t)hdr.n_rows;
-    const size_t R = (size_t)hdr.T * h->k;
+    const size_t T = (size_t)hdr.T;
+    const size_t R = T * h->k;
     if (fc2_rows && n) e = hipMemcpy(fc2_rows, w + L.obuf, 4 * n * h->H, hipMemcpyDeviceToHost);
     if (e == hipSuccess && fc1_out_rows && n) {
         if (h->precision == MOE_BF16) {
@@ -419,6 +422,10 @@ moe_status moe_get_rows(moe_handle h, const void* ws, int64_t T_cap, float* fc2_
         e = hipMemcpy(sorted_ids, w + L.sorted_ids, 4 * R, hipMemcpyDeviceToHost);
     if (e == hipSuccess && sorted_probs && R)
         e = hipMemcpy(sorted_probs, w + L.sorted_probs, 4 * R, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && x_codes && T)
+        e = hipMemcpy(x_codes, w + L.xq, T * h->H, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && x_scales && T)
+        e = hipMemcpy(x_scales, w + L.xs, T * (h->H / 32), hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "moe_get_rows: copy");
     return MOE_OK;
 }
@@ -436,15 +443,23 @@ moe_status moe_set_stage_events(moe_handle h, hipEvent_t* events, int n_events)
 moe_status moe_check(moe_handle h, void* ws, hipStream_t stream, uint32_t* err_bits)
 {
     if (!h || !ws || !err_bits) return fail(MOE_ERR_INVALID_ARG, "moe_check: NULL argument");
-    uint32_t words[2] = {0, 0};
-    hipError_t e = hipMemcpyAsync(words, ws, sizeof(words), hipMemcpyDeviceToHost, stream);
+    uint32_t word = 0;
+    hipError_t e = hipMemcpyAsync(&word, ws, sizeof(word), hipMemcpyDeviceToHost, stream);
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return hip_fail(e, "moe_check: read");
-    *err_bits = words[0] | words[1];
-    uint32_t zero[2] = {0, 0};
-    e = hipMemcpyAsync(ws, zero, sizeof(zero), hipMemcpyHostToDevice, stream);
+    *err_bits = word;
+    const uint32_t zero = 0;
+    e = hipMemcpyAsync(ws, &zero, sizeof(zero), hipMemcpyHostToDevice, stream);
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return hip_fail(e, "moe_check: clear");
+    if (*err_bits) {
+        const uint32_t b = *err_bits;
+        return fail(MOE_ERR_DEVICE_CONTRACT, "moe_check: contract violations 0x%x:%s%s%s%s", b,
+                    (b & kErrBadId) ? " expert id outside [0, E) (route dropped);" : "",
+                    (b & kErrDupId) ? " expert id repeated within a token (repeat dropped);" : "",
+                    (b & kErrLiveHigh) ? " live count above capacity (clamped);" : "",
+                    (b & kErrLiveNeg) ? " negative live count (taken as 0);" : "");
+    }
     return MOE_OK;
 }
 

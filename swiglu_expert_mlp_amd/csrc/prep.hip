@@ -8,23 +8,24 @@
 // Megatron-LM PR #8367, "Problem": the token count is a device-side value,
 // so every kernel here reads it from device memory.
 //
-// Two launches, with grids that never depend on the live count:
+// Launches, with grids that never depend on the live count:
 //   prep_kernel    one workgroup per 256-token chunk (chunks past the live
 //                  count exit at once): canonical sort, then per expert a
 //                  256-bit map of the chunk's tokens that route to it (LDS
 //                  atomic OR, order-independent); a route's stable rank inside
 //                  the chunk is the number of set bits below its token, and
-//                  the chunk's count the bits set in all.  The workgroup that
-//                  finishes last (atomic ticket, no waiting) does the prefix
-//                  over chunks (per expert, staged through LDS in coalesced
-//                  slabs) and over experts, the M-tile table and the error word.
+//                  the chunk's count the bits set in all.
+//   prep_finish    one workgroup: the prefix over chunks (per expert, staged
+//                  through LDS in coalesced slabs) and over experts, the M-tile
+//                  tables and the header (error word, live count, tile counts).
 //   prep_scatter   one thread per route: position = expert offset + the
 //                  chunk's base inside the expert + rank; perm_src[position] =
 //                  route, dst[route] = position.
 // A launch whose capacity fits one chunk (T_cap <= 256 tokens, the decode
 // sizes) runs as a single workgroup that keeps the counts in LDS, finishes
-// without device-scope fences or a ticket, and scatters its own routes; the
-// host then skips the scatter launch.
+// and scatters its own routes; the host then launches neither prep_finish
+// nor prep_scatter.  No launch reads a value that an earlier forward left in
+// the workspace, so a new workspace needs no initialisation.
 // A route whose id is outside [0, E), or repeats an id already listed for the
 // token (contract violations), is dropped: it has no row and dst = -1.
 #include "common.h"
@@ -97,7 +98,7 @@ struct PrepArgs {
 // With local_cnt (single-chunk launch) the per-expert counts come from LDS,
 // the expert offsets go to local_off (LDS) instead of the chunk bases, and
 // local_err is the chunk's error bits.
-__device__ void prep_finish(const PrepArgs& a, int T, int nch, int k, int32_t live, int* lds,
+__device__ void prep_finish(const PrepArgs& a, int T, int nch, int32_t live, int* lds,
                             int* slab /* kSlab ints of LDS */, const int* local_cnt = nullptr,
                             int* local_off = nullptr, uint32_t local_err = 0)
 {
@@ -183,7 +184,7 @@ __device__ void prep_finish(const PrepArgs& a, int T, int nch, int k, int32_t li
     if (threadIdx.x == 0) {
         uint32_t all = (live < 0 ? kErrLiveNeg : 0u) | (live > a.T_cap ? kErrLiveHigh : 0u);
         for (int w = 0; w < (int)(blockDim.x >> 6); ++w) all |= (uint32_t)lds[w];
-        a.hdr->fwd_err = all;
+        a.hdr->err = all;
         a.hdr->T = T;
         a.hdr->n_tiles = ntotal;
         a.hdr->n_tiles_big = nbig;
@@ -196,7 +197,6 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a)
 {
     __shared__ uint32_t bm[kMaxExperts * (kChunkTok / 32)];
     __shared__ int lds[96];
-    __shared__ int s_last;
     __shared__ int loc[2 * kMaxExperts];         // single-chunk launch: counts, offsets
     const int32_t live = *a.live;
     const int T = clamp_live(live, a.T_cap);
@@ -204,10 +204,6 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a)
     const int c = blockIdx.x;
     const int E = a.E;
     const bool single = gridDim.x == 1;          // T_cap <= one chunk
-    if (nch == 0 && !single) {
-        if (c == 0) prep_finish(a, T, 0, K, live, lds, (int*)bm);
-        return;
-    }
     if (c >= nch && !single) return;
     for (int i = threadIdx.x; i < E * (kChunkTok / 32); i += blockDim.x) bm[i] = 0;
     const int t = c * kChunkTok + threadIdx.x;
@@ -288,7 +284,7 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a)
     if (single) {
         // the only chunk: finish from LDS, then each thread places its own routes
         __syncthreads();
-        prep_finish(a, T, nch, K, live, lds, (int*)bm, loc, loc + kMaxExperts, ce);
+        prep_finish(a, T, nch, live, lds, (int*)bm, loc, loc + kMaxExperts, ce);
         __syncthreads();
         if (valid) {
 #pragma unroll
@@ -306,20 +302,18 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a)
         return;
     }
     if (threadIdx.x == 0) a.chunk_err[c] = ce;
-    // the last workgroup to finish does the scan: publish this chunk's data
-    // (device-scope release), take a ticket, and only the last ticket holder
-    // reads every chunk's data (acquire).  Nobody waits.
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t prev = atomicAdd(&a.hdr->ticket, 1u);
-        s_last = (prev == (uint32_t)(nch - 1));
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    prep_finish(a, T, nch, K, live, lds, (int*)bm);
-    if (threadIdx.x == 0) atomicExch(&a.hdr->ticket, 0u);
+}
+
+// The prefix over every chunk's counts, run as its own single-workgroup launch
+// once every prep_kernel workgroup has written its chunk (stream order).
+__global__ void __launch_bounds__(256) prep_finish_kernel(PrepArgs a)
+{
+    __shared__ int slab[kSlab];
+    __shared__ int lds[96];
+    const int32_t live = *a.live;
+    const int T = clamp_live(live, a.T_cap);
+    const int nch = (T + kChunkTok - 1) / kChunkTok;
+    prep_finish(a, T, nch, live, lds, slab);
 }
 
 __global__ void __launch_bounds__(256) prep_scatter_kernel(
@@ -376,6 +370,7 @@ hipError_t launch_prep(const int32_t* ids, const float* probs, int64_t T_cap, co
     }
 #undef PREP_CASE
     if (L.nchunks == 1) return hipGetLastError();   // single workgroup scattered its routes
+    hipLaunchKernelGGL(prep_finish_kernel, dim3(1), dim3(256), 0, s, a);
     int64_t R = T_cap * k;
     int64_t blocks = (R + 255) / 256;
     if (blocks > (int64_t)num_cu * 4) blocks = (int64_t)num_cu * 4;

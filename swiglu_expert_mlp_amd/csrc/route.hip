@@ -66,7 +66,7 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ lo
     const int32_t live = *live_ptr;
     const int64_t T = live < 0 ? 0 : (live > T_cap ? T_cap : live);
     if (blockIdx.x == 0 && threadIdx.x == 0 && hdr != nullptr)
-        hdr->route_err = (live < 0 ? kErrLiveNeg : 0u) | (live > T_cap ? kErrLiveHigh : 0u);
+        hdr->err = (live < 0 ? kErrLiveNeg : 0u) | (live > T_cap ? kErrLiveHigh : 0u);
 
     const int64_t wave0 = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
     const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);

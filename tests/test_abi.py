@@ -108,3 +108,46 @@ def test_python_binding_errors():
         MoE(8, 128, 256, 2, "nvfp4")
     with pytest.raises(ValueError):
         MoE(8, 130, 256, 2, "bf16")
+
+
+def _enum_values():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return {n: int(v) for n, v in re.findall(r"\b(MOE_[A-Z0-9_]+)\s*=\s*(-?\d+)", text)}
+
+
+def test_status_codes_match_the_boundary():
+    """The status codes of the C boundary, including the device-contract code
+    that moe_check returns when the device set violation bits."""
+    v = _enum_values()
+    assert v["MOE_OK"] == 0 and v["MOE_ERR_INVALID_ARG"] == -1
+    assert v["MOE_ERR_UNSUPPORTED"] == -2 and v["MOE_ERR_NOT_LOADED"] == -3
+    assert v["MOE_ERR_HIP"] == -4 and v["MOE_ERR_DEVICE_CONTRACT"] == -5
+    import swiglu_expert_mlp_amd as m
+    assert m.MOE_ERR_DEVICE_CONTRACT == v["MOE_ERR_DEVICE_CONTRACT"]
+
+
+def test_host_checks_of_inspection_calls(L):
+    """moe_check / moe_get_rows reject NULL arguments on the host, and
+    moe_get_rows refuses activation codes for bf16 (there are none), without
+    touching the (fake) workspace."""
+    st, h = _create(L, 8, 128, 256, 2, 0)
+    P = ctypes.c_void_p
+    fake = P(1 << 20)
+    bits = ctypes.c_uint32(7)
+    assert L.moe_check(h, None, None, ctypes.byref(bits)) == -1
+    assert L.moe_check(None, fake, None, ctypes.byref(bits)) == -1
+    assert L.moe_get_rows(h, None, 64, None, None, None, None, None, None, None) == -1
+    st = L.moe_get_rows(h, fake, 64, None, None, None, None, fake, None, None)
+    assert st == -1 and b"bf16" in L.moe_last_error()
+    L.moe_destroy(h)
+
+
+def test_workspace_needs_no_initialisation_documented():
+    """The header documents that a workspace needs no initial contents (the
+    launches of one call write everything a later launch reads); the GPU test
+    test_garbage_workspace_gives_identical_results checks the behaviour."""
+    text = open(HEADER).read()
+    i = text.index("size_t moe_workspace_bytes")
+    doc = " ".join(text[text.rindex("/*", 0, i): i].replace("*", " ").split())
+    assert "no required initial contents" in doc
+    assert "must be zero" not in text

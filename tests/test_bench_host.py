@@ -87,3 +87,22 @@ def test_workload_shapes():
     assert shapes["mxfp8_16k"] == (16384, 16384, 2048, 1024, 128, 8, "mxfp8")
     assert shapes["bf16_16k"] == (16384, 16384, 2048, 1024, 128, 8, "bf16")
     assert shapes["bounded_decode"] == (512, 65536, 2688, 1856, 128, 6, "bf16")
+
+
+def test_default_run_covers_every_workload_and_picks_the_roofline():
+    """The default run measures every benchmark workload with decode as the
+    headline; the FC1 roofline is the one whose floor is higher (MFMA for the
+    16K-token workloads, HBM for the decode-sized ones)."""
+    b = _bench()
+    from workloads import WORKLOADS
+    assert set(b.ALL_WORKLOADS) == set(WORKLOADS) and b.ALL_WORKLOADS[0] == b.HEADLINE == "decode"
+    w = WORKLOADS["bf16_16k"]
+    ab = b.alg_bytes(w, "bf16", 128)
+    r = b.roofline_of(w, ab, 1000.0)
+    assert r["bound"] == "mfma" and r["peak"] == 2500.0
+    assert r["achieved"] == pytest.approx(4 * 2048 * 1024 * 131072 / 1e-3 / 1e12)
+    assert r["other_bound"]["bound"] == "hbm"
+    w = WORKLOADS["decode"]
+    r = b.roofline_of(w, b.alg_bytes(w, "bf16", 64), 100.0)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s"
+    assert r["frac"] == pytest.approx(b.alg_bytes(w, "bf16", 64)["fc1"] / 100e-6 / 1e9 / 8000.0)

@@ -21,10 +21,17 @@ def _gpu():
     import swiglu_expert_mlp_amd  # noqa: F401
 
 
-def _sample(T, n=24, seed=3):
+def _sample(T, prep, k, n=24, seed=3):
+    """24 seeded tokens (first, last, middle and random) plus, for every expert
+    with rows, the token of its last grouped row: that row sits in the expert's
+    last (ragged) M tile, whichever tile design runs it, so every expert's last
+    tile contributes a checked row."""
     rng = np.random.default_rng(seed)
     pick = {0, 1, T - 1, T // 2}
     pick.update(rng.choice(T, size=min(T, n) - len(pick), replace=False).tolist())
+    offs, counts, perm = prep["offsets"], prep["counts"], prep["perm_src"]
+    for e in np.nonzero(counts)[0]:
+        pick.add(int(perm[offs[e + 1] - 1]) // k)
     return np.array(sorted(pick), dtype=np.int64)
 
 
@@ -67,6 +74,7 @@ def test_full_size(name):
     for key in ("counts", "offsets", "perm_src", "dst"):
         assert np.array_equal(idx[key], ref[key]), key
 
-    toks = _sample(w.T)
+    toks = _sample(w.T, ref, w.k)
+    print(f"[full-size] {name}: {len(toks)} sampled tokens", flush=True)
     ref_rows = c.oracle_model().forward_tokens(c.inp["x_bits"], c.ids, c.probs, toks)
     assert_close(got[toks], ref_rows, f"{name} sampled tokens")

@@ -303,3 +303,33 @@ def test_stage_events_leave_outputs_unchanged(name):
     t = [evs[0].elapsed_time(e) for e in evs]
     assert t[3] - t[2] > 0, t
     assert all(b >= a - 1e-3 for a, b in zip(t, t[1:])), t
+
+
+@pytest.mark.parametrize("name", ["decode_T300", "mxfp8_T300", "odd_bf16_T300", "decode_mxfp4"])
+@pytest.mark.parametrize("fill", [0xFF, 0xA5])
+def test_garbage_workspace_gives_identical_results(name, fill):
+    """A workspace needs no initialisation: one filled with garbage bytes gives
+    the same output bits, indices and (no) error bits as a zeroed one, for the
+    router and the forward, in the single-chunk (capacity <= 256 tokens) and
+    the multi-chunk prep paths."""
+    c, m = case(name), handle(name)
+    x, ids, probs = c.dev()
+    T = c.w.T
+    out0 = sentinel_out(T, m.H)
+    ws0 = torch.zeros(m.workspace_bytes(T), dtype=torch.uint8, device="cuda")
+    m.forward(x, ids, probs, live_tensor(T), out=out0, ws=ws0)
+    ref_idx = m.get_indices(ws0, T)
+    out1 = sentinel_out(T, m.H)
+    ws1 = torch.full((m.workspace_bytes(T),), fill, dtype=torch.uint8, device="cuda")
+    m.forward(x, ids, probs, live_tensor(T), out=out1, ws=ws1)
+    assert np.array_equal(bits(out1), bits(out0))
+    idx = m.get_indices(ws1, T)
+    for key in ("counts", "offsets", "perm_src", "dst"):
+        assert np.array_equal(idx[key], ref_idx[key]), key
+    assert m.check(ws1) == 0
+    # the router on a garbage workspace: no stale error bits, same ids
+    logits = torch.from_numpy(c.inp["logits"]).cuda()
+    ws2 = torch.full((m.workspace_bytes(T),), fill, dtype=torch.uint8, device="cuda")
+    gi, gp = m.route(logits, live_tensor(T), ws=ws2)
+    assert m.check(ws2) == 0
+    assert np.array_equal(gi.cpu().numpy()[:T], c.ids[:T])
