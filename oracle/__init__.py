@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
             "orc_weights_destroy": (None, [P]),
             "orc_forward": (u32, [P, P, P, P, i64, i32, P, P, P]),
             "orc_forward_tokens": (None, [P, P, P, P, P, i64, P]),
+            "orc_forward_tokens_ex": (None, [P, P, P, P, P, i64, ctypes.c_int, P]),
+            "orc_finalize_sum": (None, [P, P, i32, ctypes.c_int, ctypes.c_int, ctypes.c_int, P]),
             "orc_pack_bf16": (None, [ctypes.c_int] * 3 + [P, P, P]),
             "orc_pack_mxfp8": (None, [ctypes.c_int] * 3 + [P, P, P]),
             "orc_pack_mxfp4": (None, [ctypes.c_int] * 3 + [P, P, P]),
@@ -258,6 +260,19 @@ def finalize_rows(O: np.ndarray, dst: np.ndarray, H: int) -> np.ndarray:
 
 
 COMBINES = {"fp32": 0, "bf16": 1, "rows": 2}
+# added to a combine: the probabilities are applied inside FC1 (fp32 / bf16 combines)
+APPLY_TOPK_IN_FC1 = 0x100
+
+
+def finalize_sum(O: np.ndarray, dst: np.ndarray, H: int, to_bf16: bool = False) -> np.ndarray:
+    """The apply_topk_in_fc1 finalize: each token's (already weighted) rows added
+    as an fp32 chain from +0 in canonical order; fp32 [T, H] or bf16 bits."""
+    O = np.ascontiguousarray(O, dtype=np.float32)
+    dst = np.ascontiguousarray(dst, dtype=np.int32)
+    T, k = dst.shape
+    out = np.zeros((T, H), dtype=np.uint16 if to_bf16 else np.float32)
+    lib().orc_finalize_sum(_p(O), _p(dst), T, k, H, int(to_bf16), _p(out))
+    return out
 
 
 # ---------------------------------------------------------------- forward
@@ -286,7 +301,8 @@ class Model:
             lib().orc_weights_destroy(h)
             self._h = None
 
-    def forward(self, x_bits, ids, probs, live, want_rows: bool = False, combine: str = "fp32"):
+    def forward(self, x_bits, ids, probs, live, want_rows: bool = False, combine: str = "fp32",
+                topk_in_fc1: bool = False):
         """Whole forward.  Returns (out, err, extras); out is fp32 [T_cap, H] (combine
         "fp32"), bf16 bits [T_cap, H] ("bf16") or fp32 [T_cap, k, H] ("rows"), with rows
         of tokens >= T left NaN (0xFFFF for bf16); extras holds O rows and FC2 operand
@@ -310,21 +326,25 @@ class Model:
             n = max(1, T_cap * self.k)
             O = np.zeros((n, self.H), dtype=np.float32)
             Hr = np.zeros((n, self.F), dtype=np.float32)
+        if topk_in_fc1:
+            assert combine in ("fp32", "bf16"), "row mode has no probabilities to apply"
+        code = COMBINES[combine] | (APPLY_TOPK_IN_FC1 if topk_in_fc1 else 0)
         err = lib().orc_forward_ex(self._h, _p(x_bits), _p(ids), _p(probs), T_cap, int(live),
-                                   COMBINES[combine], _p(out), _p(O), _p(Hr))
+                                   code, _p(out), _p(O), _p(Hr))
         if want_rows:
             extras = dict(O=O, H=Hr)
         return out, err, extras
 
-    def forward_tokens(self, x_bits, ids, probs, tokens) -> np.ndarray:
-        """Naive per-token loop for the listed token indices: [len(tokens), H]."""
+    def forward_tokens(self, x_bits, ids, probs, tokens, topk_in_fc1: bool = False) -> np.ndarray:
+        """Naive per-token loop for the listed token indices: [len(tokens), H]
+        (with topk_in_fc1, the probabilities applied inside FC1)."""
         x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
         ids = np.ascontiguousarray(ids, dtype=np.int32)
         probs = np.ascontiguousarray(probs, dtype=np.float32)
         tokens = np.ascontiguousarray(tokens, dtype=np.int64)
         out = np.empty((len(tokens), self.H), dtype=np.float32)
-        lib().orc_forward_tokens(self._h, _p(x_bits), _p(ids), _p(probs), _p(tokens),
-                                 len(tokens), _p(out))
+        lib().orc_forward_tokens_ex(self._h, _p(x_bits), _p(ids), _p(probs), _p(tokens),
+                                    len(tokens), int(topk_in_fc1), _p(out))
         return out
 
 

@@ -46,6 +46,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+/* Flag added to a forward's combine: the probabilities are applied inside FC1. */
+#define ORC_APPLY_TOPK_IN_FC1 0x100
+
 #define ORC_ERR_BAD_ID 1u      /* an expert id outside [0, E) in a live token */
 #define ORC_ERR_DUP_ID 2u      /* the same expert id twice in one live token  */
 #define ORC_ERR_LIVE_HIGH 4u   /* live count above capacity: clamped           */
@@ -435,16 +438,20 @@ static float dot_w2(const orc_model* m, const double* hr, int64_t row)
 
 /* The expert MLP of one routed row: FC1 gate/up from the operand row xr
  * (length H), SwiGLU, the FC2-input rounding (bf16, or MXFP8 per 32-block),
- * then FC2 into o (length H, fp32).  Scratch a (F doubles) and hbuf (F). */
-static void expert_row(const orc_model* m, int e, const double* xr, float* o,
-                       float* a32, double* hrow)
+ * then FC2 into o (length H, fp32).  Scratch a (F doubles) and hbuf (F).
+ * With fc1_prob (the route's probability applied inside FC1, the MoeEp
+ * apply_topk_in_fc1 option of cudnn-frontend PR #448), each SwiGLU value is
+ * multiplied by p in fp32 before the FC2-input rounding, so FC2 returns the
+ * weighted row; otherwise pass 1.0f (the product is then exact). */
+static void expert_row_p(const orc_model* m, int e, const double* xr, float* o,
+                         float* a32, double* hrow, float fc1_prob)
 {
     const int64_t H = m->H, F = m->F;
     const int64_t r1 = (int64_t)e * 2 * F, r2 = (int64_t)e * H;
     for (int64_t n = 0; n < F; ++n) {
         float g = dot_w1(m, xr, r1 + n);
         float u = dot_w1(m, xr, r1 + F + n);
-        a32[n] = swiglu_f32(g, u);
+        a32[n] = swiglu_f32(g, u) * fc1_prob;
     }
     if (!m->mx) {
         for (int64_t n = 0; n < F; ++n) hrow[n] = orc_bf16_round(a32[n]);
@@ -463,6 +470,12 @@ static void expert_row(const orc_model* m, int e, const double* xr, float* o,
         }
     }
     for (int64_t mo = 0; mo < H; ++mo) o[mo] = dot_w2(m, hrow, r2 + mo);
+}
+
+static void expert_row(const orc_model* m, int e, const double* xr, float* o,
+                       float* a32, double* hrow)
+{
+    expert_row_p(m, e, xr, o, a32, hrow, 1.0f);
 }
 
 /* Finalize ([VALUE] "What is changed"; [BOUND] "Problem"): for each live
@@ -506,6 +519,29 @@ void orc_finalize_bf16(const float* O, const int32_t* dst, const float* sorted_p
             out[t * H + mo] = orc_bf16_bits(acc);
         }
     }
+}
+
+/* Finalize of the apply_topk_in_fc1 option (cudnn-frontend PR #448, MoeEp
+ * constructor): the FC2 rows already carry their route's probability, so a
+ * token's rows are added as an fp32 chain from +0.0f in canonical order,
+ * acc = acc + O[dst[t*k+j]][m] (the fused multiply-add of [VALUE] with a
+ * probability of 1, which is exact); to_bf16 rounds the sum to bf16 (nearest
+ * even) as the bf16 combine does.  Dropped routes (dst < 0) add nothing. */
+void orc_finalize_sum(const float* O, const int32_t* dst, int32_t T, int k, int H, int to_bf16,
+                      void* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t mo = 0; mo < H; ++mo) {
+            float acc = 0.0f;
+            for (int j = 0; j < k; ++j) {
+                int32_t d = dst[t * k + j];
+                if (d < 0) continue;
+                acc = acc + O[(int64_t)d * H + mo];
+            }
+            if (to_bf16) ((uint16_t*)out)[t * H + mo] = orc_bf16_bits(acc);
+            else ((float*)out)[t * H + mo] = acc;
+        }
 }
 
 /* Row mode ([VALUE] "What is changed", expert compute; [API]
@@ -625,7 +661,9 @@ void orc_weights_destroy(void* p)
  * (orc_prepare), the expert MLP of every permuted row, in permuted order,
  * into O rows, then the finalize.  combine 0: out fp32 [T_cap][H] (orc_finalize);
  * 1: out bf16 bits [T_cap][H] (orc_finalize_bf16); 2: out fp32 [T_cap][k][H]
- * (orc_finalize_rows).  Optional outputs: O_out [T*k][H] fp32 (permuted order)
+ * (orc_finalize_rows).  combine 0 or 1 with ORC_APPLY_TOPK_IN_FC1 added: the
+ * probabilities multiply the SwiGLU rows (expert_row_p) and the finalize
+ * sums the weighted rows (orc_finalize_sum).  Optional outputs: O_out [T*k][H] fp32 (permuted order)
  * and H_out [T*k][F] fp32 (the FC2 operand values).  Returns error bits. */
 uint32_t orc_forward_ex(void* wp, const uint16_t* x, const int32_t* ids, const float* probs,
                         int64_t T_cap, int32_t live, int combine, void* out, float* O_out,
@@ -634,6 +672,8 @@ uint32_t orc_forward_ex(void* wp, const uint16_t* x, const int32_t* ids, const f
     orc_weights* w = (orc_weights*)wp;
     const orc_model* m = &w->m;
     const int E = m->E, H = m->H, F = m->F, k = m->k;
+    const int fc1_topk = (combine & ORC_APPLY_TOPK_IN_FC1) != 0;
+    combine &= ~ORC_APPLY_TOPK_IN_FC1;
     int32_t T;
     int32_t* sorted_ids = (int32_t*)malloc(sizeof(int32_t) * (T_cap * k + 1));
     float* sorted_probs = (float*)malloc(sizeof(float) * (T_cap * k + 1));
@@ -655,13 +695,16 @@ uint32_t orc_forward_ex(void* wp, const uint16_t* x, const int32_t* ids, const f
             int32_t r = perm_src[i];
             int32_t t = r / k;
             int32_t e = sorted_ids[r];
-            expert_row(m, e, xo + (int64_t)t * H, O + i * H, a32, hrow);
+            expert_row_p(m, e, xo + (int64_t)t * H, O + i * H, a32, hrow,
+                         fc1_topk ? sorted_probs[r] : 1.0f);
             if (H_out)
                 for (int64_t n = 0; n < F; ++n) H_out[i * F + n] = (float)hrow[n];
         }
         free(a32); free(hrow);
     }
-    if (combine == 1)
+    if (fc1_topk)
+        orc_finalize_sum(O, dst, T, k, H, combine == 1, out);
+    else if (combine == 1)
         orc_finalize_bf16(O, dst, sorted_probs, T, k, H, (uint16_t*)out);
     else if (combine == 2)
         orc_finalize_rows(O, dst, T, k, H, (float*)out);
@@ -685,8 +728,19 @@ uint32_t orc_forward(void* wp, const uint16_t* x, const int32_t* ids, const floa
  * the rows with the same fp32 fma chain.  out_rows is [n_tok][H].  Used to
  * pin the permutation bookkeeping of orc_forward, and to check sampled
  * tokens of large launches one by one. */
+void orc_forward_tokens_ex(void* wp, const uint16_t* x, const int32_t* ids, const float* probs,
+                           const int64_t* tokens, int64_t n_tok, int fc1_topk, float* out_rows);
+
 void orc_forward_tokens(void* wp, const uint16_t* x, const int32_t* ids, const float* probs,
                         const int64_t* tokens, int64_t n_tok, float* out_rows)
+{
+    orc_forward_tokens_ex(wp, x, ids, probs, tokens, n_tok, 0, out_rows);
+}
+
+/* As orc_forward_tokens; with fc1_topk the probability is applied inside FC1
+ * (expert_row_p) and the weighted rows are summed (orc_finalize_sum). */
+void orc_forward_tokens_ex(void* wp, const uint16_t* x, const int32_t* ids, const float* probs,
+                           const int64_t* tokens, int64_t n_tok, int fc1_topk, float* out_rows)
 {
     orc_weights* w = (orc_weights*)wp;
     const orc_model* m = &w->m;
@@ -715,11 +769,15 @@ void orc_forward_tokens(void* wp, const uint16_t* x, const int32_t* ids, const f
             for (int j = 0; j < k; ++j)
                 use[j] = id[j] >= 0 && id[j] < E && !(j > 0 && id[j] == id[j - 1]);
             for (int j = 0; j < k; ++j)
-                if (use[j]) expert_row(m, id[j], xr, o + (int64_t)j * H, a32, hrow);
+                if (use[j])
+                    expert_row_p(m, id[j], xr, o + (int64_t)j * H, a32, hrow,
+                                 fc1_topk ? p[j] : 1.0f);
             for (int64_t mo = 0; mo < H; ++mo) {
                 float acc = 0.0f;
                 for (int j = 0; j < k; ++j)
-                    if (use[j]) acc = fmaf(p[j], o[(int64_t)j * H + mo], acc);
+                    if (use[j])
+                        acc = fc1_topk ? acc + o[(int64_t)j * H + mo]
+                                       : fmaf(p[j], o[(int64_t)j * H + mo], acc);
                 out_rows[q * H + mo] = acc;
             }
         }

@@ -778,3 +778,107 @@ def test_pack_mxfp4_layout_definition(H, F):
             grp = 1 * nt * KQ + g * 32 * KQ + (b // 16) * w + cl % 32
             assert buf[off[scales_at] + grp * 256 + ((b % 4) * 16 + 5) * 4 + (b // 4) % 4] == \
                 qs.reshape(E, N, K // 32)[1, n, b]
+
+
+# ------------------------------------------------------------------ apply_topk_in_fc1
+
+def _load_fc1_topk_cases():
+    with open(os.path.join(GOLDEN, "fc1_topk_cases.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("precision", ["bf16", "mxfp8", "mxfp4"])
+@pytest.mark.parametrize("c", _load_fc1_topk_cases(), ids=lambda c: c["name"])
+def test_fc1_topk_hand_cases(c, precision):
+    """The probability applied inside FC1 (before the FC2-input rounding), the
+    weighted rows summed: exact hand cases (tests/golden/make_fc1_topk_cases.py)."""
+    x, ids, pr, w1, w2 = hand_case_arrays(c)
+    m = oracle.Model(c["E"], c["H"], c["F"], c["k"], w1, w2, precision)
+    out, err, _ = m.forward(x, ids, pr, c["live"], topk_in_fc1=True)
+    assert err == 0
+    assert np.array_equal(out, np.array(c["expected"][precision], np.float32))
+    naive = m.forward_tokens(x, ids, pr, np.arange(c["live"]), topk_in_fc1=True)
+    assert np.array_equal(naive, out[: c["live"]])
+    if "default_combine_bf16" in c and precision == "bf16":
+        # the default combine (probability after FC2) differs: the case pins the
+        # rounding point, not just the value
+        ref, _, _ = m.forward(x, ids, pr, c["live"])
+        assert np.array_equal(ref, np.array(c["default_combine_bf16"], np.float32))
+        assert not np.array_equal(ref, out)
+
+
+def _random_case(precision, seed, probs_kind):
+    w = WORKLOADS["tiny"]
+    inp = make_inputs(w, seed=seed, outliers=precision != "bf16")
+    ids, probs, _ = oracle.route(inp["logits"], w.T, w.k)
+    rng = np.random.default_rng(seed)
+    if probs_kind == "pow2":
+        probs = (2.0 ** -rng.integers(0, 4, probs.shape)).astype(np.float32)
+    elif probs_kind == "ones":
+        probs = np.ones_like(probs)
+    m = oracle.Model(w.E, w.H, w.F, w.k, inp["w1_bits"], inp["w2_bits"], precision)
+    return w, inp, ids, probs, m
+
+
+@pytest.mark.parametrize("precision", ["bf16", "mxfp8", "mxfp4"])
+@pytest.mark.parametrize("probs_kind", ["ones", "pow2"])
+def test_fc1_topk_equals_default_for_exact_scalings(precision, probs_kind):
+    """Scaling by p = 1, or by a power of two, commutes with every rounding step
+    (bf16 RNE, the MX block scale shifts by the same exponent, fp32 products and
+    the fp32 chain), so the two placements of the probability agree bit for bit:
+    out = sum_j O'_j with O'_j = p_j O_j exactly, and fma(p_j, O_j, acc) =
+    acc + p_j O_j."""
+    w, inp, ids, probs, m = _random_case(precision, 11, probs_kind)
+    a, _, _ = m.forward(inp["x_bits"], ids, probs, w.T)
+    b, _, _ = m.forward(inp["x_bits"], ids, probs, w.T, topk_in_fc1=True)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("precision", ["bf16", "mxfp8", "mxfp4"])
+def test_fc1_topk_vs_dense_fp64_formulation(precision):
+    """Whole layer with the probability inside FC1 vs an independent dense fp64
+    formulation: the SwiGLU row scaled by p in fp32, rounded to the FC2 operand
+    (torch's bf16 cast, or MX quantization), FC2 in fp64, rows summed."""
+    w, inp, ids, probs, m = _random_case(precision, 12, "router")
+    out, err, _ = m.forward(inp["x_bits"], ids, probs, w.T, topk_in_fc1=True)
+    assert err == 0
+    xv = oracle.bf16_value(inp["x_bits"]).astype(np.float64)
+    w1v = oracle.bf16_value(inp["w1_bits"]).astype(np.float64)
+    w2v = oracle.bf16_value(inp["w2_bits"]).astype(np.float64)
+    xv, w1v, w2v = _operand_values(precision, xv, w1v, w2v, w)
+    ref = np.zeros((w.T, w.H))
+    for t in range(w.T):
+        for j in range(w.k):
+            e = ids[t, j]
+            x = torch.from_numpy(xv[t:t + 1])
+            w1 = torch.from_numpy(w1v[e])
+            g = (x @ w1[: w.F].T).float().double()
+            u = (x @ w1[w.F:].T).float().double()
+            a = (g / (1.0 + torch.exp(-g)) * u).float() * float(probs[t, j])
+            if precision == "bf16":
+                h = a.float().to(torch.bfloat16).double()
+            else:
+                h = torch.from_numpy(oracle.mx_dequantize(*oracle.mx_quantize(a.float().numpy())))
+            ref[t] += (h @ torch.from_numpy(w2v[e]).T).float().numpy()[0]
+    rel = np.linalg.norm(out - ref) / np.linalg.norm(ref)
+    assert rel < 1e-5, rel
+    # and it is a different computation from the default placement
+    dflt, _, _ = m.forward(inp["x_bits"], ids, probs, w.T)
+    assert not np.array_equal(dflt, out)
+
+
+def test_finalize_sum_is_fma_chain_with_unit_probabilities():
+    """The weighted-row finalize is the fp32 FMA chain with p = 1 (fma(1, o, acc)
+    = acc + o exactly), including dropped routes; its bf16 variant is torch's
+    bf16 cast of the fp32 result."""
+    rng = np.random.default_rng(7)
+    T, k, H = 9, 5, 64
+    O = (rng.standard_normal((T * k, H)) * 10.0 ** rng.integers(-3, 4, (T * k, 1))).astype(np.float32)
+    dst = rng.permutation(T * k).astype(np.int32).reshape(T, k)
+    dst[2, 1] = -1
+    dst[5, 0] = -1
+    s = oracle.finalize_sum(O, dst, H)
+    f = oracle.finalize(O, dst, np.ones((T, k), np.float32), H)
+    assert np.array_equal(s.view(np.uint32), f.view(np.uint32))
+    b = oracle.finalize_sum(O, dst, H, to_bf16=True)
+    assert np.array_equal(b, torch.from_numpy(s).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
