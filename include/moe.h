@@ -200,6 +200,27 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
                           const float* probs, int64_t T_cap, const int32_t* live_rows_dev,
                           int combine, void* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_forward_ex without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  The workspace is a 64 MiB device array that the
+ * library holds on each GPU it runs on until the process ends; its address is
+ * looked up once per GPU (hipGetSymbolAddress) at the first call there.  The
+ * call allocates nothing and enqueues the same kernels as moe_forward_ex.
+ *   Arguments as moe_forward_ex, minus ws / ws_bytes.
+ *   Limit: T_cap with moe_workspace_bytes(h, T_cap) <= 64 MiB (about 600
+ *   tokens at hidden 2048, FFN 1024, top-6); a larger T_cap returns
+ *   MOE_ERR_INVALID_ARG with nothing enqueued.
+ *   Every call on one GPU shares that GPU's array, from any handle or stream:
+ *   calls that overlap in time on one GPU race and must be ordered by the
+ *   caller.  Nothing needs to start at zero (see moe_workspace_bytes); the
+ *   array keeps the last call's contents, and contract-violation bits are
+ *   not reported (moe_check needs a caller workspace).
+ * Errors: as moe_forward_ex; MOE_ERR_HIP if the array's address cannot be
+ * looked up. */
+moe_status moe_forward_noalloc(moe_handle h, const void* x, const int32_t* expert_ids,
+                               const float* probs, int64_t T_cap, const int32_t* live_rows_dev,
+                               int combine, void* out, hipStream_t stream);
+
 /* Copy the permutation of the last forward to host arrays (synchronizes the
  * stream).  The grouping is cudnn-frontend PR #448's route index (MoeEp class
  * docstring): rows grouped by local expert in ascending order, token-major

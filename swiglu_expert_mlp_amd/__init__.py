@@ -47,6 +47,8 @@ _SIGNATURES = {
     "moe_forward": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_forward_ex": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, _P, ctypes.c_int, _P, _P,
                                       ctypes.c_size_t, _P]),
+    "moe_forward_noalloc": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, _P, ctypes.c_int, _P,
+                                           _P]),
     "moe_get_indices": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P]),
     "moe_get_rows": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P]),
     "moe_check": (ctypes.c_int, [_P, _P, _P, ctypes.POINTER(ctypes.c_uint32)]),
@@ -212,6 +214,24 @@ class MoE:
         pw = _dev(ws, "ws", (torch.uint8,))
         _check(lib().moe_forward_ex(self._h, px, pi, pp, T_cap, plive, COMBINES[combine], po, pw,
                                     ws.numel(), _stream(stream)), "moe_forward")
+        return out
+
+    def forward_noalloc(self, x, ids, probs, live, out=None, stream=None, combine="fp32"):
+        """moe_forward_noalloc: the forward with the library's own per-GPU scratch
+        as workspace (no caller workspace, nothing allocated by the library).
+        Calls that overlap on one GPU race; the capacity is bounded."""
+        torch = _torch()
+        T_cap = x.shape[0]
+        dts, shape, alloc = self._out_spec(T_cap, combine)
+        px = _dev(x, "x", (torch.bfloat16, torch.int16, torch.uint16), (T_cap, self.H))
+        pi = _dev(ids, "expert_ids", (torch.int32,), (T_cap, self.topk))
+        pp = None if probs is None else _dev(probs, "probs", (torch.float32,), (T_cap, self.topk))
+        plive = _dev(live, "live", (torch.int32,))
+        if out is None:
+            out = torch.empty(shape, dtype=alloc, device=x.device)
+        po = _dev(out, "out", dts, shape)
+        _check(lib().moe_forward_noalloc(self._h, px, pi, pp, T_cap, plive, COMBINES[combine], po,
+                                         _stream(stream)), "moe_forward_noalloc")
         return out
 
     # ------------------------------------------------------------- inspection

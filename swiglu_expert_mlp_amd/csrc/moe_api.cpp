@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/moe.h"
@@ -140,6 +141,36 @@ static moe_status ensure_device(moe_ctx* h)
         h->device = dev;
         h->num_cu = cus > 0 ? cus : 1;
     }
+    return MOE_OK;
+}
+
+// Workspace of moe_forward_noalloc: device memory the library itself holds, one
+// copy per GPU (the array is a device global of this code object), kept until
+// the process ends.  Host code never uses the array's name as an address: the
+// name is a host-side stand-in, so the device address of each GPU's copy is
+// taken once with hipGetSymbolAddress while that GPU is current.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kMaxScratchDevices = 64;
+static __device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+static void* g_scratch_ptr[kMaxScratchDevices];
+static std::mutex g_scratch_mu;
+
+static moe_status scratch_of_current_device(void** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(MOE_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
     return MOE_OK;
 }
 
@@ -364,6 +395,27 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
     if (e != hipSuccess) return hip_fail(e, "moe_forward: finalize launch");
     if ((e = mark(h, 5, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     return MOE_OK;
+}
+
+moe_status moe_forward_noalloc(moe_handle h, const void* x, const int32_t* expert_ids,
+                               const float* probs, int64_t T_cap, const int32_t* live_rows_dev,
+                               int combine, void* out, hipStream_t stream)
+{
+    if (!h) return fail(MOE_ERR_INVALID_ARG, "moe_forward_noalloc: NULL handle");
+    if (T_cap < 0 || T_cap > (int64_t)1 << 26)
+        return fail(MOE_ERR_INVALID_ARG, "moe_forward_noalloc: T_cap=%lld out of range",
+                    (long long)T_cap);
+    const size_t need = layout_of(h, T_cap).total;
+    if (need > kScratchBytes)
+        return fail(MOE_ERR_INVALID_ARG,
+                    "moe_forward_noalloc: T_cap=%lld needs a %zu-byte workspace, above the "
+                    "%zu-byte library scratch; use moe_forward with a caller workspace",
+                    (long long)T_cap, need, kScratchBytes);
+    void* ws = nullptr;
+    moe_status st = scratch_of_current_device(&ws);
+    if (st != MOE_OK) return st;
+    return moe_forward_ex(h, x, expert_ids, probs, T_cap, live_rows_dev, combine, out, ws,
+                          kScratchBytes, stream);
 }
 
 moe_status moe_get_indices(moe_handle h, const void* ws, int64_t T_cap, int32_t* counts,
