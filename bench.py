@@ -80,7 +80,7 @@ def copy_calibration():
 
 
 GEMM_SOURCES = ["swiglu_expert_mlp_amd/csrc/gemm_bf16.hip", "swiglu_expert_mlp_amd/csrc/gemm_bf16_small.h",
-                "swiglu_expert_mlp_amd/csrc/gemm_bf16_lds.h", "swiglu_expert_mlp_amd/csrc/gemm_mxfp8.hip",
+                "swiglu_expert_mlp_amd/csrc/gemm_bf16_big.h", "swiglu_expert_mlp_amd/csrc/gemm_mxfp8.hip",
                 "swiglu_expert_mlp_amd/csrc/gemm_mxfp8_stream.h", "swiglu_expert_mlp_amd/csrc/gemm_mxfp8_lds.h",
                 "swiglu_expert_mlp_amd/csrc/gemm_mx4_small.h",
                 "swiglu_expert_mlp_amd/csrc/gemm_args.h", "swiglu_expert_mlp_amd/csrc/common.h"]
@@ -306,12 +306,15 @@ def run_workload(name: str, a, cpu_seconds: float, threads1: bool) -> dict:
     tflops = flops / (ms_step * 1e-3) / 1e12
     roof = roofline_of(w, ab, fc1_us)
     # the FC1 + SwiGLU stage: its tiles are 256-row tiles (experts with more than
-    # 128 rows) or 64-row tiles (the others); one launch, except MXFP4 above a
-    # 1024-token capacity (the 256-row launch, then the 64-row launch)
-    roof["kernel"] = {"bf16": "moe::gemm_bf16_kernel<true>",
-                      "mxfp8": "moe::gemm_mxfp8_kernel<true, false>",
-                      "mxfp4": "moe::gemm_mx4_small_kernel<true>" if w.T_cap <= 1024 else
-                               "moe::gemm_mxfp8_kernel<true, true> + moe::gemm_mx4_small_kernel<true>"
+    # 128 rows) or 64-row tiles (the others); one launch at token capacities up
+    # to 1024 (the 64-row kernel takes every tile), else the 256-row launch and
+    # then the 64-row launch (MXFP8: one launch for both)
+    small = w.T_cap <= 1024
+    roof["kernel"] = {"bf16": "moe::gemm_bf16_small_kernel<true, false>" if small else
+                              "moe::gemm_bf16_big_kernel<true, false> + moe::gemm_bf16_small_kernel<true, false>",
+                      "mxfp8": "moe::gemm_mxfp8_kernel<true, false, false>",
+                      "mxfp4": "moe::gemm_mx4_small_kernel<true, false>" if small else
+                               "moe::gemm_mxfp8_kernel<true, true, false> + moe::gemm_mx4_small_kernel<true, false>"
                       }[w.precision]
     roof["tiles"] = "256-row" if int(loads.min()) > 128 else (
         "64-row" if int(loads.max()) <= 128 else "256-row + 64-row")

@@ -177,8 +177,20 @@ typedef enum {
     MOE_COMBINE_ROWS = 2,  /* each route unscaled: out fp32 [T_cap][topk][H]              */
 } moe_combine;
 
+/* Added to MOE_COMBINE_FP32 or MOE_COMBINE_BF16: apply each route's
+ * probability inside FC1 instead of in the combine (cudnn-frontend PR #448,
+ * the MoeEp constructor's apply_topk_in_fc1 option).  The pages give no
+ * arithmetic for it; here the fp32 SwiGLU row is multiplied by the route's
+ * probability before the FC2-input rounding (bf16 nearest even, or the MXFP8
+ * requantization per 32-block), FC2 returns the weighted row, and the combine
+ * adds a token's weighted rows as an fp32 chain from +0 in canonical order
+ * (the fused multiply-add of the default combine with p = 1); MOE_COMBINE_BF16
+ * rounds that sum to bf16.  Not valid with MOE_COMBINE_ROWS. */
+#define MOE_APPLY_TOPK_IN_FC1 0x100
+
 /* moe_forward with a choice of combine; every stage before the combine is
- * moe_forward's, so the FC2 rows are bit-identical across the three.
+ * moe_forward's, so the FC2 rows are bit-identical across the three (without
+ * MOE_APPLY_TOPK_IN_FC1, which changes the FC2 rows).
  *   MOE_COMBINE_FP32: exactly moe_forward.
  *   MOE_COMBINE_BF16 (Megatron-LM PR #7798, "What is changed": the
  *     BF16_RANK_PARTIALS unpermute, which on one rank adds a token's routes as
@@ -194,8 +206,10 @@ typedef enum {
  *     route's fp32 FC2 row; -0 comes back as +0 and a dropped route (invalid
  *     or repeated id) as a row of +0.  out is fp32 [T_cap][topk][H].  probs
  *     is not read and may be NULL.
+ * combine may carry MOE_APPLY_TOPK_IN_FC1 (fp32 and bf16 combines).
  * Rows of tokens >= live are never written in any mode.  Errors: an unknown
- * combine is MOE_ERR_INVALID_ARG; otherwise as moe_forward. */
+ * combine, or MOE_APPLY_TOPK_IN_FC1 with row mode, is MOE_ERR_INVALID_ARG;
+ * otherwise as moe_forward. */
 moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids,
                           const float* probs, int64_t T_cap, const int32_t* live_rows_dev,
                           int combine, void* out, void* ws, size_t ws_bytes, hipStream_t stream);

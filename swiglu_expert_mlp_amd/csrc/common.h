@@ -47,6 +47,16 @@ constexpr uint32_t kErrLiveNeg = 8u;
 
 // ---------------------------------------------------------------- formats
 
+// SwiGLU of one gate/up pair in fp32, silu(g) * u = g / (1 + exp(-g)) * u, the
+// division as a multiply by the hardware reciprocal (v_rcp_f32, within 1 ulp).
+// Every bf16 GEMM epilogue calls this one function, so the tile designs agree
+// bit for bit.  Large negative g: exp(-g) = inf, rcp(inf) = 0, so the result
+// is a signed zero; large positive g: rcp(1) = 1, so the result is g * u.
+__device__ __forceinline__ float swiglu_f32(float g, float u)
+{
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
 // fp32 -> bf16 bits, round to nearest even (gfx950 converts in hardware).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float v)
 {

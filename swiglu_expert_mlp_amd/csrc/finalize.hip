@@ -12,6 +12,10 @@
 // neither read nor written.  One workgroup (512 threads) walks tokens; 4
 // columns per thread.
 //
+// With sorted_probs == nullptr (the probabilities were applied inside FC1, the
+// MoeEp apply_topk_in_fc1 option of cudnn-frontend PR #448) every p_j is 1:
+// the chain adds the already weighted rows, fma(1, o, acc) = acc + o exactly.
+//
 // Two more combines (the value pass of Megatron-LM PR #7798, "What is
 // changed"):
 //   bf16: the same fp32 chain rounded to bf16 (round to nearest even), which
@@ -49,7 +53,7 @@ __global__ void __launch_bounds__(512) finalize_kernel(
 #pragma unroll
         for (int j = 0; j < K; ++j) {
             d[j] = dst[t * K + j];
-            p[j] = MODE == 2 ? 1.0f : sorted_probs[t * K + j];
+            p[j] = (MODE == 2 || !sorted_probs) ? 1.0f : sorted_probs[t * K + j];
         }
         for (int c = threadIdx.x; c < H4; c += blockDim.x) {
             f4v o[K];

@@ -25,6 +25,17 @@ __device__ __forceinline__ T ld_const(const T* p)
     return *(const __attribute__((address_space(4))) T*)p;
 }
 
+// FC1 with the routes' probabilities applied inside FC1 (row_prob: the
+// canonical probabilities, indexed by route t * k + j): the probability of a
+// grouped row.  The kernels take this path as a compile-time variant (PROB):
+// a run-time branch around the load made the compiler wait on every load in
+// flight in the default epilogues.
+__device__ __forceinline__ float fc1_row_prob(const float* row_prob, const int32_t* perm_src,
+                                              int64_t row)
+{
+    return row_prob[perm_src[row]];
+}
+
 // bf16 operands.
 struct GemmArgs {
     const uint16_t* A;         // FC1: x [T_cap][H]; FC2: hbuf [rows][F]
@@ -40,6 +51,10 @@ struct GemmArgs {
     int topk;
     int n_tiles_n;             // N tiles per M tile (4 waves x 64 columns each)
     int max_tiles;             // capacity of `tiles` (entries)
+    int small_takes_big;       // 1: one launch, the 64-row kernel also runs the 256-row
+                               // tiles (as four 64-row tiles each): token capacity <= 1024,
+                               // or a shape the 256-row kernel does not take
+    const float* row_prob;     // FC1: probabilities applied to the SwiGLU rows, or null
 };
 
 // MXFP8 operands: E4M3 codes with one E8M0 scale byte per 32 elements of K.
@@ -66,6 +81,7 @@ struct MxGemmArgs {
                                // 256-row tiles (four 64-row tiles each, no 256-row launch)
     int small_batch;           // 1: decode-sized batch (the caller's token capacity <= 1024)
     int64_t a_bytes;           // bytes of A (rows x K)
+    const float* row_prob;     // FC1: probabilities applied to the SwiGLU rows, or null
 };
 
 }  // namespace moe

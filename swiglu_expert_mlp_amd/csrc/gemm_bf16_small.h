@@ -8,16 +8,17 @@
 // FC2 (the FC2 rows here are unweighted).
 //
 // Arithmetic contract (what makes every token's output independent of the
-// launch): each output element is  acc = 0; for k0 = 0, 32, 64, ... :
-// acc = MFMA_16x16x32_bf16(A[row, k0:k0+32], B[col, k0:k0+32], acc), with the
+// launch): each output element is  acc = 0; for k0 = 0, 16, 32, ... :
+// acc = MFMA_32x32x16_bf16(A[row, k0:k0+16], B[col, k0:k0+16], acc), with the
 // same instruction and the same K order whatever the tile, the row's position
 // inside its tile, or the number of rows of the launch.  Nothing splits K.
-// The 256-row tiles (gemm_bf16_lds.h) follow the same contract.
+// The 256-row tiles (gemm_bf16_big.h) follow the same contract.
 //
 // These tiles stream the expert weights (each weight byte serves at most 64
 // rows).  A workgroup of 8 waves takes a tile of up to 64 rows x 512 columns,
 // wave w owning 64 columns (FC1: one gate/up interleave block = 32 SwiGLU
-// outputs).  Each 32-wide K step moves the tile's 32 weight blocks (1 KB each,
+// outputs, the gate half and the up half one 32-column MFMA block each, so
+// the gate and up of an output sit in the same lane).  Each 32-wide K step moves the tile's 32 weight blocks (1 KB each,
 // stored in MFMA lane order; the 32 blocks of one step of a 512-column group
 // are one contiguous 32 KB run of the kernel-weight buffer) and one 16-row x
 // 64-byte activation block per row group (a quad of lanes per row, chunks
@@ -31,7 +32,7 @@
 // column's K steps contiguous instead) reach ~4.8 TB/s.
 #pragma once
 
-#include "gemm_bf16_lds.h"
+#include "gemm_bf16_big.h"
 
 namespace moe {
 
@@ -45,43 +46,64 @@ constexpr int kSmallLds = kSmallRing * kSmallStage;
 __device__ __forceinline__ void wait_vmcnt_upto15(int n)
 {
     switch (n) {
-        case 0: WAIT_VMCNT(0); break;
-        case 1: WAIT_VMCNT(1); break;
-        case 2: WAIT_VMCNT(2); break;
-        case 3: WAIT_VMCNT(3); break;
-        case 4: WAIT_VMCNT(4); break;
-        case 5: WAIT_VMCNT(5); break;
-        case 6: WAIT_VMCNT(6); break;
-        case 7: WAIT_VMCNT(7); break;
-        case 8: WAIT_VMCNT(8); break;
-        case 9: WAIT_VMCNT(9); break;
-        case 10: WAIT_VMCNT(10); break;
-        default: WAIT_VMCNT(0); break;
+        case 0: BIG_WAIT_VMCNT(0); break;
+        case 1: BIG_WAIT_VMCNT(1); break;
+        case 2: BIG_WAIT_VMCNT(2); break;
+        case 3: BIG_WAIT_VMCNT(3); break;
+        case 4: BIG_WAIT_VMCNT(4); break;
+        case 5: BIG_WAIT_VMCNT(5); break;
+        case 6: BIG_WAIT_VMCNT(6); break;
+        case 7: BIG_WAIT_VMCNT(7); break;
+        case 8: BIG_WAIT_VMCNT(8); break;
+        case 9: BIG_WAIT_VMCNT(9); break;
+        case 10: BIG_WAIT_VMCNT(10); break;
+        default: BIG_WAIT_VMCNT(0); break;
     }
 }
 
 __device__ __forceinline__ int small_col_tiles(const GemmArgs& g) { return (g.N + kSmallCols - 1) / kSmallCols; }
 
-// n_mt: the number of 64-row M tiles; (e0, row00): the table entry of this
-// workgroup's first tile (blockIdx.x), read by the caller before n_mt was known.
-template <bool FC1>
-__device__ __forceinline__ void small_tiles(const GemmArgs& g, char* smem, int n_mt, int e0, int row00)
+// n_small: the number of 64-row M tiles; n_big: the number of 256-row M
+// tiles this launch also runs, as four 64-row tiles each (0 when a launch of
+// the 256-row design takes them); (e0, row00): the table entry of this
+// workgroup's first tile (blockIdx.x), read by the caller before the counts
+// were known.
+template <bool FC1, bool PROB>
+__device__ __forceinline__ void small_tiles(const GemmArgs& g, char* smem, int n_small, int n_big,
+                                            int e0, int row00)
 {
     const int NTs = small_col_tiles(g);
-    const int total = n_mt * NTs;
+    const int total = (n_small + 4 * n_big) * NTs;
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int K = g.K;
     const int nsteps = K / 32;
     const int nt16 = g.N / 16;
     const int n_cb = g.N / 64 + ((g.N % 64) ? 1 : 0);
-    const int a_off = 16 * (4 * (lane & 15) + ((lane >> 4) ^ a_swz(lane & 15)));
-    const int r16 = lane & 15, kg = lane >> 4;
+    // 32 x 16 fragment lanes of sub-step q (8-wide K chunks 2 q, 2 q + 1): A row
+    // l % 32 of a 32-row block, chunk 2 q + l / 32; B column l % 32, lane
+    // 16 (2 q + l / 32) + l % 16 of its 16-column block
+    int a_off[2], b_off[2];
+    {
+        const int r = lane & 31, r16 = r & 15, hi = lane >> 5;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int c = 2 * q + hi;
+            a_off[q] = (r >> 4) * 1024 + 16 * (4 * r16 + (c ^ big_swz(r16)));
+            b_off[q] = (r >> 4) * 1024 + 16 * (16 * c + r16);
+        }
+    }
+    const int c32 = lane & 31, hi = lane >> 5;
 
     for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
         const int mt = tile / NTs, ct = tile - mt * NTs;
         int e = e0, row0 = row00;
-        if (tile != (int)blockIdx.x) {
+        if (mt >= n_small) {
+            // a 256-row tile run as four 64-row tiles
+            const int* te = (const int*)(g.tiles_big + ((mt - n_small) >> 2));
+            e = ld_const(te);
+            row0 = ld_const(te + 1) + kBM * ((mt - n_small) & 3);
+        } else if (tile != (int)blockIdx.x) {
             const int* te = (const int*)(g.tiles + mt);
             e = ld_const(te);
             row0 = ld_const(te + 1);
@@ -101,17 +123,24 @@ __device__ __forceinline__ void small_tiles(const GemmArgs& g, char* smem, int n
             if (has_cols) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    load_block_to_lds(bblk[j] + (int64_t)bstep[j] * s, st + (4 + 4 * wid + j) * 1024);
+                    big_load_block(bblk[j] + (int64_t)bstep[j] * s, st + (4 + 4 * wid + j) * 1024);
             }
         };
+        // a 64-row part of a 256-row tile may lie past its expert's rows
+        int rows = 0;
+        if (mt >= n_small) {
+            rows = min(kBM, ld_const(g.offsets + e + 1) - row0);
+            if (rows <= 0) continue;                 // uniform across the workgroup
+        }
         // every wave finished the previous tile's LDS reads before the ring is
         // refilled; step 0's weights go out before the row count and the
         // gathered rows (a further round trip) are known
         __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         issue_b(0);
-        const int rows = min(kBM, ld_const(g.offsets + e + 1) - row0);
-        const int ng = (rows + 15) >> 4;
+        if (mt < n_small) rows = min(kBM, ld_const(g.offsets + e + 1) - row0);
+        const int ng = (rows + 15) >> 4;             // 16-row activation blocks
+        const int nb = (rows + 31) >> 5;             // 32-row MFMA blocks
         const bool has_a = wid < ng;                 // this wave loads activation block wid
         const int nl = (has_a ? 1 : 0) + (has_cols ? 4 : 0);
 
@@ -120,18 +149,20 @@ __device__ __forceinline__ void small_tiles(const GemmArgs& g, char* smem, int n
             const int r = min(16 * wid + (lane >> 2), rows - 1);
             int64_t src = row0 + r;
             if constexpr (FC1) src = g.perm_src[src] / g.topk;
-            arow = g.A + src * K + 8 * ((lane & 3) ^ a_swz(lane >> 2));
+            arow = g.A + src * K + 8 * ((lane & 3) ^ big_swz(lane >> 2));
         }
         auto issue_a = [&](int s) {
-            if (has_a) load_block_to_lds(arow + 32 * s, smem + (s % kSmallRing) * kSmallStage + wid * 1024);
+            if (has_a) big_load_block(arow + 32 * s, smem + (s % kSmallRing) * kSmallStage + wid * 1024);
         };
         auto issue = [&](int s) { issue_a(s); issue_b(s); };
 
-        f32x4 acc[4][4];
+        f32x16 acc[2][2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
         // a step's loads stay contiguous in issue order (step 0: weights, then rows)
         issue_a(0);
@@ -145,59 +176,61 @@ __device__ __forceinline__ void small_tiles(const GemmArgs& g, char* smem, int n
             if (s + kSmallRing - 1 < nsteps) issue(s + kSmallRing - 1);
             if (has_cols) {
                 const char* st = smem + (s % kSmallRing) * kSmallStage;
-                bf16x8 a[4], b[4];
+                // B blocks 4 wid + 2 j and + 1 hold the wave's 32-column block j
+                bf16x8 a[2][2], b[2][2];
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    b[j] = __builtin_bit_cast(bf16x8, *(const uint4*)(st + (4 + 4 * wid + j) * 1024 + 16 * lane));
+                for (int q = 0; q < 2; ++q) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (i < ng) a[i] = __builtin_bit_cast(bf16x8, *(const uint4*)(st + i * 1024 + a_off));
+                    for (int j = 0; j < 2; ++j)
+                        b[q][j] = big_frag(st + (4 + 4 * wid + 2 * j) * 1024 + b_off[q]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (i < ng)
+                    for (int i = 0; i < 2; ++i)
+                        if (i < nb) a[q][i] = big_frag(st + 2 * i * 1024 + a_off[q]);
+                }
 #pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+                        if (i < nb)
+#pragma unroll
+                            for (int j = 0; j < 2; ++j)
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[q][i], b[q][j], acc[i][j], 0, 0, 0);
             }
         }
 
-        // epilogue: lane holds rows 4 kg + v of each 16-row group, column r16 of each block
+        // epilogue: lane holds column l % 32 of each 32-column block and rows
+        // 8 (v / 4) + 4 (l / 32) + v % 4 of each 32-row block
         if (!has_cols) continue;
         if constexpr (FC1) {
+            // column block 0 is the gate half, 1 the up half of interleave block cb
             const int F = g.N / 2;
             uint16_t* hb = (uint16_t*)g.out;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int r = 16 * i + 4 * kg + v;
-                    if (i < ng && r < rows) {
-                        const int64_t row = row0 + r;
-#pragma unroll
-                        for (int h = 0; h < 2; ++h) {
-                            const float gt = acc[i][h][v];
-                            const float up = acc[i][h + 2][v];
-                            const float hv = gt / (1.0f + __expf(-gt)) * up;
-                            hb[row * F + cb * 32 + 16 * h + r16] = f32_to_bf16_bits(hv);
-                        }
+                for (int v = 0; v < 16; ++v) {
+                    const int r = 32 * i + 8 * (v >> 2) + 4 * hi + (v & 3);
+                    if (i < nb && r < rows) {
+                        const float pr = PROB ? fc1_row_prob(g.row_prob, g.perm_src, row0 + r) : 1.0f;
+                        hb[(int64_t)(row0 + r) * F + cb * 32 + c32] =
+                            f32_to_bf16_bits(swiglu_f32(acc[i][0][v], acc[i][1][v]) * pr);
                     }
                 }
         } else {
             float* ob = (float*)g.out;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 2; ++j) {
+                const int col = cb * 64 + 32 * j + c32;
+                if (cb * 64 + 32 * j < g.N) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int r = 16 * i + 4 * kg + v;
-                    if (i < ng && r < rows) {
-                        const int64_t row = row0 + r;
+                    for (int i = 0; i < 2; ++i)
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const int col = cb * 64 + 16 * j + r16;
-                            if (col < g.N) ob[row * g.N + col] = acc[i][j][v];
+                        for (int v = 0; v < 16; ++v) {
+                            const int r = 32 * i + 8 * (v >> 2) + 4 * hi + (v & 3);
+                            if (i < nb && r < rows) ob[(int64_t)(row0 + r) * g.N + col] = acc[i][j][v];
                         }
-                    }
                 }
+            }
         }
     }
 }

@@ -38,7 +38,19 @@ constexpr int kMx4Cols = 512;                    // columns per tile (8 waves x 
 constexpr int kMx4Slot = 4096 + 1024 + 256;      // one wave's weight slot: codes, scale groups, activation scales
 constexpr int kMx4SlotAll = 8 * kMx4Slot;         // one weight slot of all 8 waves
 constexpr int kMx4ASlot = 64 * 128;              // one activation-code slot: 64 rows x 128 bytes
-constexpr int kMx4Loads = 10;                    // direct loads per wave and step
+// Direct loads per wave and step, by what issues them (the waits below are
+// derived from these counts; each issuing loop is bounded by its constant)
+constexpr int kMx4CodeLoads = 4;                 // issue_w: 4 weight-code blocks of 1 KB
+constexpr int kMx4ScaleLoads = 4;                // issue_w: 4 weight-scale groups
+constexpr int kMx4ActScaleLoads = 1;             // issue_w: the activation scales
+constexpr int kMx4WLoads = kMx4CodeLoads + kMx4ScaleLoads + kMx4ActScaleLoads;
+constexpr int kMx4ALoads = 1;                    // issue_a: the activation codes
+constexpr int kMx4Loads = kMx4WLoads + kMx4ALoads;
+// Issue order: W(0) A(0) W(1) A(1) W(2), then step t issues A(t + 2) W(t + 3).
+// At step s's wait, after the last load of A(s) come W(s+1) A(s+1) W(s+2) and
+// after the last load of W(s) one more (A(s)); the smaller count is the bound.
+constexpr int kMx4StepWait = 2 * kMx4WLoads + kMx4ALoads;
+static_assert(kMx4StepWait == 2 * kMx4Loads - 1 && kMx4StepWait <= 63, "vmcnt bound");
 
 typedef __attribute__((address_space(3))) void mx4_lds_void;
 
@@ -55,7 +67,7 @@ struct Mx4Ring {
     char *w0, *w1, *w2, *q0, *q1, *q2;
 };
 
-template <bool FC1, int NG>
+template <bool FC1, int NG, bool PROB>
 __device__ __forceinline__ void mx4_tile(const MxGemmArgs& g, const Mx4Ring& rg, int wid, int e, int row0,
                                          int rows, int cb, bool has_cols)
 {
@@ -106,18 +118,21 @@ __device__ __forceinline__ void mx4_tile(const MxGemmArgs& g, const Mx4Ring& rg,
     // activation codes of step s into shared slot q: 1 load
     auto issue_a = [&](int s, char* q) {
         const int t = min(s, KS - 1);
+        static_assert(kMx4ALoads == 1, "issue_a issues one load");
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (mx4_lds_void*)(q + wid * 1024), 16, aoff, 128 * t, 0, 0);
         __builtin_amdgcn_sched_barrier(0);      // the vmcnt count below assumes source order
     };
-    // weights of step s (+ activation scales) into this wave's slot w: 9 loads
+    // weights of step s (+ activation scales) into this wave's slot w: kMx4WLoads loads
     auto issue_w = [&](int s, char* w) {
         const int t = min(s, KS - 1);
+        static_assert(kMx4CodeLoads == 4 && kMx4ScaleLoads == 4 && kMx4ActScaleLoads == 1,
+                      "a wave loads its 4 column blocks' codes and scale groups");
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < kMx4CodeLoads; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (mx4_lds_void*)(w + j * 1024), 16, boff,
                                                      (b0[j] + t * bw[j]) * 1024, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < kMx4ScaleLoads; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (mx4_lds_void*)(w + 4096 + j * 256), 4, qoff,
                                                      (q0[j] + (t >> 2) * bw[j]) * 256, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (mx4_lds_void*)(w + 5120), 4, soff, 4 * t, 0, 0);
@@ -134,13 +149,12 @@ __device__ __forceinline__ void mx4_tile(const MxGemmArgs& g, const Mx4Ring& rg,
     const int a_lo = r16 * 128 + ((kg ^ (r16 & 7)) << 4);
     const int a_hi = r16 * 128 + (((kg + 4) ^ (r16 & 7)) << 4);
 
-    // Load order: weights of step 0, codes of 0, weights of 1, codes of 1,
-    // weights of 2; then step t issues the codes of t + 2 and the weights of
-    // t + 3.  After the codes of step s come 19 loads (weights of s + 1, codes
-    // of s + 1, weights of s + 2) and after the weights of step s 20, so
-    // vmcnt(19) covers both.
+    // Step s waits until its weights and codes landed (kMx4StepWait).  Only
+    // direct loads may be in flight here: vmcnt also counts plain vector loads
+    // and stores, and one more of them anywhere between two steps' loads would
+    // let the count pass before step s's data is in LDS.
     auto step = [&](int s, const char* w, const char* q, char* qn) {
-        MX4_WAIT_VMCNT(2 * kMx4Loads - 1);
+        MX4_WAIT_VMCNT(kMx4StepWait);
         __builtin_amdgcn_s_barrier();
         i32x8 a[NG];
 #pragma unroll
@@ -208,17 +222,19 @@ __device__ __forceinline__ void mx4_tile(const MxGemmArgs& g, const Mx4Ring& rg,
         for (int i = 0; i < NG; ++i)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
+                const int r = 16 * i + 4 * kg + v;
+                // the 16 lanes of one requantization block hold one row: one probability
+                const float pr = (PROB && r < rows) ? fc1_row_prob(g.row_prob, g.perm_src, row0 + r) : 1.0f;
                 float gt = acc[i][0][v], up = acc[i][2][v];
-                const float h0 = gt / (1.0f + __expf(-gt)) * up;
+                const float h0 = gt / (1.0f + __expf(-gt)) * up * pr;
                 gt = acc[i][1][v]; up = acc[i][3][v];
-                const float h1 = gt / (1.0f + __expf(-gt)) * up;
+                const float h1 = gt / (1.0f + __expf(-gt)) * up * pr;
                 float amax = fmaxf(fabsf(h0), fabsf(h1));
 #pragma unroll
                 for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
                 const int e8 = e8m0_exponent(amax);
                 const float inv = e8 == 127 ? __uint_as_float(1u << 22)
                                             : __uint_as_float((uint32_t)(127 - e8) << 23);
-                const int r = 16 * i + 4 * kg + v;
                 if (r < rows) {
                     const int64_t row = row0 + r;
                     const uint32_t c2 = cvt_e4m3x2(h0 * inv, h1 * inv);
@@ -249,7 +265,7 @@ __device__ __forceinline__ void mx4_tile(const MxGemmArgs& g, const Mx4Ring& rg,
 // The 64-row tile loop of one 8-wave workgroup; K % 128 == 0.  Every wave
 // takes part in every tile (the barriers), a wave past N without columns.
 // With lds_small == 2 the 256-row table follows, four 64-row tiles per entry.
-template <bool FC1>
+template <bool FC1, bool PROB>
 __device__ __forceinline__ void mx4_small_tiles(const MxGemmArgs& g, const Mx4Ring& ring)
 {
     const int n_small = ld_const(&g.hdr->n_tiles);
@@ -271,10 +287,10 @@ __device__ __forceinline__ void mx4_small_tiles(const MxGemmArgs& g, const Mx4Ri
         const int cb = ct * 8 + wid;
         const bool has_cols = cb < n_cb;
         switch ((rows + 15) >> 4) {
-            case 1: mx4_tile<FC1, 1>(g, rg, wid, e, row0, rows, cb, has_cols); break;
-            case 2: mx4_tile<FC1, 2>(g, rg, wid, e, row0, rows, cb, has_cols); break;
-            case 3: mx4_tile<FC1, 3>(g, rg, wid, e, row0, rows, cb, has_cols); break;
-            default: mx4_tile<FC1, 4>(g, rg, wid, e, row0, rows, cb, has_cols); break;
+            case 1: mx4_tile<FC1, 1, PROB>(g, rg, wid, e, row0, rows, cb, has_cols); break;
+            case 2: mx4_tile<FC1, 2, PROB>(g, rg, wid, e, row0, rows, cb, has_cols); break;
+            case 3: mx4_tile<FC1, 3, PROB>(g, rg, wid, e, row0, rows, cb, has_cols); break;
+            default: mx4_tile<FC1, 4, PROB>(g, rg, wid, e, row0, rows, cb, has_cols); break;
         }
     }
 }

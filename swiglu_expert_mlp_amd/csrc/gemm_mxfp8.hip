@@ -15,18 +15,21 @@
 
 namespace moe {
 
-template <bool FC1, bool W4>
+// PROB: FC1 with the routes' probabilities applied to the SwiGLU rows (a
+// compile-time variant; the default epilogues carry no probability loads)
+template <bool FC1, bool W4, bool PROB>
 __global__ void __launch_bounds__(512, 1) gemm_mxfp8_kernel(MxGemmArgs g)
 {
-    if (!g.stream_big) mx_lds_tiles<FC1, W4>(g);
+    if (!g.stream_big) mx_lds_tiles<FC1, W4, PROB>(g);
     if (g.lds_small) return;          // the 64-row tiles have a launch of their own
     // the two halves of a workgroup are workers b and b + grid: consecutive
     // tiles (the N tiles of one M tile) go to different CUs
-    mx_stream_tiles<FC1, W4>(g, blockIdx.x + (threadIdx.x >> 8) * gridDim.x, 2 * gridDim.x, (threadIdx.x >> 6) & 3);
+    mx_stream_tiles<FC1, W4, PROB>(g, blockIdx.x + (threadIdx.x >> 8) * gridDim.x, 2 * gridDim.x,
+                                   (threadIdx.x >> 6) & 3);
 }
 
 // MXFP4, the LDS-staged 64-row tiles (gemm_mx4_small.h)
-template <bool FC1>
+template <bool FC1, bool PROB>
 __global__ void __launch_bounds__(512, 1) gemm_mx4_small_kernel(MxGemmArgs g)
 {
     __shared__ __attribute__((aligned(1024))) char w0[kMx4SlotAll];
@@ -35,7 +38,7 @@ __global__ void __launch_bounds__(512, 1) gemm_mx4_small_kernel(MxGemmArgs g)
     __shared__ __attribute__((aligned(1024))) char q0[kMx4ASlot];
     __shared__ __attribute__((aligned(1024))) char q1[kMx4ASlot];
     __shared__ __attribute__((aligned(1024))) char q2[kMx4ASlot];
-    mx4_small_tiles<FC1>(g, Mx4Ring{w0, w1, w2, q0, q1, q2});
+    mx4_small_tiles<FC1, PROB>(g, Mx4Ring{w0, w1, w2, q0, q1, q2});
 }
 
 // t0 / t1 (optional): events that receive the launch's own start and end
@@ -58,23 +61,28 @@ hipError_t launch_gemm_mxfp8(bool fc1, bool w4, const MxGemmArgs& g, int num_cu,
     // alone (taking the 256-row tiles too) at decode-sized batches
     const bool mx4_lds = w4 && !g.stream_big && g.a_bytes < ((int64_t)1 << 31) &&
                          (int64_t)g.N * g.K / 2 < ((int64_t)1 << 31);
+    const bool prob = fc1 && g.row_prob != nullptr;
     if (mx4_lds) {
         a.lds_small = g.small_batch ? 2 : 1;
         if (a.lds_small == 1) {
-            if (fc1) go(gemm_mxfp8_kernel<true, true>, t0, nullptr, a);
-            else go(gemm_mxfp8_kernel<false, true>, t0, nullptr, a);
+            if (prob) go(gemm_mxfp8_kernel<true, true, true>, t0, nullptr, a);
+            else if (fc1) go(gemm_mxfp8_kernel<true, true, false>, t0, nullptr, a);
+            else go(gemm_mxfp8_kernel<false, true, false>, t0, nullptr, a);
         }
         hipEvent_t e0 = a.lds_small == 2 ? t0 : nullptr;
-        if (fc1) go(gemm_mx4_small_kernel<true>, e0, t1, a);
-        else go(gemm_mx4_small_kernel<false>, e0, t1, a);
+        if (prob) go(gemm_mx4_small_kernel<true, true>, e0, t1, a);
+        else if (fc1) go(gemm_mx4_small_kernel<true, false>, e0, t1, a);
+        else go(gemm_mx4_small_kernel<false, false>, e0, t1, a);
         return hipGetLastError();
     }
     if (w4) {
-        if (fc1) go(gemm_mxfp8_kernel<true, true>, t0, t1, a);
-        else go(gemm_mxfp8_kernel<false, true>, t0, t1, a);
+        if (prob) go(gemm_mxfp8_kernel<true, true, true>, t0, t1, a);
+        else if (fc1) go(gemm_mxfp8_kernel<true, true, false>, t0, t1, a);
+        else go(gemm_mxfp8_kernel<false, true, false>, t0, t1, a);
     } else {
-        if (fc1) go(gemm_mxfp8_kernel<true, false>, t0, t1, a);
-        else go(gemm_mxfp8_kernel<false, false>, t0, t1, a);
+        if (prob) go(gemm_mxfp8_kernel<true, false, true>, t0, t1, a);
+        else if (fc1) go(gemm_mxfp8_kernel<true, false, false>, t0, t1, a);
+        else go(gemm_mxfp8_kernel<false, false, false>, t0, t1, a);
     }
     return hipGetLastError();
 }

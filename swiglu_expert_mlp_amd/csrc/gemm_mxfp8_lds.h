@@ -68,7 +68,7 @@ __device__ __forceinline__ i32x8 mx_frag(uint4 lo, uint4 hi)
 
 // The LDS-staged tile loop of one 8-wave workgroup (one workgroup per CU).
 // Requires K % 128 == 0.
-template <bool FC1, bool W4>
+template <bool FC1, bool W4, bool PROB>
 __device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
 {
     // the two stages are separate LDS objects, always addressed with
@@ -284,10 +284,13 @@ __device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
                 for (int i = 0; i < 8; ++i)
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
+                        const int r = 128 * wm + 16 * i + 4 * kg + v;
+                        // the 16 lanes of one requantization block hold one row: one probability
+                        const float pr = (PROB && r < rows) ? fc1_row_prob(g.row_prob, g.perm_src, row0 + r) : 1.0f;
                         float gt = acc[i][0][v], up = acc[i][2][v];
-                        const float h0 = gt / (1.0f + __expf(-gt)) * up;
+                        const float h0 = gt / (1.0f + __expf(-gt)) * up * pr;
                         gt = acc[i][1][v]; up = acc[i][3][v];
-                        const float h1 = gt / (1.0f + __expf(-gt)) * up;
+                        const float h1 = gt / (1.0f + __expf(-gt)) * up * pr;
                         float amax = fmaxf(fabsf(h0), fabsf(h1));
 #pragma unroll
                         for (int off = 1; off < 16; off <<= 1)
@@ -295,7 +298,6 @@ __device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
                         const int e8 = e8m0_exponent(amax);
                         const float inv = e8 == 127 ? __uint_as_float(1u << 22)
                                                     : __uint_as_float((uint32_t)(127 - e8) << 23);
-                        const int r = 128 * wm + 16 * i + 4 * kg + v;
                         if (r < rows) {
                             const int64_t row = row0 + r;
                             const uint32_t c2 = cvt_e4m3x2(h0 * inv, h1 * inv);

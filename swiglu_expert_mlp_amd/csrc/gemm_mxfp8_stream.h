@@ -19,8 +19,8 @@
 // K = 64 + 16 * (l / 16) + [0, 16).  The scale byte of lane l applies to the
 // 32-block (l / 16) of the step, i.e. 32-block q is made of the first halves
 // (q < 2) or second halves (q >= 2) of lane groups 2 (q % 2) and 2 (q % 2) + 1.
-// Work decomposition is the same as the bf16 streaming kernel: persistent
-// grid over (M tile, N tile), 4 waves x 64 columns, up to 64 rows per M tile.
+// Work decomposition: a persistent grid over (M tile, N tile), a worker of 4
+// waves x 64 columns per tile, up to 64 rows per M tile.
 //
 // W4: MXFP4 weights (E2M1 codes with one E8M0 scale per 32 elements of K)
 // against the same MXFP8 activations: the B operand of a 128-wide K step is
@@ -34,7 +34,7 @@
 
 namespace moe {
 
-template <bool FC1, int NG, bool W4>
+template <bool FC1, int NG, bool W4, bool PROB>
 __device__ __forceinline__ void mx_tile_body(const MxGemmArgs& g, int e, int row0, int rows,
                                              int cb)
 {
@@ -137,11 +137,14 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs& g, int e, int row
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float h0, h1;
+                int r = 16 * rg + 4 * kg + i;
                 {
+                    // the 16 lanes of one requantization block hold one row: one probability
+                    const float pr = (PROB && r < rows) ? fc1_row_prob(g.row_prob, g.perm_src, row0 + r) : 1.0f;
                     float gt = acc[rg][0][i], up = acc[rg][2][i];
-                    h0 = gt / (1.0f + __expf(-gt)) * up;
+                    h0 = gt / (1.0f + __expf(-gt)) * up * pr;
                     gt = acc[rg][1][i]; up = acc[rg][3][i];
-                    h1 = gt / (1.0f + __expf(-gt)) * up;
+                    h1 = gt / (1.0f + __expf(-gt)) * up * pr;
                 }
                 float amax = fmaxf(fabsf(h0), fabsf(h1));
 #pragma unroll
@@ -149,7 +152,6 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs& g, int e, int row
                 int e8 = e8m0_exponent(amax);
                 float inv = e8 == 127 ? __uint_as_float(1u << 22)
                                       : __uint_as_float((uint32_t)(127 - e8) << 23);
-                int r = 16 * rg + 4 * kg + i;
                 if (r < rows) {
                     int64_t row = row0 + r;
                     const uint32_t c2 = cvt_e4m3x2(h0 * inv, h1 * inv);
@@ -181,7 +183,7 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs& g, int e, int row
 // 64-row tiles of the streaming table, and the large experts' 256-row tiles as
 // four 64-row tiles each when the LDS-staged loop does not apply (K not a
 // multiple of 128).
-template <bool FC1, bool W4>
+template <bool FC1, bool W4, bool PROB>
 __device__ __forceinline__ void mx_stream_tiles(const MxGemmArgs& g, int worker, int nworkers, int wid)
 {
     const int n_small = g.hdr->n_tiles;
@@ -206,10 +208,10 @@ __device__ __forceinline__ void mx_stream_tiles(const MxGemmArgs& g, int worker,
         if (cb >= n_cb || rows <= 0) continue;
         const int ng = (rows + 15) >> 4;
         switch (ng) {
-            case 1: mx_tile_body<FC1, 1, W4>(g, e, row0, rows, cb); break;
-            case 2: mx_tile_body<FC1, 2, W4>(g, e, row0, rows, cb); break;
-            case 3: mx_tile_body<FC1, 3, W4>(g, e, row0, rows, cb); break;
-            default: mx_tile_body<FC1, 4, W4>(g, e, row0, rows, cb); break;
+            case 1: mx_tile_body<FC1, 1, W4, PROB>(g, e, row0, rows, cb); break;
+            case 2: mx_tile_body<FC1, 2, W4, PROB>(g, e, row0, rows, cb); break;
+            case 3: mx_tile_body<FC1, 3, W4, PROB>(g, e, row0, rows, cb); break;
+            default: mx_tile_body<FC1, 4, W4, PROB>(g, e, row0, rows, cb); break;
         }
     }
 }

@@ -283,8 +283,13 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
     if (!h->kbuf) return fail(MOE_ERR_NOT_LOADED, "moe_forward: no weights loaded (moe_load_weights)");
     if (T_cap < 0 || T_cap > (int64_t)1 << 26)
         return fail(MOE_ERR_INVALID_ARG, "moe_forward: T_cap=%lld out of range", (long long)T_cap);
+    const bool fc1_topk = (combine & MOE_APPLY_TOPK_IN_FC1) != 0;
+    combine &= ~MOE_APPLY_TOPK_IN_FC1;
     if (combine != MOE_COMBINE_FP32 && combine != MOE_COMBINE_BF16 && combine != MOE_COMBINE_ROWS)
         return fail(MOE_ERR_INVALID_ARG, "moe_forward: unknown combine %d", combine);
+    if (fc1_topk && combine == MOE_COMBINE_ROWS)
+        return fail(MOE_ERR_INVALID_ARG,
+                    "moe_forward: MOE_APPLY_TOPK_IN_FC1 with row mode (which uses no probabilities)");
     // row mode does not use the probabilities (every route has probability 1)
     if (!x || !expert_ids || (!probs && combine != MOE_COMBINE_ROWS) || !live_rows_dev || !out ||
         !ws)
@@ -323,6 +328,12 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         g1.topk = h->k;
         g1.n_tiles_n = ((2 * F / 64) + 3) / 4;
         g1.max_tiles = (int)L.max_tiles;
+        // the 256-row design: capacities above 1024, K a multiple of its 64-wide
+        // stage, and byte offsets inside x and inside one expert's weights that
+        // fit its 32-bit buffer offsets
+        g1.small_takes_big = T_cap <= 1024 || H % 64 != 0 || (int64_t)T_cap * H * 2 >= ((int64_t)1 << 31) ||
+                             (int64_t)2 * F * H * 2 >= ((int64_t)1 << 31);
+        g1.row_prob = fc1_topk ? (const float*)(w + L.sorted_probs) : nullptr;
         e = launch_gemm_bf16(true, g1, h->num_cu, stream, stage_event(h, 2), stage_event(h, 3));
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC1 launch");
         GemmArgs g2 = g1;
@@ -333,6 +344,8 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         g2.N = H;
         g2.K = F;
         g2.n_tiles_n = ((H + 63) / 64 + 3) / 4;
+        g2.row_prob = nullptr;
+        g2.small_takes_big = T_cap <= 1024 || F % 64 != 0 || (int64_t)H * F * 2 >= ((int64_t)1 << 31);
         e = launch_gemm_bf16(false, g2, h->num_cu, stream, nullptr, nullptr);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
         if ((e = mark(h, 4, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
@@ -370,6 +383,7 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         g1.stream_big = H % 128 != 0;
         g1.small_batch = T_cap <= 1024;
         g1.a_bytes = T_cap * H;
+        g1.row_prob = fc1_topk ? (const float*)(w + L.sorted_probs) : nullptr;
         e = launch_gemm_mxfp8(true, w4, g1, h->num_cu, stream, stage_event(h, 2), stage_event(h, 3));
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC1 launch");
         MxGemmArgs g2 = g1;
@@ -385,13 +399,15 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         g2.n_tiles_n = ((H + 63) / 64 + 3) / 4;
         g2.stream_big = F % 128 != 0;
         g2.a_bytes = T_cap * h->k * F;
+        g2.row_prob = nullptr;
         e = launch_gemm_mxfp8(false, w4, g2, h->num_cu, stream, nullptr, nullptr);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
         if ((e = mark(h, 4, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     }
+    // with the probabilities applied inside FC1 the finalize adds the rows
     e = launch_finalize((const float*)(w + L.obuf), (const int32_t*)(w + L.dst),
-                        (const float*)(w + L.sorted_probs), T_cap, live_rows_dev, h->k, H, combine,
-                        out, h->num_cu, stream);
+                        fc1_topk ? nullptr : (const float*)(w + L.sorted_probs), T_cap,
+                        live_rows_dev, h->k, H, combine, out, h->num_cu, stream);
     if (e != hipSuccess) return hip_fail(e, "moe_forward: finalize launch");
     if ((e = mark(h, 5, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     return MOE_OK;

@@ -16,7 +16,9 @@
 // The rows are then tiled into MFMA operand blocks so that one wave's operand
 // load is one contiguous 1 KB read (layout formulas in include/moe.h):
 //   bf16:  16 rows x 32 K per 1 KB block, lane order (lane = 16 * (k%32 / 8)
-//          + n%16, 8 elements per lane); blocks [expert][n/16][k/32].
+//          + n%16, 8 elements per lane); an expert's blocks in 512-row groups
+//          [n/512][k/32][(n/16)%32] (the last group as wide as what is left),
+//          so one K step of a group is one contiguous run of blocks.
 //   MXFP8: 16 rows x 128 K per 2 KB block = two 1 KB halves (K%128 < 64 and
 //          >= 64), lane = 16 * (k%64 / 16) + n%16, 16 codes per lane; blocks
 //          [expert][n/16][k/128]; E8M0 scales 4 K-steps per lane dword:
@@ -24,8 +26,9 @@
 //          16 * ((k/32)%4) + n%16.
 //   MXFP4: 16 rows x 128 K per 1 KB block, lane = 16 * (k%128 / 32) + n%16,
 //          32 E2M1 codes per lane as 16 bytes (the lower K in the low nibble);
-//          blocks [expert][n/16][k/128]; scales as MXFP8.  The scale is the
-//          power-of-two ceiling of the block's max magnitude / 6.
+//          blocks in 512-row groups [n/512][k/128][(n/16)%32] like bf16;
+//          scale groups [n/512][k/512][(n/16)%32], otherwise as MXFP8.  The
+//          scale is the power-of-two ceiling of the block's max magnitude / 6.
 #include "common.h"
 
 namespace moe {

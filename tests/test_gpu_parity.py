@@ -56,6 +56,24 @@ SMALL = {
     # one expert of 129 rows (a ragged 256-row tile) beside 64-row tiles in the
     # same launches
     "mixed129_bf16": Workload("mixed129_bf16", 180, 192, 96, 160, 3, 2, "bf16"),
+    # token capacities above 1024, where the 256-row tiles run on the 8-wave
+    # 256 x 256 kernel when K is a multiple of its 64-wide stage (below 1024,
+    # or with other K, the 64-row kernel takes them as four 64-row tiles):
+    # K = 96 / 160 (the 64-row kernel takes everything at this capacity too)
+    "odd_bf16_big_cap": Workload("odd_bf16_big_cap", 700, 1100, 96, 160, 5, 3, "bf16"),
+    "mixed129_bf16_cap": Workload("mixed129_bf16_cap", 180, 1040, 96, 160, 3, 2, "bf16"),
+    # the 256 x 256 kernel: 4 stages and a partial 256-column tile (FC1 N =
+    # 384), 3 stages (odd: the repeated last stage) in FC2
+    "mid_bf16_big_cap": Workload("mid_bf16_big_cap", 600, 1200, 256, 192, 4, 2, "bf16"),
+    # 3 and 5 stages, FC1 N = 640 (two and a half column tiles), FC2 N = 192
+    # (the last quarter of the tile's columns stored by no wave), second row
+    # tiles of 150..190 rows (the lower waves partly past the rows)
+    "odd64_bf16_big_cap": Workload("odd64_bf16_big_cap", 700, 1100, 192, 320, 5, 3, "bf16"),
+    # second row tiles of under 128 rows (the lower waves wholly past them and
+    # idle), 2 stages in FC1, FC2 N = 128
+    "idle_bf16_big_cap": Workload("idle_bf16_big_cap", 700, 1100, 128, 192, 4, 2, "bf16"),
+    # an expert of 129 rows beside two of 64-row tiles, both kernels in one stage
+    "mixed129_64_cap": Workload("mixed129_64_cap", 182, 1040, 128, 192, 3, 2, "bf16"),
     # MXFP8 experts past 128 rows with K a multiple of 128 (LDS-staged kernel):
     # ragged 256-row tiles, a partial 256-column tile, 2 and 3 K steps
     "mx_big": Workload("mx_big", 600, 600, 256, 384, 4, 2, "mxfp8"),
