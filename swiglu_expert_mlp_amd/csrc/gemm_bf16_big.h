@@ -70,7 +70,12 @@ constexpr int kBigStage = 64 * 1024;            // activations 32 KB | weights 2
 constexpr int kBigWOff = 32 * 1024;             // weight part of a stage
 constexpr int kBigALoads = 4, kBigWLoads = 4;   // direct loads per wave per stage
 constexpr int kBigLoads = kBigALoads + kBigWLoads;
-constexpr int kBigEpi = 8 * 1024;               // a wave's epilogue region (in a stage)
+constexpr int kBigEpi = 4 * 1024;               // a wave's epilogue region (LDS of its own)
+constexpr int kBigPOff = 2 * 1024;              // FC1: the wave's row probabilities in it
+// 16-byte stores per wave per tile (FC1: 128 rows x 32 bf16; FC2: 128 rows x
+// 64 fp32); every wave issues exactly this many, and the next K loop counts them
+template <bool FC1>
+constexpr int big_stores() { return FC1 ? 8 : 32; }
 
 // third dword of a raw buffer descriptor on CDNA (32-bit data format, no
 // swizzle, no stride): byte-addressed accesses with a range check on the
@@ -166,38 +171,41 @@ __device__ __forceinline__ void big_phase(f32x16 (&acc)[4][2], const BigFrag& cu
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// The K loop of a tile.  On entry stage 0 (in s0) and, with two or more
-// stages, stage 1 (in s1; the last kBigLoads loads of this wave) are in
-// flight.  MMA = false: a wave whose 128 rows all lie past the tile's rows
-// only keeps the loads and barriers in step with the others.  Every stage
-// boundary inside the loop is unconditional, so that the compiler sees each
-// stage's loads waited for before its reads and adds no waits of its own.
-template <bool MMA>
+// The K loop of a tile (two or more stages).  On entry this wave's loads of
+// stage 0 (into s0) and stage 1 (into s1) are in flight, followed by AFTER
+// further vector-memory operations (the previous tile's stores, which may
+// drain while this tile runs).  Every load issue is unconditional (a load
+// issued on one path only made the compiler wait on all loads in flight before
+// later fragment reads): where no stage is left to load, the last stage is
+// loaded once more into s0, which no later fragment read of the tile uses.
+template <int AFTER>
 __device__ __forceinline__ void big_kloop(const BigSrc& t, char* s0, char* s1, const BigLanes& ln, int wm,
                                           int wn, f32x16 (&acc)[4][2])
 {
-    const int nst = t.nst;
+    static_assert(AFTER + kBigLoads <= 63, "vmcnt bound");
+    const int nst = t.nst;                           // >= 2
     BigFrag x, y;
-    if (nst > 1) BIG_WAIT_VMCNT(kBigLoads);
-    else BIG_WAIT_VMCNT(0);
+    // both stages landed (waiting for stage 0 alone made the compiler add a
+    // wait for everything in flight before the first fragment reads)
+    BIG_WAIT_VMCNT(AFTER);
     __builtin_amdgcn_s_barrier();
-    if constexpr (MMA) big_read<0>(s0, ln, wm, wn, x);
+    big_read<0>(s0, ln, wm, wn, x);
 
     // sub-steps 0 .. 2 of the stage in cur (sub-step 0's fragments in x),
     // reading sub-steps 1 .. 3 (the last into y)
     auto body = [&](const char* cur) {
-        if constexpr (MMA) {
-            big_phase<1>(acc, x, cur, ln, wm, wn, y);
-            big_phase<2>(acc, y, cur, ln, wm, wn, x);
-            big_phase<3>(acc, x, cur, ln, wm, wn, y);
-        }
+        big_phase<1>(acc, x, cur, ln, wm, wn, y);
+        big_phase<2>(acc, y, cur, ln, wm, wn, x);
+        big_phase<3>(acc, x, cur, ln, wm, wn, y);
     };
-    // a stage boundary: this wave's loads of the next stage landed and its
-    // reads of the current one are done; after the barrier both hold for every
-    // wave, and the current stage's buffer may be refilled
-    auto boundary = [&]() {
+    // a stage boundary: this wave's loads of the next stage landed (N: the
+    // vector-memory operations issued after them) and its reads of the current
+    // one are done; after the barrier both hold for every wave, and the current
+    // stage's buffer may be refilled
+    auto boundary = [&](auto NC) {
+        constexpr int N = decltype(NC)::value;
         __builtin_amdgcn_sched_barrier(0);
-        BIG_WAIT_VMCNT(0);
+        BIG_WAIT_VMCNT(N);
         __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
@@ -205,43 +213,44 @@ __device__ __forceinline__ void big_kloop(const BigSrc& t, char* s0, char* s1, c
     // sub-step 3 of the stage before (in y) with sub-step 0 of the stage in nxt read
     auto into = [&](const char* nxt) {
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (MMA) big_phase<0>(acc, y, nxt, ln, wm, wn, x);
+        big_phase<0>(acc, y, nxt, ln, wm, wn, x);
     };
-    int s = 0;
-    for (; s + 2 < nst; s += 2) {
-        body(s0);
-        boundary();
-        big_issue(t, s0, s + 2);
-        into(s1);
-        body(s1);
-        boundary();
-        // issued on every path (a load issued on one path only made the
-        // compiler wait on all loads in flight before later fragment reads):
-        // with an odd number of stages the last pass loads the last stage
-        // once more, into s1, which no later fragment read uses (the caller
-        // waits for it before s1 serves the epilogue)
-        big_issue(t, s1, min(s + 3, nst - 1));
-        into(s0);
-    }
-    // the last one or two stages (already issued)
+    using Now = std::integral_constant<int, 0>;
+    // stage 0 (stage 1 has landed too)
     body(s0);
-    if (s + 1 < nst) {
-        boundary();
-        into(s1);
+    boundary(std::integral_constant<int, AFTER>{});
+    big_issue(t, s0, min(2, nst - 1));
+    into(s1);
+    int s = 1;
+    // stage s in s1, stage s + 1 (if any) in flight into s0
+    for (; s + 2 < nst; s += 2) {
         body(s1);
+        boundary(Now{});
+        big_issue(t, s1, s + 2);
+        into(s0);
+        body(s0);
+        boundary(Now{});
+        big_issue(t, s0, min(s + 3, nst - 1));
+        into(s1);
     }
-    if constexpr (MMA) big_mma(acc, y);              // the last sub-step
+    body(s1);
+    if (s + 1 < nst) {
+        boundary(Now{});
+        into(s0);
+        body(s0);
+    }
+    big_mma(acc, y);                                 // the last sub-step
 }
 
 // The 256-row tile loop of one 8-wave workgroup (one workgroup per CU).
-// n_mt: the number of 256-row M tiles.  Requires K % 64 == 0 (the launch
-// sends other shapes to the 64-row kernel).
+// n_mt: the number of 256-row M tiles.  Requires K % 64 == 0 and K >= 128
+// (the launch sends other shapes to the 64-row kernel).
 template <bool FC1, bool PROB>
 __device__ __forceinline__ void big_tiles(const GemmArgs& g, int n_mt)
 {
     __shared__ __attribute__((aligned(1024))) char lds0[kBigStage];
     __shared__ __attribute__((aligned(1024))) char lds1[kBigStage];
-    __shared__ float lds_p[PROB ? kBigTM : 1];
+    __shared__ __attribute__((aligned(1024))) char lds_x[8 * kBigEpi];   // the waves' epilogue regions
 
     const int NT = (g.N + kBigTN - 1) / kBigTN;
     const int total = n_mt * NT;
@@ -315,8 +324,20 @@ __device__ __forceinline__ void big_tiles(const GemmArgs& g, int n_mt)
     TilePos pos = locate(tile);
     sources(pos);
     big_issue(t, lds0, 0);
-    if (t.nst > 1) big_issue(t, lds1, 1);
-    char* const ep = lds1 + wid * kBigEpi;          // this wave's epilogue region
+    big_issue(t, lds1, 1);
+    // the K loop counts the previous tile's stores among the operations after
+    // its first stages; before the first tile the same number of stores go to
+    // an empty descriptor (the range check drops them all; distinct offsets, so
+    // that none is merged away)
+    constexpr int kStores = big_stores<FC1>();
+    {
+        const __amdgpu_buffer_rsrc_t none =
+            __builtin_amdgcn_make_buffer_rsrc(g.out, (short)0, 0, kBigRsrcWord3);
+#pragma unroll
+        for (int k = 0; k < kStores; ++k)
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{0u, 0u, 0u, 0u}, none, 16 * lane + 1024 * k, 0, 0);
+    }
+    char* const ep = lds_x + wid * kBigEpi;         // this wave's epilogue region
     while (true) {
         const int row0 = pos.row0, rows = pos.rows, n0 = pos.n0;
         f32x16 acc[4][2];
@@ -327,104 +348,120 @@ __device__ __forceinline__ void big_tiles(const GemmArgs& g, int n_mt)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-        const bool active = rows > 128 * wm;        // wave-uniform
-        if (active) big_kloop<true>(t, lds0, lds1, ln, wm, wn, acc);
-        else big_kloop<false>(t, lds0, lds1, ln, wm, wn, acc);
+        // every wave runs the same K loop, also one whose 128 rows all lie past
+        // the tile's rows (its results are dropped by the store descriptor): a
+        // second, load-only loop for such waves made the compiler wait for all
+        // loads and stores in flight at every tile's first fragment reads
+        big_kloop<kStores>(t, lds0, lds1, ln, wm, wn, acc);
 
-        // every wave finished reading the stages (and, with an odd number of
-        // stages, the K loop's repeated last stage landed in lds1); the next
-        // tile's stage 0 goes out before this tile's epilogue, stage 1 after it
-        // (the epilogue passes through lds1)
+        // every wave finished reading the stages: the next tile's two stages go
+        // out before this tile's epilogue (which has LDS of its own), so they
+        // land while it runs, and its stores drain while the next tile runs.
+        // The loads go out on every path (after the last tile they load its
+        // first stages again, waited for before the exit): a load issued on one
+        // path only made the compiler wait on all loads in flight before the
+        // next K loop's first fragment reads.
         const int next = tile + per_xcd;
         const bool more = next < t_end;
-        if (t.nst & 1) BIG_WAIT_VMCNT(0);
         __builtin_amdgcn_s_waitcnt(0xC07F);         // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
-        TilePos npos{};
+        // FC1 with the probabilities applied inside FC1: the wave's 128 row
+        // probabilities, fetched before the loads below so that waiting for
+        // them does not wait for those
+        float pr0 = 1.0f, pr1 = 1.0f;
+        if constexpr (FC1 && PROB) {
+            const int r0 = 128 * wm + lane, r1 = r0 + 64;
+            if (r0 < rows) pr0 = g.row_prob[g.perm_src[row0 + r0]];
+            if (r1 < rows) pr1 = g.row_prob[g.perm_src[row0 + r1]];
+        }
+        TilePos npos = pos;
         if (more) {
             npos = locate(next);
             sources(npos);
-            big_issue(t, lds0, 0);
         }
-        // FC1 with the probabilities applied inside FC1: the tile's row
-        // probabilities, staged once for all waves
-        if constexpr (FC1 && PROB) {
-            if (threadIdx.x < kBigTM) {
-                const int r = threadIdx.x;
-                lds_p[r] = r < rows ? g.row_prob[g.perm_src[row0 + r]] : 1.0f;
-            }
-            __builtin_amdgcn_s_waitcnt(0xC07F);
-            __builtin_amdgcn_s_barrier();
-        }
+        big_issue(t, lds0, 0);
+        big_issue(t, lds1, 1);
 
         // epilogue: lane holds column l % 32 of each 32-column block and rows
-        // 8 (v / 4) + 4 (l / 32) + v % 4 of each 32-row block
-        if (active) {
-            const int hi = lane >> 5, c32 = lane & 31;
-            if constexpr (FC1) {
-                // interleave block ib: column block 0 the gate half, 1 the up half
-                const int F = g.N / 2;
-                const int ib = n0 / 64 + wn;
-                if (ib * 64 < g.N) {
-                    // the wave's 128 x 32 SwiGLU outputs as bf16 rows of 64 bytes in
-                    // ep, rows 4 m .. 4 m + 3 with odd m in swapped row pairs (the two
-                    // rows a write instruction covers fall in different bank halves)
+        // 8 (v / 4) + 4 (l / 32) + v % 4 of each 32-row block.  The lane index
+        // goes through an opaque copy so that the compiler derives the epilogue's
+        // many per-lane offsets here instead of hoisting them out of the tile
+        // loop (they would stay live across the K loop and spill).  Every wave
+        // issues exactly kStores stores: rows past the tile's rows (all of an
+        // idle wave's) fall outside the store descriptor, and columns past N get
+        // an offset outside it.
+        int elane = lane;
+        asm volatile("" : "+v"(elane));
+        const int hi = elane >> 5, c32 = elane & 31;
+        if constexpr (FC1) {
+            // interleave block ib: column block 0 the gate half, 1 the up half;
+            // one 32-row block at a time as bf16 rows of 64 bytes in ep, rows
+            // 4 m .. 4 m + 3 with odd m in swapped row pairs (the two rows a write
+            // instruction covers fall in different bank halves)
+            const int F = g.N / 2;
+            const int ib = n0 / 64 + wn;
+            const bool cols = ib * 64 < g.N;
+            const __amdgpu_buffer_rsrc_t orr = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)((uint16_t*)g.out + (int64_t)row0 * F), (short)0, rows * F * 2, kBigRsrcWord3);
+            const float* pw = (const float*)(ep + kBigPOff);
+            if constexpr (PROB) {
+                ((float*)(ep + kBigPOff))[elane] = pr0;
+                ((float*)(ep + kBigPOff))[elane + 64] = pr1;
+            }
+            const int c = elane & 3;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i) {
 #pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            const int rr = 32 * i + 8 * (v >> 2) + 4 * hi + (v & 3);
-                            float h = swiglu_f32(acc[i][0][v], acc[i][1][v]);
-                            if constexpr (PROB) h *= lds_p[128 * wm + rr];
-                            *(uint16_t*)(ep + ((rr * 64 + 2 * c32) ^ (((rr >> 2) & 1) << 6))) =
-                                f32_to_bf16_bits(h);
-                        }
-                    const __amdgpu_buffer_rsrc_t orr = __builtin_amdgcn_make_buffer_rsrc(
-                        (void*)((uint16_t*)g.out + (int64_t)row0 * F), (short)0, rows * F * 2, kBigRsrcWord3);
-                    const int c = lane & 3;
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        const int rr = (lane >> 2) + 16 * k;
-                        const u32x4_t val =
-                            *(const u32x4_t*)(ep + ((rr * 64 + 16 * c) ^ (((rr >> 2) & 1) << 6)));
-                        __builtin_amdgcn_raw_buffer_store_b128(
-                            val, orr, ((128 * wm + rr) * F + ib * 32 + 8 * c) * 2, 0, 0);
-                    }
+                for (int v = 0; v < 16; ++v) {
+                    const int rr = 8 * (v >> 2) + 4 * hi + (v & 3);
+                    float h = swiglu_f32(acc[i][0][v], acc[i][1][v]);
+                    if constexpr (PROB) h *= pw[32 * i + rr];
+                    *(uint16_t*)(ep + ((rr * 64 + 2 * c32) ^ (((rr >> 2) & 1) << 6))) = f32_to_bf16_bits(h);
                 }
-            } else {
-                const __amdgpu_buffer_rsrc_t orr = __builtin_amdgcn_make_buffer_rsrc(
-                    (void*)((float*)g.out + (int64_t)row0 * g.N), (short)0, rows * g.N * 4, kBigRsrcWord3);
-                const int c = lane & 15;
-                const int col = n0 + 64 * wn + 4 * c;   // this lane's 4 stored columns
+                static_assert(big_stores<true>() == 4 * 2, "4 row blocks x 2 stores");
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    // one 32-row block at a time: 32 x 64 fp32 in ep, rows of 256
+                for (int k = 0; k < 2; ++k) {
+                    const int rr = (elane >> 2) + 16 * k;
+                    const u32x4_t val = *(const u32x4_t*)(ep + ((rr * 64 + 16 * c) ^ (((rr >> 2) & 1) << 6)));
+                    const int off = cols ? ((128 * wm + 32 * i + rr) * F + ib * 32 + 8 * c) * 2 : 0x7ffffff0;
+                    __builtin_amdgcn_raw_buffer_store_b128(val, orr, off, 0, 0);
+                }
+            }
+        } else {
+            const __amdgpu_buffer_rsrc_t orr = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)((float*)g.out + (int64_t)row0 * g.N), (short)0, rows * g.N * 4, kBigRsrcWord3);
+            const int c = elane & 15;
+            const int col = n0 + 64 * wn + 4 * c;       // this lane's 4 stored columns
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int hv = 0; hv < 2; ++hv) {
+                    // 16 rows (v in 8 hv .. 8 hv + 7) x 64 fp32 in ep, rows of 256
                     // bytes, halves swapped in rows 4 m .. 4 m + 3 with odd m
 #pragma unroll
                     for (int j = 0; j < 2; ++j)
 #pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            const int rr = 8 * (v >> 2) + 4 * hi + (v & 3);
-                            *(float*)(ep + ((rr * 256 + 4 * (32 * j + c32)) ^ (((rr >> 2) & 1) << 7))) =
+                        for (int v = 8 * hv; v < 8 * hv + 8; ++v) {
+                            const int lr = 8 * ((v >> 2) & 1) + 4 * hi + (v & 3);
+                            *(float*)(ep + ((lr * 256 + 4 * (32 * j + c32)) ^ (((lr >> 2) & 1) << 7))) =
                                 acc[i][j][v];
                         }
+                    static_assert(big_stores<false>() == 4 * 2 * 4, "4 row blocks x 2 halves x 4 stores");
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        const int rr = (lane >> 4) + 4 * k;
+                    for (int k = 0; k < 4; ++k) {
+                        const int lr = (elane >> 4) + 4 * k;
                         const u32x4_t val =
-                            *(const u32x4_t*)(ep + ((rr * 256 + 16 * c) ^ (((rr >> 2) & 1) << 7)));
-                        if (col < g.N)
-                            __builtin_amdgcn_raw_buffer_store_b128(
-                                val, orr, ((128 * wm + 32 * i + rr) * g.N + col) * 4, 0, 0);
+                            *(const u32x4_t*)(ep + ((lr * 256 + 16 * c) ^ (((lr >> 2) & 1) << 7)));
+                        const int off = col < g.N ? ((128 * wm + 32 * i + 16 * hv + lr) * g.N + col) * 4
+                                                  : 0x7ffffff0;
+                        __builtin_amdgcn_raw_buffer_store_b128(val, orr, off, 0, 0);
                     }
                 }
-            }
         }
-        // every wave is done with lds1 before the next tile's stage 1 fills it
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_s_barrier();
-        if (!more) break;
-        if (t.nst > 1) big_issue(t, lds1, 1);
+        if (!more) {
+            BIG_WAIT_VMCNT(0);          // the repeated loads land before the LDS is released
+            break;
+        }
         tile = next;
         pos = npos;
     }

@@ -331,7 +331,8 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         // the 256-row design: capacities above 1024, K a multiple of its 64-wide
         // stage, and byte offsets inside x and inside one expert's weights that
         // fit its 32-bit buffer offsets
-        g1.small_takes_big = T_cap <= 1024 || H % 64 != 0 || (int64_t)T_cap * H * 2 >= ((int64_t)1 << 31) ||
+        g1.small_takes_big = T_cap <= 1024 || H % 64 != 0 || H < 128 ||
+                             (int64_t)T_cap * H * 2 >= ((int64_t)1 << 31) ||
                              (int64_t)2 * F * H * 2 >= ((int64_t)1 << 31);
         g1.row_prob = fc1_topk ? (const float*)(w + L.sorted_probs) : nullptr;
         e = launch_gemm_bf16(true, g1, h->num_cu, stream, stage_event(h, 2), stage_event(h, 3));
@@ -345,7 +346,7 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         g2.K = F;
         g2.n_tiles_n = ((H + 63) / 64 + 3) / 4;
         g2.row_prob = nullptr;
-        g2.small_takes_big = T_cap <= 1024 || F % 64 != 0 || (int64_t)H * F * 2 >= ((int64_t)1 << 31);
+        g2.small_takes_big = T_cap <= 1024 || F % 64 != 0 || F < 128 || (int64_t)H * F * 2 >= ((int64_t)1 << 31);
         e = launch_gemm_bf16(false, g2, h->num_cu, stream, nullptr, nullptr);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
         if ((e = mark(h, 4, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
