@@ -72,6 +72,10 @@ typedef enum {
 #define MOE_DEVERR_DUP_EXPERT_ID 2u   /* same id twice in a live token: repeat dropped    */
 #define MOE_DEVERR_LIVE_ABOVE_CAP 4u  /* live > T_cap: clamped to T_cap                  */
 #define MOE_DEVERR_LIVE_NEGATIVE 8u   /* live < 0: treated as 0                          */
+#define MOE_DEVERR_FUSED_WAIT 16u     /* MOE_FUSED_FFN: an FC2 tile's wait for its FC1
+                                         rows ran past 0.2 s (workgroups not all
+                                         resident, e.g. other work on the GPU): the
+                                         outputs of that call are invalid            */
 
 /* Create a handle for E experts, hidden size H, expert FFN size F, top-k.
  * Checks (Megatron-LM PR #7830, construction-time validation; cudnn-frontend
@@ -188,6 +192,21 @@ typedef enum {
  * rounds that sum to bf16.  Not valid with MOE_COMBINE_ROWS. */
 #define MOE_APPLY_TOPK_IN_FC1 0x100
 
+/* Added to any combine (bf16 weights only): run FC1 and FC2 as one persistent
+ * launch instead of two (Megatron-LM PR #7830, "What does this PR do?": one
+ * fused kernel for the expert MLP; cudnn-frontend PR #448's MegaMoE files
+ * fc1_fc2_fuse_sched, grid_sync).  Every 64-row M tile has a readiness
+ * counter; an FC1 tile releases its SwiGLU rows at device scope and counts
+ * itself; an FC2 tile first issues its weight loads, then waits until all
+ * FC1 column tiles of its M tile are counted, then reads the rows.  The
+ * 64-row tile design takes every tile in this mode (also above 1024 tokens),
+ * with the same arithmetic as always, so the outputs are bit-identical to the
+ * two-launch path.  The waits are bounded: if one runs past 0.2 s (possible
+ * only when not every workgroup is resident, e.g. with other work on the
+ * GPU), it flags MOE_DEVERR_FUSED_WAIT for moe_check and the call's outputs
+ * are invalid.  With another precision: MOE_ERR_INVALID_ARG. */
+#define MOE_FUSED_FFN 0x200
+
 /* moe_forward with a choice of combine; every stage before the combine is
  * moe_forward's, so the FC2 rows are bit-identical across the three (without
  * MOE_APPLY_TOPK_IN_FC1, which changes the FC2 rows).
@@ -206,7 +225,8 @@ typedef enum {
  *     route's fp32 FC2 row; -0 comes back as +0 and a dropped route (invalid
  *     or repeated id) as a row of +0.  out is fp32 [T_cap][topk][H].  probs
  *     is not read and may be NULL.
- * combine may carry MOE_APPLY_TOPK_IN_FC1 (fp32 and bf16 combines).
+ * combine may carry MOE_APPLY_TOPK_IN_FC1 (fp32 and bf16 combines) and
+ * MOE_FUSED_FFN (bf16 weights).
  * Rows of tokens >= live are never written in any mode.  Errors: an unknown
  * combine, or MOE_APPLY_TOPK_IN_FC1 with row mode, is MOE_ERR_INVALID_ARG;
  * otherwise as moe_forward. */

@@ -44,6 +44,7 @@ constexpr uint32_t kErrBadId = 1u;
 constexpr uint32_t kErrDupId = 2u;
 constexpr uint32_t kErrLiveHigh = 4u;
 constexpr uint32_t kErrLiveNeg = 8u;
+constexpr uint32_t kErrFusedWait = 16u;
 
 // ---------------------------------------------------------------- formats
 
@@ -141,6 +142,7 @@ struct WsLayout {
     size_t dst;            // int32 [T_cap * k]
     size_t tiles;          // int2 [max_tiles]: (expert, first row), 64-row GEMM tiles
     size_t tiles_big;      // int2 [max_tiles_big]: (expert, first row), LDS-staged GEMM tiles
+    size_t ready;          // int32 [max_tiles + 4 max_tiles_big]: single-launch FFN readiness counters
     size_t hbuf;           // bf16 [T_cap * k][F] or E4M3 [T_cap * k][F]
     size_t hscale;         // E8M0 [T_cap * k][F / 32] (mxfp8)
     size_t obuf;           // float [T_cap * k][H]

@@ -55,6 +55,10 @@ struct GemmArgs {
                                // tiles (as four 64-row tiles each): token capacity <= 1024,
                                // or a shape the 256-row kernel does not take
     const float* row_prob;     // FC1: probabilities applied to the SwiGLU rows, or null
+    // single-launch FFN (FC1 and FC2 in one persistent launch): per 64-row M
+    // tile, the count of FC1 column tiles whose SwiGLU rows are released
+    int32_t* ready;
+    uint32_t* err;             // the header's error word (a readiness wait past its limit)
 };
 
 // MXFP8 operands: E4M3 codes with one E8M0 scale byte per 32 elements of K.

@@ -40,6 +40,43 @@ __global__ void __launch_bounds__(512, 1) gemm_bf16_big_kernel(GemmArgs g)
     big_tiles<FC1, PROB>(g, ld_const(&g.hdr->n_tiles_big));
 }
 
+// The single-launch FFN: FC1 then FC2 in one persistent launch of the 64-row
+// design (it takes every tile, a 256-row tile as four 64-row tiles), FC2
+// tiles waiting on per-M-tile readiness counters instead of the launch
+// boundary (gemm_bf16_small.h).  The grid is at most one workgroup per CU, so
+// every workgroup is resident and every FC1 tile is taken.
+template <bool PROB>
+__global__ void __launch_bounds__(512, 1) gemm_bf16_fused_kernel(GemmArgs g1, GemmArgs g2)
+{
+    __shared__ __attribute__((aligned(1024))) char smem[kSmallLds];
+    const int n_big = ld_const(&g1.hdr->n_tiles_big);
+    const int n_small = ld_const(&g1.hdr->n_tiles);
+    const int* te0 = (const int*)(g1.tiles + min((int)blockIdx.x / small_col_tiles(g1), g1.max_tiles - 1));
+    const int e0 = ld_const(te0), row00 = ld_const(te0 + 1);
+    asm volatile("" : : "s"(n_big), "s"(n_small), "s"(e0), "s"(row00));
+    small_tiles<true, PROB, 1>(g1, smem, n_small, n_big, e0, row00);
+    const int* te1 = (const int*)(g2.tiles + min((int)blockIdx.x / small_col_tiles(g2), g2.max_tiles - 1));
+    small_tiles<false, false, 2>(g2, smem, n_small, n_big, ld_const(te1), ld_const(te1 + 1),
+                                 small_col_tiles(g1));
+}
+
+hipError_t launch_gemm_bf16_fused(const GemmArgs& g1, const GemmArgs& g2, int num_cu, hipStream_t s,
+                                  hipEvent_t t0, hipEvent_t t1)
+{
+    if (!g1.small_takes_big || !g2.small_takes_big || !g1.ready || !g1.err) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(num_cu >= 8 ? num_cu / 8 * 8 : 8)), block(512);
+    const bool prob = g1.row_prob != nullptr;
+    auto go = [&](auto kernel) {
+        if (t0 || t1)
+            hipExtLaunchKernelGGL(kernel, grid, block, 0, s, t0, t1, 0, g1, g2);
+        else
+            hipLaunchKernelGGL(kernel, grid, block, 0, s, g1, g2);
+    };
+    if (prob) go(gemm_bf16_fused_kernel<true>);
+    else go(gemm_bf16_fused_kernel<false>);
+    return hipGetLastError();
+}
+
 // t0 / t1 (optional): events that receive the stage's start (the first
 // launch's) and end (the last launch's), recorded by the dispatches themselves
 // (no separate marker in the stream)

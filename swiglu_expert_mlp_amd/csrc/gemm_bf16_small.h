@@ -63,14 +63,35 @@ __device__ __forceinline__ void wait_vmcnt_upto15(int n)
 
 __device__ __forceinline__ int small_col_tiles(const GemmArgs& g) { return (g.N + kSmallCols - 1) / kSmallCols; }
 
+// FC1 tile done (single-launch FFN): every wave's stores complete, then one
+// thread releases them at device scope (the L2's dirty lines written back)
+// and counts the tile in its M tile's readiness counter.
+__device__ __forceinline__ void small_release(const GemmArgs& g, int mt)
+{
+    BIG_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(g.ready + mt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The single-launch FFN (FC1 and FC2 tiles in one persistent launch, every
+// workgroup running all its FC1 tiles before any FC2 tile): FUSE = 1, an FC1
+// tile releases its SwiGLU rows (device scope) and counts itself in its M
+// tile's readiness counter; FUSE = 2, an FC2 tile issues its first weight
+// loads, waits until `need` FC1 column tiles of its M tile are counted (a
+// bounded wait: past about 0.2 s it flags kErrFusedWait and goes on), and
+// reads the rows with coherent loads.  The wait always ends, since every
+// FC1 tile is taken by a workgroup that is already running (one per CU).
+constexpr int kFuseWaitTicks = 20000000;        // wall-clock ticks (100 MHz): 0.2 s
+constexpr int kCoherentLoad = 16;               // cache policy sc1 (device-coherent)
+
 // n_small: the number of 64-row M tiles; n_big: the number of 256-row M
 // tiles this launch also runs, as four 64-row tiles each (0 when a launch of
 // the 256-row design takes them); (e0, row00): the table entry of this
 // workgroup's first tile (blockIdx.x), read by the caller before the counts
 // were known.
-template <bool FC1, bool PROB>
+template <bool FC1, bool PROB, int FUSE = 0>
 __device__ __forceinline__ void small_tiles(const GemmArgs& g, char* smem, int n_small, int n_big,
-                                            int e0, int row00)
+                                            int e0, int row00, int need = 0)
 {
     const int NTs = small_col_tiles(g);
     const int total = (n_small + 4 * n_big) * NTs;
@@ -151,8 +172,32 @@ __device__ __forceinline__ void small_tiles(const GemmArgs& g, char* smem, int n
             if constexpr (FC1) src = g.perm_src[src] / g.topk;
             arow = g.A + src * K + 8 * ((lane & 3) ^ big_swz(lane >> 2));
         }
+        if constexpr (FUSE == 2) {
+            // the waves that load rows wait for the FC1 tiles of this M tile
+            if (has_a) {
+                const int32_t* rp = g.ready + mt;
+                int v = __hip_atomic_load(rp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (v < need) {
+                    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+                    while (v < need) {
+                        __builtin_amdgcn_s_sleep(2);
+                        v = __hip_atomic_load(rp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if (__builtin_amdgcn_s_memrealtime() - t0 > (uint64_t)kFuseWaitTicks) {
+                            if (lane == 0) atomicOr(g.err, kErrFusedWait);
+                            break;
+                        }
+                    }
+                }
+            }
+        }
         auto issue_a = [&](int s) {
-            if (has_a) big_load_block(arow + 32 * s, smem + (s % kSmallRing) * kSmallStage + wid * 1024);
+            if (has_a) {
+                char* dst = smem + (s % kSmallRing) * kSmallStage + wid * 1024;
+                if constexpr (FUSE == 2)
+                    __builtin_amdgcn_global_load_lds(arow + 32 * s, (lds_void_t*)dst, 16, 0, kCoherentLoad);
+                else
+                    big_load_block(arow + 32 * s, dst);
+            }
         };
         auto issue = [&](int s) { issue_a(s); issue_b(s); };
 
@@ -200,7 +245,10 @@ __device__ __forceinline__ void small_tiles(const GemmArgs& g, char* smem, int n
 
         // epilogue: lane holds column l % 32 of each 32-column block and rows
         // 8 (v / 4) + 4 (l / 32) + v % 4 of each 32-row block
-        if (!has_cols) continue;
+        if (!has_cols) {
+            if constexpr (FUSE == 1) small_release(g, mt);
+            continue;
+        }
         if constexpr (FC1) {
             // column block 0 is the gate half, 1 the up half of interleave block cb
             const int F = g.N / 2;
@@ -232,6 +280,7 @@ __device__ __forceinline__ void small_tiles(const GemmArgs& g, char* smem, int n
                 }
             }
         }
+        if constexpr (FUSE == 1) small_release(g, mt);
     }
 }
 

@@ -36,6 +36,8 @@ hipError_t launch_quant_x(const uint16_t* x, int64_t T_cap, const int32_t* live,
 namespace moe {
 hipError_t launch_gemm_bf16(bool fc1, const GemmArgs& g, int num_cu, hipStream_t s, hipEvent_t t0,
                             hipEvent_t t1);
+hipError_t launch_gemm_bf16_fused(const GemmArgs& g1, const GemmArgs& g2, int num_cu, hipStream_t s,
+                                  hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_gemm_mxfp8(bool fc1, bool w4, const MxGemmArgs& g, int num_cu, hipStream_t s,
                              hipEvent_t t0, hipEvent_t t1);
 }  // namespace moe
@@ -114,6 +116,7 @@ static WsLayout layout_of(const moe_ctx* h, int64_t T_cap)
     L.dst = take(4 * R);
     L.tiles = take(8 * L.max_tiles);
     L.tiles_big = take(8 * L.max_tiles_big);
+    L.ready = take(4 * (L.max_tiles + 4 * L.max_tiles_big));
     if (h->precision == MOE_BF16) {
         L.hbuf = take(2 * R * F);
         L.hscale = 0;
@@ -284,12 +287,15 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
     if (T_cap < 0 || T_cap > (int64_t)1 << 26)
         return fail(MOE_ERR_INVALID_ARG, "moe_forward: T_cap=%lld out of range", (long long)T_cap);
     const bool fc1_topk = (combine & MOE_APPLY_TOPK_IN_FC1) != 0;
-    combine &= ~MOE_APPLY_TOPK_IN_FC1;
+    const bool fused = (combine & MOE_FUSED_FFN) != 0;
+    combine &= ~(MOE_APPLY_TOPK_IN_FC1 | MOE_FUSED_FFN);
     if (combine != MOE_COMBINE_FP32 && combine != MOE_COMBINE_BF16 && combine != MOE_COMBINE_ROWS)
         return fail(MOE_ERR_INVALID_ARG, "moe_forward: unknown combine %d", combine);
     if (fc1_topk && combine == MOE_COMBINE_ROWS)
         return fail(MOE_ERR_INVALID_ARG,
                     "moe_forward: MOE_APPLY_TOPK_IN_FC1 with row mode (which uses no probabilities)");
+    if (fused && h->precision != MOE_BF16)
+        return fail(MOE_ERR_INVALID_ARG, "moe_forward: MOE_FUSED_FFN is implemented for bf16 only");
     // row mode does not use the probabilities (every route has probability 1)
     if (!x || !expert_ids || (!probs && combine != MOE_COMBINE_ROWS) || !live_rows_dev || !out ||
         !ws)
@@ -335,8 +341,13 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
                              (int64_t)T_cap * H * 2 >= ((int64_t)1 << 31) ||
                              (int64_t)2 * F * H * 2 >= ((int64_t)1 << 31);
         g1.row_prob = fc1_topk ? (const float*)(w + L.sorted_probs) : nullptr;
-        e = launch_gemm_bf16(true, g1, h->num_cu, stream, stage_event(h, 2), stage_event(h, 3));
-        if (e != hipSuccess) return hip_fail(e, "moe_forward: FC1 launch");
+        g1.ready = (int32_t*)(w + L.ready);
+        g1.err = &hdr->err;
+        if (fused) g1.small_takes_big = 1;
+        if (!fused) {
+            e = launch_gemm_bf16(true, g1, h->num_cu, stream, stage_event(h, 2), stage_event(h, 3));
+            if (e != hipSuccess) return hip_fail(e, "moe_forward: FC1 launch");
+        }
         GemmArgs g2 = g1;
         g2.A = (const uint16_t*)(w + L.hbuf);
         g2.W = (const uint16_t*)h->kbuf + (size_t)E * 2 * F * H;
@@ -347,8 +358,16 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         g2.n_tiles_n = ((H + 63) / 64 + 3) / 4;
         g2.row_prob = nullptr;
         g2.small_takes_big = T_cap <= 1024 || F % 64 != 0 || F < 128 || (int64_t)H * F * 2 >= ((int64_t)1 << 31);
-        e = launch_gemm_bf16(false, g2, h->num_cu, stream, nullptr, nullptr);
-        if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
+        if (fused) {
+            // one persistent launch, the 64-row design taking every tile; the
+            // FC1 stage's events bracket it
+            g2.small_takes_big = 1;
+            e = launch_gemm_bf16_fused(g1, g2, h->num_cu, stream, stage_event(h, 2), stage_event(h, 3));
+            if (e != hipSuccess) return hip_fail(e, "moe_forward: fused FFN launch");
+        } else {
+            e = launch_gemm_bf16(false, g2, h->num_cu, stream, nullptr, nullptr);
+            if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
+        }
         if ((e = mark(h, 4, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     } else {
         // MXFP8, or MXFP4 weights with MXFP8 activations

@@ -89,6 +89,7 @@ struct PrepArgs {
     int32_t* offsets;
     int2* tiles;
     int2* tiles_big;
+    int32_t* ready;          // single-launch FFN readiness counters (zeroed here)
     WsHeader* hdr;
     int32_t* perm_src;
     int32_t* dst;
@@ -173,6 +174,9 @@ __device__ void prep_finish(const PrepArgs& a, int T, int nch, int32_t live, int
         off += cnt[q];
     }
     if (threadIdx.x == 0) a.offsets[E] = total;
+    // the readiness counters of every 64-row M tile (a 256-row tile counts as
+    // four) start at zero for the forward that follows
+    for (int i = threadIdx.x; i < ntotal + 4 * nbig; i += blockDim.x) a.ready[i] = 0;
     uint32_t err = 0;
     if (local_cnt) err = threadIdx.x == 0 ? local_err : 0u;
     else
@@ -354,6 +358,7 @@ hipError_t launch_prep(const int32_t* ids, const float* probs, int64_t T_cap, co
     a.offsets = (int32_t*)(ws + L.offsets);
     a.tiles = (int2*)(ws + L.tiles);
     a.tiles_big = (int2*)(ws + L.tiles_big);
+    a.ready = (int32_t*)(ws + L.ready);
     a.hdr = (WsHeader*)(ws + L.hdr);
     a.perm_src = (int32_t*)(ws + L.perm_src);
     a.dst = (int32_t*)(ws + L.dst);
