@@ -8,6 +8,11 @@
 
 namespace moe {
 
+// Cache policy of the weight streams of the 64-row tiles (each weight byte is
+// read once per launch): non-temporal.  Measured at decode sizes (64 experts,
+// hidden 2048, FFN 1024): FC1 90.5 -> 82.8 us, FC2 53.5 -> 49.6 us.
+constexpr int kNonTemporal = 2;
+
 // 16-byte load with the non-temporal (streaming) cache policy.
 __device__ __forceinline__ uint4 load_stream16(const void* p)
 {

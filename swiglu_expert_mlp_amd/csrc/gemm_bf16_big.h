@@ -97,7 +97,11 @@ struct BigSrc {
 };
 
 // the 8 direct loads of stage s into st: activation blocks 4 wid + i (rows
-// 32 wid + 8 i + lane / 8), weight blocks 2 wid + i of both K steps
+// 32 wid + 8 i + lane / 8), weight blocks 2 wid + i of both K steps.  WPOL:
+// the weights' cache policy (FC2: non-temporal, measured 686 -> 664 us at
+// 16K tokens; FC1: default, which its row tiles' L2 reuse needs, 989 -> 1049
+// us with non-temporal)
+template <int WPOL>
 __device__ __forceinline__ void big_issue(const BigSrc& t, char* st, int s)
 {
 #pragma unroll
@@ -114,7 +118,7 @@ __device__ __forceinline__ void big_issue(const BigSrc& t, char* st, int s)
         for (int i = 0; i < 2; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 t.wr, (lds_void_t*)(st + kBigWOff + h * 16384 + (2 * t.wid + i) * 1024), 16, lane16,
-                t.woff[i] + t.wstep * (2 * s + h), 0, 0);
+                t.woff[i] + t.wstep * (2 * s + h), 0, WPOL);
 }
 
 struct BigFrag {
@@ -178,7 +182,7 @@ __device__ __forceinline__ void big_phase(f32x16 (&acc)[4][2], const BigFrag& cu
 // issued on one path only made the compiler wait on all loads in flight before
 // later fragment reads): where no stage is left to load, the last stage is
 // loaded once more into s0, which no later fragment read of the tile uses.
-template <int AFTER>
+template <int AFTER, int WPOL>
 __device__ __forceinline__ void big_kloop(const BigSrc& t, char* s0, char* s1, const BigLanes& ln, int wm,
                                           int wn, f32x16 (&acc)[4][2])
 {
@@ -219,18 +223,18 @@ __device__ __forceinline__ void big_kloop(const BigSrc& t, char* s0, char* s1, c
     // stage 0 (stage 1 has landed too)
     body(s0);
     boundary(std::integral_constant<int, AFTER>{});
-    big_issue(t, s0, min(2, nst - 1));
+    big_issue<WPOL>(t, s0, min(2, nst - 1));
     into(s1);
     int s = 1;
     // stage s in s1, stage s + 1 (if any) in flight into s0
     for (; s + 2 < nst; s += 2) {
         body(s1);
         boundary(Now{});
-        big_issue(t, s1, s + 2);
+        big_issue<WPOL>(t, s1, s + 2);
         into(s0);
         body(s0);
         boundary(Now{});
-        big_issue(t, s0, min(s + 3, nst - 1));
+        big_issue<WPOL>(t, s0, min(s + 3, nst - 1));
         into(s1);
     }
     body(s1);
@@ -323,8 +327,9 @@ __device__ __forceinline__ void big_tiles(const GemmArgs& g, int n_mt)
     if (tile >= t_end) return;
     TilePos pos = locate(tile);
     sources(pos);
-    big_issue(t, lds0, 0);
-    big_issue(t, lds1, 1);
+    constexpr int kWPol = FC1 ? 0 : kNonTemporal;
+    big_issue<kWPol>(t, lds0, 0);
+    big_issue<kWPol>(t, lds1, 1);
     // the K loop counts the previous tile's stores among the operations after
     // its first stages; before the first tile the same number of stores go to
     // an empty descriptor (the range check drops them all; distinct offsets, so
@@ -352,7 +357,7 @@ __device__ __forceinline__ void big_tiles(const GemmArgs& g, int n_mt)
         // the tile's rows (its results are dropped by the store descriptor): a
         // second, load-only loop for such waves made the compiler wait for all
         // loads and stores in flight at every tile's first fragment reads
-        big_kloop<kStores>(t, lds0, lds1, ln, wm, wn, acc);
+        big_kloop<kStores, kWPol>(t, lds0, lds1, ln, wm, wn, acc);
 
         // every wave finished reading the stages: the next tile's two stages go
         // out before this tile's epilogue (which has LDS of its own), so they
@@ -379,8 +384,8 @@ __device__ __forceinline__ void big_tiles(const GemmArgs& g, int n_mt)
             npos = locate(next);
             sources(npos);
         }
-        big_issue(t, lds0, 0);
-        big_issue(t, lds1, 1);
+        big_issue<kWPol>(t, lds0, 0);
+        big_issue<kWPol>(t, lds1, 1);
 
         // epilogue: lane holds column l % 32 of each 32-column block and rows
         // 8 (v / 4) + 4 (l / 32) + v % 4 of each 32-row block.  The lane index

@@ -144,7 +144,9 @@ __device__ __forceinline__ void small_tiles(const GemmArgs& g, char* smem, int n
             if (has_cols) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    big_load_block(bblk[j] + (int64_t)bstep[j] * s, st + (4 + 4 * wid + j) * 1024);
+                    __builtin_amdgcn_global_load_lds(bblk[j] + (int64_t)bstep[j] * s,
+                                                     (lds_void_t*)(st + (4 + 4 * wid + j) * 1024), 16, 0,
+                                                     kNonTemporal);
             }
         };
         // a 64-row part of a 256-row tile may lie past its expert's rows

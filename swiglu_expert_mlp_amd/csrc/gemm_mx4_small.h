@@ -130,11 +130,11 @@ __device__ __forceinline__ void mx4_tile(const MxGemmArgs& g, const Mx4Ring& rg,
 #pragma unroll
         for (int j = 0; j < kMx4CodeLoads; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (mx4_lds_void*)(w + j * 1024), 16, boff,
-                                                     (b0[j] + t * bw[j]) * 1024, 0, 0);
+                                                     (b0[j] + t * bw[j]) * 1024, 0, kNonTemporal);
 #pragma unroll
         for (int j = 0; j < kMx4ScaleLoads; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (mx4_lds_void*)(w + 4096 + j * 256), 4, qoff,
-                                                     (q0[j] + (t >> 2) * bw[j]) * 256, 0, 0);
+                                                     (q0[j] + (t >> 2) * bw[j]) * 256, 0, kNonTemporal);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (mx4_lds_void*)(w + 5120), 4, soff, 4 * t, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     };

@@ -202,25 +202,33 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a)
     __shared__ uint32_t bm[kMaxExperts * (kChunkTok / 32)];
     __shared__ int lds[96];
     __shared__ int loc[2 * kMaxExperts];         // single-chunk launch: counts, offsets
+    const int c = blockIdx.x;
+    const int t = c * kChunkTok + threadIdx.x;
+    // this token's (id, prob) pairs, read for every row inside the capacity so
+    // that these loads go out beside the live count's instead of after it
+    int id[K];
+    float p[K];
+    const bool in_cap = t < a.T_cap;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        id[j] = in_cap ? a.ids[(int64_t)t * K + j] : -1;
+        // no probabilities (row mode): every route has probability 1
+        p[j] = in_cap ? (a.probs ? a.probs[(int64_t)t * K + j] : 1.0f) : 0.0f;
+    }
     const int32_t live = *a.live;
     const int T = clamp_live(live, a.T_cap);
     const int nch = (T + kChunkTok - 1) / kChunkTok;
-    const int c = blockIdx.x;
     const int E = a.E;
     const bool single = gridDim.x == 1;          // T_cap <= one chunk
     if (c >= nch && !single) return;
     for (int i = threadIdx.x; i < E * (kChunkTok / 32); i += blockDim.x) bm[i] = 0;
-    const int t = c * kChunkTok + threadIdx.x;
     const bool valid = t < T;
 
-    // canonical sort of this token's (id, prob) pairs (stable insertion sort)
-    int id[K];
-    float p[K];
+    // canonical sort of this token's pairs (stable insertion sort)
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-        id[j] = valid ? a.ids[(int64_t)t * K + j] : -1;
-        // no probabilities (row mode): every route has probability 1
-        p[j] = valid ? (a.probs ? a.probs[(int64_t)t * K + j] : 1.0f) : 0.0f;
+        id[j] = valid ? id[j] : -1;
+        p[j] = valid ? p[j] : 0.0f;
     }
 #pragma unroll
     for (int x = 1; x < K; ++x)
