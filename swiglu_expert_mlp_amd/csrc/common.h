@@ -158,7 +158,7 @@ struct WsLayout {
 // launch reads it, so the header needs no initialisation.
 struct WsHeader {
     uint32_t err;          // contract-violation bits of the last route or forward
-    uint32_t unused;
+    int32_t multi_tile;    // 1: some expert needs more than one 64-row M tile
     int32_t T;             // live tokens of the last forward (clamped)
     int32_t n_tiles;       // M tiles in the tile table
     int32_t n_rows;        // routed rows with a valid expert

@@ -8,9 +8,13 @@
 
 namespace moe {
 
-// Cache policy of the weight streams of the 64-row tiles (each weight byte is
-// read once per launch): non-temporal.  Measured at decode sizes (64 experts,
-// hidden 2048, FFN 1024): FC1 90.5 -> 82.8 us, FC2 53.5 -> 49.6 us.
+// Cache policy of the weight streams of the 64-row tiles when every expert's
+// rows fit one 64-row M tile (each weight byte then read once per launch):
+// non-temporal.  Measured at decode sizes (64 experts, hidden 2048, FFN 1024):
+// FC1 90.5 -> 82.8 us, FC2 53.5 -> 49.6 us.  With experts of several 64-row
+// tiles, which share a weight slice through the L2, the default policy (the
+// single-launch FFN at 16K tokens: 3.73 ms/step with it, 5.08 with
+// non-temporal loads).
 constexpr int kNonTemporal = 2;
 
 // 16-byte load with the non-temporal (streaming) cache policy.

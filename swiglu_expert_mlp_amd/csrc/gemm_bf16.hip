@@ -28,10 +28,12 @@ __global__ void __launch_bounds__(512, 1) gemm_bf16_small_kernel(GemmArgs g)
     // the tile does not exist), so the first weight loads wait for one round trip
     const int n_big = g.small_takes_big ? ld_const(&g.hdr->n_tiles_big) : 0;
     const int n_small = ld_const(&g.hdr->n_tiles);
+    const int multi = ld_const(&g.hdr->multi_tile);
     const int* te0 = (const int*)(g.tiles + min((int)blockIdx.x / small_col_tiles(g), g.max_tiles - 1));
     const int e0 = ld_const(te0), row00 = ld_const(te0 + 1);
-    asm volatile("" : : "s"(n_big), "s"(n_small), "s"(e0), "s"(row00));   // one round trip for all four
-    small_tiles<FC1, PROB>(g, smem, n_small, n_big, e0, row00);
+    asm volatile("" : : "s"(n_big), "s"(n_small), "s"(multi), "s"(e0), "s"(row00));   // one round trip
+    if (multi) small_tiles<FC1, PROB, 0, 0>(g, smem, n_small, n_big, e0, row00);
+    else small_tiles<FC1, PROB, 0, kNonTemporal>(g, smem, n_small, n_big, e0, row00);
 }
 
 template <bool FC1, bool PROB>
@@ -51,13 +53,20 @@ __global__ void __launch_bounds__(512, 1) gemm_bf16_fused_kernel(GemmArgs g1, Ge
     __shared__ __attribute__((aligned(1024))) char smem[kSmallLds];
     const int n_big = ld_const(&g1.hdr->n_tiles_big);
     const int n_small = ld_const(&g1.hdr->n_tiles);
+    const int multi = ld_const(&g1.hdr->multi_tile);
     const int* te0 = (const int*)(g1.tiles + min((int)blockIdx.x / small_col_tiles(g1), g1.max_tiles - 1));
     const int e0 = ld_const(te0), row00 = ld_const(te0 + 1);
-    asm volatile("" : : "s"(n_big), "s"(n_small), "s"(e0), "s"(row00));
-    small_tiles<true, PROB, 1>(g1, smem, n_small, n_big, e0, row00);
+    asm volatile("" : : "s"(n_big), "s"(n_small), "s"(multi), "s"(e0), "s"(row00));
     const int* te1 = (const int*)(g2.tiles + min((int)blockIdx.x / small_col_tiles(g2), g2.max_tiles - 1));
-    small_tiles<false, false, 2>(g2, smem, n_small, n_big, ld_const(te1), ld_const(te1 + 1),
-                                 small_col_tiles(g1));
+    if (multi) {
+        small_tiles<true, PROB, 1, 0>(g1, smem, n_small, n_big, e0, row00);
+        small_tiles<false, false, 2, 0>(g2, smem, n_small, n_big, ld_const(te1), ld_const(te1 + 1),
+                                        small_col_tiles(g1));
+    } else {
+        small_tiles<true, PROB, 1, kNonTemporal>(g1, smem, n_small, n_big, e0, row00);
+        small_tiles<false, false, 2, kNonTemporal>(g2, smem, n_small, n_big, ld_const(te1),
+                                                   ld_const(te1 + 1), small_col_tiles(g1));
+    }
 }
 
 hipError_t launch_gemm_bf16_fused(const GemmArgs& g1, const GemmArgs& g2, int num_cu, hipStream_t s,

@@ -89,7 +89,10 @@ constexpr int kCoherentLoad = 16;               // cache policy sc1 (device-cohe
 // the 256-row design takes them); (e0, row00): the table entry of this
 // workgroup's first tile (blockIdx.x), read by the caller before the counts
 // were known.
-template <bool FC1, bool PROB, int FUSE = 0>
+// WPOL: the cache policy of the weight stream (kNonTemporal when every
+// expert's rows fit one 64-row tile, else the default; the caller reads which
+// from the header).
+template <bool FC1, bool PROB, int FUSE, int WPOL>
 __device__ __forceinline__ void small_tiles(const GemmArgs& g, char* smem, int n_small, int n_big,
                                             int e0, int row00, int need = 0)
 {
@@ -146,7 +149,7 @@ __device__ __forceinline__ void small_tiles(const GemmArgs& g, char* smem, int n
                 for (int j = 0; j < 4; ++j)
                     __builtin_amdgcn_global_load_lds(bblk[j] + (int64_t)bstep[j] * s,
                                                      (lds_void_t*)(st + (4 + 4 * wid + j) * 1024), 16, 0,
-                                                     kNonTemporal);
+                                                     WPOL);
             }
         };
         // a 64-row part of a 256-row tile may lie past its expert's rows

@@ -150,6 +150,10 @@ __device__ void prep_finish(const PrepArgs& a, int T, int nch, int32_t live, int
         if (cnt[q] > kBigMin) nbig_mine += (cnt[q] + kBigBMRows - 1) / kBigBMRows;
         else ntile_mine += (cnt[q] + kBM - 1) / kBM;
     }
+    bool multi_mine = false;                       // an expert of more than one 64-row tile
+#pragma unroll
+    for (int q = 0; q < PER; ++q) multi_mine |= cnt[q] > kBM;
+    const int multi = __syncthreads_or(multi_mine);
     int sc[3] = {mine, ntile_mine, nbig_mine}, tot[3];
     block_exclusive_scan3(sc, tot, lds);
     int off = sc[0], tfirst = sc[1], bfirst = sc[2];
@@ -192,6 +196,7 @@ __device__ void prep_finish(const PrepArgs& a, int T, int nch, int32_t live, int
         a.hdr->T = T;
         a.hdr->n_tiles = ntotal;
         a.hdr->n_tiles_big = nbig;
+        a.hdr->multi_tile = multi ? 1 : 0;
         a.hdr->n_rows = total;
     }
 }
