@@ -50,12 +50,31 @@ constexpr uint32_t kErrFusedWait = 16u;
 
 // SwiGLU of one gate/up pair in fp32, silu(g) * u = g / (1 + exp(-g)) * u, the
 // division as a multiply by the hardware reciprocal (v_rcp_f32, within 1 ulp).
-// Every bf16 GEMM epilogue calls this one function, so the tile designs agree
-// bit for bit.  Large negative g: exp(-g) = inf, rcp(inf) = 0, so the result
+// Every GEMM epilogue (bf16 and MX) calls this one function, so the tile
+// designs agree bit for bit.  Large negative g: exp(-g) = inf, rcp(inf) = 0, so the result
 // is a signed zero; large positive g: rcp(1) = 1, so the result is g * u.
 __device__ __forceinline__ float swiglu_f32(float g, float u)
 {
     return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
+// Maximum over the 16 lanes of a DPP row (lanes 16 m .. 16 m + 15), the lanes
+// that hold one row of a 16 x 16 MFMA block: v_max_f32 with the row rotated
+// by 1, 2, 4, 8 on its first operand.  Each s_nop gives the two wait states a
+// DPP read of a VGPR needs after a VALU write to it.  Equal to an fmaxf
+// reduction for every value the epilogues produce (no signaling NaN).
+__device__ __forceinline__ float row16_max(float x)
+{
+    asm("s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 row_ror:1 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 row_ror:2 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf"
+        : "+v"(x));
+    return x;
 }
 
 // fp32 -> bf16 bits, round to nearest even (gfx950 converts in hardware).
@@ -74,11 +93,12 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b)
 // amax <= 448 * 2^e.  With amax = 1.m * 2^E (normal), 448 = 1.75 * 2^8, so
 // e = E - 8 when 1.m <= 1.75 (mantissa field <= 0x600000), else E - 7.
 // Zero and subnormal amax fall below 448 * 2^-127 and give -127.
+// (The zero / subnormal case needs no branch: exponent field 0 gives e <= -134,
+// which the clamp takes to -127.)
 __device__ __forceinline__ int e8m0_exponent(float amax)
 {
     uint32_t u = __float_as_uint(amax) & 0x7fffffffu;
     int ef = (int)(u >> 23);
-    if (ef == 0) return -127;
     int e = ef - 127 - 8 + ((u & 0x7fffffu) > 0x600000u ? 1 : 0);
     return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
@@ -91,8 +111,7 @@ __device__ __forceinline__ int e8m0_exponent(float amax)
 __device__ __forceinline__ int e8m0_exponent_fp4(float amax)
 {
     uint32_t u = __float_as_uint(amax) & 0x7fffffffu;
-    int ef = (int)(u >> 23);
-    if (ef == 0) return -127;
+    int ef = (int)(u >> 23);   // 0 gives e <= -128, clamped to -127 below
     int e = ef - 127 - 2 + ((u & 0x7fffffu) > 0x400000u ? 1 : 0);
     return e < -127 ? -127 : (e > 127 ? 127 : e);
 }

@@ -226,12 +226,10 @@ __device__ __forceinline__ void mx4_tile(const MxGemmArgs& g, const Mx4Ring& rg,
                 // the 16 lanes of one requantization block hold one row: one probability
                 const float pr = (PROB && r < rows) ? fc1_row_prob(g.row_prob, g.perm_src, row0 + r) : 1.0f;
                 float gt = acc[i][0][v], up = acc[i][2][v];
-                const float h0 = gt / (1.0f + __expf(-gt)) * up * pr;
+                const float h0 = swiglu_f32(gt, up) * pr;
                 gt = acc[i][1][v]; up = acc[i][3][v];
-                const float h1 = gt / (1.0f + __expf(-gt)) * up * pr;
-                float amax = fmaxf(fabsf(h0), fabsf(h1));
-#pragma unroll
-                for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+                const float h1 = swiglu_f32(gt, up) * pr;
+                const float amax = row16_max(fmaxf(fabsf(h0), fabsf(h1)));
                 const int e8 = e8m0_exponent(amax);
                 const float inv = e8 == 127 ? __uint_as_float(1u << 22)
                                             : __uint_as_float((uint32_t)(127 - e8) << 23);

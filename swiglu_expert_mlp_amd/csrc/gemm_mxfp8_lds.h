@@ -42,30 +42,12 @@ namespace moe {
 
 constexpr int kMxBigBM = 256;
 constexpr int kMxBigBN = 256;
-// one stage: A codes 32 KB | B codes 32 KB | A scales 1 KB | B scales 4 KB
-constexpr int kMxStage = 69 * 1024;
-constexpr int kMxAsOff = 64 * 1024, kMxBsOff = 65 * 1024;
+// one stage: A codes 32 KB | B codes 32 KB | A scales 1 KB (waves 0-3) | the
+// dropped A-scale loads of waves 4-7 1 KB | B scales 4 KB
+constexpr int kMxStage = 70 * 1024;
+constexpr int kMxAsOff = 64 * 1024, kMxBsOff = 66 * 1024;
 
 typedef __attribute__((address_space(3))) void mx_lds_void;
-
-__device__ __forceinline__ void mx_load_block_to_lds(const void* gsrc, void* lds_dst)
-{
-    __builtin_amdgcn_global_load_lds(gsrc, (mx_lds_void*)lds_dst, 16, 0, 0);
-}
-
-// weight blocks: FC2's with the non-temporal cache policy (measured at 16K
-// tokens: FC2 466 -> 447 us; FC1, whose row tiles reuse them through the L2,
-// 728 -> 766 us with it, so FC1 keeps the default)
-template <bool FC1>
-__device__ __forceinline__ void mx_load_wblock_to_lds(const void* gsrc, void* lds_dst)
-{
-    __builtin_amdgcn_global_load_lds(gsrc, (mx_lds_void*)lds_dst, 16, 0, FC1 ? 0 : kNonTemporal);
-}
-
-__device__ __forceinline__ void mx_load_dword_to_lds(const void* gsrc, void* lds_dst)
-{
-    __builtin_amdgcn_global_load_lds(gsrc, (mx_lds_void*)lds_dst, 4, 0, 0);
-}
 
 __device__ __forceinline__ i32x8 mx_frag(uint4 lo, uint4 hi)
 {
@@ -73,7 +55,41 @@ __device__ __forceinline__ i32x8 mx_frag(uint4 lo, uint4 hi)
                  (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-#define MX_WAIT_VMCNT0() __builtin_amdgcn_s_waitcnt(0x0F70)
+// s_waitcnt with only a vector-memory bound (expcnt and lgkmcnt left at max)
+#define MX_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+
+typedef unsigned mx_u32x4 __attribute__((ext_vector_type(4)));
+
+// third dword of a raw buffer descriptor (32-bit format, no swizzle or
+// stride): byte-addressed stores with a range check on the offset, which
+// drops the rows past a tile's valid rows
+constexpr int kMxRsrcWord3 = 0x00020000;
+
+// Epilogue (after the K loop; the second stage's LDS holds no operands then).
+// FC1: the tile's 256 rows x 128 code bytes, row r's four 32-byte segments
+// (one per wave column, one interleave block each) at slot wn ^ ((r / 4) mod 4),
+// which spreads the rows one write instruction covers over the banks; inside
+// a segment the code pair (column q, column 16 + q) at bytes 2 q, 2 q + 1.
+// The waves' row probabilities (PROB) after the codes.
+constexpr int kMxEpiProb = 32 * 1024;
+// FC2: 8 KB per wave (32 rows x 64 fp32 at a time).
+constexpr int kMxEpiWave = 8 * 1024;
+static_assert(kMxEpiProb + 8 * 512 <= kMxStage && 8 * kMxEpiWave <= kMxStage, "epilogue fits a stage");
+// stores per wave per tile (every wave issues exactly these; the next tile's
+// first wait lets them drain while its first stage is already in)
+template <bool FC1>
+constexpr int mx_stores() { return FC1 ? 4 + 2 : 32; }
+
+// The lane index computed afresh (mbcnt, in a volatile asm statement, which
+// the compiler neither hoists nor merges): values derived from it are not
+// hoisted out of the tile loop, where they would outlive the K loop and spill
+// (a spill reload waits for every load in flight).
+__device__ __forceinline__ int mx_lane_fresh()
+{
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
 
 // The LDS-staged tile loop of one 8-wave workgroup (one workgroup per CU).
 // Requires K % 128 == 0.
@@ -107,232 +123,387 @@ __device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
     const int chunk = (total + 7) / 8;
     const int t_begin = xcd * chunk;
     const int t_end = min(total, t_begin + chunk);
-    for (int tile = t_begin + (blockIdx.x >> 3); tile < t_end; tile += per_xcd) {
+    int tile = t_begin + (blockIdx.x >> 3);
+    if (tile >= t_end) return;
+
+    // A tile's place: its expert, first grouped row, row count and first column.
+    struct MxPos { int e, row0, rows, n0; };
+    auto locate = [&](int t) {
         // the tiles of one expert (its m_e row tiles x NT column tiles) keep their
         // index range but are walked column tile by column tile: the expert's
         // row tiles for one column tile run together and share its weight slice
-        const int2 te0 = g.tiles_big[tile / NT];
+        const int2 te0 = g.tiles_big[t / NT];
         const int e = te0.x;
         const int base = g.offsets[e], cnt = g.offsets[e + 1] - base;
         const int m_e = (cnt + kMxBigBM - 1) / kMxBigBM;
-        const int b_e = tile / NT - (te0.y - base) / kMxBigBM;     // the expert's first row tile
-        const int u = tile - b_e * NT;
+        const int b_e = t / NT - (te0.y - base) / kMxBigBM;     // the expert's first row tile
+        const int u = t - b_e * NT;
         const int nt = u / m_e, mi = u - nt * m_e;
-        const int row0 = base + mi * kMxBigBM;
-        int rows = cnt - mi * kMxBigBM;
-        if (rows > kMxBigBM) rows = kMxBigBM;
-        const int n0 = nt * kMxBigBN;
+        return MxPos{e, base + mi * kMxBigBM, min(kMxBigBM, cnt - mi * kMxBigBM), nt * kMxBigBN};
+    };
 
+    // Operand sources of one tile.  Direct loads go through buffer descriptors
+    // (wave-uniform); the per-lane offsets are fixed for the tile and the K
+    // step is a scalar offset, so no address register changes inside the K
+    // loop (the instruction's immediate offset would move the LDS destination
+    // too, so it stays 0).
+    __amdgpu_buffer_rsrc_t ar, asr, wr, wsr;
+    int aoff[4], soff;           // per lane: activation rows (codes, scales)
+    int woff[2], wstep[2];       // the wave's two weight column blocks: K step 0, bytes per K step
+    int qoff[2], qstep[2];       // their scale groups: step 0, bytes per 4 steps
+    const int lane16 = 16 * lane, lane4 = 4 * lane;
+    const __amdgpu_buffer_rsrc_t anone = __builtin_amdgcn_make_buffer_rsrc(g.out, (short)0, 0, kMxRsrcWord3);
+    auto sources = [&](const MxPos& p) {
+        const int lane = mx_lane_fresh();
         // activation code loads: blocks 4 wid + i (8 rows each); lane -> row
-        // 8 j + lane / 8, LDS position lane % 8 <- chunk (lane % 8) ^ (row % 8)
-        const uint8_t* aptr[4];
+        // 8 j + lane / 8, LDS position lane % 8 <- chunk (lane % 8) ^ (row % 8);
+        // activation scale loads (waves 0-3 real, 4-7 dropped): dword q = 64
+        // (wid mod 4) + lane holds tile row 128 (q / 128) + 16 (q % 8) + (q / 8)
+        // % 16, 4 bytes per step.  FC1 gathers the rows: all five row lookups
+        // go out before any is used (one round trip, not five).
+        const int64_t abase = FC1 ? 0 : (int64_t)p.row0;
+        ar = __builtin_amdgcn_make_buffer_rsrc((void*)(g.A + abase * K), (short)0, 0x7fffffff, kMxRsrcWord3);
+        asr = __builtin_amdgcn_make_buffer_rsrc((void*)(g.As + abase * KB), (short)0, 0x7fffffff, kMxRsrcWord3);
+        int src[5];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rr = 8 * (4 * wid + i) + (lane >> 3);
-            const int r = rr < rows ? rr : rows - 1;
-            int64_t src = row0 + r;
-            if constexpr (FC1) src = g.perm_src[row0 + r] / g.topk;
-            aptr[i] = g.A + src * K + 16 * ((lane & 7) ^ (rr & 7));
+        for (int i = 0; i < 5; ++i) {
+            int rr;
+            if (i < 4) {
+                rr = 8 * (4 * wid + i) + (lane >> 3);
+            } else {
+                const int q = 64 * (wid & 3) + lane;
+                rr = 128 * (q >> 7) + 16 * (q & 7) + ((q >> 3) & 15);
+            }
+            src[i] = rr < p.rows ? rr : p.rows - 1;
+            if constexpr (FC1) src[i] = g.perm_src[p.row0 + src[i]];
         }
-        // activation scale loads (waves 0-3): dword q = 64 wid + lane holds tile
-        // row 128 (q / 128) + 16 (q % 8) + (q / 8) % 16, 4 bytes per step
-        const uint8_t* sptr;
-        {
-            const int q = 64 * (wid & 3) + lane;
-            const int rr = 128 * (q >> 7) + 16 * (q & 7) + ((q >> 3) & 15);
-            const int r = rr < rows ? rr : rows - 1;
-            int64_t src = row0 + r;
-            if constexpr (FC1) src = g.perm_src[row0 + r] / g.topk;
-            sptr = g.As + src * KB;
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            if constexpr (FC1) src[i] /= g.topk;
+            if (i < 4) {
+                const int rr = 8 * (4 * wid + i) + (lane >> 3);
+                aoff[i] = src[i] * K + 16 * ((lane & 7) ^ (rr & 7));
+            } else {
+                soff = src[i] * KB;
+            }
         }
-        // weight code and scale loads: column blocks 2 wid + i
-        // weight blocks of K step s: MXFP8 [expert][c16][s] (2 KB); MXFP4 in
-        // 512-column groups (wblock_index, 1 KB codes / 256-byte scale groups)
-        int64_t bblk[2], b4[2], q4[2], w4s[2];
+        // weight code and scale loads: column blocks 2 wid + i of the expert's
+        // section; codes MXFP8 [c16][s] (2 KB blocks), MXFP4 in 512-column
+        // groups (wblock_index, 1 KB blocks); scales in 256-byte groups of 4 steps
+        wr = __builtin_amdgcn_make_buffer_rsrc((void*)(g.W + (int64_t)p.e * nt16 * KS * (W4 ? 1024 : 2048)),
+                                               (short)0, 0x7fffffff, kMxRsrcWord3);
+        wsr = __builtin_amdgcn_make_buffer_rsrc((void*)(g.Ws + (int64_t)p.e * nt16 * KQ * 256), (short)0,
+                                                0x7fffffff, kMxRsrcWord3);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            int c16 = n0 / 16 + 2 * wid + i;
+            int c16 = p.n0 / 16 + 2 * wid + i;
             if (c16 >= nt16) c16 = nt16 - 1;
-            bblk[i] = (int64_t)e * nt16 + c16;
-            b4[i] = (int64_t)e * nt16 * KS + wblock_index(c16, 0, nt16, KS);
-            q4[i] = (int64_t)e * nt16 * KQ + wblock_index(c16, 0, nt16, KQ);
-            w4s[i] = wblock_step(c16, nt16);
-        }
-        // loads of step s into stage Q
-        auto issue = [&](auto QC, int s) {
-            constexpr int Q = decltype(QC)::value;
-            char* st = (Q & 1) ? st1 : st0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                mx_load_block_to_lds(aptr[i] + 128 * s, st + (4 * wid + i) * 1024);
             if constexpr (W4) {
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    mx_load_wblock_to_lds<FC1>(g.W + (b4[i] + s * w4s[i]) * 1024 + 16 * lane,
-                                         st + 32768 + (2 * wid + i) * 1024);
+                woff[i] = (int)wblock_index(c16, 0, nt16, KS) * 1024;
+                wstep[i] = (int)wblock_step(c16, nt16) * 1024;
+                qoff[i] = (int)wblock_index(c16, 0, nt16, KQ) * 256;
+                qstep[i] = (int)wblock_step(c16, nt16) * 256;
             } else {
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int h = 0; h < 2; ++h)
-                        mx_load_wblock_to_lds<FC1>(g.W + (bblk[i] * KS + s) * 2048 + h * 1024 + 16 * lane,
-                                             st + 32768 + ((2 * wid + i) * 2 + h) * 1024);
+                woff[i] = c16 * KS * 2048;
+                wstep[i] = 2048;
+                qoff[i] = c16 * KQ * 256;
+                qstep[i] = 256;
             }
-            if (wid < 4) mx_load_dword_to_lds(sptr + 4 * s, st + kMxAsOff + 256 * wid);
+        }
+    };
+    // loads of step s into stage Q
+    auto issue = [&](auto QC, int s) {
+        constexpr int Q = decltype(QC)::value;
+        char* st = (Q & 1) ? st1 : st0;
+        // the weights' cache policy: FC2's non-temporal (measured at 16K tokens:
+        // FC2 466 -> 447 us); FC1, whose row tiles reuse a weight slice through
+        // the L2, keeps the default (728 -> 766 us with non-temporal loads)
+        constexpr int wpol = FC1 ? 0 : kNonTemporal;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (mx_lds_void*)(st + (4 * wid + i) * 1024), 16, aoff[i],
+                                                     128 * s, 0, 0);
+        if constexpr (W4) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                mx_load_dword_to_lds(g.Ws + (W4 ? q4[i] + (s >> 2) * w4s[i] : bblk[i] * KQ + (s >> 2)) * 256 +
-                                         4 * lane,
-                                     st + kMxBsOff + (2 * wid + i) * 256);
-        };
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (mx_lds_void*)(st + 32768 + (2 * wid + i) * 1024), 16,
+                                                         lane16, woff[i] + s * wstep[i], 0, wpol);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        wr, (mx_lds_void*)(st + 32768 + ((2 * wid + i) * 2 + h) * 1024), 16, lane16,
+                        woff[i] + s * 2048 + h * 1024, 0, wpol);
+        }
+        // waves 4-7 issue the same load through an empty descriptor (the range
+        // check drops it) into an unused area of the stage: no branch, every
+        // wave counts the same loads, and the destination stays inside one LDS
+        // object (a destination chosen between objects makes the compiler wait
+        // for every direct load before any later LDS access)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wid < 4 ? asr : anone,
+                                                 (mx_lds_void*)(st + kMxAsOff + 256 * wid), 4, soff, 4 * s, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wsr, (mx_lds_void*)(st + kMxBsOff + (2 * wid + i) * 256), 4,
+                                                     lane4, qoff[i] + (s >> 2) * qstep[i], 0, 0);
+    };
 
-        f32x4 acc[8][4];
+    f32x4 acc[8][4];
+    int kst = KS;       // the step count, re-derived per tile (see the tile loop)
+
+    // one K step in stage P: wait for its loads (issued one step ago; before a
+    // tile's first step, the AFTER stores of the previous tile's epilogue came
+    // after them) in every wave, refill the other stage (read by every wave in
+    // the previous step), compute
+    auto step = [&](auto PC, auto AC, int s) {
+        constexpr int P = decltype(PC)::value;
+        constexpr int AFTER = decltype(AC)::value;
+        MX_WAIT_VMCNT(AFTER);
+        __builtin_amdgcn_s_barrier();
+        const char* As = P ? st1 : st0;
+        const char* Bs = As + 32768 + 16 * lane;
+        const char* Sa = As + kMxAsOff + (16 * wm + r16) * 32;
+        const uint8_t* Sb = (const uint8_t*)As + kMxBsOff + 4 * lane + (s & 3);
+        // the weight fragments and all scales are read before the next
+        // stage's loads are issued
+        i32x8 b[4];
+        int sb[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            if constexpr (W4)   // the upper half of an E2M1 operand is not read
+                b[ct] = mx_frag(*(const uint4*)(Bs + (4 * wn + ct) * 1024), make_uint4(0, 0, 0, 0));
+            else
+                b[ct] = mx_frag(*(const uint4*)(Bs + (4 * wn + ct) * 2048),
+                                *(const uint4*)(Bs + (4 * wn + ct) * 2048 + 1024));
+            sb[ct] = Sb[(4 * wn + ct) * 256];
+        }
+        const uint4 sa_lo = *(const uint4*)Sa, sa_hi = *(const uint4*)(Sa + 16);
+        if (s + 1 < kst) issue(std::integral_constant<int, P ^ 1>{}, s + 1);
+        const uint32_t sad[8] = {sa_lo.x, sa_lo.y, sa_lo.z, sa_lo.w,
+                                 sa_hi.x, sa_hi.y, sa_hi.z, sa_hi.w};
+        // FC1: activation fragments in four groups of two, each group's reads
+        // issued while the previous group's MFMAs run; the explicit
+        // lgkmcnt(0) before a group's reads is what tells the compiler that
+        // the previous group has landed (after the direct loads above it
+        // would otherwise wait for every LDS read before each MFMA)
+        i32x8 af[2][2];
+        auto read_group = [&](int gr, i32x8 (&dst)[2]) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const char* ag = As + (8 * wm + 2 * gr + q) * 2048;
+                dst[q] = mx_frag(*(const uint4*)(ag + a_lo), *(const uint4*)(ag + a_hi));
+            }
+        };
+        auto mfma_group = [&](int gr, const i32x8 (&src)[2]) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int i = 2 * gr + q;
+                const int sa = (int)((sad[i] >> (8 * kg)) & 0xffu);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct)
+                    // A format 0 (E4M3); B format 0 (E4M3) or 4 (E2M1)
+                    acc[i][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        src[q], b[ct], acc[i][ct], 0, W4 ? 4 : 0, 0, sa, 0, sb[ct]);
+            }
+        };
+        if constexpr (FC1) {
+            read_group(0, af[0]);
+#pragma unroll
+            for (int gr = 0; gr < 4; ++gr) {
+                __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): group gr is in
+                if (gr + 1 < 4) read_group(gr + 1, af[(gr + 1) & 1]);
+                mfma_group(gr, af[gr & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            // FC2 is bound by its loads and output stores; the grouped reads
+            // only added register spills there
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const char* ag = As + (8 * wm + i) * 2048;
+                const i32x8 a = mx_frag(*(const uint4*)(ag + a_lo), *(const uint4*)(ag + a_hi));
+                const int sa = (int)((sad[i] >> (8 * kg)) & 0xffu);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct)
+                    acc[i][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        a, b[ct], acc[i][ct], 0, W4 ? 4 : 0, 0, sa, 0, sb[ct]);
+            }
+        }
+    };
+
+    MxPos pos = locate(tile);
+    sources(pos);
+    issue(std::integral_constant<int, 0>{}, 0);
+    // the first tile's first wait counts the previous epilogue's stores too:
+    // before the first tile the same number of stores go to an empty
+    // descriptor (the range check drops them; distinct offsets, so that none
+    // is merged away)
+    constexpr int kStores = mx_stores<FC1>();
+    static_assert(kStores + 16 <= 63, "vmcnt bound");
+    {
+        const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(g.out, (short)0, 0, kMxRsrcWord3);
+#pragma unroll
+        for (int k = 0; k < kStores; ++k)
+            __builtin_amdgcn_raw_buffer_store_b128(mx_u32x4{0u, 0u, 0u, 0u}, none, 16 * lane + 1024 * k, 0, 0);
+    }
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    while (true) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        // one K step in stage P: wait for its loads (issued one step ago) in
-        // every wave, refill the other stage (read by every wave in the
-        // previous step), compute
-        auto step = [&](auto PC, int s) {
-            constexpr int P = decltype(PC)::value;
-            MX_WAIT_VMCNT0();
-            __builtin_amdgcn_s_barrier();
-            const char* As = P ? st1 : st0;
-            const char* Bs = As + 32768 + 16 * lane;
-            const char* Sa = As + kMxAsOff + (16 * wm + r16) * 32;
-            const uint8_t* Sb = (const uint8_t*)As + kMxBsOff + 4 * lane + (s & 3);
-            // the weight fragments and all scales are read before the next
-            // stage's loads are issued
-            i32x8 b[4];
-            int sb[4];
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-                if constexpr (W4)   // the upper half of an E2M1 operand is not read
-                    b[ct] = mx_frag(*(const uint4*)(Bs + (4 * wn + ct) * 1024), make_uint4(0, 0, 0, 0));
-                else
-                    b[ct] = mx_frag(*(const uint4*)(Bs + (4 * wn + ct) * 2048),
-                                    *(const uint4*)(Bs + (4 * wn + ct) * 2048 + 1024));
-                sb[ct] = Sb[(4 * wn + ct) * 256];
-            }
-            const uint4 sa_lo = *(const uint4*)Sa, sa_hi = *(const uint4*)(Sa + 16);
-            if (s + 1 < KS) issue(std::integral_constant<int, P ^ 1>{}, s + 1);
-            const uint32_t sad[8] = {sa_lo.x, sa_lo.y, sa_lo.z, sa_lo.w,
-                                     sa_hi.x, sa_hi.y, sa_hi.z, sa_hi.w};
-            // FC1: activation fragments in four groups of two, each group's reads
-            // issued while the previous group's MFMAs run; the explicit
-            // lgkmcnt(0) before a group's reads is what tells the compiler that
-            // the previous group has landed (after the direct loads above it
-            // would otherwise wait for every LDS read before each MFMA)
-            i32x8 af[2][2];
-            auto read_group = [&](int gr, i32x8 (&dst)[2]) {
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const char* ag = As + (8 * wm + 2 * gr + q) * 2048;
-                    dst[q] = mx_frag(*(const uint4*)(ag + a_lo), *(const uint4*)(ag + a_hi));
-                }
-            };
-            auto mfma_group = [&](int gr, const i32x8 (&src)[2]) {
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const int i = 2 * gr + q;
-                    const int sa = (int)((sad[i] >> (8 * kg)) & 0xffu);
-#pragma unroll
-                    for (int ct = 0; ct < 4; ++ct)
-                        // A format 0 (E4M3); B format 0 (E4M3) or 4 (E2M1)
-                        acc[i][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            src[q], b[ct], acc[i][ct], 0, W4 ? 4 : 0, 0, sa, 0, sb[ct]);
-                }
-            };
-            if constexpr (FC1) {
-                read_group(0, af[0]);
-#pragma unroll
-                for (int gr = 0; gr < 4; ++gr) {
-                    __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): group gr is in
-                    if (gr + 1 < 4) read_group(gr + 1, af[(gr + 1) & 1]);
-                    mfma_group(gr, af[gr & 1]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            } else {
-                // FC2 is bound by its loads and output stores; the grouped reads
-                // only added register spills there
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const char* ag = As + (8 * wm + i) * 2048;
-                    const i32x8 a = mx_frag(*(const uint4*)(ag + a_lo), *(const uint4*)(ag + a_hi));
-                    const int sa = (int)((sad[i] >> (8 * kg)) & 0xffu);
-#pragma unroll
-                    for (int ct = 0; ct < 4; ++ct)
-                        acc[i][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            a, b[ct], acc[i][ct], 0, W4 ? 4 : 0, 0, sa, 0, sb[ct]);
-                }
-            }
-        };
-
-        // every wave finished the previous tile's LDS reads before the stages refill
-        __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0)
-        __builtin_amdgcn_s_barrier();
-        issue(std::integral_constant<int, 0>{}, 0);
-        for (int s2 = 0; s2 < KS; s2 += 2) {
-            step(std::integral_constant<int, 0>{}, s2);
-            if (s2 + 1 < KS) step(std::integral_constant<int, 1>{}, s2 + 1);
+        // an opaque copy: the compiler otherwise hoists the steps' loop-invariant
+        // conditions out of the tile loop, where they outlive everything and spill
+        kst = KS;
+        asm volatile("" : "+s"(kst));
+        step(I0{}, std::integral_constant<int, kStores>{}, 0);
+        for (int s2 = 1; s2 < kst; s2 += 2) {
+            step(I1{}, I0{}, s2);
+            if (s2 + 1 < kst) step(I0{}, I0{}, s2 + 1);
         }
 
-        // epilogue: lane holds rows 4 (lane / 16) + v of each 16-row group, column lane % 16
+        // every wave finished its fragment reads of both stages: the next
+        // tile's first stage goes out before this tile's epilogue, which works
+        // in the second stage's LDS, so it lands while the epilogue runs, and
+        // the epilogue's stores drain while the next tile's first step runs.
+        // The load goes out on every path (after the last tile it loads that
+        // tile's first stage again, waited for before the exit): a load issued
+        // on one path only makes the compiler wait on every load in flight.
+        __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        const int next = tile + per_xcd;
+        const bool more = next < t_end;
+        const int row0 = pos.row0, rows = pos.rows, n0 = pos.n0;
+        // FC1 with the probabilities applied inside FC1: the wave's 128 row
+        // probabilities, fetched before the loads below so that waiting for
+        // them does not wait for those
+        float pr0 = 1.0f, pr1 = 1.0f;
+        if constexpr (FC1 && PROB) {
+            const int r0 = 128 * wm + lane, r1 = r0 + 64;
+            if (r0 < rows) pr0 = fc1_row_prob(g.row_prob, g.perm_src, row0 + r0);
+            if (r1 < rows) pr1 = fc1_row_prob(g.row_prob, g.perm_src, row0 + r1);
+        }
+        if (more) {
+            pos = locate(next);
+            sources(pos);
+        }
+        issue(I0{}, 0);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // epilogue: lane holds rows 16 i + 4 (lane / 16) + v of the wave's 128
+        // rows, column 16 j + lane % 16 of its 64 columns (per-lane offsets from
+        // a fresh lane index, derived here).
+        const int elane = mx_lane_fresh();
+        const int er16 = elane & 15, ekg = elane >> 4;
         const int c0 = n0 + 64 * wn;                 // this wave's 64 columns
         if constexpr (FC1) {
             // SwiGLU of one interleave block (tiles 0, 1 gate and 2, 3 up of the
             // same 32 outputs), then the per-32 requantization of each row's 32
             // outputs, held by the 16 lanes of one lane group
             const int F = g.N / 2, FB = F / 32;
-            const int cb = c0 / 64;
-            uint8_t* hq = (uint8_t*)g.out;
-            if (c0 < g.N) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int r = 128 * wm + 16 * i + 4 * kg + v;
-                        // the 16 lanes of one requantization block hold one row: one probability
-                        const float pr = (PROB && r < rows) ? fc1_row_prob(g.row_prob, g.perm_src, row0 + r) : 1.0f;
-                        float gt = acc[i][0][v], up = acc[i][2][v];
-                        const float h0 = gt / (1.0f + __expf(-gt)) * up * pr;
-                        gt = acc[i][1][v]; up = acc[i][3][v];
-                        const float h1 = gt / (1.0f + __expf(-gt)) * up * pr;
-                        float amax = fmaxf(fabsf(h0), fabsf(h1));
-#pragma unroll
-                        for (int off = 1; off < 16; off <<= 1)
-                            amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
-                        const int e8 = e8m0_exponent(amax);
-                        const float inv = e8 == 127 ? __uint_as_float(1u << 22)
-                                                    : __uint_as_float((uint32_t)(127 - e8) << 23);
-                        if (r < rows) {
-                            const int64_t row = row0 + r;
-                            const uint32_t c2 = cvt_e4m3x2(h0 * inv, h1 * inv);
-                            hq[row * F + cb * 32 + r16] = (uint8_t)c2;
-                            hq[row * F + cb * 32 + 16 + r16] = (uint8_t)(c2 >> 8);
-                            if (r16 == 0) g.out_scale[row * FB + cb] = (uint8_t)(e8 + 127);
-                        }
-                    }
+            const int cb0 = n0 / 64;                 // the tile's first interleave block
+            float* const xpr = (float*)(st1 + kMxEpiProb) + 128 * wid;
+            if constexpr (PROB) {
+                xpr[elane] = pr0;
+                xpr[elane + 64] = pr1;
             }
-        } else {
-            float* ob = (float*)g.out;
+            // scale bytes: after the loop, lane (q, kg) keeps the scale of row
+            // 16 (4 h + q / 4) + 4 kg + q % 4 in sc[h]
+            uint32_t sc[2] = {0u, 0u};
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const int r = 128 * wm + 16 * i + 4 * kg + v;
-                    if (r < rows) {
-                        const int64_t row = row0 + r;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const int col = c0 + 16 * j + r16;
-                            if (col < g.N) ob[row * g.N + col] = acc[i][j][v];
-                        }
-                    }
+                    const int lr = 16 * i + 4 * ekg + v;
+                    const float pr = PROB ? xpr[lr] : 1.0f;
+                    float gt = acc[i][0][v], up = acc[i][2][v];
+                    const float h0 = swiglu_f32(gt, up) * pr;
+                    gt = acc[i][1][v]; up = acc[i][3][v];
+                    const float h1 = swiglu_f32(gt, up) * pr;
+                    const float amax = row16_max(fmaxf(fabsf(h0), fabsf(h1)));
+                    const int e8 = e8m0_exponent(amax);
+                    const float inv = e8 == 127 ? __uint_as_float(1u << 22)
+                                                : __uint_as_float((uint32_t)(127 - e8) << 23);
+                    int ea = (128 * wm + lr) * 128 + 32 * (wn ^ ekg) + 2 * er16;
+                    asm volatile("" : "+v"(ea));
+                    *(uint16_t*)(st1 + ea) = (uint16_t)cvt_e4m3x2(h0 * inv, h1 * inv);
+                    if (er16 == 4 * (i & 3) + v) sc[i >> 2] = (uint32_t)(e8 + 127);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
+            // scale bytes [row][F / 32]: one per row and interleave block
+            {
+                const __amdgpu_buffer_rsrc_t srr = __builtin_amdgcn_make_buffer_rsrc(
+                    (void*)(g.out_scale + (int64_t)row0 * FB), (short)0, rows * FB, kMxRsrcWord3);
+                const bool cols = c0 < g.N;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int r = 128 * wm + 16 * (4 * h + (er16 >> 2)) + 4 * ekg + (er16 & 3);
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc[h], srr,
+                                                         cols ? r * FB + cb0 + wn : 0x7ffffff0, 0, 0);
+                }
+            }
+            // codes: every wave's segments are in; a thread takes two (row,
+            // segment) items and stores each as two 16-byte pieces (the
+            // segment's even bytes are columns 0 .. 15, its odd bytes 16 .. 31)
+            __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0)
+            __builtin_amdgcn_s_barrier();
+            const __amdgpu_buffer_rsrc_t orr = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)((uint8_t*)g.out + (int64_t)row0 * F), (short)0, rows * F, kMxRsrcWord3);
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int item = 64 * wid + elane + 512 * k;
+                const int r = item >> 2, w = item & 3;
+                const char* seg = st1 + r * 128 + 32 * (w ^ ((r >> 2) & 3));
+                const uint4 d0 = *(const uint4*)seg, d1 = *(const uint4*)(seg + 16);
+                const mx_u32x4 lo{__builtin_amdgcn_perm(d0.y, d0.x, 0x06040200u),
+                                  __builtin_amdgcn_perm(d0.w, d0.z, 0x06040200u),
+                                  __builtin_amdgcn_perm(d1.y, d1.x, 0x06040200u),
+                                  __builtin_amdgcn_perm(d1.w, d1.z, 0x06040200u)};
+                const mx_u32x4 hi{__builtin_amdgcn_perm(d0.y, d0.x, 0x07050301u),
+                                  __builtin_amdgcn_perm(d0.w, d0.z, 0x07050301u),
+                                  __builtin_amdgcn_perm(d1.y, d1.x, 0x07050301u),
+                                  __builtin_amdgcn_perm(d1.w, d1.z, 0x07050301u)};
+                const int off = (cb0 + w) * 64 < g.N ? r * F + (cb0 + w) * 32 : 0x7ffffff0;
+                __builtin_amdgcn_raw_buffer_store_b128(lo, orr, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(hi, orr, off + 16, 0, 0);
+            }
+        } else {
+            // 32 rows x 64 fp32 at a time in the wave's region, rows of 256
+            // bytes, 64-byte column groups at group ^ ((row / 4) mod 4)
+            char* const ep = st1 + wid * kMxEpiWave;
+            const __amdgpu_buffer_rsrc_t orr = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)((float*)g.out + (int64_t)row0 * g.N), (short)0, rows * g.N * 4, kMxRsrcWord3);
+            const int c = er16;
+            const int col = c0 + 4 * c;              // this lane's 4 stored columns
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const int lr = 16 * ii + 4 * ekg + v;
+                            *(float*)(ep + lr * 256 + ((64 * j + 4 * er16) ^ (64 * ekg))) = acc[2 * p + ii][j][v];
+                        }
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int lr = ekg + 4 * k;
+                    const mx_u32x4 val = *(const mx_u32x4*)(ep + lr * 256 + ((16 * c) ^ (64 * ((lr >> 2) & 3))));
+                    const int off = col < g.N ? ((128 * wm + 32 * p + lr) * g.N + col) * 4 : 0x7ffffff0;
+                    __builtin_amdgcn_raw_buffer_store_b128(val, orr, off, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
+        if (!more) {
+            MX_WAIT_VMCNT(0);          // the repeated loads land before the LDS is released
+            break;
+        }
+        tile = next;
     }
 }
 

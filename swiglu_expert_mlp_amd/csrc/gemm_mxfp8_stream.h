@@ -142,13 +142,11 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs& g, int e, int row
                     // the 16 lanes of one requantization block hold one row: one probability
                     const float pr = (PROB && r < rows) ? fc1_row_prob(g.row_prob, g.perm_src, row0 + r) : 1.0f;
                     float gt = acc[rg][0][i], up = acc[rg][2][i];
-                    h0 = gt / (1.0f + __expf(-gt)) * up * pr;
+                    h0 = swiglu_f32(gt, up) * pr;
                     gt = acc[rg][1][i]; up = acc[rg][3][i];
-                    h1 = gt / (1.0f + __expf(-gt)) * up * pr;
+                    h1 = swiglu_f32(gt, up) * pr;
                 }
-                float amax = fmaxf(fabsf(h0), fabsf(h1));
-#pragma unroll
-                for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+                const float amax = row16_max(fmaxf(fabsf(h0), fabsf(h1)));
                 int e8 = e8m0_exponent(amax);
                 float inv = e8 == 127 ? __uint_as_float(1u << 22)
                                       : __uint_as_float((uint32_t)(127 - e8) << 23);

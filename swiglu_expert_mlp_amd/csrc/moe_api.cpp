@@ -400,7 +400,11 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         g1.K = H;
         g1.topk = h->k;
         g1.n_tiles_n = ((2 * F / 64) + 3) / 4;
-        g1.stream_big = H % 128 != 0;
+        // the 256-row LDS-staged tiles take K multiples of 128 and address their
+        // operands with 32-bit buffer offsets (activation rows x K, one expert's
+        // weight section); other shapes go to the streaming tiles
+        g1.stream_big = H % 128 != 0 || T_cap * H >= ((int64_t)1 << 31) ||
+                        (int64_t)2 * F * H >= ((int64_t)1 << 31);
         g1.small_batch = T_cap <= 1024;
         g1.a_bytes = T_cap * H;
         g1.row_prob = fc1_topk ? (const float*)(w + L.sorted_probs) : nullptr;
@@ -417,7 +421,7 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         g2.N = H;
         g2.K = F;
         g2.n_tiles_n = ((H + 63) / 64 + 3) / 4;
-        g2.stream_big = F % 128 != 0;
+        g2.stream_big = F % 128 != 0 || (int64_t)H * F >= ((int64_t)1 << 31);
         g2.a_bytes = T_cap * h->k * F;
         g2.row_prob = nullptr;
         e = launch_gemm_mxfp8(false, w4, g2, h->num_cu, stream, nullptr, nullptr);
