@@ -21,10 +21,11 @@
 //  * weight codes: the kernel-weight buffer holds 2 KB blocks (16 columns x
 //    128 K, two 1 KB halves in MFMA lane order), moved into LDS as they are.
 //    W4 (MXFP4 weights, E2M1 B format): 1 KB blocks, half of the B region.
-//  * activation scales: the step's 4 scale bytes of each of the 256 rows, one
-//    dword per lane (rows are 4-byte aligned because K is a multiple of 128),
-//    placed so that the 8 row groups of a fragment lane are 8 consecutive
-//    dwords (tile row 128 m + 16 i + r at dword (16 m + r) * 8 + i).
+//  * activation scales: in chunks of 8 K steps (a row's 32 scale bytes, one
+//    16-byte load per lane, row r at r * 32), double buffered beside the
+//    stages; a chunk is loaded while the one before it is in use.  (A 4-byte
+//    load of every row at every step had each step request 256 cache lines
+//    for 1 KB of scales: 55 us of a 630 us FC1 at 16K tokens.)
 //  * weight scales: the 256-byte group (4 steps of one 16-column block) of
 //    the kernel-weight buffer that holds the step, for each column block.
 //
@@ -42,10 +43,13 @@ namespace moe {
 
 constexpr int kMxBigBM = 256;
 constexpr int kMxBigBN = 256;
-// one stage: A codes 32 KB | B codes 32 KB | A scales 1 KB (waves 0-3) | the
-// dropped A-scale loads of waves 4-7 1 KB | B scales 4 KB
-constexpr int kMxStage = 70 * 1024;
-constexpr int kMxAsOff = 64 * 1024, kMxBsOff = 66 * 1024;
+// one stage: A codes 32 KB | B codes 32 KB | B scales 4 KB
+constexpr int kMxStage = 68 * 1024;
+constexpr int kMxBsOff = 64 * 1024;
+// activation scales: two 8 KB chunk buffers (256 rows x 32 bytes) and a 1 KB
+// landing area for the scale loads of the steps that start no chunk
+constexpr int kMxScChunk = 8 * 1024;
+constexpr int kMxScBytes = 2 * kMxScChunk + 1024;
 
 typedef __attribute__((address_space(3))) void mx_lds_void;
 
@@ -102,6 +106,7 @@ __device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
     // and does not drain the loads in flight
     __shared__ __attribute__((aligned(1024))) char st0[kMxStage];
     __shared__ __attribute__((aligned(1024))) char st1[kMxStage];
+    __shared__ __attribute__((aligned(1024))) char scl[kMxScBytes];
     const int n_mt = g.hdr->n_tiles_big;
     const int NT = (g.N + kMxBigBN - 1) / kMxBigBN;
     const int total = n_mt * NT;
@@ -109,15 +114,10 @@ __device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
     // wave-uniform: scalar registers for everything derived from the wave index
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // 8 waves
     const int wm = wid >> 2, wn = wid & 3;                               // 2 x 4 waves
-    const int r16 = lane & 15, kg = lane >> 4;
     const int K = g.K, KB = K / 32;
     const int KS = K / 128, KQ = (KS + 3) / 4;
     const int nt16 = g.N / 16;
 
-    // fragment offsets inside a 16-row activation group (2 KB): first and
-    // second 16-byte K chunk of the lane's row
-    const int a_lo = r16 * 128 + ((kg ^ (r16 & 7)) << 4);
-    const int a_hi = r16 * 128 + (((kg + 4) ^ (r16 & 7)) << 4);
 
     const int xcd = blockIdx.x & 7, per_xcd = gridDim.x >> 3;
     const int chunk = (total + 7) / 8;
@@ -148,22 +148,26 @@ __device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
     // loop (the instruction's immediate offset would move the LDS destination
     // too, so it stays 0).
     __amdgpu_buffer_rsrc_t ar, asr, wr, wsr;
-    int aoff[4], soff;           // per lane: activation rows (codes, scales)
+    int aoff[4], soff;           // per lane: activation rows (codes; scales of row (64 wid + lane) / 2)
     int woff[2], wstep[2];       // the wave's two weight column blocks: K step 0, bytes per K step
     int qoff[2], qstep[2];       // their scale groups: step 0, bytes per 4 steps
-    const int lane16 = 16 * lane, lane4 = 4 * lane;
     const __amdgpu_buffer_rsrc_t anone = __builtin_amdgcn_make_buffer_rsrc(g.out, (short)0, 0, kMxRsrcWord3);
     auto sources = [&](const MxPos& p) {
         const int lane = mx_lane_fresh();
         // activation code loads: blocks 4 wid + i (8 rows each); lane -> row
         // 8 j + lane / 8, LDS position lane % 8 <- chunk (lane % 8) ^ (row % 8);
-        // activation scale loads (waves 0-3 real, 4-7 dropped): dword q = 64
-        // (wid mod 4) + lane holds tile row 128 (q / 128) + 16 (q % 8) + (q / 8)
-        // % 16, 4 bytes per step.  FC1 gathers the rows: all five row lookups
-        // go out before any is used (one round trip, not five).
+        // activation scale loads: thread 64 wid + lane loads half lane % 2 of
+        // tile row (64 wid + lane) / 2's chunk (16 of its 32 bytes).  FC1
+        // gathers the rows: all five row lookups go out before any is used (one
+        // round trip, not five).
         const int64_t abase = FC1 ? 0 : (int64_t)p.row0;
         ar = __builtin_amdgcn_make_buffer_rsrc((void*)(g.A + abase * K), (short)0, 0x7fffffff, kMxRsrcWord3);
-        asr = __builtin_amdgcn_make_buffer_rsrc((void*)(g.As + abase * KB), (short)0, 0x7fffffff, kMxRsrcWord3);
+        // the scale range ends exactly at the scale tensor's end: the last
+        // chunk of a row whose K is not a multiple of 8 steps reads on into the
+        // next row (never used), and past the last row the range check drops it
+        const int64_t sc_left = g.a_bytes / 32 - abase * KB;
+        asr = __builtin_amdgcn_make_buffer_rsrc((void*)(g.As + abase * KB), (short)0,
+                                                (int)(sc_left < 0x7fffffff ? sc_left : 0x7fffffff), kMxRsrcWord3);
         int src[5];
 #pragma unroll
         for (int i = 0; i < 5; ++i) {
@@ -171,8 +175,7 @@ __device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
             if (i < 4) {
                 rr = 8 * (4 * wid + i) + (lane >> 3);
             } else {
-                const int q = 64 * (wid & 3) + lane;
-                rr = 128 * (q >> 7) + 16 * (q & 7) + ((q >> 3) & 15);
+                rr = (64 * wid + lane) >> 1;
             }
             src[i] = rr < p.rows ? rr : p.rows - 1;
             if constexpr (FC1) src[i] = g.perm_src[p.row0 + src[i]];
@@ -184,7 +187,7 @@ __device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
                 const int rr = 8 * (4 * wid + i) + (lane >> 3);
                 aoff[i] = src[i] * K + 16 * ((lane & 7) ^ (rr & 7));
             } else {
-                soff = src[i] * KB;
+                soff = src[i] * KB + 16 * (lane & 1);
             }
         }
         // weight code and scale loads: column blocks 2 wid + i of the expert's
@@ -211,9 +214,10 @@ __device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
             }
         }
     };
-    // loads of step s into stage Q
-    auto issue = [&](auto QC, int s) {
+    // loads of step s into stage Q (fl: the lane index)
+    auto issue = [&](auto QC, int s, int fl) {
         constexpr int Q = decltype(QC)::value;
+        const int lane16 = 16 * fl, lane4 = 4 * fl;
         char* st = (Q & 1) ? st1 : st0;
         // the weights' cache policy: FC2's non-temporal (measured at 16K tokens:
         // FC2 466 -> 447 us); FC1, whose row tiles reuse a weight slice through
@@ -237,17 +241,29 @@ __device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
                         wr, (mx_lds_void*)(st + 32768 + ((2 * wid + i) * 2 + h) * 1024), 16, lane16,
                         woff[i] + s * 2048 + h * 1024, 0, wpol);
         }
-        // waves 4-7 issue the same load through an empty descriptor (the range
-        // check drops it) into an unused area of the stage: no branch, every
-        // wave counts the same loads, and the destination stays inside one LDS
-        // object (a destination chosen between objects makes the compiler wait
-        // for every direct load before any later LDS access)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wid < 4 ? asr : anone,
-                                                 (mx_lds_void*)(st + kMxAsOff + 256 * wid), 4, soff, 4 * s, 0, 0);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(wsr, (mx_lds_void*)(st + kMxBsOff + (2 * wid + i) * 256), 4,
                                                      lane4, qoff[i] + (s >> 2) * qstep[i], 0, 0);
+    };
+    // the activation-scale load of K step s: chunk c = s / 8 + 1 (into buffer
+    // c mod 2) when s starts chunk s / 8 and chunk c exists; otherwise the
+    // same load through an empty descriptor (the range check drops it) into
+    // the landing area.  No branch: a branch around it made the compiler
+    // wait for the previous tile's stores before the first step's fragment
+    // reads, and this form measured no slower.  The destination stays inside
+    // one LDS object, its offset through an opaque copy (as a choice between
+    // two pointers the compiler can no longer tell it apart from the stages
+    // and waits for every direct load before any later LDS access).  The
+    // tile's first chunk goes out with its first stage.
+    const int nch = (KS + 7) >> 3;
+    auto issue_scales = [&](bool first, int s) {
+        const int c = first ? 0 : (s >> 3) + 1;
+        const bool real = first || ((s & 7) == 0 && c < nch);
+        int dst = real ? (c & 1) * kMxScChunk + 1024 * wid : 2 * kMxScChunk;
+        asm volatile("" : "+s"(dst));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(real ? asr : anone, (mx_lds_void*)(scl + dst), 16, soff, 32 * c,
+                                                 0, 0);
     };
 
     f32x4 acc[8][4];
@@ -262,10 +278,18 @@ __device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
         constexpr int AFTER = decltype(AC)::value;
         MX_WAIT_VMCNT(AFTER);
         __builtin_amdgcn_s_barrier();
+        // per-lane offsets from a fresh lane index (kept across the steps they
+        // would take registers the K loop needs)
+        const int fl = mx_lane_fresh();
+        const int r16 = fl & 15, kg = fl >> 4;
+        // fragment offsets inside a 16-row activation group (2 KB): first and
+        // second 16-byte K chunk of the lane's row
+        const int a_lo = r16 * 128 + ((kg ^ (r16 & 7)) << 4);
+        const int a_hi = r16 * 128 + (((kg + 4) ^ (r16 & 7)) << 4);
         const char* As = P ? st1 : st0;
-        const char* Bs = As + 32768 + 16 * lane;
-        const char* Sa = As + kMxAsOff + (16 * wm + r16) * 32;
-        const uint8_t* Sb = (const uint8_t*)As + kMxBsOff + 4 * lane + (s & 3);
+        const char* Bs = As + 32768 + 16 * fl;
+        const char* Sa = scl + ((s >> 3) & 1) * kMxScChunk + (128 * wm + r16) * 32 + (s & 7) * 4;
+        const uint8_t* Sb = (const uint8_t*)As + kMxBsOff + 4 * fl + (s & 3);
         // the weight fragments and all scales are read before the next
         // stage's loads are issued
         i32x8 b[4];
@@ -279,11 +303,12 @@ __device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
                                 *(const uint4*)(Bs + (4 * wn + ct) * 2048 + 1024));
             sb[ct] = Sb[(4 * wn + ct) * 256];
         }
-        const uint4 sa_lo = *(const uint4*)Sa, sa_hi = *(const uint4*)(Sa + 16);
-        if (s + 1 < kst) issue(std::integral_constant<int, P ^ 1>{}, s + 1);
-        const uint32_t sad[8] = {sa_lo.x, sa_lo.y, sa_lo.z, sa_lo.w,
-                                 sa_hi.x, sa_hi.y, sa_hi.z, sa_hi.w};
-        // FC1: activation fragments in four groups of two, each group's reads
+        uint32_t sad[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sad[i] = *(const uint32_t*)(Sa + 512 * i);   // tile row + 16 i
+        if (s + 1 < kst) issue(std::integral_constant<int, P ^ 1>{}, s + 1, fl);
+        issue_scales(false, s);
+        // activation fragments in four groups of two, each group's reads
         // issued while the previous group's MFMAs run; the explicit
         // lgkmcnt(0) before a group's reads is what tells the compiler that
         // the previous group has landed (after the direct loads above it
@@ -308,34 +333,20 @@ __device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
                         src[q], b[ct], acc[i][ct], 0, W4 ? 4 : 0, 0, sa, 0, sb[ct]);
             }
         };
-        if constexpr (FC1) {
-            read_group(0, af[0]);
+        read_group(0, af[0]);
 #pragma unroll
-            for (int gr = 0; gr < 4; ++gr) {
-                __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): group gr is in
-                if (gr + 1 < 4) read_group(gr + 1, af[(gr + 1) & 1]);
-                mfma_group(gr, af[gr & 1]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        } else {
-            // FC2 is bound by its loads and output stores; the grouped reads
-            // only added register spills there
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const char* ag = As + (8 * wm + i) * 2048;
-                const i32x8 a = mx_frag(*(const uint4*)(ag + a_lo), *(const uint4*)(ag + a_hi));
-                const int sa = (int)((sad[i] >> (8 * kg)) & 0xffu);
-#pragma unroll
-                for (int ct = 0; ct < 4; ++ct)
-                    acc[i][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        a, b[ct], acc[i][ct], 0, W4 ? 4 : 0, 0, sa, 0, sb[ct]);
-            }
+        for (int gr = 0; gr < 4; ++gr) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): group gr is in
+            if (gr + 1 < 4) read_group(gr + 1, af[(gr + 1) & 1]);
+            mfma_group(gr, af[gr & 1]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
     MxPos pos = locate(tile);
     sources(pos);
-    issue(std::integral_constant<int, 0>{}, 0);
+    issue(std::integral_constant<int, 0>{}, 0, lane);
+    issue_scales(true, 0);
     // the first tile's first wait counts the previous epilogue's stores too:
     // before the first tile the same number of stores go to an empty
     // descriptor (the range check drops them; distinct offsets, so that none
@@ -390,7 +401,8 @@ __device__ __forceinline__ void mx_lds_tiles(const MxGemmArgs& g)
             pos = locate(next);
             sources(pos);
         }
-        issue(I0{}, 0);
+        issue(I0{}, 0, mx_lane_fresh());
+        issue_scales(true, 0);
         __builtin_amdgcn_sched_barrier(0);
 
         // epilogue: lane holds rows 16 i + 4 (lane / 16) + v of the wave's 128
