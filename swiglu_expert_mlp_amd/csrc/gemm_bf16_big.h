@@ -421,7 +421,12 @@ __device__ __forceinline__ void big_tiles(const GemmArgs& g, int n_mt)
                     const int rr = 8 * (v >> 2) + 4 * hi + (v & 3);
                     float h = swiglu_f32(acc[i][0][v], acc[i][1][v]);
                     if constexpr (PROB) h *= pw[32 * i + rr];
-                    *(uint16_t*)(ep + ((rr * 64 + 2 * c32) ^ (((rr >> 2) & 1) << 6))) = f32_to_bf16_bits(h);
+                    // (the offset through an opaque copy: a 16-bit LDS store whose
+                    // constant part the compiler folds into the instruction made
+                    // it wait for the next tile's direct loads first)
+                    int ea = (rr * 64 + 2 * c32) ^ (((rr >> 2) & 1) << 6);
+                    asm volatile("" : "+v"(ea));
+                    *(uint16_t*)(ep + ea) = f32_to_bf16_bits(h);
                 }
                 static_assert(big_stores<true>() == 4 * 2, "4 row blocks x 2 stores");
 #pragma unroll
