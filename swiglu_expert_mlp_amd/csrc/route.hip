@@ -16,45 +16,31 @@
 
 namespace moe {
 
-// (value, id) order of the selection: larger value first, equal values go to
-// the smaller id.
-__device__ __forceinline__ bool ahead(float ov, int oid, float v, int id)
+// Order-preserving integer key of a logit: a larger logit has a larger key;
+// -0 and +0 share one key (they compare equal); NaN gets key 0, below every
+// number (-inf is 0x007fffff), as does the padding past E.
+__device__ __forceinline__ uint32_t route_key(float v)
 {
-    return ov > v || (ov == v && oid < id);
+    uint32_t b = __float_as_uint(v);
+    if (b == 0x80000000u) b = 0u;
+    const uint32_t key = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return v != v ? 0u : key;
 }
 
-template <int CTRL>
-__device__ __forceinline__ void dpp_amax_step(float& v, int& id)
+// lanes below this one with their bit set in mask
+__device__ __forceinline__ int lanes_below(uint64_t mask)
 {
-    const float ov = __builtin_bit_cast(float,
-        __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-    const int oid = __builtin_amdgcn_mov_dpp(id, CTRL, 0xF, 0xF, false);
-    if (ahead(ov, oid, v, id)) { v = ov; id = oid; }
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Wave-wide argmax of (value, id).  Within each 16-lane row: DPP exchanges
-// (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror),
-// after which every lane of a row holds the row's winner; the four row
-// winners are then combined from lanes 0, 16, 32, 48.  The result is
-// wave-uniform.
-__device__ __forceinline__ void wave_argmax(float& v, int& id)
-{
-    dpp_amax_step<0xB1>(v, id);
-    dpp_amax_step<0x4E>(v, id);
-    dpp_amax_step<0x141>(v, id);
-    dpp_amax_step<0x140>(v, id);
-    float bv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-    int bid = __builtin_amdgcn_readlane(id, 0);
-#pragma unroll
-    for (int r = 16; r < 64; r += 16) {
-        const float ov = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), r));
-        const int oid = __builtin_amdgcn_readlane(id, r);
-        if (ahead(ov, oid, bv, bid)) { bv = ov; bid = oid; }
-    }
-    v = bv;
-    id = bid;
-}
-
+// Selection: the top k of (logit, id) in the order larger logit first, equal
+// logits by the smaller id.  The k-th largest key T is found bit by bit (the
+// largest T with at least k keys >= T: 32 compare-and-count steps, the counts
+// from the wave's comparison masks); keys above T are taken, and of the keys
+// equal to T the smallest ids fill the remaining places.  Ids run in the
+// order (i, lane), e = lane + 64 i, so a prefix count over the masks gives both
+// the tie rank and the output position (ascending id).
 template <int PER_LANE>
 __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ logits,
                                                     int64_t T_cap, const int32_t* __restrict__ live_ptr,
@@ -62,55 +48,71 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ lo
                                                     float* __restrict__ probs,
                                                     WsHeader* __restrict__ hdr)
 {
+    __shared__ int32_t sel_id[4][kMaxTopk];
+    __shared__ float sel_z[4][kMaxTopk];
     const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x / kWave;
     const int32_t live = *live_ptr;
     const int64_t T = live < 0 ? 0 : (live > T_cap ? T_cap : live);
     if (blockIdx.x == 0 && threadIdx.x == 0 && hdr != nullptr)
         hdr->err = (live < 0 ? kErrLiveNeg : 0u) | (live > T_cap ? kErrLiveHigh : 0u);
 
-    const int64_t wave0 = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int64_t wave0 = (int64_t)blockIdx.x * (blockDim.x / kWave) + wv;
     const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
     for (int64_t t = wave0; t < T; t += nwaves) {
         const float* row = logits + t * E;
         float l[PER_LANE];
-        bool taken[PER_LANE];
+        uint32_t key[PER_LANE];
+        float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < PER_LANE; ++i) {
-            int e = lane + kWave * i;
+            const int e = lane + kWave * i;
             l[i] = e < E ? row[e] : -INFINITY;
-            taken[i] = e >= E;
+            key[i] = e < E ? route_key(l[i]) : 0u;
+            if (e < E) mx = fmaxf(mx, l[i]);
         }
-        // k rounds of argmax over the experts not yet taken; lane j keeps the
-        // j-th winner (descending logit)
-        int my_id = 0x7fffffff;
-        float my_v = -INFINITY, m = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < kMaxTopk; ++j) {
-            if (j >= k) continue;
-            float bv = -INFINITY;
-            int bid = 0x7fffffff;
-#pragma unroll
-            for (int i = 0; i < PER_LANE; ++i) {
-                int e = lane + kWave * i;
-                if (!taken[i] && ahead(l[i], e, bv, bid)) { bv = l[i]; bid = e; }
-            }
-            wave_argmax(bv, bid);
-            if (j == 0) m = bv;                       // the largest logit
-            if (lane == j) { my_id = bid; my_v = bv; }
+        uint32_t thr = 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = thr | (1u << bit);
+            int cnt = 0;
 #pragma unroll
             for (int i = 0; i < PER_LANE; ++i)
-                if (lane + kWave * i == bid) taken[i] = true;
+                cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[i] >= cand));
+            if (cnt >= k) thr = cand;
         }
-        // canonical order: the rank of lane j's id among the k selected ids;
-        // lane j's pair moves to lane rank_j (ids are distinct)
-        int rank = 0;
+        int above = 0;
 #pragma unroll
-        for (int i = 0; i < kMaxTopk; ++i)
-            if (i < k && __builtin_amdgcn_readlane(my_id, i) < my_id) ++rank;
-        const float z = lane < k ? expf(my_v - m) : 0.0f;
-        const int dest = (lane < k ? rank : lane) * 4;
-        const int c_id = __builtin_amdgcn_ds_permute(dest, my_id);
-        const float c_z = __builtin_bit_cast(float, __builtin_amdgcn_ds_permute(dest, __builtin_bit_cast(int, z)));
+        for (int i = 0; i < PER_LANE; ++i)
+            above += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[i] > thr));
+        const int need = k - above;
+        bool sel[PER_LANE];
+        int before = 0;
+#pragma unroll
+        for (int i = 0; i < PER_LANE; ++i) {
+            const uint64_t eq = __builtin_amdgcn_ballot_w64(key[i] == thr);
+            sel[i] = key[i] > thr || (key[i] == thr && before + lanes_below(eq) < need);
+            before += __builtin_popcountll(eq);
+        }
+        // the largest logit (no selected logit is NaN unless fewer than k are numbers)
+        mx = row16_max(mx);
+        float m = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), 0));
+#pragma unroll
+        for (int r = 16; r < 64; r += 16)
+            m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), r)));
+        // each selected route to its place in ascending-id order
+        before = 0;
+#pragma unroll
+        for (int i = 0; i < PER_LANE; ++i) {
+            const uint64_t sm = __builtin_amdgcn_ballot_w64(sel[i]);
+            if (sel[i]) {
+                const int pos = before + lanes_below(sm);
+                sel_id[wv][pos] = lane + kWave * i;
+                sel_z[wv][pos] = expf(l[i] - m);
+            }
+            before += __builtin_popcountll(sm);
+        }
+        const int c_id = lane < k ? sel_id[wv][lane] : 0;
+        const float c_z = lane < k ? sel_z[wv][lane] : 0.0f;
         // the selected mass, summed in ascending-id order
         float S = 0.0f;
 #pragma unroll
