@@ -107,6 +107,30 @@ def test_64_row_and_256_row_tiles_agree_bitwise(name):
         assert np.array_equal(bits(part), wide[t0:t0 + 128]), f"tokens {t0}.."
 
 
+@pytest.mark.parametrize("precision", ["mxfp8", "mxfp4"])
+def test_partial_scale_chunk_shapes_agree_bitwise(precision):
+    """Hidden 1280 and FFN 1152 are 10 and 9 K steps of 128: the 256-row MX
+    tiles load the activation scales in chunks of 8 steps, so both GEMMs end
+    on a partial chunk.  Experts with more than 128 rows (256-row tiles) and
+    the same tokens in launches of 128 (every expert on the 64-row tiles, which
+    take no chunks) must give the same bits."""
+    from swiglu_expert_mlp_amd import MoE
+    w = Workload("mx_chunks", 2048, 2048, 1280, 1152, 64, 4, precision)
+    c = Case(w, seed=17, outliers=True)
+    m = MoE(w.E, w.H, w.F, w.k, w.precision)
+    w1, w2 = c.weights_dev()
+    m.load_weights(w1, w2)
+    x, ids, probs = c.dev()
+    wide, ws = forward(m, x, ids, probs, w.T)
+    counts = m.get_indices(ws, w.T)["counts"]
+    assert (counts > 128).sum() > 10, counts
+    wide = bits(wide)
+    for t0 in range(0, w.T, 128):
+        part, _ = forward(m, x[t0:t0 + 128].contiguous(), ids[t0:t0 + 128].contiguous(),
+                          probs[t0:t0 + 128].contiguous(), 128)
+        assert np.array_equal(bits(part), wide[t0:t0 + 128]), f"tokens {t0}.."
+
+
 def test_mxfp4_small_capacity_runs_large_experts_as_64_row_tiles_bitwise():
     """MXFP4 at a token capacity <= 1024 runs experts with more than 128 rows as
     four 64-row tiles each (one launch); at a larger capacity they take the

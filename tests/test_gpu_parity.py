@@ -212,6 +212,31 @@ def test_route_ties_go_to_lower_id():
     np.testing.assert_allclose(probs.cpu().numpy(), rp, rtol=2e-6)
 
 
+@pytest.mark.parametrize("E,k", [(40, 5), (200, 16), (1024, 16)])
+def test_route_edge_values_and_threshold_ties(E, k):
+    """Logits drawn from a handful of values (many ties at the k-th place),
+    with -0 and +0, subnormals of both signs and -inf among them; E not a
+    multiple of the wave width except for 1024.  Ids must match the oracle's
+    sort on (-logit, id) bit for bit (-0 and +0 compare equal there too)."""
+    T = 96
+    rng = np.random.default_rng(E + k)
+    # three larger logits per row, the rest from small sets, so that the k-th
+    # place falls among the zeros (even rows) or the positive subnormals (odd)
+    lo_a = np.array([0.0, -0.0, -1e-40, -2.0, -np.inf], np.float32)
+    lo_b = np.array([1e-40, 1e-40, 0.0, -0.0, -1e-40, -np.inf], np.float32)
+    lg = np.where((np.arange(T) % 2 == 0)[:, None], rng.choice(lo_a, size=(T, E)),
+                  rng.choice(lo_b, size=(T, E))).astype(np.float32)
+    for t in range(T):
+        a, b = rng.choice(E, size=2, replace=False)
+        lg[t, a], lg[t, b] = 7.0, 3.25
+    lg[:, E // 2] = np.float32(0.5)            # every row has a finite largest logit
+    moe = _moe()(E, 32, 32, k, "bf16")
+    ids, probs = moe.route(torch.from_numpy(lg).cuda(), live_tensor(T))
+    ri, rp, _ = oracle.route(lg, T, k)
+    assert np.array_equal(ids.cpu().numpy(), ri)
+    np.testing.assert_allclose(probs.cpu().numpy(), rp, rtol=2e-6, atol=1e-30)
+
+
 # ------------------------------------------------------------------ permutation
 
 @pytest.mark.parametrize("name", ["tiny", "decode_T64", "logprob_T128", "bounded_T40_cap512",
