@@ -124,15 +124,29 @@ __device__ void prep_finish(const PrepArgs& a, int T, int nch, int32_t live, int
             for (int i = threadIdx.x; i < nc * E; i += blockDim.x)
                 slab[i] = __builtin_nontemporal_load(&g[i]);
             __syncthreads();
+            // eight chunks' counts read before any is replaced (one LDS round
+            // trip per eight chunks instead of one per chunk)
 #pragma unroll
             for (int q = 0; q < PER; ++q) {
                 const int e = threadIdx.x * PER + q;
-                if (e < E)
-                    for (int c = 0; c < nc; ++c) {
+                if (e < E) {
+                    int c = 0;
+                    for (; c + 8 <= nc; c += 8) {
+                        int v[8];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) v[j] = slab[(c + j) * E + e];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            slab[(c + j) * E + e] = cnt[q];
+                            cnt[q] += v[j];
+                        }
+                    }
+                    for (; c < nc; ++c) {
                         const int v = slab[c * E + e];
                         slab[c * E + e] = cnt[q];
                         cnt[q] += v;
                     }
+                }
             }
             __syncthreads();
             for (int i = threadIdx.x; i < nc * E; i += blockDim.x) g[i] = slab[i];
