@@ -131,13 +131,17 @@ class MoE:
         _check(lib().moe_create(E, H, F, topk, _PRECISION[precision], ctypes.byref(h)),
                "moe_create")
         self._h = h
+        # kept on the handle: at interpreter exit the module's globals may be
+        # cleared before the last handle is collected
+        self._destroy = lib().moe_destroy
         self.E, self.H, self.F, self.topk, self.precision = E, H, F, topk, precision
         self.kbuf = None
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and h.value:
-            lib().moe_destroy(h)
+        destroy = getattr(self, "_destroy", None)
+        if h is not None and h.value and destroy is not None:
+            destroy(h)
             self._h = None
 
     # ------------------------------------------------------------- sizes

@@ -157,6 +157,39 @@ def test_mxfp4_small_capacity_runs_large_experts_as_64_row_tiles_bitwise():
     assert np.all(large[w.T:] == SENTINEL_BITS)
 
 
+def test_mxfp4_fc2_streaming_64_row_tiles_past_2gib_bitwise():
+    """The 64-row MXFP4 LDS-staged kernel addresses its activation codes with
+    32-bit byte offsets, so FC2's 64-row tiles go to the streaming tiles once
+    the SwiGLU buffer (capacity x top-k x FFN bytes) reaches 2 GiB, with K
+    (= FFN 1024) still a multiple of 128.  The same 2048 live tokens at
+    capacity 2048 (LDS-staged) and 2^20 + 64 (streaming) give the same bits."""
+    from swiglu_expert_mlp_amd import MoE
+    w = Workload("mx4_w2g", 2048, 2048, 128, 1024, 32, 2, "mxfp4")
+    c = Case(w, seed=19, outliers=True)
+    m = MoE(w.E, w.H, w.F, w.k, w.precision)
+    w1, w2 = c.weights_dev()
+    m.load_weights(w1, w2)
+    x, ids, probs = c.dev()
+    small, ws = forward(m, x, ids, probs, w.T)
+    counts = m.get_indices(ws, w.T)["counts"]
+    assert ((counts > 0) & (counts <= 128)).sum() >= 2 and (counts > 128).sum() >= 2, counts
+    small = bits(small)
+    del ws
+    cap = (1 << 20) + 64
+    assert cap * w.k * w.F >= 1 << 31 and cap * w.H < 1 << 31
+    xb = torch.full((cap, w.H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    xb[:w.T] = x
+    ib = torch.full((cap, w.k), 0x7FC00000, dtype=torch.int32, device="cuda")
+    ib[:w.T] = ids
+    pb = torch.full((cap, w.k), float("nan"), dtype=torch.float32, device="cuda")
+    pb[:w.T] = probs
+    out, ws = forward(m, xb, ib, pb, w.T)
+    del ws, xb, ib, pb
+    large = bits(out)
+    assert np.array_equal(large[:w.T], small)
+    assert np.all(large[w.T:] == SENTINEL_BITS)
+
+
 @pytest.mark.parametrize("name", ["decode_T300", "mxfp8_T300", "mxfp4_T300"])
 def test_capacity_and_live_count_invariance(name):
     """Same tokens: capacity T vs 4T (rows past live are NaN), and live counts
