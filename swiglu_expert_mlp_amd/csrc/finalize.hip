@@ -9,8 +9,9 @@
 //
 // out[t][m] = fma(p_{k-1}, O[dst[t,k-1]][m], ... fma(p_0, O[dst[t,0]][m], +0.0f))
 // A route with dst < 0 (an invalid expert id) adds nothing.  Rows >= live are
-// neither read nor written.  One workgroup (512 threads) walks tokens; 4
-// columns per thread.
+// neither read nor written.  A workgroup (512 threads) takes a token at a
+// time (one token, or a strided run of tokens: launch_finalize); 4 columns
+// per thread.
 //
 // With sorted_probs == nullptr (the probabilities were applied inside FC1, the
 // MoeEp apply_topk_in_fc1 option of cudnn-frontend PR #448) every p_j is 1:
@@ -102,13 +103,27 @@ hipError_t launch_finalize(const float* O, const int32_t* dst, const float* sort
                            int64_t T_cap, const int32_t* live, int k, int H, int mode, void* out,
                            int num_cu, hipStream_t s)
 {
-    int64_t blocks = T_cap < (int64_t)num_cu * 8 ? T_cap : (int64_t)num_cu * 8;
+    // Two launch shapes, chosen by the capacity (never the live count):
+    //  * capacity above 16 and up to 64 tokens per CU: a workgroup per token,
+    //    at most two resident per CU (the launch asks for 56 KB of dynamic
+    //    LDS, which the kernel does not use, so that only two fit in a CU's
+    //    160 KB);
+    //  * otherwise at most 8 workgroups per CU, each looping over tokens, as
+    //    many resident as the registers allow.
+    // A/B on one MI355X (hidden 2048, us): 16K tokens, top-8: 226.5 -> 206.7
+    // (bf16 FC2 rows; MXFP8 233.6 -> 215); 4,096 tokens 47.2 -> 49.1; a
+    // 65,536-token capacity with 512 live 10.0 -> 16.3 (the 16,384 workgroups
+    // past the live tokens still start and exit, two per CU at a time), which
+    // is why the larger capacities keep the looping grid.
+    const bool per_token = T_cap > (int64_t)num_cu * 16 && T_cap <= (int64_t)num_cu * 64;
+    int64_t blocks = per_token ? T_cap : (T_cap < (int64_t)num_cu * 8 ? T_cap : (int64_t)num_cu * 8);
     if (blocks < 1) blocks = 1;
     const dim3 g((unsigned)blocks), b(512);
+    const unsigned occupancy_lds = per_token ? 56 * 1024 : 0;
     if (mode < 0 || mode > 2) return hipErrorInvalidValue;
 #define FIN_MODE(KK, MM)                                                                     \
-    hipLaunchKernelGGL((finalize_kernel<KK, MM>), g, b, 0, s, O, dst, sorted_probs, T_cap, live, \
-                       H, out)
+    hipLaunchKernelGGL((finalize_kernel<KK, MM>), g, b, occupancy_lds, s, O, dst, sorted_probs, \
+                       T_cap, live, H, out)
 #define FIN_CASE(KK)                                                                         \
     case KK:                                                                                 \
         if (mode == 0) FIN_MODE(KK, 0);                                                      \

@@ -192,23 +192,25 @@ def test_mxfp4_fc2_streaming_64_row_tiles_past_2gib_bitwise():
 
 @pytest.mark.parametrize("name", ["decode_T300", "mxfp8_T300", "mxfp4_T300"])
 def test_capacity_and_live_count_invariance(name):
-    """Same tokens: capacity T vs 4T (rows past live are NaN), and live counts
-    T, 171, 1, 0 at a fixed capacity give the same bits for the live tokens and
-    leave every other output row untouched."""
+    """Same tokens: capacity T vs 4T, 6000 and 20000 (rows past live are NaN;
+    on a 256-CU device the finalize runs a workgroup per token at 6000 and
+    loops over tokens at the others), and live counts T, 171, 1, 0 at a fixed
+    capacity give the same bits for the live tokens and leave every other
+    output row untouched."""
     c, m = case(name), handle(name)
     x, ids, probs = c.dev()
     T = c.w.T
     ref = bits(forward(m, x, ids, probs, T)[0])
-    cap = 4 * T
-    xb = torch.full((cap, c.w.H), float("nan"), dtype=torch.bfloat16, device="cuda")
-    xb[:T] = x
-    ib = torch.full((cap, c.w.k), 0x7FC00000, dtype=torch.int32, device="cuda")
-    ib[:T] = ids
-    pb = torch.full((cap, c.w.k), float("nan"), dtype=torch.float32, device="cuda")
-    pb[:T] = probs
-    got = bits(forward(m, xb, ib, pb, T)[0])
-    assert np.array_equal(got[:T], ref)
-    assert np.all(got[T:] == SENTINEL_BITS)
+    for cap in (4 * T, 6000, 20000):
+        xb = torch.full((cap, c.w.H), float("nan"), dtype=torch.bfloat16, device="cuda")
+        xb[:T] = x
+        ib = torch.full((cap, c.w.k), 0x7FC00000, dtype=torch.int32, device="cuda")
+        ib[:T] = ids
+        pb = torch.full((cap, c.w.k), float("nan"), dtype=torch.float32, device="cuda")
+        pb[:T] = probs
+        got = bits(forward(m, xb, ib, pb, T)[0])
+        assert np.array_equal(got[:T], ref), cap
+        assert np.all(got[T:] == SENTINEL_BITS), cap
     for live in (T, 171, 1, 0):
         got = bits(forward(m, x, ids, probs, live)[0])
         assert np.array_equal(got[:live], ref[:live]), live
