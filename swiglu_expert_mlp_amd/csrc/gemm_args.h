@@ -34,6 +34,19 @@ __device__ __forceinline__ T ld_const(const T* p)
     return *(const __attribute__((address_space(4))) T*)p;
 }
 
+// A persistent 64-row tile loop's first tile; the loop then steps by the grid.
+// Each round of the grid is split into 8 contiguous runs, one per XCD
+// (workgroups are dispatched round-robin over the XCDs; the grid is a multiple
+// of 8), so that the column tiles of one M tile run on one XCD and share its
+// L2: at decode sizes an expert's whole FC1 (and FC2) runs on one XCD, and in
+// the single-launch FFN an FC2 tile waits only for FC1 tiles of its own XCD.
+// Measured (bf16, one MI355X): decode 148.4 -> 146.1 us per forward, a
+// 65,536-token capacity with 512 live 670 -> 655 us.
+__device__ __forceinline__ int xcd_first_tile()
+{
+    return (int)((blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3));
+}
+
 // FC1 with the routes' probabilities applied inside FC1 (row_prob: the
 // canonical probabilities, indexed by route t * k + j): the probability of a
 // grouped row.  The kernels take this path as a compile-time variant (PROB):

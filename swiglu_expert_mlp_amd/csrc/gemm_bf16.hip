@@ -29,7 +29,7 @@ __global__ void __launch_bounds__(512, 1) gemm_bf16_small_kernel(GemmArgs g)
     const int n_big = g.small_takes_big ? ld_const(&g.hdr->n_tiles_big) : 0;
     const int n_small = ld_const(&g.hdr->n_tiles);
     const int multi = ld_const(&g.hdr->multi_tile);
-    const int* te0 = (const int*)(g.tiles + min(small_first_tile() / small_col_tiles(g), g.max_tiles - 1));
+    const int* te0 = (const int*)(g.tiles + min(xcd_first_tile() / small_col_tiles(g), g.max_tiles - 1));
     const int e0 = ld_const(te0), row00 = ld_const(te0 + 1);
     asm volatile("" : : "s"(n_big), "s"(n_small), "s"(multi), "s"(e0), "s"(row00));   // one round trip
     if (multi) small_tiles<FC1, PROB, 0, 0>(g, smem, n_small, n_big, e0, row00);
@@ -54,10 +54,10 @@ __global__ void __launch_bounds__(512, 1) gemm_bf16_fused_kernel(GemmArgs g1, Ge
     const int n_big = ld_const(&g1.hdr->n_tiles_big);
     const int n_small = ld_const(&g1.hdr->n_tiles);
     const int multi = ld_const(&g1.hdr->multi_tile);
-    const int* te0 = (const int*)(g1.tiles + min(small_first_tile() / small_col_tiles(g1), g1.max_tiles - 1));
+    const int* te0 = (const int*)(g1.tiles + min(xcd_first_tile() / small_col_tiles(g1), g1.max_tiles - 1));
     const int e0 = ld_const(te0), row00 = ld_const(te0 + 1);
     asm volatile("" : : "s"(n_big), "s"(n_small), "s"(multi), "s"(e0), "s"(row00));
-    const int* te1 = (const int*)(g2.tiles + min(small_first_tile() / small_col_tiles(g2), g2.max_tiles - 1));
+    const int* te1 = (const int*)(g2.tiles + min(xcd_first_tile() / small_col_tiles(g2), g2.max_tiles - 1));
     if (multi) {
         small_tiles<true, PROB, 1, 0>(g1, smem, n_small, n_big, e0, row00);
         small_tiles<false, false, 2, 0>(g2, smem, n_small, n_big, ld_const(te1), ld_const(te1 + 1),

@@ -63,17 +63,6 @@ __device__ __forceinline__ void wait_vmcnt_upto15(int n)
 
 __device__ __forceinline__ int small_col_tiles(const GemmArgs& g) { return (g.N + kSmallCols - 1) / kSmallCols; }
 
-// A workgroup's first tile; it then steps by the grid.  Each round of the grid
-// is split into 8 contiguous runs, one per XCD (workgroups are dispatched
-// round-robin over the XCDs; the grid is a multiple of 8), so that the column
-// tiles of one M tile run on one XCD and share its L2: at decode sizes an
-// expert's whole FC1 (and FC2) runs on one XCD, and in the single-launch FFN
-// an FC2 tile waits only for FC1 tiles of its own XCD, which run at its
-// speed (the XCDs do not stream weights at the same rate).
-__device__ __forceinline__ int small_first_tile()
-{
-    return (int)((blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3));
-}
 
 // FC1 tile done (single-launch FFN): every wave's stores complete, then one
 // thread releases them at device scope (the L2's dirty lines written back)
@@ -99,7 +88,7 @@ constexpr int kCoherentLoad = 16;               // cache policy sc1 (device-cohe
 // n_small: the number of 64-row M tiles; n_big: the number of 256-row M
 // tiles this launch also runs, as four 64-row tiles each (0 when a launch of
 // the 256-row design takes them); (e0, row00): the table entry of this
-// workgroup's first tile (small_first_tile()), read by the caller before the counts
+// workgroup's first tile (xcd_first_tile()), read by the caller before the counts
 // were known.
 // WPOL: the cache policy of the weight stream (kNonTemporal when every
 // expert's rows fit one 64-row tile, else the default; the caller reads which
@@ -131,7 +120,7 @@ __device__ __forceinline__ void small_tiles(const GemmArgs& g, char* smem, int n
     }
     const int c32 = lane & 31, hi = lane >> 5;
 
-    const int first = small_first_tile();
+    const int first = xcd_first_tile();
     for (int tile = first; tile < total; tile += gridDim.x) {
         const int mt = tile / NTs, ct = tile - mt * NTs;
         int e = e0, row0 = row00;

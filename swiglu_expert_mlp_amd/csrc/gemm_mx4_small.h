@@ -276,7 +276,7 @@ __device__ __forceinline__ void mx4_small_tiles(const MxGemmArgs& g, const Mx4Ri
     rg.w0 += wid * kMx4Slot;
     rg.w1 += wid * kMx4Slot;
     rg.w2 += wid * kMx4Slot;
-    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    for (int tile = xcd_first_tile(); tile < total; tile += gridDim.x) {
         const int mt = tile / NTs, ct = tile - mt * NTs;
         const int* te = mt < n_small ? (const int*)(g.tiles + mt) : (const int*)(g.tiles_big + ((mt - n_small) >> 2));
         const int e = ld_const(te), row0 = ld_const(te + 1) + (mt < n_small ? 0 : kBM * ((mt - n_small) & 3));
