@@ -22,9 +22,10 @@ __global__ void __launch_bounds__(512, 1) gemm_mxfp8_kernel(MxGemmArgs g)
 {
     if (!g.stream_big) mx_lds_tiles<FC1, W4, PROB>(g);
     if (g.lds_small) return;          // the 64-row tiles have a launch of their own
-    // the two halves of a workgroup are workers b and b + grid: consecutive
-    // tiles (the N tiles of one M tile) go to different CUs
-    mx_stream_tiles<FC1, W4, PROB>(g, blockIdx.x + (threadIdx.x >> 8) * gridDim.x, 2 * gridDim.x,
+    // the two halves of a workgroup are workers f and f + grid (f: the
+    // workgroup's XCD-contiguous first tile): consecutive tiles (the N tiles of
+    // one M tile) go to different CUs of one XCD
+    mx_stream_tiles<FC1, W4, PROB>(g, xcd_first_tile() + (threadIdx.x >> 8) * gridDim.x, 2 * gridDim.x,
                                    (threadIdx.x >> 6) & 3);
 }
 
