@@ -296,30 +296,37 @@ def run_workload(name: str, a, cpu_seconds: float, threads1: bool) -> dict:
     ms_step_instrumented = ev.ms(p0, p1) / a.steps
     fc1_us = float(np.mean([ev.ms(p, q) for p, q in fc1_ev]) * 1e3)
 
-    # the single-launch FFN mode (MOE_FUSED_FFN), timed the same way
+    # the single-launch modes, timed the same way: FC1 + FC2 in one launch
+    # (MOE_FUSED_FFN), and FC1 + FC2 + finalize in one launch (MOE_FUSED_FINALIZE)
     fused = None
     if w.precision == "bf16" and name in FUSED_REPORT:
-        fused_fn = [m.bind_forward(x, ids, probs, live, out, ws, combine=a.combine, fused_ffn=True)
-                    for m in moes]
-        for i in range(min(a.warmup, 5)):
-            route_fn[i % n_rot]()
-            fused_fn[i % n_rot]()
-        f0, f1 = ev.new(), ev.new()
-        torch.cuda.synchronize()
-        ev.record(f0, sh)
-        for i in range(a.steps):
-            route_fn[i % n_rot]()
-            fused_fn[i % n_rot]()
-        ev.record(f1, sh)
-        torch.cuda.synchronize()
-        bits = moe0.check(ws)
-        if bits:
-            raise RuntimeError(f"{name}: fused FFN mode: device contract violation bits {bits}")
-        ms_f = ev.ms(f0, f1) / a.steps
-        fused = {"ms_per_step": ms_f, "tokens_per_s": w.T / (ms_f * 1e-3),
-                 "speedup_vs_two_launches": ms_step / ms_f,
-                 "kernel": "moe::gemm_bf16_fused_kernel<false> (every tile as a 64-row tile)"}
-        del fused_fn
+        fused = {}
+        for key, kw in (("ffn", {"fused_ffn": True}), ("ffn_finalize", {"fused_finalize": True})):
+            fused_fn = [m.bind_forward(x, ids, probs, live, out, ws, combine=a.combine, **kw)
+                        for m in moes]
+            for i in range(min(a.warmup, 5)):
+                route_fn[i % n_rot]()
+                fused_fn[i % n_rot]()
+            f0, f1 = ev.new(), ev.new()
+            torch.cuda.synchronize()
+            ev.record(f0, sh)
+            for i in range(a.steps):
+                route_fn[i % n_rot]()
+                fused_fn[i % n_rot]()
+            ev.record(f1, sh)
+            torch.cuda.synchronize()
+            bits = moe0.check(ws)
+            if bits:
+                raise RuntimeError(f"{name}: single-launch {key}: device contract violation bits {bits}")
+            ms_f = ev.ms(f0, f1) / a.steps
+            fin = key == "ffn_finalize"
+            fused[key] = {"ms_per_step": ms_f, "tokens_per_s": w.T / (ms_f * 1e-3),
+                          "speedup_vs_separate_launches": ms_step / ms_f,
+                          "kernel": f"moe::gemm_bf16_fused_kernel<false, {str(fin).lower()}> "
+                                    "(every tile as a 64-row tile"
+                                    + (", the last FC2 tile of a token's 512 columns combines them)"
+                                       if fin else ")")}
+            del fused_fn
 
     # stage breakdown (untimed diagnostic pass)
     n_diag = min(10, a.steps)
@@ -378,7 +385,7 @@ def run_workload(name: str, a, cpu_seconds: float, threads1: bool) -> dict:
         "roofline": roof,
     }
     if fused is not None:
-        res["fused_ffn"] = fused
+        res["single_launch"] = fused
     if w.name == "bounded_decode":
         res["live_tracking"] = live_tracking(w, moes, x, logits, route_fn, fwd_fn, ids, probs, out,
                                              ws, live, sh, n_rot, a.combine)
@@ -427,7 +434,7 @@ def main():
                    "combine": a.combine, "parallelism": "one GPU, all experts local"},
     }
     for key in ("tflops", "mfma_frac", "hbm_gbs_step", "hbm_frac_step", "stages_us", "expert_load",
-                "weight_buffers_rotated", "roofline", "fused_ffn", "live_tracking", "cpu_baseline"):
+                "weight_buffers_rotated", "roofline", "single_launch", "live_tracking", "cpu_baseline"):
         if key in h:
             res[key] = h[key]
     if every:

@@ -207,6 +207,23 @@ typedef enum {
  * are invalid.  With another precision: MOE_ERR_INVALID_ARG. */
 #define MOE_FUSED_FFN 0x200
 
+/* Added to any combine (bf16 weights only; implies MOE_FUSED_FFN): the
+ * finalize runs in the same persistent launch as FC1 and FC2, so the whole
+ * forward after the permutation is one launch (Megatron-LM PR #7830, "What
+ * does this PR do?": dispatch, expert MLP and combine in one fused kernel;
+ * cudnn-frontend PR #448's MegaMoE file list, fc1_fc2_fuse_sched).  The
+ * permutation stage sets, for every live token and 512-column block of the
+ * output, the number of the token's kept routes; an FC2 tile, once its fp32
+ * rows are released at device scope, counts each of its rows' tokens down,
+ * and the workgroup that takes a count to zero combines that token's
+ * 512-column block at once (no workgroup ever waits for another here).  The
+ * combine is the finalize's own arithmetic (the fp32 chain from +0 in
+ * canonical order, its bf16 rounding, or row mode), so outputs are
+ * bit-identical to the separate finalize.  A live token whose routes were all
+ * dropped is written by the permutation stage (+0 in every mode).  Errors as
+ * MOE_FUSED_FFN. */
+#define MOE_FUSED_FINALIZE 0x400
+
 /* moe_forward with a choice of combine; every stage before the combine is
  * moe_forward's, so the FC2 rows are bit-identical across the three (without
  * MOE_APPLY_TOPK_IN_FC1, which changes the FC2 rows).

@@ -39,6 +39,9 @@ COMBINES = {"fp32": 0, "bf16": 1, "rows": 2}
 APPLY_TOPK_IN_FC1 = 0x100
 # added to a combine: FC1 and FC2 in one persistent launch (MOE_FUSED_FFN, bf16)
 FUSED_FFN = 0x200
+# added to a combine: FC1, FC2 and the finalize in one persistent launch
+# (MOE_FUSED_FINALIZE, bf16; implies FUSED_FFN)
+FUSED_FINALIZE = 0x400
 
 # every symbol include/moe.h declares, with its ctypes signature
 _P = ctypes.c_void_p
@@ -206,18 +209,20 @@ class MoE:
         raise ValueError(f"combine must be one of {sorted(COMBINES)}")
 
     @staticmethod
-    def _combine_code(combine: str, topk_in_fc1: bool, fused_ffn: bool = False) -> int:
+    def _combine_code(combine: str, topk_in_fc1: bool, fused_ffn: bool = False,
+                      fused_finalize: bool = False) -> int:
         if combine not in COMBINES:
             raise ValueError(f"combine must be one of {sorted(COMBINES)}")
         return (COMBINES[combine] | (APPLY_TOPK_IN_FC1 if topk_in_fc1 else 0) |
-                (FUSED_FFN if fused_ffn else 0))
+                (FUSED_FFN if fused_ffn else 0) | (FUSED_FINALIZE if fused_finalize else 0))
 
     def forward(self, x, ids, probs, live, out=None, ws=None, stream=None, combine="fp32",
-                topk_in_fc1=False, fused_ffn=False):
+                topk_in_fc1=False, fused_ffn=False, fused_finalize=False):
         """The forward (moe_forward_ex).  combine: "fp32" (out fp32 [T_cap, H]), "bf16"
         (out bf16 [T_cap, H]) or "rows" (out fp32 [T_cap, topk, H]; probs may be None).
         topk_in_fc1: apply the probabilities inside FC1 (fp32 and bf16 combines).
-        fused_ffn: FC1 and FC2 in one persistent launch (bf16 weights)."""
+        fused_ffn: FC1 and FC2 in one persistent launch (bf16 weights).
+        fused_finalize: FC1, FC2 and the finalize in one persistent launch (bf16 weights)."""
         torch = _torch()
         T_cap = x.shape[0]
         dts, shape, alloc = self._out_spec(T_cap, combine)
@@ -232,12 +237,12 @@ class MoE:
             ws = self.new_workspace(T_cap, x.device)
         pw = _dev(ws, "ws", (torch.uint8,))
         _check(lib().moe_forward_ex(self._h, px, pi, pp, T_cap, plive,
-                                    self._combine_code(combine, topk_in_fc1, fused_ffn), po, pw,
+                                    self._combine_code(combine, topk_in_fc1, fused_ffn, fused_finalize), po, pw,
                                     ws.numel(), _stream(stream)), "moe_forward")
         return out
 
     def forward_noalloc(self, x, ids, probs, live, out=None, stream=None, combine="fp32",
-                        topk_in_fc1=False, fused_ffn=False):
+                        topk_in_fc1=False, fused_ffn=False, fused_finalize=False):
         """moe_forward_noalloc: the forward with the library's own per-GPU scratch
         as workspace (no caller workspace, nothing allocated by the library).
         Calls that overlap on one GPU race; the capacity is bounded."""
@@ -252,7 +257,7 @@ class MoE:
             out = torch.empty(shape, dtype=alloc, device=x.device)
         po = _dev(out, "out", dts, shape)
         _check(lib().moe_forward_noalloc(self._h, px, pi, pp, T_cap, plive,
-                                         self._combine_code(combine, topk_in_fc1, fused_ffn), po,
+                                         self._combine_code(combine, topk_in_fc1, fused_ffn, fused_finalize), po,
                                          _stream(stream)), "moe_forward_noalloc")
         return out
 
@@ -326,7 +331,7 @@ class MoE:
         _check(lib().moe_set_stage_events(self._h, arr, 6), "moe_set_stage_events")
 
     def bind_forward(self, x, ids, probs, live, out, ws, stream=None, combine="fp32",
-                     topk_in_fc1=False, fused_ffn=False):
+                     topk_in_fc1=False, fused_ffn=False, fused_finalize=False):
         """Check the arguments once and return a no-argument callable that
         enqueues this forward (for launch loops where per-call checks would
         cost more host time than the GPU work)."""
@@ -337,7 +342,7 @@ class MoE:
                 _dev(ids, "expert_ids", (torch.int32,), (T_cap, self.topk)),
                 None if probs is None else _dev(probs, "probs", (torch.float32,), (T_cap, self.topk)),
                 T_cap, _dev(live, "live", (torch.int32,)),
-                self._combine_code(combine, topk_in_fc1, fused_ffn),
+                self._combine_code(combine, topk_in_fc1, fused_ffn, fused_finalize),
                 _dev(out, "out", dts, shape),
                 _dev(ws, "ws", (torch.uint8,)), ws.numel(), _stream(stream))
         fn = lib().moe_forward_ex

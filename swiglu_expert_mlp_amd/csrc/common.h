@@ -38,6 +38,8 @@ __host__ __device__ inline int64_t wblock_step(int64_t n16, int64_t nt16)
 constexpr int kBM = 64;              // rows per M tile of the small-expert GEMM tiles
 constexpr int kBigBMRows = 256;      // rows per M tile of the LDS-staged GEMMs
 constexpr int kBigMin = 128;         // experts with more rows than this use the LDS-staged GEMMs
+constexpr int kFinCols = 512;        // output columns per count of the single-launch finalize
+                                     // (the 64-row tiles' column width)
 
 // Error bits reported by moe_check (same values as the header's MOE_DEVERR_*).
 constexpr uint32_t kErrBadId = 1u;
@@ -162,6 +164,7 @@ struct WsLayout {
     size_t tiles;          // int2 [max_tiles]: (expert, first row), 64-row GEMM tiles
     size_t tiles_big;      // int2 [max_tiles_big]: (expert, first row), LDS-staged GEMM tiles
     size_t ready;          // int32 [max_tiles + 4 max_tiles_big]: single-launch FFN readiness counters
+    size_t fin_cnt;        // int32 [T_cap][ceil(H / 512)]: single-launch finalize, routes still to come
     size_t hbuf;           // bf16 [T_cap * k][F] or E4M3 [T_cap * k][F]
     size_t hscale;         // E8M0 [T_cap * k][F / 32] (mxfp8)
     size_t obuf;           // float [T_cap * k][H]

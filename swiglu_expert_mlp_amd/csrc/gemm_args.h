@@ -81,6 +81,15 @@ struct GemmArgs {
     // tile, the count of FC1 column tiles whose SwiGLU rows are released
     int32_t* ready;
     uint32_t* err;             // the header's error word (a readiness wait past its limit)
+    // single-launch finalize (the FC2 half of the fused launch): per live token
+    // and 512-column block of the output, the number of the token's FC2 rows
+    // not yet written (prep sets it to the token's kept routes)
+    int32_t* fin_cnt;
+    const int32_t* fin_route;  // grouped row -> route (t * k + j)
+    const int32_t* fin_dst;    // route -> grouped row, -1 for a dropped route
+    const float* fin_prob;     // canonical probabilities, or null (every p is 1)
+    void* fin_out;             // the forward's output
+    int fin_mode;              // 0: fp32 chain, 1: bf16 of it, 2: rows
 };
 
 // MXFP8 operands: E4M3 codes with one E8M0 scale byte per 32 elements of K.

@@ -46,11 +46,15 @@ __global__ void __launch_bounds__(512, 1) gemm_bf16_big_kernel(GemmArgs g)
 // design (it takes every tile, a 256-row tile as four 64-row tiles), FC2
 // tiles waiting on per-M-tile readiness counters instead of the launch
 // boundary (gemm_bf16_small.h).  The grid is at most one workgroup per CU, so
-// every workgroup is resident and every FC1 tile is taken.
-template <bool PROB>
+// every workgroup is resident and every FC1 tile is taken.  FIN: the FC2
+// tiles also run the finalize (small_finalize: the last FC2 tile of a token's
+// 512-column block combines it).
+template <bool PROB, bool FIN>
 __global__ void __launch_bounds__(512, 1) gemm_bf16_fused_kernel(GemmArgs g1, GemmArgs g2)
 {
     __shared__ __attribute__((aligned(1024))) char smem[kSmallLds];
+    __shared__ int fin_lds[1 + kBM];
+    constexpr int F2 = FIN ? 3 : 2;
     const int n_big = ld_const(&g1.hdr->n_tiles_big);
     const int n_small = ld_const(&g1.hdr->n_tiles);
     const int multi = ld_const(&g1.hdr->multi_tile);
@@ -60,12 +64,12 @@ __global__ void __launch_bounds__(512, 1) gemm_bf16_fused_kernel(GemmArgs g1, Ge
     const int* te1 = (const int*)(g2.tiles + min(xcd_first_tile() / small_col_tiles(g2), g2.max_tiles - 1));
     if (multi) {
         small_tiles<true, PROB, 1, 0>(g1, smem, n_small, n_big, e0, row00);
-        small_tiles<false, false, 2, 0>(g2, smem, n_small, n_big, ld_const(te1), ld_const(te1 + 1),
-                                        small_col_tiles(g1));
+        small_tiles<false, false, F2, 0>(g2, smem, n_small, n_big, ld_const(te1), ld_const(te1 + 1),
+                                         small_col_tiles(g1), fin_lds);
     } else {
         small_tiles<true, PROB, 1, kNonTemporal>(g1, smem, n_small, n_big, e0, row00);
-        small_tiles<false, false, 2, kNonTemporal>(g2, smem, n_small, n_big, ld_const(te1),
-                                                   ld_const(te1 + 1), small_col_tiles(g1));
+        small_tiles<false, false, F2, kNonTemporal>(g2, smem, n_small, n_big, ld_const(te1),
+                                                    ld_const(te1 + 1), small_col_tiles(g1), fin_lds);
     }
 }
 
@@ -73,6 +77,10 @@ hipError_t launch_gemm_bf16_fused(const GemmArgs& g1, const GemmArgs& g2, int nu
                                   hipEvent_t t0, hipEvent_t t1)
 {
     if (!g1.small_takes_big || !g2.small_takes_big || !g1.ready || !g1.err) return hipErrorInvalidValue;
+    const bool fin = g2.fin_cnt != nullptr;
+    if (fin && (!g2.fin_route || !g2.fin_dst || !g2.fin_out || g2.fin_mode < 0 || g2.fin_mode > 2 ||
+                g2.topk < 1 || g2.topk > kMaxTopk))
+        return hipErrorInvalidValue;
     const dim3 grid((unsigned)(num_cu >= 8 ? num_cu / 8 * 8 : 8)), block(512);
     const bool prob = g1.row_prob != nullptr;
     auto go = [&](auto kernel) {
@@ -81,8 +89,13 @@ hipError_t launch_gemm_bf16_fused(const GemmArgs& g1, const GemmArgs& g2, int nu
         else
             hipLaunchKernelGGL(kernel, grid, block, 0, s, g1, g2);
     };
-    if (prob) go(gemm_bf16_fused_kernel<true>);
-    else go(gemm_bf16_fused_kernel<false>);
+    if (fin) {
+        if (prob) go(gemm_bf16_fused_kernel<true, true>);
+        else go(gemm_bf16_fused_kernel<false, true>);
+    } else {
+        if (prob) go(gemm_bf16_fused_kernel<true, false>);
+        else go(gemm_bf16_fused_kernel<false, false>);
+    }
     return hipGetLastError();
 }
 

@@ -85,6 +85,86 @@ __device__ __forceinline__ void small_release(const GemmArgs& g, int mt)
 constexpr int kFuseWaitTicks = 20000000;        // wall-clock ticks (100 MHz): 0.2 s
 constexpr int kCoherentLoad = 16;               // cache policy sc1 (device-coherent)
 
+// Single-launch finalize (FUSE = 3: an FC2 tile of the fused launch): once
+// the tile's fp32 rows are stored, they are released at device scope (every
+// wave's stores complete, the L2's dirty lines written back) and each row's
+// token counts its 512-column block down; the workgroup that takes a count
+// to zero holds the last of that token's rows in the block and combines the
+// block at once, reading the other routes' rows (written by workgroups on any
+// XCD) with device-coherent loads.  No wait: a workgroup that is not the last
+// goes on to its next tile.  A tile holds one expert's rows, and a token
+// routes to an expert at most once, so a token appears at most once per tile.
+// The combine is the separate finalize's arithmetic (fp32 fused multiply-adds
+// of probability and row from +0 in canonical order, skipping dropped
+// routes; its bf16 rounding; or row mode), one column per thread.
+// fl: 65 ints of LDS (a count, then the tokens this workgroup combines).
+static_assert(kFinCols == kSmallCols, "a finalize count per 64-row tile column block");
+__device__ __forceinline__ void small_finalize(const GemmArgs& g, int* fl, int ct, int row0,
+                                               int rows)
+{
+    const int lane = threadIdx.x & 63;
+    const int NT = small_col_tiles(g);           // g.N = H: output column blocks per token
+    BIG_WAIT_VMCNT(0);                           // this wave's row stores are complete
+    __builtin_amdgcn_s_barrier();                // and every wave's
+    if (threadIdx.x < 64) {
+        int t = 0;
+        bool last = false;
+        if (lane < rows) {
+            t = g.fin_route[row0 + lane] / g.topk;
+            last = __hip_atomic_fetch_add(g.fin_cnt + (int64_t)t * NT + ct, -1, __ATOMIC_RELEASE,
+                                          __HIP_MEMORY_SCOPE_AGENT) == 1;
+        }
+        const uint64_t m = __ballot(last);
+        if (last) fl[1 + __popcll(m & ((1ull << lane) - 1ull))] = t;
+        if (lane == 0) fl[0] = __popcll(m);
+    }
+    __syncthreads();
+    const int n = fl[0];
+    const int H = g.N, k = g.topk;
+    const int c = ct * kSmallCols + threadIdx.x;  // this thread's output column
+    const float* O = (const float*)g.out;
+    const int jl = min(lane, k - 1);
+    for (int i = 0; i < n; ++i) {
+        const int t = fl[1 + i];
+        // the token's k row indices and probabilities in one load each (lane
+        // j holds route j), so every row load below is issued without waiting
+        const int dl = g.fin_dst[(int64_t)t * k + jl];
+        const float pl = g.fin_prob ? g.fin_prob[(int64_t)t * k + jl] : 1.0f;
+        int d[kMaxTopk];
+        float o[kMaxTopk];
+#pragma unroll
+        for (int j = 0; j < kMaxTopk; ++j) {
+            const int r = __builtin_amdgcn_readlane(dl, j);   // every lane holds a route
+            d[j] = j < k ? r : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < kMaxTopk; ++j) {
+            o[j] = 0.0f;
+            // a relaxed device-scope atomic load is a device-coherent (sc1) load
+            if (d[j] >= 0 && c < H)
+                o[j] = __uint_as_float(__hip_atomic_load((const uint32_t*)(O + (int64_t)d[j] * H + c),
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        }
+        if (c >= H) continue;
+        if (g.fin_mode == 2) {
+            // row mode: every route alone, one fma from +0 (a dropped route stays +0)
+            float* out = (float*)g.fin_out + (int64_t)t * k * H + c;
+#pragma unroll
+            for (int j = 0; j < kMaxTopk; ++j)
+                if (j < k) out[(int64_t)j * H] = d[j] >= 0 ? __builtin_fmaf(1.0f, o[j], 0.0f) : 0.0f;
+        } else {
+            float acc = 0.0f;
+#pragma unroll
+            for (int j = 0; j < kMaxTopk; ++j)
+                if (j < k && d[j] >= 0)
+                    acc = __builtin_fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(pl), j)),
+                                         o[j], acc);
+            if (g.fin_mode == 0) ((float*)g.fin_out)[(int64_t)t * H + c] = acc;
+            else ((uint16_t*)g.fin_out)[(int64_t)t * H + c] = f32_to_bf16_bits(acc);
+        }
+    }
+}
+
 // n_small: the number of 64-row M tiles; n_big: the number of 256-row M
 // tiles this launch also runs, as four 64-row tiles each (0 when a launch of
 // the 256-row design takes them); (e0, row00): the table entry of this
@@ -95,7 +175,7 @@ constexpr int kCoherentLoad = 16;               // cache policy sc1 (device-cohe
 // from the header).
 template <bool FC1, bool PROB, int FUSE, int WPOL>
 __device__ __forceinline__ void small_tiles(const GemmArgs& g, char* smem, int n_small, int n_big,
-                                            int e0, int row00, int need = 0)
+                                            int e0, int row00, int need = 0, int* fin_lds = nullptr)
 {
     const int NTs = small_col_tiles(g);
     const int total = (n_small + 4 * n_big) * NTs;
@@ -179,7 +259,7 @@ __device__ __forceinline__ void small_tiles(const GemmArgs& g, char* smem, int n
             if constexpr (FC1) src = g.perm_src[src] / g.topk;
             arow = g.A + src * K + 8 * ((lane & 3) ^ big_swz(lane >> 2));
         }
-        if constexpr (FUSE == 2) {
+        if constexpr (FUSE >= 2) {
             // the waves that load rows wait for the FC1 tiles of this M tile
             if (has_a) {
                 const int32_t* rp = g.ready + mt;
@@ -200,7 +280,7 @@ __device__ __forceinline__ void small_tiles(const GemmArgs& g, char* smem, int n
         auto issue_a = [&](int s) {
             if (has_a) {
                 char* dst = smem + (s % kSmallRing) * kSmallStage + wid * 1024;
-                if constexpr (FUSE == 2)
+                if constexpr (FUSE >= 2)
                     __builtin_amdgcn_global_load_lds(arow + 32 * s, (lds_void_t*)dst, 16, 0, kCoherentLoad);
                 else
                     big_load_block(arow + 32 * s, dst);
@@ -254,6 +334,7 @@ __device__ __forceinline__ void small_tiles(const GemmArgs& g, char* smem, int n
         // 8 (v / 4) + 4 (l / 32) + v % 4 of each 32-row block
         if (!has_cols) {
             if constexpr (FUSE == 1) small_release(g, mt);
+            if constexpr (FUSE == 3) small_finalize(g, fin_lds, ct, row0, rows);
             continue;
         }
         if constexpr (FC1) {
@@ -288,6 +369,7 @@ __device__ __forceinline__ void small_tiles(const GemmArgs& g, char* smem, int n
             }
         }
         if constexpr (FUSE == 1) small_release(g, mt);
+        if constexpr (FUSE == 3) small_finalize(g, fin_lds, ct, row0, rows);
     }
 }
 

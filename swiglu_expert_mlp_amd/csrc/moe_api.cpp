@@ -15,7 +15,8 @@ namespace moe {
 hipError_t launch_route(const float* logits, int64_t T_cap, const int32_t* live, int E, int k,
                         int32_t* ids, float* probs, WsHeader* hdr, int num_cu, hipStream_t s);
 hipError_t launch_prep(const int32_t* ids, const float* probs, int64_t T_cap, const int32_t* live,
-                       int E, int k, int num_cu, char* ws, const WsLayout& L, hipStream_t s);
+                       int E, int k, int num_cu, char* ws, const WsLayout& L, hipStream_t s,
+                       int fin_H, int fin_mode, void* fin_out);
 hipError_t launch_finalize(const float* O, const int32_t* dst, const float* sorted_probs,
                            int64_t T_cap, const int32_t* live, int k, int H, int mode, void* out,
                            int num_cu, hipStream_t s);
@@ -117,6 +118,7 @@ static WsLayout layout_of(const moe_ctx* h, int64_t T_cap)
     L.tiles = take(8 * L.max_tiles);
     L.tiles_big = take(8 * L.max_tiles_big);
     L.ready = take(4 * (L.max_tiles + 4 * L.max_tiles_big));
+    L.fin_cnt = take(4 * T_cap * ((H + kFinCols - 1) / kFinCols));
     if (h->precision == MOE_BF16) {
         L.hbuf = take(2 * R * F);
         L.hscale = 0;
@@ -287,15 +289,18 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
     if (T_cap < 0 || T_cap > (int64_t)1 << 26)
         return fail(MOE_ERR_INVALID_ARG, "moe_forward: T_cap=%lld out of range", (long long)T_cap);
     const bool fc1_topk = (combine & MOE_APPLY_TOPK_IN_FC1) != 0;
-    const bool fused = (combine & MOE_FUSED_FFN) != 0;
-    combine &= ~(MOE_APPLY_TOPK_IN_FC1 | MOE_FUSED_FFN);
+    // the single-launch finalize implies the single-launch FFN
+    const bool fused_fin = (combine & MOE_FUSED_FINALIZE) != 0;
+    const bool fused = fused_fin || (combine & MOE_FUSED_FFN) != 0;
+    combine &= ~(MOE_APPLY_TOPK_IN_FC1 | MOE_FUSED_FFN | MOE_FUSED_FINALIZE);
     if (combine != MOE_COMBINE_FP32 && combine != MOE_COMBINE_BF16 && combine != MOE_COMBINE_ROWS)
         return fail(MOE_ERR_INVALID_ARG, "moe_forward: unknown combine %d", combine);
     if (fc1_topk && combine == MOE_COMBINE_ROWS)
         return fail(MOE_ERR_INVALID_ARG,
                     "moe_forward: MOE_APPLY_TOPK_IN_FC1 with row mode (which uses no probabilities)");
     if (fused && h->precision != MOE_BF16)
-        return fail(MOE_ERR_INVALID_ARG, "moe_forward: MOE_FUSED_FFN is implemented for bf16 only");
+        return fail(MOE_ERR_INVALID_ARG, "moe_forward: %s is implemented for bf16 only",
+                    fused_fin ? "MOE_FUSED_FINALIZE" : "MOE_FUSED_FFN");
     // row mode does not use the probabilities (every route has probability 1)
     if (!x || !expert_ids || (!probs && combine != MOE_COMBINE_ROWS) || !live_rows_dev || !out ||
         !ws)
@@ -314,8 +319,8 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
     WsHeader* hdr = (WsHeader*)(w + L.hdr);
     hipError_t e = mark(h, 0, stream);
     if (e != hipSuccess) return hip_fail(e, "moe_forward: stage event");
-    e = launch_prep(expert_ids, probs, T_cap, live_rows_dev, h->E, h->k, h->num_cu, w, L,
-                               stream);
+    e = launch_prep(expert_ids, probs, T_cap, live_rows_dev, h->E, h->k, h->num_cu, w, L, stream,
+                    h->H, combine, fused_fin ? out : nullptr);
     if (e != hipSuccess) return hip_fail(e, "moe_forward: prep launch");
     if ((e = mark(h, 1, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     const int E = h->E, H = h->H, F = h->F;
@@ -358,6 +363,18 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         g2.n_tiles_n = ((H + 63) / 64 + 3) / 4;
         g2.row_prob = nullptr;
         g2.small_takes_big = T_cap <= 1024 || F % 64 != 0 || F < 128 || (int64_t)H * F * 2 >= ((int64_t)1 << 31);
+        g1.fin_cnt = g2.fin_cnt = nullptr;
+        if (fused_fin) {
+            // the FC2 tiles combine each token's 512-column blocks as they complete
+            g2.fin_cnt = (int32_t*)(w + L.fin_cnt);
+            g2.fin_route = (const int32_t*)(w + L.perm_src);
+            g2.fin_dst = (const int32_t*)(w + L.dst);
+            // with the probabilities applied inside FC1, or in row mode, every p is 1
+            g2.fin_prob = (fc1_topk || combine == MOE_COMBINE_ROWS) ? nullptr
+                                                                     : (const float*)(w + L.sorted_probs);
+            g2.fin_out = out;
+            g2.fin_mode = combine;
+        }
         if (fused) {
             // one persistent launch, the 64-row design taking every tile; the
             // FC1 stage's events bracket it
@@ -427,6 +444,11 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         e = launch_gemm_mxfp8(false, w4, g2, h->num_cu, stream, nullptr, nullptr);
         if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
         if ((e = mark(h, 4, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
+    }
+    if (fused_fin) {
+        // the fused launch combined every live token
+        if ((e = mark(h, 5, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
+        return MOE_OK;
     }
     // with the probabilities applied inside FC1 the finalize adds the rows
     e = launch_finalize((const float*)(w + L.obuf), (const int32_t*)(w + L.dst),

@@ -90,6 +90,13 @@ struct PrepArgs {
     int2* tiles;
     int2* tiles_big;
     int32_t* ready;          // single-launch FFN readiness counters (zeroed here)
+    // single-launch finalize (null when the forward runs a separate finalize):
+    // per live token and 512-column block, the token's kept-route count
+    int32_t* fin_cnt;
+    int fin_nt;              // 512-column blocks per token: ceil(H / 512)
+    int fin_H;
+    int fin_mode;            // combine: 0 fp32, 1 bf16, 2 rows
+    void* fin_out;           // the forward's output (tokens with no kept route)
     WsHeader* hdr;
     int32_t* perm_src;
     int32_t* dst;
@@ -299,6 +306,26 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a)
             a.sorted_probs[(int64_t)t * K + j] = p[j];
         }
     }
+    if (a.fin_cnt && valid) {
+        // the single-launch finalize counts every 512-column block of this
+        // token down from its kept routes; with none kept, no FC2 tile ever
+        // reaches the token, so its output (+0 in every combine, as the
+        // separate finalize writes it) is written here
+        int nk = 0;
+#pragma unroll
+        for (int j = 0; j < K; ++j) nk += keep[j] ? 1 : 0;
+        for (int b = 0; b < a.fin_nt; ++b) a.fin_cnt[(int64_t)t * a.fin_nt + b] = nk;
+        if (nk == 0) {
+            if (a.fin_mode == 1) {
+                uint16_t* o = (uint16_t*)a.fin_out + (int64_t)t * a.fin_H;
+                for (int i = 0; i < a.fin_H; ++i) o[i] = 0;
+            } else {
+                const int64_t n = a.fin_mode == 2 ? (int64_t)K * a.fin_H : (int64_t)a.fin_H;
+                float* o = (float*)a.fin_out + (int64_t)t * n;
+                for (int64_t i = 0; i < n; ++i) o[i] = 0.0f;
+            }
+        }
+    }
     __syncthreads();
     const int word = threadIdx.x >> 5, bit = threadIdx.x & 31;
 #pragma unroll
@@ -396,9 +423,15 @@ __global__ void __launch_bounds__(256) prep_scatter_kernel(
 }
 
 hipError_t launch_prep(const int32_t* ids, const float* probs, int64_t T_cap, const int32_t* live,
-                       int E, int k, int num_cu, char* ws, const WsLayout& L, hipStream_t s)
+                       int E, int k, int num_cu, char* ws, const WsLayout& L, hipStream_t s,
+                       int fin_H, int fin_mode, void* fin_out)
 {
     PrepArgs a;
+    a.fin_cnt = fin_out ? (int32_t*)(ws + L.fin_cnt) : nullptr;
+    a.fin_nt = (fin_H + kFinCols - 1) / kFinCols;
+    a.fin_H = fin_H;
+    a.fin_mode = fin_mode;
+    a.fin_out = fin_out;
     a.ids = ids;
     a.probs = probs;
     a.T_cap = T_cap;
