@@ -53,7 +53,7 @@ template <bool PROB, bool FIN>
 __global__ void __launch_bounds__(512, 1) gemm_bf16_fused_kernel(GemmArgs g1, GemmArgs g2)
 {
     __shared__ __attribute__((aligned(1024))) char smem[kSmallLds];
-    __shared__ int fin_lds[1 + kBM];
+    __shared__ SmallFinLds fin_lds;
     constexpr int F2 = FIN ? 3 : 2;
     const int n_big = ld_const(&g1.hdr->n_tiles_big);
     const int n_small = ld_const(&g1.hdr->n_tiles);
@@ -65,11 +65,11 @@ __global__ void __launch_bounds__(512, 1) gemm_bf16_fused_kernel(GemmArgs g1, Ge
     if (multi) {
         small_tiles<true, PROB, 1, 0>(g1, smem, n_small, n_big, e0, row00);
         small_tiles<false, false, F2, 0>(g2, smem, n_small, n_big, ld_const(te1), ld_const(te1 + 1),
-                                         small_col_tiles(g1), fin_lds);
+                                         small_col_tiles(g1), &fin_lds);
     } else {
         small_tiles<true, PROB, 1, kNonTemporal>(g1, smem, n_small, n_big, e0, row00);
         small_tiles<false, false, F2, kNonTemporal>(g2, smem, n_small, n_big, ld_const(te1),
-                                                    ld_const(te1 + 1), small_col_tiles(g1), fin_lds);
+                                                    ld_const(te1 + 1), small_col_tiles(g1), &fin_lds);
     }
 }
 

@@ -96,14 +96,110 @@ constexpr int kCoherentLoad = 16;               // cache policy sc1 (device-cohe
 // routes to an expert at most once, so a token appears at most once per tile.
 // The combine is the separate finalize's arithmetic (fp32 fused multiply-adds
 // of probability and row from +0 in canonical order, skipping dropped
-// routes; its bf16 rounding; or row mode), one column per thread.
-// fl: 65 ints of LDS (a count, then the tokens this workgroup combines).
-static_assert(kFinCols == kSmallCols, "a finalize count per 64-row tile column block");
-__device__ __forceinline__ void small_finalize(const GemmArgs& g, int* fl, int ct, int row0,
+// routes; its bf16 rounding; or row mode).  The lanes that counted a token
+// to zero stage its k row indices and probabilities in LDS (one round trip
+// for all of them), then the 8 waves share the jobs: a job is one token's
+// whole 512-column block (8 columns per lane) when k <= 8, or a 256-column
+// half (4 per lane) above, so that a job's k row loads (issued back to back,
+// one round trip) fit 64 registers.
+static_assert(kFinCols == kSmallCols && kFinCols == 64 * 8, "finalize blocks");
+struct SmallFinLds {
+    int n;                                       // tokens this workgroup combines
+    int tok[kBM];
+    int dst[kBM][kMaxTopk];                      // their routes' grouped rows (-1: dropped)
+    float prob[kBM][kMaxTopk];                   // and probabilities (1 when none are applied)
+};
+
+// device-coherent 8-byte load: a relaxed device-scope atomic load (sc1)
+__device__ __forceinline__ float2 fin_load2(const float* p)
+{
+    const uint64_t v = __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+
+// The combine jobs of one wave: NR routes at most, CPL columns per lane.
+template <int NR, int CPL>
+__device__ __forceinline__ void small_fin_jobs(const GemmArgs& g, const SmallFinLds* fl, int ct)
+{
+    constexpr int kJobs = kFinCols / (64 * CPL);  // jobs per token block
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int H = g.N, k = g.topk;
+    const float* O = (const float*)g.out;
+    const int njobs = fl->n * kJobs;
+    for (int q = wid; q < njobs; q += 8) {
+        const int i = q / kJobs;
+        const int c = ct * kFinCols + (q % kJobs) * 64 * CPL + CPL * lane;
+        // H is a multiple of 32, so a lane's columns are all inside or all past it
+        const bool in = c < H;
+        const int t = __builtin_amdgcn_readfirstlane(fl->tok[i]);
+        int d[NR];
+#pragma unroll
+        for (int j = 0; j < NR; ++j) d[j] = j < k ? __builtin_amdgcn_readfirstlane(fl->dst[i][j]) : -1;
+        float2 o[NR][CPL / 2];
+#pragma unroll
+        for (int j = 0; j < NR; ++j)
+#pragma unroll
+            for (int h = 0; h < CPL / 2; ++h) {
+                o[j][h] = make_float2(0.0f, 0.0f);
+                if (d[j] >= 0 && in) o[j][h] = fin_load2(O + (int64_t)d[j] * H + c + 2 * h);
+            }
+        // the stores are per-lane predicated (no early exit)
+        if (g.fin_mode == 2) {
+            // row mode: every route alone, one fma from +0 (a dropped route stays +0)
+#pragma unroll
+            for (int j = 0; j < NR; ++j)
+                if (j < k && in) {
+                    float* dstp = (float*)g.fin_out + ((int64_t)t * k + j) * H + c;
+#pragma unroll
+                    for (int h = 0; h < CPL / 4; ++h) {
+                        float4 r = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                        if (d[j] >= 0)
+                            r = make_float4(__builtin_fmaf(1.0f, o[j][2 * h].x, 0.0f),
+                                            __builtin_fmaf(1.0f, o[j][2 * h].y, 0.0f),
+                                            __builtin_fmaf(1.0f, o[j][2 * h + 1].x, 0.0f),
+                                            __builtin_fmaf(1.0f, o[j][2 * h + 1].y, 0.0f));
+                        *(float4*)(dstp + 4 * h) = r;
+                    }
+                }
+        } else {
+            float acc[CPL];
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) acc[e] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < NR; ++j)
+                if (d[j] >= 0) {
+                    const float p = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(fl->prob[i][j])));
+#pragma unroll
+                    for (int h = 0; h < CPL / 2; ++h) {
+                        acc[2 * h] = __builtin_fmaf(p, o[j][h].x, acc[2 * h]);
+                        acc[2 * h + 1] = __builtin_fmaf(p, o[j][h].y, acc[2 * h + 1]);
+                    }
+                }
+            if (in) {
+                if (g.fin_mode == 0) {
+                    float* dstp = (float*)g.fin_out + (int64_t)t * H + c;
+#pragma unroll
+                    for (int h = 0; h < CPL / 4; ++h)
+                        *(float4*)(dstp + 4 * h) = make_float4(acc[4 * h], acc[4 * h + 1], acc[4 * h + 2], acc[4 * h + 3]);
+                } else {
+                    uint16_t* dstp = (uint16_t*)g.fin_out + (int64_t)t * H + c;
+#pragma unroll
+                    for (int h = 0; h < CPL / 4; ++h)
+                        *(uint2*)(dstp + 4 * h) = make_uint2(
+                            (uint32_t)f32_to_bf16_bits(acc[4 * h]) | ((uint32_t)f32_to_bf16_bits(acc[4 * h + 1]) << 16),
+                            (uint32_t)f32_to_bf16_bits(acc[4 * h + 2]) | ((uint32_t)f32_to_bf16_bits(acc[4 * h + 3]) << 16));
+                }
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void small_finalize(const GemmArgs& g, SmallFinLds* fl, int ct, int row0,
                                                int rows)
 {
     const int lane = threadIdx.x & 63;
     const int NT = small_col_tiles(g);           // g.N = H: output column blocks per token
+    const int k = g.topk;
     BIG_WAIT_VMCNT(0);                           // this wave's row stores are complete
     __builtin_amdgcn_s_barrier();                // and every wave's
     if (threadIdx.x < 64) {
@@ -115,54 +211,29 @@ __device__ __forceinline__ void small_finalize(const GemmArgs& g, int* fl, int c
                                           __HIP_MEMORY_SCOPE_AGENT) == 1;
         }
         const uint64_t m = __ballot(last);
-        if (last) fl[1 + __popcll(m & ((1ull << lane) - 1ull))] = t;
-        if (lane == 0) fl[0] = __popcll(m);
+        if (last) {
+            const int i = __popcll(m & ((1ull << lane) - 1ull));
+            fl->tok[i] = t;
+            int d[kMaxTopk];
+            float p[kMaxTopk];
+#pragma unroll
+            for (int j = 0; j < kMaxTopk; ++j)
+                if (j < k) {
+                    d[j] = g.fin_dst[(int64_t)t * k + j];
+                    p[j] = g.fin_prob ? g.fin_prob[(int64_t)t * k + j] : 1.0f;
+                }
+#pragma unroll
+            for (int j = 0; j < kMaxTopk; ++j)
+                if (j < k) {
+                    fl->dst[i][j] = d[j];
+                    fl->prob[i][j] = p[j];
+                }
+        }
+        if (lane == 0) fl->n = __popcll(m);
     }
     __syncthreads();
-    const int n = fl[0];
-    const int H = g.N, k = g.topk;
-    const int c = ct * kSmallCols + threadIdx.x;  // this thread's output column
-    const float* O = (const float*)g.out;
-    const int jl = min(lane, k - 1);
-    for (int i = 0; i < n; ++i) {
-        const int t = fl[1 + i];
-        // the token's k row indices and probabilities in one load each (lane
-        // j holds route j), so every row load below is issued without waiting
-        const int dl = g.fin_dst[(int64_t)t * k + jl];
-        const float pl = g.fin_prob ? g.fin_prob[(int64_t)t * k + jl] : 1.0f;
-        int d[kMaxTopk];
-        float o[kMaxTopk];
-#pragma unroll
-        for (int j = 0; j < kMaxTopk; ++j) {
-            const int r = __builtin_amdgcn_readlane(dl, j);   // every lane holds a route
-            d[j] = j < k ? r : -1;
-        }
-#pragma unroll
-        for (int j = 0; j < kMaxTopk; ++j) {
-            o[j] = 0.0f;
-            // a relaxed device-scope atomic load is a device-coherent (sc1) load
-            if (d[j] >= 0 && c < H)
-                o[j] = __uint_as_float(__hip_atomic_load((const uint32_t*)(O + (int64_t)d[j] * H + c),
-                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        }
-        if (c >= H) continue;
-        if (g.fin_mode == 2) {
-            // row mode: every route alone, one fma from +0 (a dropped route stays +0)
-            float* out = (float*)g.fin_out + (int64_t)t * k * H + c;
-#pragma unroll
-            for (int j = 0; j < kMaxTopk; ++j)
-                if (j < k) out[(int64_t)j * H] = d[j] >= 0 ? __builtin_fmaf(1.0f, o[j], 0.0f) : 0.0f;
-        } else {
-            float acc = 0.0f;
-#pragma unroll
-            for (int j = 0; j < kMaxTopk; ++j)
-                if (j < k && d[j] >= 0)
-                    acc = __builtin_fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(pl), j)),
-                                         o[j], acc);
-            if (g.fin_mode == 0) ((float*)g.fin_out)[(int64_t)t * H + c] = acc;
-            else ((uint16_t*)g.fin_out)[(int64_t)t * H + c] = f32_to_bf16_bits(acc);
-        }
-    }
+    if (k <= 8) small_fin_jobs<8, 8>(g, fl, ct);
+    else small_fin_jobs<16, 4>(g, fl, ct);
 }
 
 // n_small: the number of 64-row M tiles; n_big: the number of 256-row M
@@ -175,7 +246,7 @@ __device__ __forceinline__ void small_finalize(const GemmArgs& g, int* fl, int c
 // from the header).
 template <bool FC1, bool PROB, int FUSE, int WPOL>
 __device__ __forceinline__ void small_tiles(const GemmArgs& g, char* smem, int n_small, int n_big,
-                                            int e0, int row00, int need = 0, int* fin_lds = nullptr)
+                                            int e0, int row00, int need = 0, SmallFinLds* fin_lds = nullptr)
 {
     const int NTs = small_col_tiles(g);
     const int total = (n_small + 4 * n_big) * NTs;
