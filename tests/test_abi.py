@@ -126,6 +126,24 @@ def test_status_codes_match_the_boundary():
     assert m.MOE_ERR_DEVICE_CONTRACT == v["MOE_ERR_DEVICE_CONTRACT"]
 
 
+def test_forward_flags_match_the_boundary():
+    """The binding's combine codes and option flags are the header's values,
+    and the options are distinct bits above every combine code."""
+    text = open(HEADER).read()
+    defs = {n: int(v, 0) for n, v in re.findall(r"#define\s+(MOE_[A-Z0-9_]+)\s+(0x[0-9a-fA-F]+|\d+)u?\b", text)}
+    v = _enum_values()
+    import swiglu_expert_mlp_amd as m
+    assert m.APPLY_TOPK_IN_FC1 == defs["MOE_APPLY_TOPK_IN_FC1"]
+    assert m.FUSED_FFN == defs["MOE_FUSED_FFN"]
+    assert m.FUSED_FINALIZE == defs["MOE_FUSED_FINALIZE"]
+    flags = [defs["MOE_APPLY_TOPK_IN_FC1"], defs["MOE_FUSED_FFN"], defs["MOE_FUSED_FINALIZE"]]
+    assert all(f & (f - 1) == 0 for f in flags) and len(set(flags)) == 3
+    combines = [v["MOE_COMBINE_FP32"], v["MOE_COMBINE_BF16"], v["MOE_COMBINE_ROWS"]]
+    assert max(combines) < min(flags)
+    code = m.MoE._combine_code("bf16", True, False, True)
+    assert code == v["MOE_COMBINE_BF16"] | defs["MOE_APPLY_TOPK_IN_FC1"] | defs["MOE_FUSED_FINALIZE"]
+
+
 def test_host_checks_of_inspection_calls(L):
     """moe_check / moe_get_rows reject NULL arguments on the host, and
     moe_get_rows refuses activation codes for bf16 (there are none), without
