@@ -242,8 +242,8 @@ typedef enum {
  *     route's fp32 FC2 row; -0 comes back as +0 and a dropped route (invalid
  *     or repeated id) as a row of +0.  out is fp32 [T_cap][topk][H].  probs
  *     is not read and may be NULL.
- * combine may carry MOE_APPLY_TOPK_IN_FC1 (fp32 and bf16 combines) and
- * MOE_FUSED_FFN (bf16 weights).
+ * combine may carry MOE_APPLY_TOPK_IN_FC1 (fp32 and bf16 combines),
+ * MOE_FUSED_FFN and MOE_FUSED_FINALIZE (bf16 weights).
  * Rows of tokens >= live are never written in any mode.  Errors: an unknown
  * combine, or MOE_APPLY_TOPK_IN_FC1 with row mode, is MOE_ERR_INVALID_ARG;
  * otherwise as moe_forward. */
