@@ -101,29 +101,32 @@ hipError_t launch_gemm_bf16_fused(const GemmArgs& g1, const GemmArgs& g2, int nu
 
 // t0 / t1 (optional): events that receive the stage's start (the first
 // launch's) and end (the last launch's), recorded by the dispatches themselves
-// (no separate marker in the stream)
+// (no separate marker in the stream).  s_small (optional): the stream of the
+// 64-row launch when the stage has two launches (the caller orders it).
 hipError_t launch_gemm_bf16(bool fc1, const GemmArgs& g, int num_cu, hipStream_t s, hipEvent_t t0,
-                            hipEvent_t t1)
+                            hipEvent_t t1, hipStream_t s_small)
 {
     // a multiple of 8 workgroups: the 256-row loop splits its tiles over the 8 XCDs
     const dim3 grid((unsigned)(num_cu >= 8 ? num_cu / 8 * 8 : 8));
-    auto go = [&](auto kernel, int threads, hipEvent_t e0, hipEvent_t e1) {
+    auto go = [&](auto kernel, int threads, hipEvent_t e0, hipEvent_t e1, hipStream_t st) {
         if (e0 || e1)
-            hipExtLaunchKernelGGL(kernel, grid, dim3(threads), 0, s, e0, e1, 0, g);
+            hipExtLaunchKernelGGL(kernel, grid, dim3(threads), 0, st, e0, e1, 0, g);
         else
-            hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, s, g);
+            hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, st, g);
     };
     const bool prob = fc1 && g.row_prob != nullptr;
     hipEvent_t small_start = t0;
+    hipStream_t ss = s;
     if (!g.small_takes_big) {
-        if (prob) go(gemm_bf16_big_kernel<true, true>, 512, t0, nullptr);
-        else if (fc1) go(gemm_bf16_big_kernel<true, false>, 512, t0, nullptr);
-        else go(gemm_bf16_big_kernel<false, false>, 512, t0, nullptr);
+        if (prob) go(gemm_bf16_big_kernel<true, true>, 512, t0, nullptr, s);
+        else if (fc1) go(gemm_bf16_big_kernel<true, false>, 512, t0, nullptr, s);
+        else go(gemm_bf16_big_kernel<false, false>, 512, t0, nullptr, s);
         small_start = nullptr;
+        if (s_small) ss = s_small;
     }
-    if (prob) go(gemm_bf16_small_kernel<true, true>, 512, small_start, t1);
-    else if (fc1) go(gemm_bf16_small_kernel<true, false>, 512, small_start, t1);
-    else go(gemm_bf16_small_kernel<false, false>, 512, small_start, t1);
+    if (prob) go(gemm_bf16_small_kernel<true, true>, 512, small_start, t1, ss);
+    else if (fc1) go(gemm_bf16_small_kernel<true, false>, 512, small_start, t1, ss);
+    else go(gemm_bf16_small_kernel<false, false>, 512, small_start, t1, ss);
     return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@ hipError_t launch_quant_x(const uint16_t* x, int64_t T_cap, const int32_t* live,
 
 namespace moe {
 hipError_t launch_gemm_bf16(bool fc1, const GemmArgs& g, int num_cu, hipStream_t s, hipEvent_t t0,
-                            hipEvent_t t1);
+                            hipEvent_t t1, hipStream_t s_small = nullptr);
 hipError_t launch_gemm_bf16_fused(const GemmArgs& g1, const GemmArgs& g2, int num_cu, hipStream_t s,
                                   hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_gemm_mxfp8(bool fc1, bool w4, const MxGemmArgs& g, int num_cu, hipStream_t s,
@@ -179,6 +179,41 @@ static moe_status scratch_of_current_device(void** out)
     return MOE_OK;
 }
 
+// Side stream of the bf16 forward above a 1024-token capacity, where a GEMM
+// stage is a 256-row launch and a 64-row launch over disjoint experts: the
+// 64-row FC1 -> FC2 chain runs on the side stream while the 256-row chain runs
+// on the caller's, so the 64-row tiles fill the CUs the 256-row launch frees at
+// its tail.  One non-blocking stream (default priority) and a fork and a join
+// event per GPU, created by moe_load_weights (a set-up call, outside any graph
+// capture) and kept until the process ends.  g_side_mu serializes the
+// record / wait pairs of concurrent forwards, so each fork and join pairs with
+// its own forward's launches.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+static SideStream g_side[kMaxScratchDevices];
+static std::mutex g_side_mu;
+
+static moe_status ensure_side_stream(int dev)
+{
+    if (dev < 0 || dev >= kMaxScratchDevices) return MOE_OK;   // forwards there stay on one stream
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream& ss = g_side[dev];
+    if (ss.s) return MOE_OK;
+    hipError_t e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming);
+    if (e != hipSuccess) {
+        if (ss.join) (void)hipEventDestroy(ss.join);
+        if (ss.fork) (void)hipEventDestroy(ss.fork);
+        if (ss.s) (void)hipStreamDestroy(ss.s);
+        ss = SideStream();
+        return hip_fail(e, "moe_load_weights: side stream");
+    }
+    return MOE_OK;
+}
+
 extern "C" {
 
 const char* moe_last_error(void) { return g_err.c_str(); }
@@ -238,6 +273,7 @@ moe_status moe_load_weights(moe_handle h, const void* w1, const void* w2, void* 
                     moe_weight_bytes(h));
     moe_status st = ensure_device(h);
     if (st != MOE_OK) return st;
+    if (h->precision == MOE_BF16 && (st = ensure_side_stream(h->device)) != MOE_OK) return st;
     const uint16_t* a = (const uint16_t*)w1;
     const uint16_t* b = (const uint16_t*)w2;
     uint8_t* kb = (uint8_t*)kbuf;
@@ -349,10 +385,6 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
         g1.ready = (int32_t*)(w + L.ready);
         g1.err = &hdr->err;
         if (fused) g1.small_takes_big = 1;
-        if (!fused) {
-            e = launch_gemm_bf16(true, g1, h->num_cu, stream, stage_event(h, 2), stage_event(h, 3));
-            if (e != hipSuccess) return hip_fail(e, "moe_forward: FC1 launch");
-        }
         GemmArgs g2 = g1;
         g2.A = (const uint16_t*)(w + L.hbuf);
         g2.W = (const uint16_t*)h->kbuf + (size_t)E * 2 * F * H;
@@ -382,8 +414,52 @@ moe_status moe_forward_ex(moe_handle h, const void* x, const int32_t* expert_ids
             e = launch_gemm_bf16_fused(g1, g2, h->num_cu, stream, stage_event(h, 2), stage_event(h, 3));
             if (e != hipSuccess) return hip_fail(e, "moe_forward: fused FFN launch");
         } else {
-            e = launch_gemm_bf16(false, g2, h->num_cu, stream, nullptr, nullptr);
-            if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
+            const bool split1 = !g1.small_takes_big, split2 = !g2.small_takes_big;
+            const SideStream* ss = (h->device >= 0 && h->device < kMaxScratchDevices)
+                                       ? &g_side[h->device] : nullptr;
+            // with stage events on (profiling) the stages stay serial, so that
+            // the FC1 events bracket the whole stage.  The fork and join only
+            // pay when the 64-row launches have tiles: forked while the
+            // capacity's mean rows per expert, T_cap k / E, is under four
+            // 128-row thresholds (bf16 at 4,096 tokens, 128 experts, top-8:
+            // 748 -> 721-728 us/step); above it, as at 16,384 tokens, the
+            // 64-row launches rarely find a tile and the stages stay serial
+            const bool few_small = (int64_t)T_cap * h->k >= (int64_t)4 * kBigMin * E;
+            if ((split1 || split2) && ss && ss->s && !h->record_stages && !few_small) {
+                // the 256-row chain on `stream`, the 64-row chain on the side
+                // stream: the two launches of a stage cover disjoint experts,
+                // and FC2's tiles of a design read only the rows its own
+                // design's FC1 tiles wrote; a stage of one launch (the 64-row
+                // kernel taking every tile) waits for both chains
+                std::lock_guard<std::mutex> lock(g_side_mu);
+                auto fork = [&]() {
+                    hipError_t r = hipEventRecord(ss->fork, stream);
+                    return r == hipSuccess ? hipStreamWaitEvent(ss->s, ss->fork, 0) : r;
+                };
+                auto join = [&]() {
+                    hipError_t r = hipEventRecord(ss->join, ss->s);
+                    return r == hipSuccess ? hipStreamWaitEvent(stream, ss->join, 0) : r;
+                };
+                if (split1) {
+                    if ((e = fork()) != hipSuccess) return hip_fail(e, "moe_forward: fork");
+                    e = launch_gemm_bf16(true, g1, h->num_cu, stream, nullptr, nullptr, ss->s);
+                    if (e != hipSuccess) return hip_fail(e, "moe_forward: FC1 launch");
+                    if (!split2 && (e = join()) != hipSuccess) return hip_fail(e, "moe_forward: join");
+                } else {
+                    e = launch_gemm_bf16(true, g1, h->num_cu, stream, nullptr, nullptr);
+                    if (e != hipSuccess) return hip_fail(e, "moe_forward: FC1 launch");
+                    if (split2 && (e = fork()) != hipSuccess) return hip_fail(e, "moe_forward: fork");
+                }
+                e = launch_gemm_bf16(false, g2, h->num_cu, stream, nullptr, nullptr,
+                                     split2 ? ss->s : nullptr);
+                if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
+                if (split2 && (e = join()) != hipSuccess) return hip_fail(e, "moe_forward: join");
+            } else {
+                e = launch_gemm_bf16(true, g1, h->num_cu, stream, stage_event(h, 2), stage_event(h, 3));
+                if (e != hipSuccess) return hip_fail(e, "moe_forward: FC1 launch");
+                e = launch_gemm_bf16(false, g2, h->num_cu, stream, nullptr, nullptr);
+                if (e != hipSuccess) return hip_fail(e, "moe_forward: FC2 launch");
+            }
         }
         if ((e = mark(h, 4, stream)) != hipSuccess) return hip_fail(e, "moe_forward: stage event");
     } else {
