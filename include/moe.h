@@ -34,7 +34,12 @@
  *   - The library never allocates device memory and never synchronizes the
  *     stream, except moe_check (which reads the error word) and
  *     moe_get_indices (which copies to host).  moe_route and moe_forward only
- *     enqueue kernels on `stream`, so they can be captured in a HIP graph.
+ *     enqueue work on `stream`, so they can be captured in a HIP graph; a bf16
+ *     forward above 1024 tokens may run its 64-row GEMM launches on a side
+ *     stream of the library (one per GPU, default priority, created by the
+ *     first bf16 moe_load_weights there and kept until the process ends),
+ *     forked from `stream` and joined back to it with events, so the work
+ *     still completes in `stream` order and is captured with it.
  *   - The live token count is read from device memory (live_rows_dev, int32,
  *     in TOKENS).  It is clamped to [0, T_cap]; a value outside sets an error
  *     bit (see moe_check).  Token rows >= live are never read and rows >= live
