@@ -400,7 +400,7 @@ def run_workload(name: str, a, cpu_seconds: float, threads1: bool) -> dict:
 def main():
     a = _args()
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
               f"(--gpus {a.gpus} requested)", file=sys.stderr)
         sys.exit(2)
     if a.copy_calibration:
